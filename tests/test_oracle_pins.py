@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each check below ties the oracle to something it does not compute itself:
+bit patterns and closed forms, an exact brute-force rounding, torch's
+independent float->bf16 cast, numpy's float64 matmul, hand-computed cases,
+and the interleave invariant of the pages' Kernel-2 (gist.science technical
+summary, Method, Kernel-2).  ``test_planted_mistakes_are_caught`` rebuilds
+the oracle with a mistake planted (a flipped sign, a dropped term, swapped
+operands, a transposed operand, truncation instead of rounding, a swapped
+interleave) and shows that every such build fails at least one check.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as oracle_pkg
+from gated_mlp_gemm_amd import inputs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+getcontext().prec = 80
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_pkg.load()
+
+
+# ---------------------------------------------------------------------------
+# Independent exact helpers (brute force; no code shared with the oracle)
+# ---------------------------------------------------------------------------
+_POS_BITS = np.arange(0x0000, 0x7F80, dtype=np.uint32)          # +0 .. max finite
+_POS_VALS = (_POS_BITS << 16).view(np.float32).astype(np.float64)  # increasing
+
+
+def brute_bf16(x) -> int:
+    """Nearest bf16 to an exact value x (Fraction/Decimal/int), ties to even.
+
+    Searches the table of all finite non-negative bf16 values; distances are
+    compared exactly with Fractions.  Overflow follows IEEE: a value at or
+    beyond max + half a spacing becomes infinity.
+    """
+    neg = x < 0
+    a = Fraction(abs(x)) if not isinstance(x, Decimal) else Fraction(abs(x))
+    sign = 0x8000 if neg else 0
+    if a == 0:
+        return sign
+    lo = int(np.searchsorted(_POS_VALS, float(a), side="right")) - 1
+    # float(a) may be off by rounding: fix the bracket exactly
+    while lo > 0 and Fraction(float(_POS_VALS[lo])) > a:
+        lo -= 1
+    while lo + 1 < _POS_VALS.size and Fraction(float(_POS_VALS[lo + 1])) <= a:
+        lo += 1
+    vlo = Fraction(float(_POS_VALS[lo]))
+    if lo + 1 < _POS_VALS.size:
+        vhi = Fraction(float(_POS_VALS[lo + 1]))
+    else:  # beyond the largest finite value: next step would be 2^128
+        vhi = Fraction(2) ** 128
+    dlo, dhi = a - vlo, vhi - a
+    if dlo < dhi:
+        p = lo
+    elif dhi < dlo:
+        p = lo + 1
+    else:
+        p = lo if lo % 2 == 0 else lo + 1
+    if p >= _POS_VALS.size:
+        return sign | 0x7F80
+    return sign | int(_POS_BITS[p])
+
+
+def exact_silu_dec(x: Fraction) -> Decimal:
+    d = Decimal(x.numerator) / Decimal(x.denominator)
+    return d / (1 + (-d).exp())
+
+
+def parse_rational(s: str):
+    """'157/8', '-65*2^-106', '0', '-0' -> (Fraction, negative_zero)."""
+    s = s.strip()
+    if s in ("0", "+0"):
+        return Fraction(0), False
+    if s == "-0":
+        return Fraction(0), True
+    if "*2^" in s:
+        mant, ex = s.split("*2^")
+        return Fraction(int(mant)) * Fraction(2) ** int(ex), False
+    return Fraction(s), False
+
+
+def to_bits(values) -> np.ndarray:
+    """Exact-bf16 numbers -> uint16 patterns (asserts exactness)."""
+    arr = np.asarray(values, dtype=np.float32)
+    b = (arr.view(np.uint32) >> 16).astype(np.uint16)
+    back = (b.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(back, arr), "hand-case input is not an exact bf16 value"
+    return b
+
+
+def bits_to_f64(b) -> np.ndarray:
+    return oracle_pkg.bf16_bits_to_f64(b)
+
+
+# ---------------------------------------------------------------------------
+# The checks (each takes an oracle build so the mutants can be run through them)
+# ---------------------------------------------------------------------------
+def check_rounding_patterns(orc):
+    cases = [
+        (1.0, 0x3F80),
+        (-2.0, 0xC000),
+        (1.0 + 2.0 ** -8, 0x3F80),                  # tie -> even (down)
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),              # tie -> even (up)
+        (1.0 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),     # just above the tie
+        (2.0 - 2.0 ** -8, 0x4000),                  # tie, carry into exponent
+        (1.9921875, 0x3FFF),
+        (0.0, 0x0000),
+        (-0.0, 0x8000),
+        (math.inf, 0x7F80),
+        (-math.inf, 0xFF80),
+        (2.0 ** -126, 0x0080),                      # smallest normal
+        (2.0 ** -133, 0x0001),                      # smallest subnormal
+        (2.0 ** -134, 0x0000),                      # tie between 0 and 2^-133
+        (1.5 * 2.0 ** -134, 0x0001),
+        (2.0 ** -126 - 2.0 ** -134, 0x0080),        # 127.5 quanta -> 128 (even)
+        (255.0 * 2.0 ** 120, 0x7F7F),               # largest finite bf16
+        (255.0 * 2.0 ** 120 + 2.0 ** 119, 0x7F80),  # tie at the top -> inf
+        (255.0 * 2.0 ** 120 + 0.99 * 2.0 ** 119, 0x7F7F),
+        (19.640275800758168, 0x419D),
+        (-1e-45, 0x8000),
+    ]
+    for x, want in cases:
+        got = orc.double_to_bf16(x)
+        assert got == want, f"bf16({x!r}) = {got:#06x}, want {want:#06x}"
+    nan = orc.double_to_bf16(math.nan)
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x007F) != 0
+
+
+def check_rounding_vs_torch(orc):
+    rng = np.random.default_rng(1234)
+    raw = rng.integers(0, 2 ** 32, size=4000, dtype=np.uint64).astype(np.uint32)
+    f32 = raw.view(np.float32)
+    f32 = f32[np.isfinite(f32)]
+    want = inputs.bits(torch.from_numpy(f32.copy()).to(torch.bfloat16))
+    got = np.array([orc.double_to_bf16(float(v)) for v in f32], dtype=np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} differ from torch, e.g. {f32[bad[:3]]}"
+
+
+def check_rounding_vs_brute_force(orc):
+    rng = np.random.default_rng(99)
+    mant = rng.random(600) + 1.0
+    expo = rng.integers(-140, 130, size=600)
+    sign = np.where(rng.random(600) < 0.5, -1.0, 1.0)
+    xs = sign * np.ldexp(mant, expo)
+    for x in xs:
+        want = brute_bf16(Fraction(float(x)))
+        got = orc.double_to_bf16(float(x))
+        assert got == want, f"bf16({x!r}) = {got:#06x}, brute force {want:#06x}"
+
+
+def check_silu_closed_forms(orc):
+    s = orc.silu
+    assert s(0.0) == 0.0 and math.copysign(1.0, s(0.0)) == 1.0
+    assert s(-0.0) == 0.0 and math.copysign(1.0, s(-0.0)) == -1.0
+    assert s(40.0) == 40.0          # e^-40 is below half an ulp of 1
+    assert s(88.0) == 88.0
+    v = s(-1000.0)                  # e^1000 overflows: -1000/inf = -0
+    assert v == 0.0 and not math.isnan(v) and math.copysign(1.0, v) == -1.0
+    assert orc.double_to_bf16(s(-100.0)) == 0x8000
+    # sigma(ln 3) = 3/4  ->  SiLU(ln 3) = 0.75 ln 3
+    assert math.isclose(s(math.log(3.0)), 0.75 * math.log(3.0), rel_tol=1e-15)
+    assert math.isclose(s(1.0), 1.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
+    assert orc.double_to_bf16(s(1.0)) == 0x3F3B          # 0.73046875
+    assert orc.double_to_bf16(s(-1.0)) == 0xBE8A         # -0.26953125
+    # sigma(x) + sigma(-x) = 1  ->  SiLU(x) - SiLU(-x) = x
+    for x in np.linspace(-30.0, 30.0, 241):
+        assert math.isclose(s(x) - s(-x), x, rel_tol=1e-14, abs_tol=1e-14)
+    # the global minimum: at x* = -(1 + W(1/e)) the value is x* + 1 = -W(1/e)
+    from scipy.special import lambertw
+    w = float(lambertw(math.exp(-1.0)).real)
+    assert math.isclose(s(-(1.0 + w)), -w, rel_tol=1e-14)
+    grid = np.linspace(-6.0, 2.0, 4001)
+    assert min(s(x) for x in grid) >= -w - 1e-15
+    # SiLU(x) -> x for large x, -> 0 for very negative x
+    assert math.isclose(s(20.0), 20.0, rel_tol=1e-8)
+    assert abs(s(-50.0)) < 1e-19
+
+
+def _hand_cases():
+    with open(os.path.join(HERE, "golden", "hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def check_hand_cases(orc):
+    for case in _hand_cases():
+        A = to_bits(case["A"])
+        W1 = to_bits(case["W1"])
+        W2 = to_bits(case["W2"])
+        M, K = A.shape
+        N = W1.shape[1]
+        # independent brute force: exact dot products, 80-digit SiLU
+        for m in range(M):
+            for n in range(N):
+                g = sum(Fraction(case["A"][m][k]) * Fraction(case["W1"][k][n]) for k in range(K))
+                u = sum(Fraction(case["A"][m][k]) * Fraction(case["W2"][k][n]) for k in range(K))
+                assert g == Fraction(case["gate"][m][n]) and u == Fraction(case["up"][m][n])
+                want_val, want_negzero = parse_rational(case["y_bf16"][m][n])
+                y = exact_silu_dec(g) * (Decimal(u.numerator) / Decimal(u.denominator))
+                bb = brute_bf16(y)
+                if want_negzero:
+                    assert bb == 0x8000, case["name"]
+                else:
+                    assert Fraction(float(bits_to_f64(np.uint16(bb)))) == want_val, case["name"]
+        # the oracle, both formulations, and the pack
+        want = np.empty((M, N), dtype=np.uint16)
+        for m in range(M):
+            for n in range(N):
+                v, negzero = parse_rational(case["y_bf16"][m][n])
+                want[m, n] = 0x8000 if negzero else brute_bf16(v)
+        y = orc.swiglu(A, W1, W2)
+        assert np.array_equal(y, want), (case["name"], y, want)
+        Wf = to_bits(case["W_fused"])
+        assert np.array_equal(orc.pack(W1, W2), Wf), case["name"]
+        assert np.array_equal(orc.swiglu_interleaved(A, Wf), want), case["name"]
+        y_appr = np.asarray(case["y_approx"], dtype=np.float64)
+        _, y64 = orc.swiglu(A, W1, W2, want_f64=True)
+        assert np.allclose(y64, y_appr, rtol=1e-15, atol=0.0), case["name"]
+
+
+def _random_case(seed, max_dim=17):
+    rng = np.random.default_rng(seed)
+    M, K, N = (int(v) for v in rng.integers(1, max_dim + 1, size=3))
+    scale = float(rng.choice([0.05, 1.0, 8.0]))
+    A = inputs.bits(inputs.random_bf16((M, K), seed * 3 + 1, scale))
+    W1 = inputs.bits(inputs.random_bf16((K, N), seed * 3 + 2, 1.0 / math.sqrt(K)))
+    W2 = inputs.bits(inputs.random_bf16((K, N), seed * 3 + 3, 1.0 / math.sqrt(K)))
+    return A, W1, W2
+
+
+def check_matmul_vs_numpy(orc):
+    for seed in range(24):
+        A, W1, _ = _random_case(seed)
+        a, w = bits_to_f64(A), bits_to_f64(W1)
+        D = orc.matmul(A, W1)
+        ref = a @ w
+        bound = 1e-12 * (np.abs(a) @ np.abs(w)) + 1e-300
+        assert np.all(np.abs(D - ref) <= bound), seed
+
+
+def check_pipeline_vs_numpy(orc):
+    for seed in range(24):
+        A, W1, W2 = _random_case(seed)
+        a, w1, w2 = bits_to_f64(A), bits_to_f64(W1), bits_to_f64(W2)
+        G, U = a @ w1, a @ w2
+        want = G / (1.0 + np.exp(-G)) * U
+        y, y64 = orc.swiglu(A, W1, W2, want_f64=True)
+        scale = (np.abs(a) @ np.abs(w1)) * (np.abs(a) @ np.abs(w2)) + 1e-300
+        assert np.all(np.abs(y64 - want) <= 1e-12 * scale), seed
+        # the single rounding of y64, by brute force
+        for (m, n), v in np.ndenumerate(y64):
+            b = brute_bf16(Fraction(float(v))) if v != 0 else (0x8000 if math.copysign(1, v) < 0 else 0)
+            assert y[m, n] == b, (seed, m, n)
+
+
+def check_interleave_invariant(orc):
+    for seed, (M, K, N) in enumerate([(5, 24, 8), (37, 120, 72), (9, 896, 40)]):
+        A = inputs.bits(inputs.random_bf16((M, K), 100 + seed))
+        W1 = inputs.bits(inputs.random_bf16((K, N), 200 + seed, 1 / math.sqrt(K)))
+        W2 = inputs.bits(inputs.random_bf16((K, N), 300 + seed, 1 / math.sqrt(K)))
+        Wf = orc.pack(W1, W2)
+        y_sep, y64_sep = orc.swiglu(A, W1, W2, want_f64=True)
+        y_int, y64_int = orc.swiglu_interleaved(A, Wf, want_f64=True)
+        assert np.array_equal(y_sep, y_int)
+        assert np.array_equal(y64_sep.view(np.uint64), y64_int.view(np.uint64))
+
+
+def check_pack(orc):
+    rng = np.random.default_rng(5)
+    for K, N in [(1, 1), (3, 8), (64, 136)]:
+        W1 = rng.integers(0, 2 ** 16, size=(K, N), dtype=np.uint16)
+        W2 = rng.integers(0, 2 ** 16, size=(K, N), dtype=np.uint16)
+        Wf = orc.pack(W1, W2)
+        assert Wf.shape == (K, 2 * N)
+        assert np.array_equal(Wf[:, 0::2], W1) and np.array_equal(Wf[:, 1::2], W2)
+
+
+CHECKS = [
+    check_rounding_patterns,
+    check_rounding_vs_torch,
+    check_rounding_vs_brute_force,
+    check_silu_closed_forms,
+    check_hand_cases,
+    check_matmul_vs_numpy,
+    check_pipeline_vs_numpy,
+    check_interleave_invariant,
+    check_pack,
+]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
+def test_pin(orc, check):
+    check(orc)
+
+
+# ---------------------------------------------------------------------------
+# Consistency of the oracle's other entry points with the pinned ones
+# ---------------------------------------------------------------------------
+def test_rows_and_points_match_full(orc):
+    A, W1, W2 = (inputs.bits(t) for t in inputs.make_inputs(19, 64, 48, seed=7))
+    y, y64 = orc.swiglu(A, W1, W2, want_f64=True)
+    rows = np.array([18, 0, 7, 7], dtype=np.int64)
+    yr, yr64 = orc.swiglu_rows(A, W1, W2, rows, want_f64=True)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(yr64, y64[rows])
+    rng = np.random.default_rng(0)
+    r = rng.integers(0, 19, 200)
+    c = rng.integers(0, 48, 200)
+    yp, yp64 = orc.swiglu_points(A, W1, W2, r, c, want_f64=True)
+    assert np.array_equal(yp, y[r, c]) and np.array_equal(yp64, y64[r, c])
+
+
+def test_materialised_rounds_intermediates(orc):
+    A, W1, W2 = (inputs.bits(t) for t in inputs.make_inputs(11, 40, 24, seed=8))
+    g, u, y = orc.swiglu_materialised(A, W1, W2)
+    G, U = orc.matmul(A, W1), orc.matmul(A, W2)
+    assert np.array_equal(g, np.vectorize(orc.double_to_bf16, otypes=[np.uint16])(G))
+    assert np.array_equal(u, np.vectorize(orc.double_to_bf16, otypes=[np.uint16])(U))
+    assert np.array_equal(y, orc.silu_mul(g, u))
+    gf, uf = bits_to_f64(g), bits_to_f64(u)
+    want = gf / (1.0 + np.exp(-gf)) * uf
+    assert np.array_equal(y, np.vectorize(orc.double_to_bf16, otypes=[np.uint16])(want))
+
+
+def test_oracle_meets_the_bound_against_fp32_pipeline(orc):
+    """An fp32-accumulate, single-rounding pipeline is within the 1 % bound.
+
+    This is the numerical premise of the parity gate: with bf16 inputs, fp32
+    accumulation and one final rounding, zero elements exceed
+    max(1e-3, 1e-2 |ref|) (the pages report zero mismatches for the fused
+    kernels: abstract; gist.science Core contributions).
+    """
+    A, W1, W2 = inputs.make_inputs(64, 896, 256, seed=0)
+    ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
+    a, w1, w2 = A.float(), W1.float(), W2.float()
+    G = a @ w1
+    U = a @ w2
+    y = (G * torch.sigmoid(G) * U).to(torch.bfloat16)
+    rep = oracle_pkg.parity_report(inputs.bits(y), ref)
+    assert rep["mismatches"] == 0, rep
+    # and the predicate itself: one bf16 ulp at |ref| ~ 1 passes, 2 % fails
+    one = np.array([0x3F80], dtype=np.uint16)
+    assert not oracle_pkg.mismatches(np.array([0x3F81], dtype=np.uint16), one)[0]
+    assert oracle_pkg.mismatches(np.array([0x3F83], dtype=np.uint16), one)[0]
+    assert not oracle_pkg.mismatches(np.array([0x3A80], dtype=np.uint16),   # 9.8e-4
+                                     np.array([0x0000], dtype=np.uint16))[0]
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: every mutant must fail at least one check
+# ---------------------------------------------------------------------------
+MUTANTS = [
+    "PLANT_SILU_SIGN",
+    "PLANT_SKIP_LAST_K",
+    "PLANT_SWAP_GATE_UP",
+    "PLANT_TRANSPOSED_UP",
+    "PLANT_ROUND_TOWARD_ZERO",
+    "PLANT_PACK_UP_EVEN",
+]
+
+
+@pytest.mark.parametrize("macro", MUTANTS)
+def test_planted_mistakes_are_caught(tmp_path, macro):
+    path = oracle_pkg.build(out=str(tmp_path / f"lib_{macro}.so"), defines=[macro])
+    mutant = oracle_pkg.load(path)
+    failed = []
+    for check in CHECKS:
+        try:
+            check(mutant)
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, f"no pin catches {macro}"

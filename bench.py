@@ -1,0 +1,235 @@
+"""Benchmark of the fused SwiGLU GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX]
+                    [--variant auto|i|s] [--no-cpu-baseline]
+
+A step is one pass of the hot path over one batch of synthetic input: the
+fused call Y = SiLU(A.W1) (.) (A.W2) with the M-based dispatch (the weight
+pack is offline and untimed).  The default workload is M=2048, K=1536,
+N=8960 (seed 1).  Inputs are resident in HBM before timing starts; the timed
+steps rotate over R copies of (A, weights, Y) whose total exceeds 512 MB, so
+the 256 MB Infinity Cache cannot hold the working set across steps.
+
+Prints ONE JSON line: TFLOP/s (4 M N K per step), the fraction of the bf16
+dense MFMA peak, the speedup over the unfused ablation (two GEMMs + SiLU-mul
+from the same mainloop, timed the same way), a roofline record for the fused
+kernel and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "fused SwiGLU-GEMM TFLOP/s + % bf16 MFMA peak; speedup vs unfused ablation"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=1)
+    p.add_argument("--variant", default="auto", choices=["auto", "i", "s"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one device copy of known size (for HBM counter scaling)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_mlp_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}|{workload}")
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the fused SwiGLU GEMM is a single-device "
+              "kernel here (a column split of N needs no communication; see the design "
+              "notes); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from gated_mlp_gemm_amd import inputs
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    sw.load_library()
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    M, K, N = w.M, w.K, w.N
+    flops = 4 * M * N * K
+
+    A, W1, W2 = inputs.workload_inputs(w)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    Wf = sw.swiglu_pack_weights(W1d, W2d)
+    torch.cuda.synchronize()
+
+    chosen = {"auto": sw.swiglu_select_variant(M, N, K), "i": sw.SWIGLU_VARIANT_I,
+              "s": sw.SWIGLU_VARIANT_S}[args.variant]
+    vname = "i" if chosen == sw.SWIGLU_VARIANT_I else "s"
+
+    # rotation copies: fused working set (A + weights + Y) times R >= 512 MB
+    ws_bytes = 2 * (M * K + 2 * K * N + M * N)
+    R = max(1, -(-512 * 2 ** 20 // ws_bytes))
+    copies = [(Ad, W1d, W2d, Wf)]
+    for _ in range(R - 1):
+        copies.append((Ad.clone(), W1d.clone(), W2d.clone(), Wf.clone()))
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    abl_ws = [(torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+               torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(R)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def fused_step(s, variant):
+        a, w1, w2, wf = copies[s % R]
+        sw.swiglu_fused_gemm(a, w1, w2, wf, Y=outs[s % R], variant=variant)
+
+    def ablation_step(s):
+        a, w1, w2, _ = copies[s % R]
+        g, u = abl_ws[s % R]
+        sw.swiglu_unfused_ablation(a, w1, w2, gate_ws=g, up_ws=u, Y=outs[s % R])
+
+    def timed(step_fn, steps, warmup):
+        for s in range(warmup):
+            step_fn(s)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for s in range(steps):
+            step_fn(s)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        return t0.elapsed_time(t1) / steps, wall
+
+    # the headline: the dispatched fused call
+    ms, wall = timed(lambda s: fused_step(s, args.variant), args.steps, args.warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] fused {args.variant}->{vname}: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
+          f"(R={R}, wall {wall:.3f}s)", file=sys.stderr, flush=True)
+
+    # the partners: each fused variant and the unfused ablation, same protocol
+    per = {}
+    for v in ("i", "s"):
+        vms, _ = timed(lambda s, v=v: fused_step(s, v), args.steps, args.warmup)
+        per[v] = {"ms": vms, "tflops": flops / (vms * 1e-3) / 1e12}
+    ams, _ = timed(ablation_step, args.steps, args.warmup)
+    per["ablation"] = {"ms": ams, "tflops": flops / (ams * 1e-3) / 1e12}
+    # warm (one copy, cache-resident where it fits) for context
+    wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, W1d, W2d, Wf, Y=outs[0],
+                                                  variant=args.variant),
+                   args.steps, args.warmup)
+    for k, v in per.items():
+        print(f"[bench] {k}: {v['ms'] * 1e3:.1f} us, {v['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        # one plain device copy of known size, for scaling HBM byte counters
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    kernel = "fused_interleaved_kernel" if vname == "i" else "fused_sequential_kernel"
+    workload = f"M={M},K={K},N={N}"
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(tflops, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic_record(kernel, workload),
+        "kernel": kernel,
+        "algorithmic_flops_per_launch": flops,
+        "algorithmic_hbm_bytes_per_launch": ws_bytes,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.load()
+        hA, hW1, hW2 = inputs.bits(A), inputs.bits(W1), inputs.bits(W2)
+        probe = min(M, 32)
+        t = time.perf_counter()
+        orc.swiglu_rows(hA, hW1, hW2, np.arange(probe))
+        per_row = (time.perf_counter() - t) / probe
+        rows = int(min(M, max(probe, args.cpu_seconds / max(per_row, 1e-9))))
+        t = time.perf_counter()
+        orc.swiglu_rows(hA, hW1, hW2, np.arange(rows))
+        dt = time.perf_counter() - t
+        cpu = {
+            "value": round(4 * rows * N * K / dt / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of M={M} (all N={N} columns, K={K}); {dt:.1f} s",
+        }
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"fused SwiGLU GEMM M={M} K={K} N={N} (seed {w.seed}, A~N(0,1), "
+                        f"W~N(0,1/K), bf16)",
+            "M": M, "K": K, "N": N,
+            "variant": f"{args.variant}->{vname}",
+            "rotation_copies": R,
+        },
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "speedup_vs_ablation": round(per["ablation"]["ms"] / ms, 4),
+        "per_variant": {k: {"ms": round(v["ms"], 5), "tflops": round(v["tflops"], 2)}
+                        for k, v in per.items()},
+        "warm_single_copy": {"ms": round(wms, 5),
+                             "tflops": round(flops / (wms * 1e-3) / 1e12, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

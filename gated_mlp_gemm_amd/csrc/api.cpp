@@ -1,0 +1,221 @@
+// C ABI of the fused SwiGLU GEMM library: argument validation, the M-based
+// dispatcher between the two fused variants, and kernel launches.
+//
+// Every argument is checked before the first HIP call, so an invalid call
+// launches nothing (and can be exercised on a machine without a GPU).
+#include "swiglu.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return SWIGLU_OK;
+}
+
+constexpr int64_t kMaxM = 2147483647;     // 2^31 - 1
+constexpr int64_t kMaxK = int64_t(1) << 22;
+constexpr int64_t kMaxN = int64_t(1) << 23;
+constexpr int64_t kDefaultMSwitch = 2048;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0) return fail(SWIGLU_ERR_SHAPE, "negative size M=%lld N=%lld", (long long)M, (long long)N);
+    if (K < 8) return fail(SWIGLU_ERR_SHAPE, "K=%lld must be >= 8", (long long)K);
+    if (K % 8 != 0 || N % 8 != 0)
+        return fail(SWIGLU_ERR_SHAPE, "K=%lld and N=%lld must be multiples of 8", (long long)K, (long long)N);
+    if (M > kMaxM || K > kMaxK || N > kMaxN)
+        return fail(SWIGLU_ERR_SHAPE, "size beyond limits (M<=2^31-1, K<=2^22, N<=2^23)");
+    if (swiglu::max_tiles(M, 2 * N) > 2147483647)
+        return fail(SWIGLU_ERR_SHAPE, "tile grid too large");
+    return SWIGLU_OK;
+}
+
+// Per-device cache: 1 = gfx950, -1 = other architecture, 0 = not yet queried.
+std::mutex g_dev_mutex;
+int g_dev_state[256];
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SWIGLU_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 256) return fail(SWIGLU_ERR_UNSUPPORTED, "device ordinal %d", dev);
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_dev_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(SWIGLU_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    if (g_dev_state[dev] != 1)
+        return fail(SWIGLU_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+    return SWIGLU_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(SWIGLU_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *swiglu_status_string(int status) {
+    switch (status) {
+        case SWIGLU_OK: return "ok";
+        case SWIGLU_ERR_NULL: return "null pointer";
+        case SWIGLU_ERR_SHAPE: return "invalid shape";
+        case SWIGLU_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case SWIGLU_ERR_UNSUPPORTED: return "unsupported variant or device";
+        case SWIGLU_ERR_HIP: return "HIP error";
+        case SWIGLU_ERR_ALIAS: return "output overlaps another operand";
+        default: return "unknown status";
+    }
+}
+
+const char *swiglu_last_error(void) { return g_last_error; }
+
+int64_t swiglu_m_switch(void) {
+    const char *s = std::getenv("SWIGLU_M_SWITCH");
+    if (s != nullptr && *s != '\0') {
+        char *end = nullptr;
+        const long long v = std::strtoll(s, &end, 10);
+        if (end != s && *end == '\0') return v;
+    }
+    return kDefaultMSwitch;
+}
+
+int swiglu_select_variant(int64_t M, int64_t N, int64_t K) {
+    (void)N;
+    (void)K;
+    if (M < 0) return fail(SWIGLU_ERR_SHAPE, "negative M");
+    return M <= swiglu_m_switch() ? SWIGLU_VARIANT_I : SWIGLU_VARIANT_S;
+}
+
+int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2, uint16_t *W_fused, int64_t K,
+                        int64_t N, void *stream) {
+    if (K < 0 || N < 0) return fail(SWIGLU_ERR_SHAPE, "negative size");
+    if (N % 8 != 0) return fail(SWIGLU_ERR_SHAPE, "N=%lld must be a multiple of 8", (long long)N);
+    if (K > kMaxK || N > kMaxN) return fail(SWIGLU_ERR_SHAPE, "size beyond limits");
+    if (K == 0 || N == 0) return ok();
+    if (!W1 || !W2 || !W_fused) return fail(SWIGLU_ERR_NULL, "W1, W2 and W_fused are required");
+    if (!aligned16(W1) || !aligned16(W2) || !aligned16(W_fused))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t wbytes = K * N * 2;
+    if (overlap(W_fused, 2 * wbytes, W1, wbytes) || overlap(W_fused, 2 * wbytes, W2, wbytes))
+        return fail(SWIGLU_ERR_ALIAS, "W_fused overlaps W1 or W2");
+    int st = check_device();
+    if (st != SWIGLU_OK) return st;
+    return launched(swiglu::launch_pack(W1, W2, W_fused, K, N, (hipStream_t)stream), "pack");
+}
+
+int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
+                      const uint16_t *W_fused, uint16_t *Y, int64_t M, int64_t N, int64_t K,
+                      int variant, void *stream) {
+    if (variant != SWIGLU_AUTO && variant != SWIGLU_VARIANT_S && variant != SWIGLU_VARIANT_I)
+        return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
+    int st = check_gemm_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
+    if (!A || !Y) return fail(SWIGLU_ERR_NULL, "A and Y are required");
+    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = K * N * 2;
+    if (v == SWIGLU_VARIANT_I) {
+        if (!W_fused) return fail(SWIGLU_ERR_NULL, "variant I reads W_fused");
+        if (!aligned16(A) || !aligned16(W_fused) || !aligned16(Y))
+            return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+        if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W_fused, 2 * wbytes))
+            return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
+    } else {
+        if (!W1 || !W2) return fail(SWIGLU_ERR_NULL, "variant S reads W1 and W2");
+        if (!aligned16(A) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y))
+            return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+        if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W1, wbytes) ||
+            overlap(Y, ybytes, W2, wbytes))
+            return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
+    }
+    st = check_device();
+    if (st != SWIGLU_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    if (v == SWIGLU_VARIANT_I)
+        return launched(swiglu::launch_fused_interleaved(A, W_fused, Y, (int)M, (int)N, (int)K, s),
+                        "fused interleaved");
+    return launched(swiglu::launch_fused_sequential(A, W1, W2, Y, (int)M, (int)N, (int)K, s),
+                    "fused sequential");
+}
+
+int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
+                            uint16_t *gate_ws, uint16_t *up_ws, uint16_t *Y, int64_t M,
+                            int64_t N, int64_t K, void *stream) {
+    int st = check_gemm_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!A || !W1 || !W2 || !gate_ws || !up_ws || !Y)
+        return fail(SWIGLU_ERR_NULL, "A, W1, W2, gate_ws, up_ws and Y are required");
+    if (!aligned16(A) || !aligned16(W1) || !aligned16(W2) || !aligned16(gate_ws) ||
+        !aligned16(up_ws) || !aligned16(Y))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = K * N * 2;
+    const void *outs[3] = {gate_ws, up_ws, Y};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], ybytes, A, abytes) || overlap(outs[i], ybytes, W1, wbytes) ||
+            overlap(outs[i], ybytes, W2, wbytes))
+            return fail(SWIGLU_ERR_ALIAS, "an output overlaps an input");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], ybytes, outs[j], ybytes))
+                return fail(SWIGLU_ERR_ALIAS, "outputs overlap each other");
+    }
+    st = check_device();
+    if (st != SWIGLU_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = swiglu::launch_gemm_store(A, W1, gate_ws, (int)M, (int)N, (int)K, s);
+    if (e != hipSuccess) return launched(e, "ablation gate GEMM");
+    e = swiglu::launch_gemm_store(A, W2, up_ws, (int)M, (int)N, (int)K, s);
+    if (e != hipSuccess) return launched(e, "ablation up GEMM");
+    return launched(swiglu::launch_silu_mul(gate_ws, up_ws, Y, M * N, s), "ablation silu_mul");
+}
+
+int swiglu_silu_mul(const uint16_t *gate, const uint16_t *up, uint16_t *Y, int64_t count,
+                    void *stream) {
+    if (count < 0 || count % 8 != 0)
+        return fail(SWIGLU_ERR_SHAPE, "count=%lld must be a non-negative multiple of 8", (long long)count);
+    if (count == 0) return ok();
+    if (!gate || !up || !Y) return fail(SWIGLU_ERR_NULL, "gate, up and Y are required");
+    if (!aligned16(gate) || !aligned16(up) || !aligned16(Y))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    if (overlap(Y, 2 * count, gate, 2 * count) || overlap(Y, 2 * count, up, 2 * count))
+        return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
+    int st = check_device();
+    if (st != SWIGLU_OK) return st;
+    return launched(swiglu::launch_silu_mul(gate, up, Y, count, (hipStream_t)stream), "silu_mul");
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device primitives for gfx950 (CDNA4): MFMA wrappers, LDS access helpers,
+// the SiLU activation and bf16 conversion.
+//
+// Lane layouts used throughout (wave64), as exercised by the parity tests:
+//   v_mfma_f32_32x32x16_bf16, operands A (32 x 16) and B (16 x 32):
+//     lane l holds A[l % 32][8*(l/32) + j] and B[8*(l/32) + j][l % 32], j < 8;
+//     accumulator register i of lane l is D[8*(i/4) + 4*(l/32) + i%4][l % 32].
+//   ds_read_b64_tr_b16: within each group of 16 lanes, element j of lane i is
+//     element (i % 4) of the 8-byte chunk addressed by lane 4*j + i/4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swiglu {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SWIGLU_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b,
+                                                const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte LDS read (ds_read_b128).
+__device__ __forceinline__ u32x4 lds_read16(const SWIGLU_LDS char *p) {
+    return *reinterpret_cast<const SWIGLU_LDS u32x4 *>(p);
+}
+
+// 16-byte LDS write (ds_write_b128).
+__device__ __forceinline__ void lds_write16(SWIGLU_LDS char *p, const u32x4 &v) {
+    *reinterpret_cast<SWIGLU_LDS u32x4 *>(p) = v;
+}
+
+// 8-byte transposing LDS read (ds_read_b64_tr_b16), see the layout note above.
+__device__ __forceinline__ u32x2 lds_read_tr8(const SWIGLU_LDS char *p) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<SWIGLU_LDS i16x4 *>(const_cast<SWIGLU_LDS char *>(p)));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// 16-byte global load / store (global_load_dwordx4 / global_store_dwordx4).
+__device__ __forceinline__ u32x4 gload16(const uint16_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void gstore16(uint16_t *p, const u32x4 &v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// Value of lane (l ^ 1) (DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ float swap_adjacent_lanes(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+
+// SiLU(x) = x / (1 + e^{-x}) = x * rcp(1 + 2^{-x log2 e}) with the hardware
+// exp2 and reciprocal (about 1 ulp each in fp32).  Very negative x: the exp2
+// overflows to +inf, the reciprocal is 0 and the result is -0; large x:
+// exp2 -> 0 and the result is x.
+__device__ __forceinline__ float silu(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Two floats -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed
+// low = a, high = b.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+    return static_cast<uint16_t>(pack_bf16x2(a, 0.0f) & 0xFFFFu);
+}
+
+}  // namespace swiglu

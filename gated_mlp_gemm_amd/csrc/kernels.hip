@@ -1,0 +1,338 @@
+// HIP kernels of the fused SwiGLU GEMM library (gfx950 only).
+//
+// Citations are to the pages on "Tile-Level Activation Overlap for Efficient
+// LLM Inference" (arXiv 2607.02521): [paper s1] = the paper's own text,
+// section 1 Introduction; [abstract] = its abstract; [gist: X] = the
+// gist.science technical summary, section X.
+#include "launch.hpp"
+
+#include "device.hpp"
+#include "gemm_core.hpp"
+
+namespace swiglu {
+
+// ---------------------------------------------------------------------------
+// Weight packer [gist: Method, Kernel-2]: W_fused[k][2n] = W1[k][n],
+// W_fused[k][2n+1] = W2[k][n].  Each thread takes 8 columns of one row:
+// two 16-byte loads, two 16-byte stores; a pure 16-bit permutation.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ W1,
+                                                   const uint16_t *__restrict__ W2,
+                                                   uint16_t *__restrict__ Wf, int64_t K,
+                                                   int64_t N) {
+    const int64_t chunks_per_row = N / 8;
+    const int64_t total = K * chunks_per_row;
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k = c / chunks_per_row;
+        const int64_t j = c - k * chunks_per_row;
+        const u32x4 g = gload16(W1 + k * N + j * 8);   // Gate columns 8j .. 8j+7
+        const u32x4 u = gload16(W2 + k * N + j * 8);   // Up   columns 8j .. 8j+7
+        u32x4 lo, hi;
+        // dword d of a row chunk holds columns (2d, 2d+1) as (low, high) halves
+        lo.x = (g.x & 0xFFFFu) | (u.x << 16);
+        lo.y = (g.x >> 16) | (u.x & 0xFFFF0000u);
+        lo.z = (g.y & 0xFFFFu) | (u.y << 16);
+        lo.w = (g.y >> 16) | (u.y & 0xFFFF0000u);
+        hi.x = (g.z & 0xFFFFu) | (u.z << 16);
+        hi.y = (g.z >> 16) | (u.z & 0xFFFF0000u);
+        hi.z = (g.w & 0xFFFFu) | (u.w << 16);
+        hi.w = (g.w >> 16) | (u.w & 0xFFFF0000u);
+        uint16_t *dst = Wf + k * 2 * N + j * 16;
+        gstore16(dst, lo);
+        gstore16(dst + 8, hi);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Ablation activation stage: Y = bf16(SiLU(gate) * up), fp32 arithmetic,
+// one rounding.  HBM-bound: 8 elements (three 16-byte accesses) per thread
+// per iteration, grid-stride.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) {
+    return __builtin_bit_cast(float, v & 0xFFFF0000u);
+}
+
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t *__restrict__ g,
+                                                       const uint16_t *__restrict__ u,
+                                                       uint16_t *__restrict__ y,
+                                                       int64_t nchunks) {
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const u32x4 gv = gload16(g + c * 8);
+        const u32x4 uv = gload16(u + c * 8);
+        u32x4 out;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            out[d] = pack_bf16x2(silu(bf16_lo(gv[d])) * bf16_lo(uv[d]),
+                                 silu(bf16_hi(gv[d])) * bf16_hi(uv[d]));
+        }
+        gstore16(y + c * 8, out);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Accumulator geometry: row of register i of 32x32 block (tm) for this lane.
+// ---------------------------------------------------------------------------
+template <class S>
+__device__ __forceinline__ int acc_row(int wm, int tm, int i, int lane) {
+    return wm * S::kWaveM + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Variant I [gist: Method, Kernel-2]: one GEMM D = A . W_fused over a tile of
+// the [M, 2N] grid; the epilogue pairs adjacent accumulator columns
+// (D[m,2n], D[m,2n+1]) and stores SiLU(D[m,2n]) * D[m,2n+1].
+//
+// In the 32x32 MFMA accumulator layout every lane holds one column, so the
+// Gate column 2n sits in an even lane and its Up partner 2n+1 in the next
+// lane, at the same register indices.  The pair splits the work: the even lane
+// finishes registers 0..7 (it receives the partner's Up values), the odd lane
+// registers 8..15 (it receives Gate values); one DPP lane swap per output.
+// ---------------------------------------------------------------------------
+template <class S>
+__global__ __launch_bounds__(S::kThreads, 1) void fused_interleaved_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, uint16_t *__restrict__ Y,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+    SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
+
+    int tm_, tn_;
+    tile_coords(tiles_m, tiles_n, 8, tm_, tn_);
+    const int m0 = tm_ * S::BM;
+    const int n0 = tn_ * S::BN;            // first W_fused column of the tile
+    const int rows_valid = min(S::BM, M - m0);
+    const int ldb = 2 * N;
+
+    Mainloop<S> ml;
+    ml.init_a(A + (int64_t)m0 * K, K, rows_valid, K);
+    ml.init_b_offsets(ldb);
+    f32x16 acc[S::TM][S::TN];
+    zero_acc<S>(acc);
+    gemm_tile<S>(lds, ml, Wf + n0, ldb, n0, ldb, K, acc);
+
+    // PairMul epilogue
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    const bool odd = lane & 1;
+    const int y0 = n0 / 2;                 // first Y column of the tile
+    const int ycols_valid = min(S::BN / 2, N - y0);
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm) {
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn) {
+            const int ycol = (wn * S::kWaveN + tn * 32 + (lane & 31)) >> 1;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const float send = odd ? acc[tm][tn][p] : acc[tm][tn][8 + p];
+                const float recv = swap_adjacent_lanes(send);
+                const float gate = odd ? recv : acc[tm][tn][p];
+                const float up = odd ? acc[tm][tn][8 + p] : recv;
+                const int row = acc_row<S>(wm, tm, odd ? 8 + p : p, lane);
+                if (row < rows_valid && ycol < ycols_valid)
+                    Y[(int64_t)(m0 + row) * N + y0 + ycol] = to_bf16(silu(gate) * up);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Variant S [abstract; gist: Method, Kernel-1]: per output tile, the Gate
+// contraction, then SiLU on the register-resident Gate accumulator while the
+// loads of the next Up tiles are in flight, then the Up contraction and the
+// multiply-and-store epilogue.  The prefetch runs straight across the Gate->Up
+// boundary: the last Gate step already stages Up tile 0, and Up tile 1 is
+// requested before the SiLU pass starts, so SiLU overlaps those loads (and the
+// scheduler may interleave it with the first Up MFMAs, which use other
+// registers).
+// ---------------------------------------------------------------------------
+template <class S>
+__global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ W1,
+    const uint16_t *__restrict__ W2, uint16_t *__restrict__ Y, int M, int N, int K,
+    int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+    SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
+
+    int tm_, tn_;
+    tile_coords(tiles_m, tiles_n, 8, tm_, tn_);
+    const int m0 = tm_ * S::BM;
+    const int n0 = tn_ * S::BN;
+    const int rows_valid = min(S::BM, M - m0);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    const int nk = (K + S::BK - 1) / S::BK;
+
+    Mainloop<S> ml;
+    ml.init_a(A + (int64_t)m0 * K, K, rows_valid, K);
+    ml.init_b_offsets(N);
+    f32x16 g[S::TM][S::TN], u[S::TM][S::TN];
+    zero_acc<S>(g);
+    zero_acc<S>(u);
+
+    // Gate loop (its last step stages Up tile 0)
+    ml.load(0, W1 + n0, N, n0, N);
+    ml.store(lds);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk)
+            ml.load(kt + 1, W1 + n0, N, n0, N);
+        else
+            ml.load(0, W2 + n0, N, n0, N);
+        mma_stage<S>(lds + (kt & 1) * S::kStageBytes, g, wm, wn, lane);
+        ml.store(lds + ((kt + 1) & 1) * S::kStageBytes);
+        __syncthreads();
+    }
+
+    // SiLU window: Up tile 1 is requested first, then Gate is activated in
+    // registers while those loads fly.
+    if (nk > 1) ml.load(1, W2 + n0, N, n0, N);
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) g[tm][tn][i] = silu(g[tm][tn][i]);
+
+    // Up loop
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        if (kt > 0 && more) ml.load(kt + 1, W2 + n0, N, n0, N);
+        mma_stage<S>(lds + ((nk + kt) & 1) * S::kStageBytes, u, wm, wn, lane);
+        if (more) ml.store(lds + ((nk + kt + 1) & 1) * S::kStageBytes);
+        __syncthreads();
+    }
+
+    // multiply and store
+    const int cols_valid = min(S::BN, N - n0);
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm) {
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn) {
+            const int col = wn * S::kWaveN + tn * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = acc_row<S>(wm, tm, i, lane);
+                if (row < rows_valid && col < cols_valid)
+                    Y[(int64_t)(m0 + row) * N + n0 + col] = to_bf16(g[tm][tn][i] * u[tm][tn][i]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Ablation GEMM: C = bf16(A . B), the same mainloop with a plain store, so
+// that Gate and Up are materialised as an eager pipeline does [paper s1].
+// ---------------------------------------------------------------------------
+template <class S>
+__global__ __launch_bounds__(S::kThreads, 1) void gemm_store_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+    SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
+
+    int tm_, tn_;
+    tile_coords(tiles_m, tiles_n, 8, tm_, tn_);
+    const int m0 = tm_ * S::BM;
+    const int n0 = tn_ * S::BN;
+    const int rows_valid = min(S::BM, M - m0);
+
+    Mainloop<S> ml;
+    ml.init_a(A + (int64_t)m0 * K, K, rows_valid, K);
+    ml.init_b_offsets(N);
+    f32x16 acc[S::TM][S::TN];
+    zero_acc<S>(acc);
+    gemm_tile<S>(lds, ml, B + n0, N, n0, N, K, acc);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    const int cols_valid = min(S::BN, N - n0);
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm) {
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn) {
+            const int col = wn * S::kWaveN + tn * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = acc_row<S>(wm, tm, i, lane);
+                if (row < rows_valid && col < cols_valid)
+                    C[(int64_t)(m0 + row) * N + n0 + col] = to_bf16(acc[tm][tn][i]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tile shapes and launchers
+// ---------------------------------------------------------------------------
+using ShapeWide = TileShape<256, 256, 64, 2, 2, 2>;    // I and ablation GEMM
+using ShapeSeq = TileShape<256, 128, 64, 2, 2, 2>;     // S: two 256x128 accumulators
+using ShapeSmall = TileShape<128, 64, 64, 2, 2, 2>;    // M <= 128: more tiles on the weights
+
+static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+template <class S, class Kern, class... Args>
+static hipError_t launch_tiles(Kern kernel, int M, int cols, hipStream_t stream, Args... args) {
+    const int tiles_m = cdiv(M, S::BM);
+    const int tiles_n = cdiv(cols, S::BN);
+    hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n), dim3(S::kThreads), 0, stream, args...,
+                       tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,
+                       int64_t N, hipStream_t stream) {
+    const int64_t total = K * (N / 8);
+    const int64_t blocks = (total + 255) / 256;
+    const int grid = static_cast<int>(blocks < 65536 ? blocks : 65536);
+    hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, stream, W1, W2, Wf, K, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,
+                           hipStream_t stream) {
+    const int64_t chunks = count / 8;
+    const int64_t blocks = (chunks + 255) / 256;
+    const int grid = static_cast<int>(blocks < 65536 ? blocks : 65536);
+    hipLaunchKernelGGL(silu_mul_kernel, dim3(grid), dim3(256), 0, stream, g, u, y, chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
+                                    int N, int K, hipStream_t stream) {
+    if (M <= 128)
+        return launch_tiles<ShapeSmall>(fused_interleaved_kernel<ShapeSmall>, M, 2 * N, stream,
+                                        A, Wf, Y, M, N, K);
+    return launch_tiles<ShapeWide>(fused_interleaved_kernel<ShapeWide>, M, 2 * N, stream, A,
+                                   Wf, Y, M, N, K);
+}
+
+hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
+                                   uint16_t *Y, int M, int N, int K, hipStream_t stream) {
+    if (M <= 128)
+        return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, A,
+                                        W1, W2, Y, M, N, K);
+    return launch_tiles<ShapeSeq>(fused_sequential_kernel<ShapeSeq>, M, N, stream, A, W1, W2,
+                                  Y, M, N, K);
+}
+
+hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N,
+                             int K, hipStream_t stream) {
+    if (M <= 128)
+        return launch_tiles<ShapeSmall>(gemm_store_kernel<ShapeSmall>, M, N, stream, A, B, C, M,
+                                        N, K);
+    return launch_tiles<ShapeWide>(gemm_store_kernel<ShapeWide>, M, N, stream, A, B, C, M, N, K);
+}
+
+int64_t max_tiles(int64_t M, int64_t cols) {
+    // the most workgroups any launcher above creates for an M x cols output
+    const int64_t small = ((M + 127) / 128) * ((cols + 63) / 64);
+    const int64_t wide = ((M + 255) / 256) * ((cols + 127) / 128);
+    return small > wide ? small : wide;
+}
+
+}  // namespace swiglu

@@ -1,0 +1,24 @@
+// Host-side launchers of the kernels in kernels.hip.  Arguments are assumed
+// validated by the C ABI layer (api.cpp); each launcher enqueues on `stream`
+// and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swiglu {
+
+hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,
+                       int64_t N, hipStream_t stream);
+hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,
+                           hipStream_t stream);
+hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
+                                    int N, int K, hipStream_t stream);
+hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
+                                   uint16_t *Y, int M, int N, int K, hipStream_t stream);
+hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N,
+                             int K, hipStream_t stream);
+// Largest workgroup count any launcher uses for an M x cols output tile grid.
+int64_t max_tiles(int64_t M, int64_t cols);
+
+}  // namespace swiglu

@@ -1,0 +1,216 @@
+"""Python binding of the C ABI in ``include/swiglu.h`` (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libswiglu.so``.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is not built, or a call fails,
+an exception is raised.
+
+The functions carry the C names.  Tensors are ``torch.bfloat16``, contiguous,
+on one ROCm device; outputs are allocated with torch when not given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libswiglu.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "swiglu.h")
+
+SWIGLU_OK = 0
+SWIGLU_ERR_NULL = -1
+SWIGLU_ERR_SHAPE = -2
+SWIGLU_ERR_ALIGN = -3
+SWIGLU_ERR_UNSUPPORTED = -4
+SWIGLU_ERR_HIP = -5
+SWIGLU_ERR_ALIAS = -6
+
+SWIGLU_AUTO = 0
+SWIGLU_VARIANT_S = 1
+SWIGLU_VARIANT_I = 2
+VARIANTS = {"auto": SWIGLU_AUTO, "s": SWIGLU_VARIANT_S, "i": SWIGLU_VARIANT_I}
+
+
+class SwigluError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {detail} (status {status})")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load ``libswiglu.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m gated_mlp_gemm_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.swiglu_pack_weights.argtypes = [P, P, P, I64, I64, P]
+    lib.swiglu_fused_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P]
+    lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
+    lib.swiglu_silu_mul.argtypes = [P, P, P, I64, P]
+    lib.swiglu_select_variant.argtypes = [I64, I64, I64]
+    lib.swiglu_m_switch.argtypes = []
+    lib.swiglu_m_switch.restype = I64
+    lib.swiglu_status_string.argtypes = [I32]
+    lib.swiglu_status_string.restype = ctypes.c_char_p
+    lib.swiglu_last_error.argtypes = []
+    lib.swiglu_last_error.restype = ctypes.c_char_p
+    for name in ("swiglu_pack_weights", "swiglu_fused_gemm", "swiglu_unfused_ablation",
+                 "swiglu_silu_mul", "swiglu_select_variant"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER):
+    """Names of the functions ``include/swiglu.h`` declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swiglu_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(status: int, where: str):
+    if status != SWIGLU_OK:
+        lib = load_library()
+        detail = lib.swiglu_last_error().decode() or lib.swiglu_status_string(status).decode()
+        raise SwigluError(status, where, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t: torch.Tensor, name: str, shape) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# C-named entry points
+# ---------------------------------------------------------------------------
+def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor,
+                        W_fused: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W_fused[:, 0::2] = W1, W_fused[:, 1::2] = W2 (on the GPU)."""
+    lib = load_library()
+    K, N = W1.shape
+    _dev_tensor(W1, "W1", (K, N))
+    _dev_tensor(W2, "W2", (K, N))
+    if W_fused is None:
+        W_fused = torch.empty((K, 2 * N), dtype=torch.bfloat16, device=W1.device)
+    _dev_tensor(W_fused, "W_fused", (K, 2 * N))
+    with torch.cuda.device(W1.device):
+        _check(lib.swiglu_pack_weights(_ptr(W1), _ptr(W2), _ptr(W_fused), K, N,
+                                       _stream(W1.device)), "swiglu_pack_weights")
+    return W_fused
+
+
+def swiglu_fused_gemm(A: torch.Tensor, W1: Optional[torch.Tensor] = None,
+                      W2: Optional[torch.Tensor] = None,
+                      W_fused: Optional[torch.Tensor] = None,
+                      Y: Optional[torch.Tensor] = None,
+                      variant="auto") -> torch.Tensor:
+    """Y = bf16(SiLU(A.W1) * (A.W2)); variant 'auto' | 's' | 'i' (or the enum)."""
+    lib = load_library()
+    v = VARIANTS[variant.lower()] if isinstance(variant, str) else int(variant)
+    M, K = A.shape
+    _dev_tensor(A, "A", (M, K))
+    if W_fused is not None:
+        N = W_fused.shape[1] // 2
+        _dev_tensor(W_fused, "W_fused", (K, 2 * N))
+    elif W1 is not None:
+        N = W1.shape[1]
+    else:
+        raise ValueError("need W1/W2 or W_fused")
+    if W1 is not None:
+        _dev_tensor(W1, "W1", (K, N))
+    if W2 is not None:
+        _dev_tensor(W2, "W2", (K, N))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_tensor(Y, "Y", (M, N))
+    with torch.cuda.device(A.device):
+        _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W1), _ptr(W2), _ptr(W_fused), _ptr(Y),
+                                     M, N, K, v, _stream(A.device)), "swiglu_fused_gemm")
+    return Y
+
+
+def swiglu_unfused_ablation(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,
+                            gate_ws: Optional[torch.Tensor] = None,
+                            up_ws: Optional[torch.Tensor] = None,
+                            Y: Optional[torch.Tensor] = None
+                            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Two GEMMs + SiLU-mul; returns (Y, gate_ws, up_ws)."""
+    lib = load_library()
+    M, K = A.shape
+    N = W1.shape[1]
+    _dev_tensor(A, "A", (M, K))
+    _dev_tensor(W1, "W1", (K, N))
+    _dev_tensor(W2, "W2", (K, N))
+    outs = []
+    for name, t in (("gate_ws", gate_ws), ("up_ws", up_ws), ("Y", Y)):
+        if t is None:
+            t = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+        outs.append(_dev_tensor(t, name, (M, N)))
+    gate_ws, up_ws, Y = outs
+    with torch.cuda.device(A.device):
+        _check(lib.swiglu_unfused_ablation(_ptr(A), _ptr(W1), _ptr(W2), _ptr(gate_ws),
+                                           _ptr(up_ws), _ptr(Y), M, N, K,
+                                           _stream(A.device)), "swiglu_unfused_ablation")
+    return Y, gate_ws, up_ws
+
+
+def swiglu_silu_mul(gate: torch.Tensor, up: torch.Tensor,
+                    Y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = load_library()
+    _dev_tensor(gate, "gate", gate.shape)
+    _dev_tensor(up, "up", gate.shape)
+    if Y is None:
+        Y = torch.empty_like(gate)
+    _dev_tensor(Y, "Y", gate.shape)
+    with torch.cuda.device(gate.device):
+        _check(lib.swiglu_silu_mul(_ptr(gate), _ptr(up), _ptr(Y), gate.numel(),
+                                   _stream(gate.device)), "swiglu_silu_mul")
+    return Y
+
+
+def swiglu_select_variant(M: int, N: int = 0, K: int = 0) -> int:
+    v = load_library().swiglu_select_variant(M, N, K)
+    if v < 0:
+        _check(v, "swiglu_select_variant")
+    return v
+
+
+def swiglu_m_switch() -> int:
+    return int(load_library().swiglu_m_switch())
+
+
+def swiglu_status_string(status: int) -> str:
+    return load_library().swiglu_status_string(status).decode()
+
+
+def swiglu_last_error() -> str:
+    return load_library().swiglu_last_error().decode()

@@ -1,0 +1,150 @@
+/*
+ * swiglu.h -- C ABI of the MI355X (gfx950) fused SwiGLU GEMM library.
+ *
+ *   Y = SiLU(A . W1) (.) (A . W2),   SiLU(x) = x / (1 + exp(-x))
+ *
+ * The gated MLP of "Tile-Level Activation Overlap for Efficient LLM
+ * Inference" (arXiv 2607.02521; paper text, section 1 Introduction: Gate =
+ * A x W1, Up = A x W2, Y = SiLU(Gate) (.) Up).  The fused entry point never
+ * writes Gate or Up to device memory: they live in MFMA accumulators
+ * (registers) from the contraction to the bf16 store of Y.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every matrix is bf16, passed as its 16-bit patterns (uint16_t),
+ *    row-major and contiguous: A [M][K], W1 and W2 [K][N],
+ *    W_fused [K][2N], Y / gate_ws / up_ws [M][N].
+ *  - Every matrix pointer is a DEVICE pointer, allocated and owned by the
+ *    caller.  The library allocates, frees and retains nothing: no pointer is
+ *    kept past the call.
+ *  - `stream` is a hipStream_t passed as void*; NULL selects the default
+ *    stream.  Calls only enqueue work and return; results are valid after the
+ *    stream is synchronised.  Errors raised by a kernel while it runs surface
+ *    at the caller's synchronisation, as in HIP.
+ *  - Arguments are validated before any HIP call: an invalid call launches
+ *    nothing and returns a negative swiglu_status.  Preconditions:
+ *      M >= 0, N >= 0, K >= 8;  K % 8 == 0 and N % 8 == 0 (each row is a
+ *      whole number of 16-byte chunks);  M <= 2^31 - 1, K <= 2^22,
+ *      N <= 2^23;
+ *      every pointer 16-byte aligned;  outputs do not overlap inputs or
+ *      each other.
+ *    M == 0 or N == 0 is an empty problem: SWIGLU_OK, nothing launched.
+ *  - Outputs are computed with fp32 accumulation of bf16 products and one
+ *    round-to-nearest-even to bf16 at the end; the accumulation order is not
+ *    specified (results of different variants need not be bitwise equal).
+ *  - Calls are re-entrant; the only global state is a per-device cache of
+ *    the device's architecture and compute-unit count.
+ *  - The code object targets gfx950 only: on another device every launching
+ *    call returns SWIGLU_ERR_UNSUPPORTED.
+ */
+#ifndef SWIGLU_H
+#define SWIGLU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swiglu_status {
+    SWIGLU_OK = 0,
+    SWIGLU_ERR_NULL = -1,        /* a pointer the call needs is NULL            */
+    SWIGLU_ERR_SHAPE = -2,       /* a size violates the preconditions above     */
+    SWIGLU_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned            */
+    SWIGLU_ERR_UNSUPPORTED = -4, /* unknown variant, or the device is not gfx950 */
+    SWIGLU_ERR_HIP = -5,         /* a HIP call or kernel launch failed          */
+    SWIGLU_ERR_ALIAS = -6        /* an output overlaps an input or another output */
+} swiglu_status;
+
+typedef enum swiglu_variant {
+    SWIGLU_AUTO = 0,      /* pick by M (swiglu_select_variant)                  */
+    SWIGLU_VARIANT_S = 1, /* sequential: Gate loop, SiLU, Up loop, multiply      */
+    SWIGLU_VARIANT_I = 2  /* interleaved: one GEMM over W_fused, paired epilogue */
+} swiglu_variant;
+
+/*
+ * Interleave W1 and W2 column by column into W_fused (the fused weight of the
+ * pages' Kernel-2; gist.science technical summary, Method, Kernel-2: even
+ * columns belong to Gate, odd columns to Up):
+ *
+ *     W_fused[k][2n] = W1[k][n],   W_fused[k][2n+1] = W2[k][n]   (0-based)
+ *
+ * W1, W2: [K][N] device, read only.  W_fused: [K][2N] device, written.
+ * A pure copy of 16-bit patterns (bit-exact).  Done once per weight set, off
+ * the timed path.  K >= 0 here (K == 0 is an empty problem).
+ */
+int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2,
+                        uint16_t *W_fused, int64_t K, int64_t N, void *stream);
+
+/*
+ * The fused SwiGLU GEMM, Y = bf16( SiLU(A.W1) * (A.W2) ).
+ *
+ * variant SWIGLU_VARIANT_I (the pages' Kernel-2; gist.science technical
+ *   summary, Method, Kernel-2): one GEMM over W_fused [K][2N]; its epilogue
+ *   pairs accumulator columns 2n (Gate) and 2n+1 (Up) and stores
+ *   SiLU(D[m][2n]) * D[m][2n+1].  Reads A and W_fused; W1, W2 may be NULL.
+ * variant SWIGLU_VARIANT_S (the pages' Kernel-1; paper abstract and
+ *   gist.science technical summary, Method, Kernel-1): per output tile, the
+ *   Gate contraction, then SiLU on the register-resident Gate accumulator
+ *   while the first Up tiles are loaded, then the Up contraction and a
+ *   multiply-and-store epilogue.  Reads A, W1, W2; W_fused may be NULL.
+ * variant SWIGLU_AUTO: whichever swiglu_select_variant(M, N, K) names; the
+ *   weights that variant reads must be non-NULL.
+ *
+ * A: [M][K], Y: [M][N] device.  Returns SWIGLU_ERR_NULL if a pointer the
+ * selected variant reads is NULL.
+ */
+int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W1,
+                      const uint16_t *W2, const uint16_t *W_fused, uint16_t *Y,
+                      int64_t M, int64_t N, int64_t K, int variant,
+                      void *stream);
+
+/*
+ * The unfused pipeline, kept as an ablation so the saved memory traffic can be
+ * measured (paper text, section 1: the unfused form materialises two full
+ * intermediate tensors, Gate and Up, between the GEMM and activation stages).
+ * Three stream-ordered launches built from the same mainloop as the fused
+ * kernels:
+ *     gate_ws = bf16(A.W1);  up_ws = bf16(A.W2);
+ *     Y = bf16( SiLU(gate_ws) * up_ws )   (fp32 arithmetic, one rounding)
+ * gate_ws, up_ws: caller-owned [M][N] device workspaces, written (their
+ * contents are part of the result and may be inspected).
+ */
+int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W1,
+                            const uint16_t *W2, uint16_t *gate_ws,
+                            uint16_t *up_ws, uint16_t *Y, int64_t M, int64_t N,
+                            int64_t K, void *stream);
+
+/*
+ * The ablation's activation stage on its own: Y[i] = bf16(SiLU(gate[i]) *
+ * up[i]) for i < count, fp32 arithmetic, one rounding.  count % 8 == 0,
+ * count >= 0; pointers 16-byte aligned, device.
+ */
+int swiglu_silu_mul(const uint16_t *gate, const uint16_t *up, uint16_t *Y,
+                    int64_t count, void *stream);
+
+/*
+ * The variant SWIGLU_AUTO runs for this shape: SWIGLU_VARIANT_I when
+ * M <= swiglu_m_switch(), else SWIGLU_VARIANT_S (the pages aim the interleaved
+ * kernel at small batches and the sequential one at large batches;
+ * gist.science technical summary, Method, Kernel-1 and Kernel-2).  Host only,
+ * no HIP call.  Returns SWIGLU_ERR_SHAPE for M < 0.
+ */
+int swiglu_select_variant(int64_t M, int64_t N, int64_t K);
+
+/* The M threshold used by swiglu_select_variant (environment variable
+ * SWIGLU_M_SWITCH overrides the built-in value when it parses as an integer). */
+int64_t swiglu_m_switch(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *swiglu_status_string(int status);
+
+/* Detail of the last failure on the calling thread (static storage; empty
+ * string when the last call succeeded). */
+const char *swiglu_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_H */

@@ -1,0 +1,139 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+``include/swiglu.h`` declares, and rejects invalid arguments before any HIP
+call (so nothing is launched).  Fake device addresses are used: validation
+fails before they could be dereferenced or passed to HIP."""
+import ctypes
+import os
+
+import pytest
+
+from gated_mlp_gemm_amd import swiglu as sw
+
+ERR_NULL, ERR_SHAPE, ERR_ALIGN = sw.SWIGLU_ERR_NULL, sw.SWIGLU_ERR_SHAPE, sw.SWIGLU_ERR_ALIGN
+ERR_UNSUP, ERR_ALIAS = sw.SWIGLU_ERR_UNSUPPORTED, sw.SWIGLU_ERR_ALIAS
+
+# fake, 16-byte aligned, far apart "device" addresses (never dereferenced)
+A_, W1_, W2_, WF_, Y_, G_, U_ = (0x10_0000_0000 * (i + 1) for i in range(7))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sw.LIBRARY):
+        pytest.fail("libswiglu.so is not built (python -m gated_mlp_gemm_amd.build)")
+    return sw.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = sw.header_functions()
+    assert set(names) >= {"swiglu_pack_weights", "swiglu_fused_gemm",
+                          "swiglu_unfused_ablation", "swiglu_select_variant",
+                          "swiglu_status_string"}
+    raw = ctypes.CDLL(sw.LIBRARY)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in swiglu.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert sw.swiglu_status_string(code) != "unknown status"
+    assert sw.swiglu_status_string(17) == "unknown status"
+
+
+def test_dispatcher_thresholds(lib, monkeypatch):
+    monkeypatch.delenv("SWIGLU_M_SWITCH", raising=False)
+    assert sw.swiglu_m_switch() == 2048
+    for M in (1, 128, 2047, 2048):
+        assert sw.swiglu_select_variant(M, 8960, 1536) == sw.SWIGLU_VARIANT_I
+    for M in (2049, 4096, 8192):
+        assert sw.swiglu_select_variant(M, 8960, 1536) == sw.SWIGLU_VARIANT_S
+    assert lib.swiglu_select_variant(-1, 8, 8) == ERR_SHAPE
+    monkeypatch.setenv("SWIGLU_M_SWITCH", "100")
+    assert sw.swiglu_m_switch() == 100
+    assert sw.swiglu_select_variant(100) == sw.SWIGLU_VARIANT_I
+    assert sw.swiglu_select_variant(101) == sw.SWIGLU_VARIANT_S
+    monkeypatch.setenv("SWIGLU_M_SWITCH", "not-a-number")
+    assert sw.swiglu_m_switch() == 2048
+
+
+def fused(lib, A=A_, W1=W1_, W2=W2_, WF=WF_, Y=Y_, M=256, N=256, K=256, v=2):
+    return lib.swiglu_fused_gemm(A, W1, W2, WF, Y, M, N, K, v, None)
+
+
+def test_fused_validation(lib):
+    # shapes
+    assert fused(lib, M=-1) == ERR_SHAPE
+    assert fused(lib, N=-8) == ERR_SHAPE
+    assert fused(lib, K=0) == ERR_SHAPE
+    assert fused(lib, K=4) == ERR_SHAPE
+    assert fused(lib, K=20) == ERR_SHAPE          # not a multiple of 8
+    assert fused(lib, N=12) == ERR_SHAPE
+    assert fused(lib, K=(1 << 22) + 8) == ERR_SHAPE
+    assert fused(lib, N=(1 << 23) + 8) == ERR_SHAPE
+    assert fused(lib, M=1 << 31) == ERR_SHAPE
+    # variant
+    assert fused(lib, v=3) == ERR_UNSUP
+    assert fused(lib, v=-1) == ERR_UNSUP
+    # null pointers, per variant
+    assert fused(lib, A=None) == ERR_NULL
+    assert fused(lib, Y=None) == ERR_NULL
+    assert fused(lib, WF=None, v=2) == ERR_NULL          # I reads W_fused
+    assert fused(lib, W1=None, v=1) == ERR_NULL          # S reads W1 and W2
+    assert fused(lib, W2=None, v=1) == ERR_NULL
+    assert fused(lib, WF=None, M=100, v=0) == ERR_NULL   # AUTO -> I at M=100
+    assert fused(lib, W1=None, M=4096, v=0) == ERR_NULL  # AUTO -> S at M=4096
+    # alignment
+    assert fused(lib, A=A_ + 2) == ERR_ALIGN
+    assert fused(lib, Y=Y_ + 8) == ERR_ALIGN
+    assert fused(lib, WF=WF_ + 4, v=2) == ERR_ALIGN
+    assert fused(lib, W1=W1_ + 2, v=1) == ERR_ALIGN
+    # aliasing: Y inside A, Y inside W_fused, Y overlapping W2
+    assert fused(lib, Y=A_ + 1024) == ERR_ALIAS
+    assert fused(lib, Y=WF_ + 4096, v=2) == ERR_ALIAS
+    assert fused(lib, Y=W2_ + 16, v=1) == ERR_ALIAS
+    assert "overlaps" in sw.swiglu_last_error()
+
+
+def test_empty_problems_succeed_without_pointers(lib):
+    assert lib.swiglu_fused_gemm(None, None, None, None, None, 0, 256, 64, 0, None) == 0
+    assert lib.swiglu_fused_gemm(None, None, None, None, None, 64, 0, 64, 0, None) == 0
+    assert lib.swiglu_unfused_ablation(None, None, None, None, None, None, 0, 64, 64, None) == 0
+    assert lib.swiglu_pack_weights(None, None, None, 0, 64, None) == 0
+    assert lib.swiglu_pack_weights(None, None, None, 64, 0, None) == 0
+    assert lib.swiglu_silu_mul(None, None, None, 0, None) == 0
+    assert sw.swiglu_last_error() == ""
+
+
+def test_pack_validation(lib):
+    P = lib.swiglu_pack_weights
+    assert P(W1_, W2_, WF_, -1, 8, None) == ERR_SHAPE
+    assert P(W1_, W2_, WF_, 8, 12, None) == ERR_SHAPE
+    assert P(None, W2_, WF_, 8, 8, None) == ERR_NULL
+    assert P(W1_, W2_, None, 8, 8, None) == ERR_NULL
+    assert P(W1_ + 2, W2_, WF_, 8, 8, None) == ERR_ALIGN
+    assert P(W1_, W2_, W1_ + 64, 8, 8, None) == ERR_ALIAS
+
+
+def test_ablation_validation(lib):
+    F = lib.swiglu_unfused_ablation
+    ok = dict(A=A_, W1=W1_, W2=W2_, G=G_, U=U_, Y=Y_)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return F(a["A"], a["W1"], a["W2"], a["G"], a["U"], a["Y"], 256, 256, 256, None)
+
+    assert call(G=None) == ERR_NULL
+    assert call(U=None) == ERR_NULL
+    assert call(G=G_ + 2) == ERR_ALIGN
+    assert call(U=G_ + 1024) == ERR_ALIAS        # two outputs overlap
+    assert call(Y=U_ + 16) == ERR_ALIAS
+    assert call(G=W1_ + 64) == ERR_ALIAS         # output inside an input
+    assert F(A_, W1_, W2_, G_, U_, Y_, 256, 20, 256, None) == ERR_SHAPE
+
+
+def test_silu_mul_validation(lib):
+    F = lib.swiglu_silu_mul
+    assert F(G_, U_, Y_, 12, None) == ERR_SHAPE
+    assert F(G_, U_, Y_, -8, None) == ERR_SHAPE
+    assert F(None, U_, Y_, 8, None) == ERR_NULL
+    assert F(G_, U_ + 2, Y_, 8, None) == ERR_ALIGN
+    assert F(G_, U_, G_ + 16, 64, None) == ERR_ALIAS

@@ -105,12 +105,18 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_interleaved_kernel(
     const int rows_valid = min(S::BM, M - m0);
     const int ldb = 2 * N;
 
-    Mainloop<S> ml;
-    ml.init_a(A + (int64_t)m0 * K, K, rows_valid, K);
-    ml.init_b_offsets(ldb);
+    const int nk = (K + S::BK - 1) / S::BK;
+    TileLoader<S> ld;
+    ld.init(A + (int64_t)m0 * K, K, rows_valid, K, ldb);
+    const uint16_t *Bt = Wf + n0;
+    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, Bt, n0, st); };
+    Pipeline<S> pl;
+    pl.init(lds);
     f32x16 acc[S::TM][S::TN];
     zero_acc<S>(acc);
-    gemm_tile<S>(lds, ml, Wf + n0, ldb, n0, ldb, K, acc);
+    pl.prologue(issue);
+    pl.run(issue, 0, nk, nk, acc);
+    pl.drain();
 
     // PairMul epilogue
     const int lane = threadIdx.x & 63;
@@ -166,45 +172,56 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
     const int wm = wave / S::WN, wn = wave % S::WN;
     const int nk = (K + S::BK - 1) / S::BK;
 
-    Mainloop<S> ml;
-    ml.init_a(A + (int64_t)m0 * K, K, rows_valid, K);
-    ml.init_b_offsets(N);
+    // One step sequence of 2*nk K steps: steps [0, nk) contract against W1,
+    // steps [nk, 2nk) against W2; the loads run ahead across the boundary.
+    TileLoader<S> ld;
+    ld.init(A + (int64_t)m0 * K, K, rows_valid, K, N);
+    const uint16_t *B1 = W1 + n0;
+    const uint16_t *B2 = W2 + n0;
+    auto issue = [&](int t, SWIGLU_LDS char *st) {
+        if (t < nk) ld.issue(t, B1, n0, st);
+        else ld.issue(t - nk, B2, n0, st);   // t - nk >= nk loads nothing
+    };
+    Pipeline<S> pl;
+    pl.init(lds);
     f32x16 g[S::TM][S::TN], u[S::TM][S::TN];
     zero_acc<S>(g);
     zero_acc<S>(u);
 
-    // Gate loop (its last step stages Up tile 0)
-    ml.load(0, W1 + n0, N, n0, N);
-    ml.store(lds);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk)
-            ml.load(kt + 1, W1 + n0, N, n0, N);
-        else
-            ml.load(0, W2 + n0, N, n0, N);
-        mma_stage<S>(lds + (kt & 1) * S::kStageBytes, g, wm, wn, lane);
-        ml.store(lds + ((kt + 1) & 1) * S::kStageBytes);
-        __syncthreads();
-    }
+    // Gate loop
+    pl.prologue(issue);
+    pl.run(issue, 0, nk, 2 * nk, g);
 
-    // SiLU window: Up tile 1 is requested first, then Gate is activated in
-    // registers while those loads fly.
-    if (nk > 1) ml.load(1, W2 + n0, N, n0, N);
+    // SiLU window: the first Up K steps run with one 32x32 Gate block activated
+    // per k-substep, so the VALU/transcendental work interleaves with the Up
+    // MFMAs (independent registers) while the Up tiles stream into LDS.
+    constexpr int kBlocks = S::TM * S::TN;
+    constexpr int kSiluSteps = (kBlocks + S::kKSub - 1) / S::kKSub;
 #pragma unroll
-    for (int tm = 0; tm < S::TM; ++tm)
+    for (int j = 0; j < kSiluSteps; ++j) {
+        if (j < nk) {
+            pl.step(issue, nk + j, 2 * nk, u, [&](int ks) {
+                const int b = j * S::kKSub + ks;
+                if (b < kBlocks) {
 #pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) g[tm][tn][i] = silu(g[tm][tn][i]);
-
-    // Up loop
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (kt > 0 && more) ml.load(kt + 1, W2 + n0, N, n0, N);
-        mma_stage<S>(lds + ((nk + kt) & 1) * S::kStageBytes, u, wm, wn, lane);
-        if (more) ml.store(lds + ((nk + kt + 1) & 1) * S::kStageBytes);
-        __syncthreads();
+                    for (int i = 0; i < 16; ++i)
+                        g[b / S::TN][b % S::TN][i] = silu(g[b / S::TN][b % S::TN][i]);
+                }
+            });
+        }
     }
+    // (only when K is shorter than the window) the blocks not yet activated
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) {
+        if (b >= nk * S::kKSub) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                g[b / S::TN][b % S::TN][i] = silu(g[b / S::TN][b % S::TN][i]);
+        }
+    }
+    // rest of the Up loop
+    pl.run(issue, nk + kSiluSteps, 2 * nk, 2 * nk, u);
+    pl.drain();
 
     // multiply and store
     const int cols_valid = min(S::BN, N - n0);
@@ -240,12 +257,18 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_store_kernel(
     const int n0 = tn_ * S::BN;
     const int rows_valid = min(S::BM, M - m0);
 
-    Mainloop<S> ml;
-    ml.init_a(A + (int64_t)m0 * K, K, rows_valid, K);
-    ml.init_b_offsets(N);
+    const int nk = (K + S::BK - 1) / S::BK;
+    TileLoader<S> ld;
+    ld.init(A + (int64_t)m0 * K, K, rows_valid, K, N);
+    const uint16_t *Bt = B + n0;
+    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, Bt, n0, st); };
+    Pipeline<S> pl;
+    pl.init(lds);
     f32x16 acc[S::TM][S::TN];
     zero_acc<S>(acc);
-    gemm_tile<S>(lds, ml, B + n0, N, n0, N, K, acc);
+    pl.prologue(issue);
+    pl.run(issue, 0, nk, nk, acc);
+    pl.drain();
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -269,9 +292,9 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_store_kernel(
 // ---------------------------------------------------------------------------
 // Tile shapes and launchers
 // ---------------------------------------------------------------------------
-using ShapeWide = TileShape<256, 256, 64, 2, 2, 2>;    // I and ablation GEMM
-using ShapeSeq = TileShape<256, 128, 64, 2, 2, 2>;     // S: two 256x128 accumulators
-using ShapeSmall = TileShape<128, 64, 64, 2, 2, 2>;    // M <= 128: more tiles on the weights
+using ShapeWide = TileShape<256, 256, 32, 2, 4, 4>;    // I and ablation GEMM
+using ShapeSeq = TileShape<256, 128, 32, 4, 2, 4>;     // S: two 256x128 accumulators
+using ShapeSmall = TileShape<128, 64, 32, 2, 2, 4>;    // M <= 128: more tiles on the weights
 
 static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 

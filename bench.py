@@ -100,12 +100,13 @@ def main():
               "s": sw.SWIGLU_VARIANT_S}[args.variant]
     vname = "i" if chosen == sw.SWIGLU_VARIANT_I else "s"
 
-    # rotation copies: fused working set (A + weights + Y) times R >= 512 MB
+    # rotation copies: fused working set (A + packed weights + Y) times R >= 512 MB
     ws_bytes = 2 * (M * K + 2 * K * N + M * N)
     R = max(1, -(-512 * 2 ** 20 // ws_bytes))
-    copies = [(Ad, W1d, W2d, Wf)]
+    del W1d, W2d
+    copies = [(Ad, Wf)]
     for _ in range(R - 1):
-        copies.append((Ad.clone(), W1d.clone(), W2d.clone(), Wf.clone()))
+        copies.append((Ad.clone(), Wf.clone()))
     outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
     abl_ws = [(torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(R)]
@@ -113,13 +114,13 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def fused_step(s, variant):
-        a, w1, w2, wf = copies[s % R]
-        sw.swiglu_fused_gemm(a, w1, w2, wf, Y=outs[s % R], variant=variant)
+        a, wf = copies[s % R]
+        sw.swiglu_fused_gemm(a, wf, Y=outs[s % R], variant=variant)
 
     def ablation_step(s):
-        a, w1, w2, _ = copies[s % R]
+        a, wf = copies[s % R]
         g, u = abl_ws[s % R]
-        sw.swiglu_unfused_ablation(a, w1, w2, gate_ws=g, up_ws=u, Y=outs[s % R])
+        sw.swiglu_unfused_ablation(a, wf, gate_ws=g, up_ws=u, Y=outs[s % R])
 
     def timed(step_fn, steps, warmup):
         for s in range(warmup):
@@ -150,8 +151,7 @@ def main():
     ams, _ = timed(ablation_step, args.steps, args.warmup)
     per["ablation"] = {"ms": ams, "tflops": flops / (ams * 1e-3) / 1e12}
     # warm (one copy, cache-resident where it fits) for context
-    wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, W1d, W2d, Wf, Y=outs[0],
-                                                  variant=args.variant),
+    wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, Wf, Y=outs[0], variant=args.variant),
                    args.steps, args.warmup)
     for k, v in per.items():
         print(f"[bench] {k}: {v['ms'] * 1e3:.1f} us, {v['tflops']:.1f} TFLOP/s",

@@ -34,7 +34,7 @@ int ok() {
 }
 
 constexpr int64_t kMaxM = 2147483647;     // 2^31 - 1
-constexpr int64_t kMaxK = int64_t(1) << 22;
+constexpr int64_t kMaxK = int64_t(1) << 21;
 constexpr int64_t kMaxN = int64_t(1) << 23;
 constexpr int64_t kDefaultMSwitch = 2048;
 
@@ -51,7 +51,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
     if (K % 8 != 0 || N % 8 != 0)
         return fail(SWIGLU_ERR_SHAPE, "K=%lld and N=%lld must be multiples of 8", (long long)K, (long long)N);
     if (M > kMaxM || K > kMaxK || N > kMaxN)
-        return fail(SWIGLU_ERR_SHAPE, "size beyond limits (M<=2^31-1, K<=2^22, N<=2^23)");
+        return fail(SWIGLU_ERR_SHAPE, "size beyond limits (M<=2^31-1, K<=2^21, N<=2^23)");
     if (swiglu::max_tiles(M, 2 * N) > 2147483647)
         return fail(SWIGLU_ERR_SHAPE, "tile grid too large");
     return SWIGLU_OK;
@@ -123,7 +123,10 @@ int swiglu_select_variant(int64_t M, int64_t N, int64_t K) {
 int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2, uint16_t *W_fused, int64_t K,
                         int64_t N, void *stream) {
     if (K < 0 || N < 0) return fail(SWIGLU_ERR_SHAPE, "negative size");
-    if (N % 8 != 0) return fail(SWIGLU_ERR_SHAPE, "N=%lld must be a multiple of 8", (long long)N);
+    // both are row lengths of 16-byte-chunked rows: N of W1/W2, K of the packed array
+    if (K % 8 != 0 || N % 8 != 0)
+        return fail(SWIGLU_ERR_SHAPE, "K=%lld and N=%lld must be multiples of 8", (long long)K,
+                    (long long)N);
     if (K > kMaxK || N > kMaxN) return fail(SWIGLU_ERR_SHAPE, "size beyond limits");
     if (K == 0 || N == 0) return ok();
     if (!W1 || !W2 || !W_fused) return fail(SWIGLU_ERR_NULL, "W1, W2 and W_fused are required");
@@ -137,57 +140,45 @@ int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2, uint16_t *W_fuse
     return launched(swiglu::launch_pack(W1, W2, W_fused, K, N, (hipStream_t)stream), "pack");
 }
 
-int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
-                      const uint16_t *W_fused, uint16_t *Y, int64_t M, int64_t N, int64_t K,
-                      int variant, void *stream) {
+int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, int64_t M,
+                      int64_t N, int64_t K, int variant, void *stream) {
     if (variant != SWIGLU_AUTO && variant != SWIGLU_VARIANT_S && variant != SWIGLU_VARIANT_I)
         return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
     int st = check_gemm_shape(M, N, K);
     if (st != SWIGLU_OK) return st;
     if (M == 0 || N == 0) return ok();
     const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
-    if (!A || !Y) return fail(SWIGLU_ERR_NULL, "A and Y are required");
-    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = K * N * 2;
-    if (v == SWIGLU_VARIANT_I) {
-        if (!W_fused) return fail(SWIGLU_ERR_NULL, "variant I reads W_fused");
-        if (!aligned16(A) || !aligned16(W_fused) || !aligned16(Y))
-            return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
-        if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W_fused, 2 * wbytes))
-            return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
-    } else {
-        if (!W1 || !W2) return fail(SWIGLU_ERR_NULL, "variant S reads W1 and W2");
-        if (!aligned16(A) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y))
-            return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
-        if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W1, wbytes) ||
-            overlap(Y, ybytes, W2, wbytes))
-            return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
-    }
+    if (!A || !W_fused || !Y) return fail(SWIGLU_ERR_NULL, "A, W_fused and Y are required");
+    if (!aligned16(A) || !aligned16(W_fused) || !aligned16(Y))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = 2 * K * N * 2;
+    if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W_fused, wbytes))
+        return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
     st = check_device();
     if (st != SWIGLU_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
     if (v == SWIGLU_VARIANT_I)
         return launched(swiglu::launch_fused_interleaved(A, W_fused, Y, (int)M, (int)N, (int)K, s),
                         "fused interleaved");
-    return launched(swiglu::launch_fused_sequential(A, W1, W2, Y, (int)M, (int)N, (int)K, s),
+    return launched(swiglu::launch_fused_sequential(A, W_fused, Y, (int)M, (int)N, (int)K, s),
                     "fused sequential");
 }
 
-int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
-                            uint16_t *gate_ws, uint16_t *up_ws, uint16_t *Y, int64_t M,
-                            int64_t N, int64_t K, void *stream) {
+int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused, uint16_t *gate_ws,
+                            uint16_t *up_ws, uint16_t *Y, int64_t M, int64_t N, int64_t K,
+                            void *stream) {
     int st = check_gemm_shape(M, N, K);
     if (st != SWIGLU_OK) return st;
     if (M == 0 || N == 0) return ok();
-    if (!A || !W1 || !W2 || !gate_ws || !up_ws || !Y)
-        return fail(SWIGLU_ERR_NULL, "A, W1, W2, gate_ws, up_ws and Y are required");
-    if (!aligned16(A) || !aligned16(W1) || !aligned16(W2) || !aligned16(gate_ws) ||
-        !aligned16(up_ws) || !aligned16(Y))
+    if (!A || !W_fused || !gate_ws || !up_ws || !Y)
+        return fail(SWIGLU_ERR_NULL, "A, W_fused, gate_ws, up_ws and Y are required");
+    if (!aligned16(A) || !aligned16(W_fused) || !aligned16(gate_ws) || !aligned16(up_ws) ||
+        !aligned16(Y))
         return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
-    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = K * N * 2;
+    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = 2 * K * N * 2;
     const void *outs[3] = {gate_ws, up_ws, Y};
     for (int i = 0; i < 3; ++i) {
-        if (overlap(outs[i], ybytes, A, abytes) || overlap(outs[i], ybytes, W1, wbytes) ||
-            overlap(outs[i], ybytes, W2, wbytes))
+        if (overlap(outs[i], ybytes, A, abytes) || overlap(outs[i], ybytes, W_fused, wbytes))
             return fail(SWIGLU_ERR_ALIAS, "an output overlaps an input");
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], ybytes, outs[j], ybytes))
@@ -196,9 +187,9 @@ int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W1, const uint16_
     st = check_device();
     if (st != SWIGLU_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
-    hipError_t e = swiglu::launch_gemm_store(A, W1, gate_ws, (int)M, (int)N, (int)K, s);
+    hipError_t e = swiglu::launch_gemm_store(A, W_fused, 0, gate_ws, (int)M, (int)N, (int)K, s);
     if (e != hipSuccess) return launched(e, "ablation gate GEMM");
-    e = swiglu::launch_gemm_store(A, W2, up_ws, (int)M, (int)N, (int)K, s);
+    e = swiglu::launch_gemm_store(A, W_fused, 1, up_ws, (int)M, (int)N, (int)K, s);
     if (e != hipSuccess) return launched(e, "ablation up GEMM");
     return launched(swiglu::launch_silu_mul(gate_ws, up_ws, Y, M * N, s), "ablation silu_mul");
 }

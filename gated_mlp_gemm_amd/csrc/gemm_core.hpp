@@ -3,42 +3,38 @@
 // ablation's plain-store GEMM all run this code, so that their timings differ
 // only by what the method changes (where Gate and Up live).
 //
-// One workgroup computes a BM x BN tile of D = A . B, where
-//   A is row-major [rows][K]   (K contiguous; the activations),
-//   B is row-major [K][cols]   (cols contiguous; W1, W2 or W_fused),
-// in K steps of BK.
+// One workgroup computes a BM x BN tile of D = A . B^T where both operands are
+// K-contiguous row panels ("NT" form):
+//   A: rows of the activations [M][K];
+//   B: rows of the packed weight W_fused^T [2N][K] (column c of W_fused is row
+//      c here), optionally every second row (the Gate or the Up columns).
+// K is consumed in steps of BK.
 //
 // Pipeline.  K steps stream through a ring of STAGES LDS buffers filled by
 // direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds: no VGPR staging,
 // no LDS write instructions), STAGES-1 steps ahead of the MFMAs.  The
-// compiler does not track those LDS writes, so completion is awaited by hand:
-// before step t+1 is read, each wave waits until at most (STAGES-2) later
-// steps' loads are outstanding (s_waitcnt vmcnt), then the workgroup meets at
-// one barrier.  That barrier also proves that every wave has finished reading
-// step t's buffer, which is refilled with step t+STAGES right after it.  The
-// barrier sits before the MFMAs of step t's last k-substep, so those MFMAs
-// overlap the first fragment reads of step t+1.  Every step issues exactly one
-// group of loads (groups past the end of K read nothing), which keeps the
-// vmcnt arithmetic uniform.
+// compiler does not track those LDS writes, so completion is awaited by hand
+// (s_waitcnt vmcnt with a count of the later steps still allowed in flight)
+// before a workgroup barrier; see the two pipeline drivers below.  Every step
+// issues exactly one group of loads (groups past the end of K read nothing),
+// which keeps the vmcnt arithmetic uniform.
 //
-// LDS layouts (16-byte chunks, XOR-swizzled so that the fragment reads of a
-// wave spread over all banks):
-//   A tile: [BM][BK]; physical chunk = chunk ^ swz_a(row);
-//           fragment read: one ds_read_b128 per lane (8 consecutive k).
-//   B tile: [BK][BN] exactly as in memory (n contiguous);
-//           physical chunk = chunk ^ swz_b(k);
-//           fragment read: two ds_read_b64_tr_b16 per lane, which transpose
-//           4 k-rows x 16 columns across each 16-lane group so that every lane
-//           receives 8 consecutive k of one column (the MFMA B layout).
-// A direct-to-LDS load writes 64 consecutive 16-byte chunks per wave, so the
-// swizzle is applied on the global side: the lane that lands on physical chunk
-// p fetches the logical chunk that belongs there.
+// LDS layout: A tile [BM][BK] then B tile [BN][BK], 16-byte chunks with the
+// chunk index XOR-swizzled by the row, so that the 16 lanes one LDS cycle
+// serves (256 B) hit 16 different bank groups.  Fragment reads are one
+// ds_read_b128 per lane per 32x32x16 MFMA operand (8 consecutive k of one
+// row), which on gfx950 streams 256 B per clock, twice the rate of the
+// transposing 64-bit reads a [K][N] weight layout would need.  A direct-to-LDS
+// load writes 64 consecutive chunks per wave, so the swizzle is applied on the
+// global side: the lane that lands on physical chunk p fetches the logical
+// chunk that belongs there.
 //
-// Edges.  Rows past the end of A and k past the end of B fall outside the
-// buffer ranges and load as zeros; the K tail of A is masked explicitly.
-// Columns of B past `cols` may load neighbouring data of the same matrix; they
-// only feed accumulator columns that are never stored.
+// Edges.  Rows past the end of an operand fall outside its buffer range and
+// load as zeros; chunks at k >= K are masked explicitly, so the K tail
+// contributes nothing.
 #pragma once
+
+#include <type_traits>
 
 #include "device.hpp"
 
@@ -55,16 +51,18 @@ struct TileShape {
     static constexpr int TM = kWaveM / 32;          // 32x32 MFMA blocks per wave (M)
     static constexpr int TN = kWaveN / 32;          // 32x32 MFMA blocks per wave (N)
     static constexpr int kKSub = BK / 16;           // MFMA k-substeps per K step
-    static constexpr int kAChunksPerRow = BK / 8;
-    static constexpr int kBChunksPerRow = BN / 8;
-    static constexpr int kABytes = BM * BK * 2;
-    static constexpr int kBBytes = BK * BN * 2;
+    static constexpr int kChunksPerRow = BK / 8;    // 16-byte chunks per tile row
+    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kABytes = BM * kRowBytes;
+    static constexpr int kBBytes = BN * kRowBytes;
     static constexpr int kStageBytes = kABytes + kBBytes;
     static constexpr int kLdsBytes = kStageBytes * STAGES;
     // direct-to-LDS loads per wave per K step (each moves 64 x 16 B = 1 KiB)
     static constexpr int kDmaA = kABytes / (kThreads * 16);
     static constexpr int kDmaB = kBBytes / (kThreads * 16);
     static constexpr int kDmaPerStep = kDmaA + kDmaB;
+    // 8 waves (two per SIMD) run the ping-pong schedule; 4 waves the plain one
+    static constexpr bool kPingPong = (kWaves == 8);
 
     static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
@@ -73,18 +71,18 @@ struct TileShape {
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup is 160 KiB");
     static_assert(STAGES >= 2 && STAGES <= 8, "ring depth");
     static_assert(kDmaPerStep * (STAGES - 1) < 64, "vmcnt is a 6-bit counter");
-    static_assert(BN >= 64, "B swizzle needs at least 8 chunks per row");
+    static_assert(kWaves == 4 || (kWaves == 8 && WM % 2 == 0),
+                  "4 waves, or 8 waves whose two groups split the tile rows");
 };
 
-// Swizzles (see the layout note above).
+// Chunk swizzle of a tile row.  The 16 lanes of one LDS cycle read 16
+// consecutive rows at the same logical chunk; the XOR spreads them over 16
+// distinct 16-byte bank groups of the 256 B bank period (and is periodic in 32
+// rows, so 32-row MFMA blocks share it).
 template <class S>
-__device__ __forceinline__ int swz_a(int row) {
-    if constexpr (S::kAChunksPerRow == 4) return ((row >> 1) ^ (row >> 3)) & 3;
-    else return (row >> 1) & 7;
-}
-template <class S>
-__device__ __forceinline__ int swz_b(int k) {
-    return (4 * (k & 3)) & (S::kBChunksPerRow - 1);
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (S::kChunksPerRow == 4) return ((row >> 1) ^ (row >> 3)) & 3;  // 64 B rows
+    else return (row >> 1) & 7;                                                 // 128 B rows
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -122,73 +120,89 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Global -> LDS loader of one tile's K steps.  The B operand may change
-// between K-step ranges (the sequential variant runs W1 steps then W2 steps).
-template <class S>
-struct TileLoader {
-    __amdgpu_buffer_rsrc_t rsrc_a;
-    uint32_t a_voff[S::kDmaA];   // byte offset of this lane's A chunk at k0 = 0
-    int a_kcol[S::kDmaA];        // first k of that chunk
-    uint32_t b_voff[S::kDmaB];   // byte offset of this lane's B chunk within a K step
-    int K;
-    int ldb;
+// A K-contiguous operand: logical row r is physical row r*stride + offset of
+// a row-major [rows*stride][K] matrix.  (stride 2 selects the Gate (offset 0)
+// or Up (offset 1) columns of the interleaved packed weight.)
+struct KMajor {
+    const uint16_t *base;
+    int rows;        // logical rows
+    int stride;
+    int offset;
+};
 
-    __device__ __forceinline__ void init(const uint16_t *A_tile, int lda, int rows_valid, int K_,
-                                         int ldb_) {
-        K = K_;
-        ldb = ldb_;
-        rsrc_a = make_rsrc(A_tile, static_cast<uint32_t>(rows_valid) * lda * 2u);
+// The direct-to-LDS loads of one tile panel (NROWS rows) of a KMajor
+// operand: NDMA loads per wave per K step.
+template <class S, int NROWS, int NDMA>
+struct PanelLoader {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff[NDMA];   // byte offset of this lane's chunk at k0 = 0 (from the panel base)
+    int kcol[NDMA];        // first k of that chunk
+    int lds_off[NDMA];     // LDS byte offset (within the panel) of the wave's 1 KiB block
+
+    // Panel = logical rows [r0, r0 + NROWS) of `op`.
+    __device__ __forceinline__ void init(const KMajor &op, int r0, int K) {
+        const int64_t phys0 = static_cast<int64_t>(r0) * op.stride + op.offset;
+        const int64_t phys_end = static_cast<int64_t>(op.rows) * op.stride;  // past the matrix
+        const uint16_t *panel = op.base + phys0 * K;
+        int64_t bytes = (phys_end - phys0) * K * 2;
+        if (bytes < 0) bytes = 0;
+        if (bytes > 0x7FFFFFF0LL) bytes = 0x7FFFFFF0LL;
+        rsrc = make_rsrc(panel, static_cast<uint32_t>(bytes));
         const int lane = threadIdx.x & 63;
         const int wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int j = 0; j < S::kDmaA; ++j) {
-            const int p = (j * S::kWaves + wave) * 64 + lane;   // physical chunk
-            const int row = p / S::kAChunksPerRow;
-            const int c = (p % S::kAChunksPerRow) ^ swz_a<S>(row);
-            a_voff[j] = static_cast<uint32_t>(row) * lda * 2u + c * 16u;
-            a_kcol[j] = c * 8;
-        }
-#pragma unroll
-        for (int j = 0; j < S::kDmaB; ++j) {
-            const int p = (j * S::kWaves + wave) * 64 + lane;
-            const int k = p / S::kBChunksPerRow;
-            const int c = (p % S::kBChunksPerRow) ^ swz_b<S>(k);
-            b_voff[j] = static_cast<uint32_t>(k) * ldb_ * 2u + c * 16u;
+        for (int j = 0; j < NDMA; ++j) {
+            const int block = j * S::kWaves + wave;
+            const int p = block * 64 + lane;                  // physical chunk in the panel
+            const int row = p / S::kChunksPerRow;
+            const int c = (p % S::kChunksPerRow) ^ swz<S>(row);
+            voff[j] = static_cast<uint32_t>(row * op.stride) * K * 2u + c * 16u;
+            kcol[j] = c * 8;
+            lds_off[j] = block * 1024;
         }
     }
 
-    // Load K step `kstep` (of a K-long contraction against B_tile = B + n0)
-    // into `stage`.  kstep >= ceil(K/BK) loads nothing (keeps vmcnt uniform).
-    __device__ __forceinline__ void issue(int kstep, const uint16_t *B_tile, int n0,
-                                          SWIGLU_LDS char *stage) const {
-        const int wave = threadIdx.x >> 6;
-        const int k0 = kstep * S::BK;
+    __device__ __forceinline__ void issue(int k0, int K, SWIGLU_LDS char *panel_lds) const {
         const bool live = k0 < K;
-        SWIGLU_LDS char *la = stage;
-        SWIGLU_LDS char *lb = stage + S::kABytes;
         const uint32_t soff = live ? static_cast<uint32_t>(k0) * 2u : 0u;
         if (live && k0 + S::BK <= K) {
 #pragma unroll
-            for (int j = 0; j < S::kDmaA; ++j)
-                dma16(rsrc_a, la + (j * S::kWaves + wave) * 1024, a_voff[j], soff);
+            for (int j = 0; j < NDMA; ++j) dma16(rsrc, panel_lds + lds_off[j], voff[j], soff);
         } else {
-            // K tail (or a step past the end): mask the chunks at k >= K
+            // K tail (or a step past the end): chunks at k >= K load nothing
 #pragma unroll
-            for (int j = 0; j < S::kDmaA; ++j) {
-                const uint32_t v = (live && k0 + a_kcol[j] < K) ? a_voff[j] : kOutOfRange;
-                dma16(rsrc_a, la + (j * S::kWaves + wave) * 1024, v, soff);
+            for (int j = 0; j < NDMA; ++j) {
+                const uint32_t v = (live && k0 + kcol[j] < K) ? voff[j] : kOutOfRange;
+                dma16(rsrc, panel_lds + lds_off[j], v, soff);
             }
         }
-        // B: rebase on row k0 so that offsets stay small; the range ends at the
-        // last element of B, so rows k >= K load as zeros.
-        int64_t remaining = live ? (static_cast<int64_t>(K - k0) * ldb - n0) * 2 : 0;
-        if (remaining > 0x7FFFFFF0LL) remaining = 0x7FFFFFF0LL;
-        const uint16_t *b_base = B_tile + (live ? static_cast<int64_t>(k0) * ldb : 0);
-        const __amdgpu_buffer_rsrc_t rsrc_b =
-            make_rsrc(b_base, static_cast<uint32_t>(remaining));
-#pragma unroll
-        for (int j = 0; j < S::kDmaB; ++j)
-            dma16(rsrc_b, lb + (j * S::kWaves + wave) * 1024, b_voff[j], 0u);
+    }
+};
+
+// Loader of one output tile: the A panel and the B panel of each K step.
+template <class S>
+struct TileLoader {
+    PanelLoader<S, S::BM, S::kDmaA> a;
+    PanelLoader<S, S::BN, S::kDmaB> b;
+    int K;
+
+    __device__ __forceinline__ void init(const KMajor &A, int m0, const KMajor &B, int n0,
+                                         int K_) {
+        K = K_;
+        a.init(A, m0, K_);
+        b.init(B, n0, K_);
+    }
+
+    // Load K step `kstep` into `stage` with B panel `bp`; kstep >= ceil(K/BK)
+    // loads nothing.
+    __device__ __forceinline__ void issue(int kstep, SWIGLU_LDS char *stage,
+                                          const PanelLoader<S, S::BN, S::kDmaB> &bp) const {
+        const int k0 = kstep * S::BK;
+        a.issue(k0, K, stage);
+        bp.issue(k0, K, stage + S::kABytes);
+    }
+    __device__ __forceinline__ void issue(int kstep, SWIGLU_LDS char *stage) const {
+        issue(kstep, stage, b);
     }
 };
 
@@ -200,108 +214,72 @@ struct Frags {
 };
 
 // LDS reads issued as inline assembly.  The compiler neither tracks their
-// completion nor sees them as LDS accesses; the pipeline waits for them with
-// wait_frags() (below).  Keeping every fragment read out of the compiler's
-// view is deliberate: its waitcnt pass treats a transposing LDS read as
-// possibly aliasing the in-flight direct-to-LDS loads and would otherwise
-// drain every outstanding load (vmcnt(0)) before each one.
+// completion nor sees them as LDS accesses; the pipelines wait for them with
+// wait_frags().  Keeping the fragment reads out of the compiler's view keeps
+// its waitcnt pass from draining the in-flight direct-to-LDS loads (vmcnt(0))
+// around LDS reads it cannot prove independent of them.
 template <int OFF>
 __device__ __forceinline__ u32x4 asm_read_b128(uint32_t addr) {
     u32x4 r;
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
     return r;
 }
-template <int OFF>
-__device__ __forceinline__ u32x2 asm_read_tr_b64(uint32_t addr) {
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
 
-// Per-lane LDS byte offsets of the fragment reads, relative to a stage base.
-// A: one per k-substep (the swizzle mixes the substep into the address);
-//    the 32-row blocks tm are +tm*32 rows (the swizzle has period 32 in rows).
-// B: one per 32-column block tn; substep ks is +16*ks rows and the second
-//    transposing read +4 rows (the swizzle has period 4 in k).
+// Per-lane LDS byte offsets of the fragment reads, relative to a stage base,
+// one per k-substep for each operand (the swizzle mixes the substep into the
+// address); 32-row blocks tm / tn are +32 rows (the swizzle has period 32).
 template <class S>
 struct FragOffsets {
     uint32_t a[S::kKSub];
-    uint32_t b[S::TN];
+    uint32_t b[S::kKSub];
 
     __device__ __forceinline__ void init(int wm, int wn, int lane) {
         const int h = lane >> 5;
-        const int s = lane & 15;
-        const int q1 = (lane >> 4) & 1;
-        const int row = wm * S::kWaveM + (lane & 31);
+        const int ra = wm * S::kWaveM + (lane & 31);
+        const int rb = wn * S::kWaveN + (lane & 31);
 #pragma unroll
         for (int ks = 0; ks < S::kKSub; ++ks) {
-            const int pc = (ks * 2 + h) ^ swz_a<S>(row);
-            a[ks] = static_cast<uint32_t>(row * (S::BK * 2) + pc * 16);
-        }
-        const int krow = 8 * h + (s >> 2);
-#pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn) {
-            const int ncol = wn * S::kWaveN + tn * 32 + 16 * q1 + 4 * (s & 3);
-            const int pc = (ncol >> 3) ^ swz_b<S>(krow);
-            b[tn] = static_cast<uint32_t>(S::kABytes + krow * (S::BN * 2) + pc * 16 +
-                                          ((ncol >> 2) & 1) * 8);
+            a[ks] = static_cast<uint32_t>(ra * S::kRowBytes + (((ks * 2 + h) ^ swz<S>(ra)) * 16));
+            b[ks] = static_cast<uint32_t>(S::kABytes + rb * S::kRowBytes +
+                                          (((ks * 2 + h) ^ swz<S>(rb)) * 16));
         }
     }
 };
 
-// Issue the fragment reads of k-substep KS from the stage at LDS byte address
-// `stage` (A: TM x ds_read_b128; B: TN x 2 ds_read_b64_tr_b16).
-template <class S, int KS>
-__device__ __forceinline__ void read_frags(uint32_t stage, const FragOffsets<S> &o,
-                                           Frags<S> &f) {
-    const uint32_t abase = stage + o.a[KS];
-#pragma unroll
-    for (int tm = 0; tm < S::TM; ++tm) {
-        // tm * 32 rows of BK bf16; the immediate must be a constant expression
-        switch (tm) {
-            case 0: f.a[0] = asm_read_b128<0>(abase); break;
-            case 1: f.a[1] = asm_read_b128<1 * 32 * S::BK * 2>(abase); break;
-            case 2: f.a[2] = asm_read_b128<2 * 32 * S::BK * 2>(abase); break;
-            case 3: f.a[3] = asm_read_b128<3 * 32 * S::BK * 2>(abase); break;
-        }
+template <class S, int I>
+__device__ __forceinline__ void read_a_blocks(uint32_t p, Frags<S> &f) {
+    if constexpr (I < S::TM) {
+        f.a[I] = asm_read_b128<I * 32 * S::kRowBytes>(p);
+        read_a_blocks<S, I + 1>(p, f);
     }
-    constexpr int kRow = S::BN * 2;
-#pragma unroll
-    for (int tn = 0; tn < S::TN; ++tn) {
-        const uint32_t p = stage + o.b[tn];
-        const u32x2 lo = asm_read_tr_b64<KS * 16 * kRow>(p);
-        const u32x2 hi = asm_read_tr_b64<KS * 16 * kRow + 4 * kRow>(p);
-        f.b[tn] = u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+template <class S, int I>
+__device__ __forceinline__ void read_b_blocks(uint32_t p, Frags<S> &f) {
+    if constexpr (I < S::TN) {
+        f.b[I] = asm_read_b128<I * 32 * S::kRowBytes>(p);
+        read_b_blocks<S, I + 1>(p, f);
     }
 }
 
+// Issue the fragment reads of k-substep KS from the stage at LDS address `stage`.
+template <class S, int KS>
+__device__ __forceinline__ void read_frags(uint32_t stage, const FragOffsets<S> &o,
+                                           Frags<S> &f) {
+    read_a_blocks<S, 0>(stage + o.a[KS], f);
+    read_b_blocks<S, 0>(stage + o.b[KS], f);
+}
+
 // Wait until every fragment read issued so far has landed, and make the
-// fragment registers of `f` depend on that wait (so no MFMA reading them can
-// be scheduled before it).
+// fragment registers of `f` depend on that wait (volatile asm statements keep
+// their order, so each empty "+v" statement, which the MFMAs depend on, stays
+// after the wait).
 template <class S>
 __device__ __forceinline__ void wait_frags(Frags<S> &f) {
-    static_assert(S::TM <= 4 && S::TN <= 4, "wait_frags ties at most 4+4 fragments");
-    if constexpr (S::TM == 4 && S::TN == 4)
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
-                       "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
-    else if constexpr (S::TM == 4 && S::TN == 2)
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
-                       "+v"(f.b[1]));
-    else if constexpr (S::TM == 2 && S::TN == 4)
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]),
-                       "+v"(f.b[3]));
-    else if constexpr (S::TM == 2 && S::TN == 2)
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0]), "+v"(f.b[1]));
-    else if constexpr (S::TM == 2 && S::TN == 1)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0]));
-    else if constexpr (S::TM == 1 && S::TN == 1)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.a[0]), "+v"(f.b[0]));
-    else
-        static_assert(S::TM == 0, "unsupported fragment count");
+    asm volatile("s_waitcnt lgkmcnt(0)");
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm) asm volatile("" : "+v"(f.a[tm]));
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn) asm volatile("" : "+v"(f.b[tn]));
 }
 
 template <class S>
@@ -324,9 +302,17 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[S::TM][S::TN]) {
             for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.0f;
 }
 
-// Pipeline driver.  A "step sequence" is a run of K steps numbered
-// 0..total-1; `issue(t, stage)` loads sequence step t into an LDS stage (the
-// sequential variant chains two contractions into one sequence).
+// ---------------------------------------------------------------------------
+// Plain pipeline (4 waves, one per SIMD).  A "step sequence" is a run of K
+// steps numbered 0..total-1; `issue(t, stage)` loads sequence step t into an
+// LDS stage.  Before step t+1 is read, each wave waits until at most
+// STAGES-2 later steps' loads are outstanding, then the workgroup meets at
+// one barrier, which also proves that every wave has finished reading step
+// t's buffer; that buffer is refilled with step t+STAGES right after it.  The
+// barrier sits before the MFMAs of step t's last k-substep, so those MFMAs
+// overlap the first fragment reads of step t+1; within a step the reads of
+// substep ks+1 overlap the MFMAs of substep ks.
+// ---------------------------------------------------------------------------
 template <class S>
 struct Pipeline {
     SWIGLU_LDS char *lds;
@@ -349,7 +335,6 @@ struct Pipeline {
         off.init(wave / S::WN, wave % S::WN, lane);
     }
 
-    // Fill the ring with steps 0..STAGES-1, wait for step 0, read its first fragments.
     template <class Issue>
     __device__ __forceinline__ void prologue(const Issue &issue) {
 #pragma unroll
@@ -359,13 +344,11 @@ struct Pipeline {
         read_frags<S, 0>(stage_addr(0), off, f[0]);
     }
 
-    // Substeps KS..last of sequence step t (helper of step()).
     template <int KS, class Issue, class Hook>
     __device__ __forceinline__ void substeps(const Issue &issue, int t, int total,
                                              f32x16 (&acc)[S::TM][S::TN], const Hook &hook) {
         constexpr int last = S::kKSub - 1;
-        // keep the previous substep's MFMAs above this wait
-        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);   // keep the previous substep's MFMAs above this wait
         wait_frags<S>(f[KS & 1]);
         if constexpr (KS < last) {
             read_frags<S, KS + 1>(stage_addr(t), off, f[(KS + 1) & 1]);
@@ -384,10 +367,6 @@ struct Pipeline {
         }
     }
 
-    // One K step (sequence step t) into acc.  `hook(ks)` runs once per
-    // k-substep, next to that substep's MFMAs (the sequential variant uses it
-    // to activate the Gate accumulator while the Up MFMAs run); `total` is the
-    // length of the whole sequence (no barrier/refill after its last step).
     template <class Issue, class Hook>
     __device__ __forceinline__ void step(const Issue &issue, int t, int total,
                                          f32x16 (&acc)[S::TM][S::TN], const Hook &hook) {
@@ -395,20 +374,125 @@ struct Pipeline {
         substeps<0>(issue, t, total, acc, hook);
     }
 
-    // Sequence steps [t_begin, t_end) into acc.
     template <class Issue>
     __device__ __forceinline__ void run(const Issue &issue, int t_begin, int t_end, int total,
                                         f32x16 (&acc)[S::TM][S::TN]) {
         for (int t = t_begin; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
     }
 
-    // Drain: no load may still be writing LDS when the caller reuses it.
     __device__ __forceinline__ void drain() {
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         block_barrier();
     }
 };
+
+// ---------------------------------------------------------------------------
+// Ping-pong pipeline (8 waves, two per SIMD).  Waves 0-3 (group 0) and 4-7
+// (group 1) sit one per SIMD each and own the top and bottom halves of the
+// tile rows.  The two groups run the same phase sequence one barrier apart:
+// while one group runs the MFMA cluster of a K step, the other issues its
+// share of the next loads and reads all fragments of its next K step, so each
+// SIMD's MFMA pipe is fed by one of its two waves at any time.
+//
+// Per wave, for K step t:
+//   memory phase: read all fragments of step t; wait for them; wait for its
+//                 own loads of step t+1 (vmcnt <= L-1 groups, L = STAGES-1);
+//                 barrier.
+//   MFMA phase:   all MFMAs of step t; barrier.
+// Group 1 starts one barrier late.  Numbering barriers from the prologue's
+// (#1): group 0's memory phase t ends at #(2t+2) and its MFMA phase t at
+// #(2t+3); group 1's memory phase t ends at #(2t+3) and its MFMA phase at
+// #(2t+4).  Both groups issue their share of the loads of step t+L in the
+// same phase, so the two halves of a stage are in flight together: group 0
+// at the start of its memory phase t (after #(2t+1)), group 1 at the start of
+// its MFMA phase t-1 (also after #(2t+1); for t = 0, before its offset
+// barrier).  Hence
+//  - group 0 reads step t+1 after #(2t+3), when both groups have waited for
+//    their loads of step t+1 (group 1 at the end of its memory phase t);
+//  - the stage refilled with step t+L held step t-1, whose last reader
+//    (group 1, memory phase t-1) finished with lgkmcnt(0) before #(2t+1);
+//  - each wave has issued steps up to t+L when it waits for step t+1, so
+//    "at most L-1 groups outstanding" is exactly "step t+1 has landed".
+// Group 1 skips its last MFMA-phase barrier so both groups execute 2*nk+1
+// barriers.
+// ---------------------------------------------------------------------------
+template <class S>
+struct PingPong {
+    static constexpr int L = S::STAGES - 1;
+    SWIGLU_LDS char *lds;
+    uint32_t lds_addr;
+    int group;
+    FragOffsets<S> off;
+    Frags<S> F[S::kKSub];
+
+    __device__ __forceinline__ SWIGLU_LDS char *stage(int t) const {
+        return lds + (t % S::STAGES) * S::kStageBytes;
+    }
+    __device__ __forceinline__ uint32_t stage_addr(int t) const {
+        return lds_addr + static_cast<uint32_t>((t % S::STAGES) * S::kStageBytes);
+    }
+
+    __device__ __forceinline__ void init(SWIGLU_LDS char *lds_) {
+        lds = lds_;
+        lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_));
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        group = wave >> 2;
+        off.init(wave / S::WN, wave % S::WN, lane);
+    }
+
+    template <class Issue>
+    __device__ __forceinline__ void prologue(const Issue &issue) {
+#pragma unroll
+        for (int t = 0; t < L; ++t) issue(t, stage(t));
+        wait_vmcnt<S::kDmaPerStep * (L - 1)>();
+        block_barrier();
+        if (group == 1) {
+            issue(L, stage(L));
+            block_barrier();
+        }
+    }
+
+    template <int KS>
+    __device__ __forceinline__ void read_all(uint32_t st) {
+        read_frags<S, KS>(st, off, F[KS]);
+        if constexpr (KS + 1 < S::kKSub) read_all<KS + 1>(st);
+    }
+
+    template <class Issue, class Hook>
+    __device__ __forceinline__ void step(const Issue &issue, int t, int total,
+                                         f32x16 (&acc)[S::TM][S::TN], const Hook &hook) {
+        // memory phase
+        if (group == 0) issue(t + L, stage(t + L));
+        read_all<0>(stage_addr(t));
+#pragma unroll
+        for (int ks = 0; ks < S::kKSub; ++ks) wait_frags<S>(F[ks]);
+        wait_vmcnt<S::kDmaPerStep * (L - 1)>();
+        block_barrier();
+        // MFMA phase (group 1 first issues its share of step t+1+L)
+        if (group == 1) issue(t + 1 + L, stage(t + 1 + L));
+#pragma unroll
+        for (int ks = 0; ks < S::kKSub; ++ks) {
+            hook(ks);
+            mma<S>(F[ks], acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (!(group == 1 && t + 1 == total)) block_barrier();
+    }
+
+    template <class Issue>
+    __device__ __forceinline__ void run(const Issue &issue, int t_begin, int t_end, int total,
+                                        f32x16 (&acc)[S::TM][S::TN]) {
+        for (int t = t_begin; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
+    }
+
+    // No load may still be writing LDS when the wave ends or LDS is reused.
+    __device__ __forceinline__ void drain() { wait_vmcnt<0>(); }
+};
+
+template <class S>
+using PipelineFor = typename std::conditional<S::kPingPong, PingPong<S>, Pipeline<S>>::type;
 
 // Workgroup -> output tile.  Workgroups are dispatched round-robin over the
 // 8 XCDs (workgroup id mod 8); re-number them so that each XCD receives a

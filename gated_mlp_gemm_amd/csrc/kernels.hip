@@ -13,34 +13,46 @@ namespace swiglu {
 
 // ---------------------------------------------------------------------------
 // Weight packer [gist: Method, Kernel-2]: W_fused[k][2n] = W1[k][n],
-// W_fused[k][2n+1] = W2[k][n].  Each thread takes 8 columns of one row:
-// two 16-byte loads, two 16-byte stores; a pure 16-bit permutation.
+// W_fused[k][2n+1] = W2[k][n], stored column-major: column c of W_fused is
+// the K-contiguous row c of the [2N][K] array the MFMA loaders read.  One
+// workgroup transposes a 64(k) x 64(n) block of W1 and of W2 through LDS
+// (coalesced 16-byte loads of rows of W, coalesced 16-byte stores of rows of
+// the packed array).  A pure 16-bit permutation.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ W1,
                                                    const uint16_t *__restrict__ W2,
-                                                   uint16_t *__restrict__ Wf, int64_t K,
-                                                   int64_t N) {
-    const int64_t chunks_per_row = N / 8;
-    const int64_t total = K * chunks_per_row;
-    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t k = c / chunks_per_row;
-        const int64_t j = c - k * chunks_per_row;
-        const u32x4 g = gload16(W1 + k * N + j * 8);   // Gate columns 8j .. 8j+7
-        const u32x4 u = gload16(W2 + k * N + j * 8);   // Up   columns 8j .. 8j+7
-        u32x4 lo, hi;
-        // dword d of a row chunk holds columns (2d, 2d+1) as (low, high) halves
-        lo.x = (g.x & 0xFFFFu) | (u.x << 16);
-        lo.y = (g.x >> 16) | (u.x & 0xFFFF0000u);
-        lo.z = (g.y & 0xFFFFu) | (u.y << 16);
-        lo.w = (g.y >> 16) | (u.y & 0xFFFF0000u);
-        hi.x = (g.z & 0xFFFFu) | (u.z << 16);
-        hi.y = (g.z >> 16) | (u.z & 0xFFFF0000u);
-        hi.z = (g.w & 0xFFFFu) | (u.w << 16);
-        hi.w = (g.w >> 16) | (u.w & 0xFFFF0000u);
-        uint16_t *dst = Wf + k * 2 * N + j * 16;
-        gstore16(dst, lo);
-        gstore16(dst + 8, hi);
+                                                   uint16_t *__restrict__ Wf, int K, int N) {
+    constexpr int T = 64, PITCH = T + 8;   // row pitch 144 B keeps 16-byte alignment
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][T][PITCH];
+    const int k0 = blockIdx.y * T;
+    const int n0 = blockIdx.x * T;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const uint16_t *W = w == 0 ? W1 : W2;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + i * 256;           // chunk of the 64 x 64 block
+            const int row = c >> 3, cc = c & 7;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (k0 + row < K && n0 + cc * 8 < N)
+                v = gload16(W + (int64_t)(k0 + row) * N + n0 + cc * 8);
+            *reinterpret_cast<u32x4 *>(&tile[w][row][cc * 8]) = v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + i * 256;               // chunk of the 128 output rows x 64 k
+        const int orow = c >> 3, kc = c & 7;
+        const int j = orow >> 1, w = orow & 1;     // even rows: Gate (W1), odd rows: Up (W2)
+        if (n0 + j >= N || k0 + kc * 8 >= K) continue;
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = static_cast<uint32_t>(tile[w][kc * 8 + 2 * e][j]) |
+                   (static_cast<uint32_t>(tile[w][kc * 8 + 2 * e + 1][j]) << 16);
+        gstore16(Wf + (int64_t)(2 * (n0 + j) + w) * K + k0 + kc * 8, v);
     }
 }
 
@@ -101,16 +113,14 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_interleaved_kernel(
     int tm_, tn_;
     tile_coords(tiles_m, tiles_n, 8, tm_, tn_);
     const int m0 = tm_ * S::BM;
-    const int n0 = tn_ * S::BN;            // first W_fused column of the tile
+    const int n0 = tn_ * S::BN;            // first W_fused column (packed row) of the tile
     const int rows_valid = min(S::BM, M - m0);
-    const int ldb = 2 * N;
-
     const int nk = (K + S::BK - 1) / S::BK;
+
     TileLoader<S> ld;
-    ld.init(A + (int64_t)m0 * K, K, rows_valid, K, ldb);
-    const uint16_t *Bt = Wf + n0;
-    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, Bt, n0, st); };
-    Pipeline<S> pl;
+    ld.init(KMajor{A, M, 1, 0}, m0, KMajor{Wf, 2 * N, 1, 0}, n0, K);
+    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, st); };
+    PipelineFor<S> pl;
     pl.init(lds);
     f32x16 acc[S::TM][S::TN];
     zero_acc<S>(acc);
@@ -156,33 +166,33 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_interleaved_kernel(
 // ---------------------------------------------------------------------------
 template <class S>
 __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ W1,
-    const uint16_t *__restrict__ W2, uint16_t *__restrict__ Y, int M, int N, int K,
-    int tiles_m, int tiles_n) {
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, uint16_t *__restrict__ Y,
+    int M, int N, int K, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
 
     int tm_, tn_;
     tile_coords(tiles_m, tiles_n, 8, tm_, tn_);
     const int m0 = tm_ * S::BM;
-    const int n0 = tn_ * S::BN;
+    const int n0 = tn_ * S::BN;            // first output (Y) column of the tile
     const int rows_valid = min(S::BM, M - m0);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / S::WN, wn = wave % S::WN;
     const int nk = (K + S::BK - 1) / S::BK;
 
-    // One step sequence of 2*nk K steps: steps [0, nk) contract against W1,
-    // steps [nk, 2nk) against W2; the loads run ahead across the boundary.
+    // One step sequence of 2*nk K steps: steps [0, nk) contract against the
+    // Gate columns of W_fused (even packed rows), steps [nk, 2nk) against the
+    // Up columns (odd packed rows); the loads run ahead across the boundary.
     TileLoader<S> ld;
-    ld.init(A + (int64_t)m0 * K, K, rows_valid, K, N);
-    const uint16_t *B1 = W1 + n0;
-    const uint16_t *B2 = W2 + n0;
+    ld.init(KMajor{A, M, 1, 0}, m0, KMajor{Wf, N, 2, 0}, n0, K);
+    PanelLoader<S, S::BN, S::kDmaB> up;
+    up.init(KMajor{Wf, N, 2, 1}, n0, K);
     auto issue = [&](int t, SWIGLU_LDS char *st) {
-        if (t < nk) ld.issue(t, B1, n0, st);
-        else ld.issue(t - nk, B2, n0, st);   // t - nk >= nk loads nothing
+        if (t < nk) ld.issue(t, st);
+        else ld.issue(t - nk, st, up);   // t - nk >= nk loads nothing
     };
-    Pipeline<S> pl;
+    PipelineFor<S> pl;
     pl.init(lds);
     f32x16 g[S::TM][S::TN], u[S::TM][S::TN];
     zero_acc<S>(g);
@@ -246,8 +256,8 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
 // ---------------------------------------------------------------------------
 template <class S>
 __global__ __launch_bounds__(S::kThreads, 1) void gemm_store_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n) {
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, int phase,
+    uint16_t *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
 
@@ -256,13 +266,13 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_store_kernel(
     const int m0 = tm_ * S::BM;
     const int n0 = tn_ * S::BN;
     const int rows_valid = min(S::BM, M - m0);
-
     const int nk = (K + S::BK - 1) / S::BK;
+
+    // phase 0: Gate = A . W1 (even packed rows); phase 1: Up = A . W2 (odd rows)
     TileLoader<S> ld;
-    ld.init(A + (int64_t)m0 * K, K, rows_valid, K, N);
-    const uint16_t *Bt = B + n0;
-    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, Bt, n0, st); };
-    Pipeline<S> pl;
+    ld.init(KMajor{A, M, 1, 0}, m0, KMajor{Wf, N, 2, phase}, n0, K);
+    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, st); };
+    PipelineFor<S> pl;
     pl.init(lds);
     f32x16 acc[S::TM][S::TN];
     zero_acc<S>(acc);
@@ -292,8 +302,8 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_store_kernel(
 // ---------------------------------------------------------------------------
 // Tile shapes and launchers
 // ---------------------------------------------------------------------------
-using ShapeWide = TileShape<256, 256, 32, 2, 4, 4>;    // I and ablation GEMM
-using ShapeSeq = TileShape<256, 128, 32, 4, 2, 4>;     // S: two 256x128 accumulators
+using ShapeWide = TileShape<256, 256, 32, 2, 4, 4>;    // I and ablation GEMM (ping-pong)
+using ShapeSeq = TileShape<256, 128, 64, 4, 2, 3>;     // S: two 256x128 accumulators (ping-pong)
 using ShapeSmall = TileShape<128, 64, 32, 2, 2, 4>;    // M <= 128: more tiles on the weights
 
 static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
@@ -309,10 +319,8 @@ static hipError_t launch_tiles(Kern kernel, int M, int cols, hipStream_t stream,
 
 hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,
                        int64_t N, hipStream_t stream) {
-    const int64_t total = K * (N / 8);
-    const int64_t blocks = (total + 255) / 256;
-    const int grid = static_cast<int>(blocks < 65536 ? blocks : 65536);
-    hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, stream, W1, W2, Wf, K, N);
+    const dim3 grid(cdiv(N, 64), cdiv(K, 64));
+    hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, W1, W2, Wf, (int)K, (int)N);
     return hipGetLastError();
 }
 
@@ -334,21 +342,22 @@ hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint1
                                    Wf, Y, M, N, K);
 }
 
-hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
-                                   uint16_t *Y, int M, int N, int K, hipStream_t stream) {
+hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
+                                   int N, int K, hipStream_t stream) {
     if (M <= 128)
-        return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, A,
-                                        W1, W2, Y, M, N, K);
-    return launch_tiles<ShapeSeq>(fused_sequential_kernel<ShapeSeq>, M, N, stream, A, W1, W2,
-                                  Y, M, N, K);
+        return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, A, Wf,
+                                        Y, M, N, K);
+    return launch_tiles<ShapeSeq>(fused_sequential_kernel<ShapeSeq>, M, N, stream, A, Wf, Y, M,
+                                  N, K);
 }
 
-hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N,
-                             int K, hipStream_t stream) {
+hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
+                             int M, int N, int K, hipStream_t stream) {
     if (M <= 128)
-        return launch_tiles<ShapeSmall>(gemm_store_kernel<ShapeSmall>, M, N, stream, A, B, C, M,
-                                        N, K);
-    return launch_tiles<ShapeWide>(gemm_store_kernel<ShapeWide>, M, N, stream, A, B, C, M, N, K);
+        return launch_tiles<ShapeSmall>(gemm_store_kernel<ShapeSmall>, M, N, stream, A, Wf,
+                                        phase, C, M, N, K);
+    return launch_tiles<ShapeWide>(gemm_store_kernel<ShapeWide>, M, N, stream, A, Wf, phase, C,
+                                   M, N, K);
 }
 
 int64_t max_tiles(int64_t M, int64_t cols) {

@@ -14,10 +14,11 @@ hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, in
                            hipStream_t stream);
 hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
                                     int N, int K, hipStream_t stream);
-hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
-                                   uint16_t *Y, int M, int N, int K, hipStream_t stream);
-hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N,
-                             int K, hipStream_t stream);
+hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
+                                   int N, int K, hipStream_t stream);
+// phase 0: C = A . W1 (Gate columns of W_fused), phase 1: C = A . W2 (Up columns)
+hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
+                             int M, int N, int K, hipStream_t stream);
 // Largest workgroup count any launcher uses for an M x cols output tile grid.
 int64_t max_tiles(int64_t M, int64_t cols);
 

@@ -56,8 +56,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.swiglu_pack_weights.argtypes = [P, P, P, I64, I64, P]
-    lib.swiglu_fused_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P]
-    lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
+    lib.swiglu_fused_gemm.argtypes = [P, P, P, I64, I64, I64, I32, P]
+    lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.swiglu_silu_mul.argtypes = [P, P, P, I64, P]
     lib.swiglu_select_variant.argtypes = [I64, I64, I64]
     lib.swiglu_m_switch.argtypes = []
@@ -114,62 +114,53 @@ def _stream(device) -> int:
 # ---------------------------------------------------------------------------
 def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor,
                         W_fused: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """W_fused[:, 0::2] = W1, W_fused[:, 1::2] = W2 (on the GPU)."""
+    """Pack W1, W2 [K, N] into W_fused, returned as its [2N, K] storage.
+
+    Row c of the result is column c of the interleaved K x 2N matrix:
+    rows 0, 2, 4, ... are the columns of W1 (Gate), rows 1, 3, ... those of W2.
+    """
     lib = load_library()
     K, N = W1.shape
     _dev_tensor(W1, "W1", (K, N))
     _dev_tensor(W2, "W2", (K, N))
     if W_fused is None:
-        W_fused = torch.empty((K, 2 * N), dtype=torch.bfloat16, device=W1.device)
-    _dev_tensor(W_fused, "W_fused", (K, 2 * N))
+        W_fused = torch.empty((2 * N, K), dtype=torch.bfloat16, device=W1.device)
+    _dev_tensor(W_fused, "W_fused", (2 * N, K))
     with torch.cuda.device(W1.device):
         _check(lib.swiglu_pack_weights(_ptr(W1), _ptr(W2), _ptr(W_fused), K, N,
                                        _stream(W1.device)), "swiglu_pack_weights")
     return W_fused
 
 
-def swiglu_fused_gemm(A: torch.Tensor, W1: Optional[torch.Tensor] = None,
-                      W2: Optional[torch.Tensor] = None,
-                      W_fused: Optional[torch.Tensor] = None,
-                      Y: Optional[torch.Tensor] = None,
-                      variant="auto") -> torch.Tensor:
-    """Y = bf16(SiLU(A.W1) * (A.W2)); variant 'auto' | 's' | 'i' (or the enum)."""
+def swiglu_fused_gemm(A: torch.Tensor, W_fused: torch.Tensor,
+                      Y: Optional[torch.Tensor] = None, variant="auto") -> torch.Tensor:
+    """Y = bf16(SiLU(A.W1) * (A.W2)) from the packed weight; variant 'auto' | 's' | 'i'."""
     lib = load_library()
     v = VARIANTS[variant.lower()] if isinstance(variant, str) else int(variant)
     M, K = A.shape
     _dev_tensor(A, "A", (M, K))
-    if W_fused is not None:
-        N = W_fused.shape[1] // 2
-        _dev_tensor(W_fused, "W_fused", (K, 2 * N))
-    elif W1 is not None:
-        N = W1.shape[1]
-    else:
-        raise ValueError("need W1/W2 or W_fused")
-    if W1 is not None:
-        _dev_tensor(W1, "W1", (K, N))
-    if W2 is not None:
-        _dev_tensor(W2, "W2", (K, N))
+    N = W_fused.shape[0] // 2
+    _dev_tensor(W_fused, "W_fused", (2 * N, K))
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _dev_tensor(Y, "Y", (M, N))
     with torch.cuda.device(A.device):
-        _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W1), _ptr(W2), _ptr(W_fused), _ptr(Y),
-                                     M, N, K, v, _stream(A.device)), "swiglu_fused_gemm")
+        _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W_fused), _ptr(Y), M, N, K, v,
+                                     _stream(A.device)), "swiglu_fused_gemm")
     return Y
 
 
-def swiglu_unfused_ablation(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,
+def swiglu_unfused_ablation(A: torch.Tensor, W_fused: torch.Tensor,
                             gate_ws: Optional[torch.Tensor] = None,
                             up_ws: Optional[torch.Tensor] = None,
                             Y: Optional[torch.Tensor] = None
                             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Two GEMMs + SiLU-mul; returns (Y, gate_ws, up_ws)."""
+    """Two GEMMs + SiLU-mul from the packed weight; returns (Y, gate_ws, up_ws)."""
     lib = load_library()
     M, K = A.shape
-    N = W1.shape[1]
+    N = W_fused.shape[0] // 2
     _dev_tensor(A, "A", (M, K))
-    _dev_tensor(W1, "W1", (K, N))
-    _dev_tensor(W2, "W2", (K, N))
+    _dev_tensor(W_fused, "W_fused", (2 * N, K))
     outs = []
     for name, t in (("gate_ws", gate_ws), ("up_ws", up_ws), ("Y", Y)):
         if t is None:
@@ -177,9 +168,9 @@ def swiglu_unfused_ablation(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,
         outs.append(_dev_tensor(t, name, (M, N)))
     gate_ws, up_ws, Y = outs
     with torch.cuda.device(A.device):
-        _check(lib.swiglu_unfused_ablation(_ptr(A), _ptr(W1), _ptr(W2), _ptr(gate_ws),
-                                           _ptr(up_ws), _ptr(Y), M, N, K,
-                                           _stream(A.device)), "swiglu_unfused_ablation")
+        _check(lib.swiglu_unfused_ablation(_ptr(A), _ptr(W_fused), _ptr(gate_ws), _ptr(up_ws),
+                                           _ptr(Y), M, N, K, _stream(A.device)),
+               "swiglu_unfused_ablation")
     return Y, gate_ws, up_ws
 
 

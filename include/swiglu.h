@@ -11,9 +11,10 @@
  *
  * Conventions shared by every call
  * --------------------------------
- *  - Every matrix is bf16, passed as its 16-bit patterns (uint16_t),
- *    row-major and contiguous: A [M][K], W1 and W2 [K][N],
- *    W_fused [K][2N], Y / gate_ws / up_ws [M][N].
+ *  - Every matrix is bf16, passed as its 16-bit patterns (uint16_t), dense
+ *    and contiguous: A [M][K], W1 and W2 [K][N], Y / gate_ws / up_ws [M][N]
+ *    row-major; the packed weight W_fused (K x 2N) column-major, i.e. a
+ *    row-major [2N][K] array whose row c is column c of W_fused.
  *  - Every matrix pointer is a DEVICE pointer, allocated and owned by the
  *    caller.  The library allocates, frees and retains nothing: no pointer is
  *    kept past the call.
@@ -24,7 +25,7 @@
  *  - Arguments are validated before any HIP call: an invalid call launches
  *    nothing and returns a negative swiglu_status.  Preconditions:
  *      M >= 0, N >= 0, K >= 8;  K % 8 == 0 and N % 8 == 0 (each row is a
- *      whole number of 16-byte chunks);  M <= 2^31 - 1, K <= 2^22,
+ *      whole number of 16-byte chunks);  M <= 2^31 - 1, K <= 2^21,
  *      N <= 2^23;
  *      every pointer 16-byte aligned;  outputs do not overlap inputs or
  *      each other.
@@ -33,7 +34,7 @@
  *    round-to-nearest-even to bf16 at the end; the accumulation order is not
  *    specified (results of different variants need not be bitwise equal).
  *  - Calls are re-entrant; the only global state is a per-device cache of
- *    the device's architecture and compute-unit count.
+ *    the device's architecture.
  *  - The code object targets gfx950 only: on another device every launching
  *    call returns SWIGLU_ERR_UNSUPPORTED.
  */
@@ -69,33 +70,36 @@ typedef enum swiglu_variant {
  *
  *     W_fused[k][2n] = W1[k][n],   W_fused[k][2n+1] = W2[k][n]   (0-based)
  *
- * W1, W2: [K][N] device, read only.  W_fused: [K][2N] device, written.
+ * W_fused is stored column-major: the output is the row-major [2N][K] array
+ * P with P[2n][k] = W1[k][n] and P[2n+1][k] = W2[k][n], so both operands of
+ * every contraction are K-contiguous (the layout the MFMA loaders read).
+ * W1, W2: [K][N] device, read only.  W_fused: 2N*K elements, device, written.
  * A pure copy of 16-bit patterns (bit-exact).  Done once per weight set, off
- * the timed path.  K >= 0 here (K == 0 is an empty problem).
+ * the timed path.  K >= 0 here (K == 0 or N == 0 is an empty problem); the
+ * other preconditions above apply (K % 8 == 0 and N % 8 == 0: both are row
+ * lengths here).
  */
 int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2,
                         uint16_t *W_fused, int64_t K, int64_t N, void *stream);
 
 /*
- * The fused SwiGLU GEMM, Y = bf16( SiLU(A.W1) * (A.W2) ).
+ * The fused SwiGLU GEMM, Y = bf16( SiLU(A.W1) * (A.W2) ), from the packed
+ * weight (swiglu_pack_weights).  Gate and Up never leave registers.
  *
  * variant SWIGLU_VARIANT_I (the pages' Kernel-2; gist.science technical
- *   summary, Method, Kernel-2): one GEMM over W_fused [K][2N]; its epilogue
- *   pairs accumulator columns 2n (Gate) and 2n+1 (Up) and stores
- *   SiLU(D[m][2n]) * D[m][2n+1].  Reads A and W_fused; W1, W2 may be NULL.
+ *   summary, Method, Kernel-2): one GEMM over all 2N columns of W_fused; its
+ *   epilogue pairs accumulator columns 2n (Gate) and 2n+1 (Up) and stores
+ *   SiLU(D[m][2n]) * D[m][2n+1].
  * variant SWIGLU_VARIANT_S (the pages' Kernel-1; paper abstract and
  *   gist.science technical summary, Method, Kernel-1): per output tile, the
- *   Gate contraction, then SiLU on the register-resident Gate accumulator
- *   while the first Up tiles are loaded, then the Up contraction and a
- *   multiply-and-store epilogue.  Reads A, W1, W2; W_fused may be NULL.
- * variant SWIGLU_AUTO: whichever swiglu_select_variant(M, N, K) names; the
- *   weights that variant reads must be non-NULL.
+ *   Gate contraction (even columns), then SiLU on the register-resident Gate
+ *   accumulator interleaved with the first Up steps while the Up tiles load,
+ *   then the Up contraction (odd columns) and a multiply-and-store epilogue.
+ * variant SWIGLU_AUTO: whichever swiglu_select_variant(M, N, K) names.
  *
- * A: [M][K], Y: [M][N] device.  Returns SWIGLU_ERR_NULL if a pointer the
- * selected variant reads is NULL.
+ * A: [M][K], W_fused: packed [2N][K], Y: [M][N]; device pointers.
  */
-int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W1,
-                      const uint16_t *W2, const uint16_t *W_fused, uint16_t *Y,
+int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
                       int64_t M, int64_t N, int64_t K, int variant,
                       void *stream);
 
@@ -103,17 +107,16 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W1,
  * The unfused pipeline, kept as an ablation so the saved memory traffic can be
  * measured (paper text, section 1: the unfused form materialises two full
  * intermediate tensors, Gate and Up, between the GEMM and activation stages).
- * Three stream-ordered launches built from the same mainloop as the fused
- * kernels:
+ * Three stream-ordered launches built from the same mainloop, and the same
+ * packed weight, as the fused kernels:
  *     gate_ws = bf16(A.W1);  up_ws = bf16(A.W2);
  *     Y = bf16( SiLU(gate_ws) * up_ws )   (fp32 arithmetic, one rounding)
  * gate_ws, up_ws: caller-owned [M][N] device workspaces, written (their
  * contents are part of the result and may be inspected).
  */
-int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W1,
-                            const uint16_t *W2, uint16_t *gate_ws,
-                            uint16_t *up_ws, uint16_t *Y, int64_t M, int64_t N,
-                            int64_t K, void *stream);
+int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused,
+                            uint16_t *gate_ws, uint16_t *up_ws, uint16_t *Y,
+                            int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
  * The ablation's activation stage on its own: Y[i] = bf16(SiLU(gate[i]) *

@@ -55,8 +55,8 @@ def test_dispatcher_thresholds(lib, monkeypatch):
     assert sw.swiglu_m_switch() == 2048
 
 
-def fused(lib, A=A_, W1=W1_, W2=W2_, WF=WF_, Y=Y_, M=256, N=256, K=256, v=2):
-    return lib.swiglu_fused_gemm(A, W1, W2, WF, Y, M, N, K, v, None)
+def fused(lib, A=A_, WF=WF_, Y=Y_, M=256, N=256, K=256, v=2):
+    return lib.swiglu_fused_gemm(A, WF, Y, M, N, K, v, None)
 
 
 def test_fused_validation(lib):
@@ -67,36 +67,32 @@ def test_fused_validation(lib):
     assert fused(lib, K=4) == ERR_SHAPE
     assert fused(lib, K=20) == ERR_SHAPE          # not a multiple of 8
     assert fused(lib, N=12) == ERR_SHAPE
-    assert fused(lib, K=(1 << 22) + 8) == ERR_SHAPE
+    assert fused(lib, K=(1 << 21) + 8) == ERR_SHAPE
     assert fused(lib, N=(1 << 23) + 8) == ERR_SHAPE
     assert fused(lib, M=1 << 31) == ERR_SHAPE
     # variant
     assert fused(lib, v=3) == ERR_UNSUP
     assert fused(lib, v=-1) == ERR_UNSUP
-    # null pointers, per variant
-    assert fused(lib, A=None) == ERR_NULL
-    assert fused(lib, Y=None) == ERR_NULL
-    assert fused(lib, WF=None, v=2) == ERR_NULL          # I reads W_fused
-    assert fused(lib, W1=None, v=1) == ERR_NULL          # S reads W1 and W2
-    assert fused(lib, W2=None, v=1) == ERR_NULL
-    assert fused(lib, WF=None, M=100, v=0) == ERR_NULL   # AUTO -> I at M=100
-    assert fused(lib, W1=None, M=4096, v=0) == ERR_NULL  # AUTO -> S at M=4096
+    # null pointers, every variant
+    for v in (0, 1, 2):
+        assert fused(lib, A=None, v=v) == ERR_NULL
+        assert fused(lib, Y=None, v=v) == ERR_NULL
+        assert fused(lib, WF=None, v=v) == ERR_NULL
     # alignment
     assert fused(lib, A=A_ + 2) == ERR_ALIGN
     assert fused(lib, Y=Y_ + 8) == ERR_ALIGN
-    assert fused(lib, WF=WF_ + 4, v=2) == ERR_ALIGN
-    assert fused(lib, W1=W1_ + 2, v=1) == ERR_ALIGN
-    # aliasing: Y inside A, Y inside W_fused, Y overlapping W2
+    assert fused(lib, WF=WF_ + 4, v=1) == ERR_ALIGN
+    # aliasing: Y inside A, Y inside W_fused (whose extent is 2*N*K elements)
     assert fused(lib, Y=A_ + 1024) == ERR_ALIAS
     assert fused(lib, Y=WF_ + 4096, v=2) == ERR_ALIAS
-    assert fused(lib, Y=W2_ + 16, v=1) == ERR_ALIAS
+    assert fused(lib, Y=WF_ + 2 * 256 * 256 * 2 - 16, v=1) == ERR_ALIAS
     assert "overlaps" in sw.swiglu_last_error()
 
 
 def test_empty_problems_succeed_without_pointers(lib):
-    assert lib.swiglu_fused_gemm(None, None, None, None, None, 0, 256, 64, 0, None) == 0
-    assert lib.swiglu_fused_gemm(None, None, None, None, None, 64, 0, 64, 0, None) == 0
-    assert lib.swiglu_unfused_ablation(None, None, None, None, None, None, 0, 64, 64, None) == 0
+    assert lib.swiglu_fused_gemm(None, None, None, 0, 256, 64, 0, None) == 0
+    assert lib.swiglu_fused_gemm(None, None, None, 64, 0, 64, 0, None) == 0
+    assert lib.swiglu_unfused_ablation(None, None, None, None, None, 0, 64, 64, None) == 0
     assert lib.swiglu_pack_weights(None, None, None, 0, 64, None) == 0
     assert lib.swiglu_pack_weights(None, None, None, 64, 0, None) == 0
     assert lib.swiglu_silu_mul(None, None, None, 0, None) == 0
@@ -107,6 +103,8 @@ def test_pack_validation(lib):
     P = lib.swiglu_pack_weights
     assert P(W1_, W2_, WF_, -1, 8, None) == ERR_SHAPE
     assert P(W1_, W2_, WF_, 8, 12, None) == ERR_SHAPE
+    assert P(W1_, W2_, WF_, 12, 8, None) == ERR_SHAPE     # K is the packed row length
+    assert P(W1_, W2_, WF_, 1, 8, None) == ERR_SHAPE
     assert P(None, W2_, WF_, 8, 8, None) == ERR_NULL
     assert P(W1_, W2_, None, 8, 8, None) == ERR_NULL
     assert P(W1_ + 2, W2_, WF_, 8, 8, None) == ERR_ALIGN
@@ -115,19 +113,21 @@ def test_pack_validation(lib):
 
 def test_ablation_validation(lib):
     F = lib.swiglu_unfused_ablation
-    ok = dict(A=A_, W1=W1_, W2=W2_, G=G_, U=U_, Y=Y_)
+    ok = dict(A=A_, WF=WF_, G=G_, U=U_, Y=Y_)
 
     def call(**kw):
         a = {**ok, **kw}
-        return F(a["A"], a["W1"], a["W2"], a["G"], a["U"], a["Y"], 256, 256, 256, None)
+        return F(a["A"], a["WF"], a["G"], a["U"], a["Y"], 256, 256, 256, None)
 
     assert call(G=None) == ERR_NULL
     assert call(U=None) == ERR_NULL
+    assert call(WF=None) == ERR_NULL
     assert call(G=G_ + 2) == ERR_ALIGN
     assert call(U=G_ + 1024) == ERR_ALIAS        # two outputs overlap
     assert call(Y=U_ + 16) == ERR_ALIAS
-    assert call(G=W1_ + 64) == ERR_ALIAS         # output inside an input
-    assert F(A_, W1_, W2_, G_, U_, Y_, 256, 20, 256, None) == ERR_SHAPE
+    assert call(G=WF_ + 64) == ERR_ALIAS         # output inside an input
+    assert call(G=A_ + 64) == ERR_ALIAS
+    assert F(A_, WF_, G_, U_, Y_, 256, 20, 256, None) == ERR_SHAPE
 
 
 def test_silu_mul_validation(lib):

@@ -69,8 +69,8 @@ def assert_parity(y_bits, ref_bits, what: str):
     return rep
 
 
-def run_fused(A, W1, W2, Wf, variant):
-    Y = sw.swiglu_fused_gemm(A, W1, W2, Wf, variant=variant)
+def run_fused(A, Wf, variant):
+    Y = sw.swiglu_fused_gemm(A, Wf, variant=variant)
     torch.cuda.synchronize()
     return Y
 
@@ -78,7 +78,7 @@ def run_fused(A, W1, W2, Wf, variant):
 # ---------------------------------------------------------------------------
 # pack
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("K,N", [(1, 8), (3, 24), (100, 1000), (896, 4864)])
+@pytest.mark.parametrize("K,N", [(8, 8), (24, 24), (104, 1000), (72, 136), (896, 4864)])
 def test_pack_bit_exact(dev, orc, K, N):
     announce(f"pack K={K} N={N}")
     rng = np.random.default_rng(K * 7919 + N)
@@ -86,7 +86,8 @@ def test_pack_bit_exact(dev, orc, K, N):
     W2 = rng.integers(0, 2 ** 16, size=(K, N), dtype=np.uint16)
     Wf = sw.swiglu_pack_weights(inputs.from_bits(W1).to(dev), inputs.from_bits(W2).to(dev))
     torch.cuda.synchronize()
-    assert np.array_equal(bits_of(Wf), orc.pack(W1, W2))
+    # the packed storage is W_fused column-major: its row c is column c
+    assert np.array_equal(bits_of(Wf).T, orc.pack(W1, W2))
 
 
 # ---------------------------------------------------------------------------
@@ -104,7 +105,7 @@ def test_small_shapes(dev, orc, M, K, N, variant):
     ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
     Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
     Wf = sw.swiglu_pack_weights(W1d, W2d)
-    Y = run_fused(Ad, W1d, W2d, Wf, variant)
+    Y = run_fused(Ad, Wf, variant)
     assert_parity(bits_of(Y), ref, f"{variant} {M}x{K}x{N}")
 
 
@@ -136,7 +137,7 @@ def test_hand_cases_padded(dev, orc, variant):
         W2t = torch.from_numpy(_pad(case["W2"], Kp, Np)).to(torch.bfloat16)
         ref = orc.swiglu(inputs.bits(At), inputs.bits(W1t), inputs.bits(W2t))
         Ad, W1d, W2d = At.to(dev), W1t.to(dev), W2t.to(dev)
-        Y = run_fused(Ad, W1d, W2d, sw.swiglu_pack_weights(W1d, W2d), variant)
+        Y = run_fused(Ad, sw.swiglu_pack_weights(W1d, W2d), variant)
         yb = bits_of(Y)
         assert_parity(yb, ref, case["name"])
         # the padded columns are exactly zero (Up = 0)
@@ -154,7 +155,7 @@ def test_saturating_gates(dev, orc):
     assert (G < -30).any() and (G > 30).any(), "inputs must reach the saturated regions"
     for variant in ("i", "s"):
         announce(f"saturating gates variant {variant}")
-        Y = run_fused(Ad, W1d, W2d, Wf, variant)
+        Y = run_fused(Ad, Wf, variant)
         yb = bits_of(Y)
         assert_parity(yb, ref, f"saturating {variant}")
         assert not np.isnan(oracle_pkg.bf16_bits_to_f64(yb)).any()
@@ -198,7 +199,7 @@ def test_workload_full_size(dev, orc, workload, variant):
     w = d["w"]
     ref_rows, ref_pts = _ref_samples(orc, d)
     announce(f"fused {variant} {w.name}")
-    Y = run_fused(d["A"], d["W1"], d["W2"], d["Wf"], variant)
+    Y = run_fused(d["A"], d["Wf"], variant)
     yb = bits_of(Y)
     assert_parity(yb[d["rows"]], ref_rows, f"{variant} {w.name} rows {list(d['rows'])}")
     assert_parity(yb[d["pr"], d["pc"]], ref_pts, f"{variant} {w.name} points")
@@ -223,9 +224,10 @@ def test_workload_pack(dev, orc, workload):
     d = workload
     announce(f"pack check {d['w'].name}")
     K, N = d["w"].K, d["w"].N
-    rows = np.unique(np.array([0, K // 3, K - 1]))
-    wf = bits_of(d["Wf"][torch.as_tensor(rows, device=dev)])
-    assert np.array_equal(wf, orc.pack(d["hW1"][rows], d["hW2"][rows]))
+    cols = np.unique(np.array([0, 1, N // 3, N - 2, N - 1]))
+    packed_rows = np.stack([2 * cols, 2 * cols + 1], axis=1).reshape(-1)
+    got = bits_of(d["Wf"][torch.as_tensor(packed_rows, device=dev)]).T
+    assert np.array_equal(got, orc.pack(d["hW1"][:, cols], d["hW2"][:, cols]))
 
 
 # ---------------------------------------------------------------------------
@@ -248,8 +250,8 @@ def _intermediate_within_bound(orc, a_bits, w_bits, got_bits, what):
 
 
 def _check_ablation(orc, A, W1, W2, rows, dev, what):
-    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
-    Y, g, u = sw.swiglu_unfused_ablation(Ad, W1d, W2d)
+    Ad = A.to(dev)
+    Y, g, u = sw.swiglu_unfused_ablation(Ad, sw.swiglu_pack_weights(W1.to(dev), W2.to(dev)))
     torch.cuda.synchronize()
     sub = inputs.bits(A)[rows]
     hW1, hW2 = inputs.bits(W1), inputs.bits(W2)
@@ -306,11 +308,11 @@ def test_determinism(dev):
     A, W1, W2 = (t.to(dev) for t in inputs.workload_inputs(w))
     Wf = sw.swiglu_pack_weights(W1, W2)
     for variant in ("i", "s"):
-        y1 = run_fused(A, W1, W2, Wf, variant).clone()
-        y2 = run_fused(A, W1, W2, Wf, variant)
+        y1 = run_fused(A, Wf, variant).clone()
+        y2 = run_fused(A, Wf, variant)
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), variant
-    Y1, g1, u1 = sw.swiglu_unfused_ablation(A, W1, W2)
-    Y2, g2, u2 = sw.swiglu_unfused_ablation(A, W1, W2)
+    Y1, g1, u1 = sw.swiglu_unfused_ablation(A, Wf)
+    Y2, g2, u2 = sw.swiglu_unfused_ablation(A, Wf)
     torch.cuda.synchronize()
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
 
@@ -321,8 +323,8 @@ def test_auto_dispatch_matches_named_variant(dev, M, expect, monkeypatch):
     announce(f"dispatch M={M}")
     A, W1, W2 = (t.to(dev) for t in inputs.make_inputs(M, 64, 64, seed=M))
     Wf = sw.swiglu_pack_weights(W1, W2)
-    ya = run_fused(A, W1, W2, Wf, "auto")
-    yv = run_fused(A, W1, W2, Wf, expect)
+    ya = run_fused(A, Wf, "auto")
+    yv = run_fused(A, Wf, expect)
     assert torch.equal(ya.view(torch.int16), yv.view(torch.int16))
 
 
@@ -335,8 +337,8 @@ def test_non_default_stream(dev, orc):
     with torch.cuda.stream(s):
         Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
         Wf = sw.swiglu_pack_weights(W1d, W2d)
-        Yi = sw.swiglu_fused_gemm(Ad, W1d, W2d, Wf, variant="i")
-        Ys = sw.swiglu_fused_gemm(Ad, W1d, W2d, Wf, variant="s")
+        Yi = sw.swiglu_fused_gemm(Ad, Wf, variant="i")
+        Ys = sw.swiglu_fused_gemm(Ad, Wf, variant="s")
     s.synchronize()
     assert_parity(bits_of(Yi), ref, "stream i")
     assert_parity(bits_of(Ys), ref, "stream s")
@@ -344,10 +346,9 @@ def test_non_default_stream(dev, orc):
 
 def test_empty_and_invalid_on_device(dev):
     A = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
-    W = torch.empty((64, 64), dtype=torch.bfloat16, device=dev)
-    Y = sw.swiglu_fused_gemm(A, W, W, sw.swiglu_pack_weights(W, W))
+    W = torch.zeros((64, 64), dtype=torch.bfloat16, device=dev)
+    Y = sw.swiglu_fused_gemm(A, sw.swiglu_pack_weights(W, W))
     assert Y.shape == (0, 64)
-    with pytest.raises(sw.SwigluError):
+    with pytest.raises(sw.SwigluError):      # K = 20 is not a multiple of 8
         sw.swiglu_fused_gemm(torch.empty((8, 20), dtype=torch.bfloat16, device=dev),
-                             torch.empty((20, 64), dtype=torch.bfloat16, device=dev),
-                             torch.empty((20, 64), dtype=torch.bfloat16, device=dev))
+                             torch.empty((128, 20), dtype=torch.bfloat16, device=dev))

@@ -110,17 +110,20 @@ def main():
     outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
     abl_ws = [(torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(R)]
+    # scratch for the split-tail schedule (one per path, reused by every step)
+    scratch = {v: sw.make_workspace(M, N, K, v, dev) for v in ("auto", "i", "s", "ablation")}
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
     def fused_step(s, variant):
         a, wf = copies[s % R]
-        sw.swiglu_fused_gemm(a, wf, Y=outs[s % R], variant=variant)
+        sw.swiglu_fused_gemm(a, wf, Y=outs[s % R], variant=variant, workspace=scratch[variant])
 
     def ablation_step(s):
         a, wf = copies[s % R]
         g, u = abl_ws[s % R]
-        sw.swiglu_unfused_ablation(a, wf, gate_ws=g, up_ws=u, Y=outs[s % R])
+        sw.swiglu_unfused_ablation(a, wf, gate_ws=g, up_ws=u, Y=outs[s % R],
+                                   workspace=scratch["ablation"])
 
     def timed(step_fn, steps, warmup):
         for s in range(warmup):
@@ -151,7 +154,8 @@ def main():
     ams, _ = timed(ablation_step, args.steps, args.warmup)
     per["ablation"] = {"ms": ams, "tflops": flops / (ams * 1e-3) / 1e12}
     # warm (one copy, cache-resident where it fits) for context
-    wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, Wf, Y=outs[0], variant=args.variant),
+    wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, Wf, Y=outs[0], variant=args.variant,
+                                                  workspace=scratch[args.variant]),
                    args.steps, args.warmup)
     for k, v in per.items():
         print(f"[bench] {k}: {v['ms'] * 1e3:.1f} us, {v['tflops']:.1f} TFLOP/s",
@@ -164,7 +168,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    kernel = "fused_interleaved_kernel" if vname == "i" else "fused_sequential_kernel"
+    kernel = "gemm_tiles_kernel<PairMulEpilogue>" if vname == "i" else "fused_sequential_kernel"
     workload = f"M={M},K={K},N={N}"
     roofline = {
         "bound": "mfma",
@@ -227,6 +231,8 @@ def main():
             "M": M, "K": K, "N": N,
             "variant": f"{args.variant}->{vname}",
             "rotation_copies": R,
+            "workspace_bytes": int(scratch[args.variant].numel()) if scratch[args.variant]
+            is not None else 0,
         },
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "speedup_vs_ablation": round(per["ablation"]["ms"] / ms, 4),

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "launch.hpp"
@@ -35,7 +36,7 @@ int ok() {
 
 constexpr int64_t kMaxM = 2147483647;     // 2^31 - 1
 constexpr int64_t kMaxK = int64_t(1) << 21;
-constexpr int64_t kMaxN = int64_t(1) << 23;
+constexpr int64_t kMaxN = int64_t(1) << 22;
 constexpr int64_t kDefaultMSwitch = 2048;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -51,17 +52,20 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
     if (K % 8 != 0 || N % 8 != 0)
         return fail(SWIGLU_ERR_SHAPE, "K=%lld and N=%lld must be multiples of 8", (long long)K, (long long)N);
     if (M > kMaxM || K > kMaxK || N > kMaxN)
-        return fail(SWIGLU_ERR_SHAPE, "size beyond limits (M<=2^31-1, K<=2^21, N<=2^23)");
+        return fail(SWIGLU_ERR_SHAPE, "size beyond limits (M<=2^31-1, K<=2^21, N<=2^22)");
     if (swiglu::max_tiles(M, 2 * N) > 2147483647)
         return fail(SWIGLU_ERR_SHAPE, "tile grid too large");
     return SWIGLU_OK;
 }
 
-// Per-device cache: 1 = gfx950, -1 = other architecture, 0 = not yet queried.
+// Per-device cache: state 1 = gfx950, -1 = other architecture, 0 = not yet
+// queried; and the device's compute-unit count (sizes the split-tail schedule).
 std::mutex g_dev_mutex;
 int g_dev_state[256];
+int g_dev_cus[256];
 
-int check_device() {
+
+int check_device(int *cus = nullptr) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(SWIGLU_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -73,9 +77,25 @@ int check_device() {
         if (e != hipSuccess)
             return fail(SWIGLU_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
         g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_dev_cus[dev] = prop.multiProcessorCount;
     }
     if (g_dev_state[dev] != 1)
         return fail(SWIGLU_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+    if (cus) *cus = g_dev_cus[dev];
+    return SWIGLU_OK;
+}
+
+swiglu::GemmWorkspace make_ws(void *workspace, uint64_t bytes, int cus) {
+    swiglu::GemmWorkspace ws{};
+    ws.base = bytes > 0 ? workspace : nullptr;
+    ws.bytes = workspace ? bytes : 0;
+    ws.cus = cus;
+    return ws;
+}
+
+int check_workspace(const void *workspace, uint64_t bytes) {
+    if (workspace && bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(SWIGLU_ERR_ALIGN, "workspace must be 256-byte aligned");
     return SWIGLU_OK;
 }
 
@@ -140,8 +160,26 @@ int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2, uint16_t *W_fuse
     return launched(swiglu::launch_pack(W1, W2, W_fused, K, N, (hipStream_t)stream), "pack");
 }
 
+int swiglu_workspace_size(int64_t M, int64_t N, int64_t K, int variant, uint64_t *bytes) {
+    if (!bytes) return fail(SWIGLU_ERR_NULL, "bytes is required");
+    *bytes = 0;
+    if (variant < -1 || variant > SWIGLU_VARIANT_I)
+        return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
+    int st = check_gemm_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != SWIGLU_OK) return st;
+    const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
+    // variant I and the ablation (-1) run the single-accumulator GEMM
+    if (v == SWIGLU_VARIANT_I || v == -1) *bytes = swiglu::workspace_bytes_for(cus);
+    return ok();
+}
+
 int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, int64_t M,
-                      int64_t N, int64_t K, int variant, void *stream) {
+                      int64_t N, int64_t K, int variant, void *workspace,
+                      uint64_t workspace_bytes, void *stream) {
     if (variant != SWIGLU_AUTO && variant != SWIGLU_VARIANT_S && variant != SWIGLU_VARIANT_I)
         return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
     int st = check_gemm_shape(M, N, K);
@@ -154,11 +192,21 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, i
     const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = 2 * K * N * 2;
     if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W_fused, wbytes))
         return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
-    st = check_device();
+    st = check_workspace(workspace, workspace_bytes);
+    if (st != SWIGLU_OK) return st;
+    if (workspace && workspace_bytes > 0 &&
+        (overlap(workspace, (int64_t)workspace_bytes, A, abytes) ||
+         overlap(workspace, (int64_t)workspace_bytes, W_fused, wbytes) ||
+         overlap(workspace, (int64_t)workspace_bytes, Y, ybytes)))
+        return fail(SWIGLU_ERR_ALIAS, "workspace overlaps an operand");
+    int cus = 0;
+    st = check_device(&cus);
     if (st != SWIGLU_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
     if (v == SWIGLU_VARIANT_I)
-        return launched(swiglu::launch_fused_interleaved(A, W_fused, Y, (int)M, (int)N, (int)K, s),
+        return launched(swiglu::launch_fused_interleaved(A, W_fused, Y, (int)M, (int)N, (int)K,
+                                                         make_ws(workspace, workspace_bytes, cus),
+                                                         s),
                         "fused interleaved");
     return launched(swiglu::launch_fused_sequential(A, W_fused, Y, (int)M, (int)N, (int)K, s),
                     "fused sequential");
@@ -166,7 +214,7 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, i
 
 int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused, uint16_t *gate_ws,
                             uint16_t *up_ws, uint16_t *Y, int64_t M, int64_t N, int64_t K,
-                            void *stream) {
+                            void *workspace, uint64_t workspace_bytes, void *stream) {
     int st = check_gemm_shape(M, N, K);
     if (st != SWIGLU_OK) return st;
     if (M == 0 || N == 0) return ok();
@@ -183,13 +231,26 @@ int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused, uint16_t
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], ybytes, outs[j], ybytes))
                 return fail(SWIGLU_ERR_ALIAS, "outputs overlap each other");
+        if (workspace && workspace_bytes > 0 &&
+            overlap(workspace, (int64_t)workspace_bytes, outs[i], ybytes))
+            return fail(SWIGLU_ERR_ALIAS, "workspace overlaps an operand");
     }
-    st = check_device();
+    st = check_workspace(workspace, workspace_bytes);
+    if (st != SWIGLU_OK) return st;
+    if (workspace && workspace_bytes > 0 &&
+        (overlap(workspace, (int64_t)workspace_bytes, A, abytes) ||
+         overlap(workspace, (int64_t)workspace_bytes, W_fused, wbytes)))
+        return fail(SWIGLU_ERR_ALIAS, "workspace overlaps an operand");
+    int cus = 0;
+    st = check_device(&cus);
     if (st != SWIGLU_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
-    hipError_t e = swiglu::launch_gemm_store(A, W_fused, 0, gate_ws, (int)M, (int)N, (int)K, s);
+    // the two GEMMs run in stream order, so they may share the workspace
+    hipError_t e = swiglu::launch_gemm_store(A, W_fused, 0, gate_ws, (int)M, (int)N, (int)K,
+                                             make_ws(workspace, workspace_bytes, cus), s);
     if (e != hipSuccess) return launched(e, "ablation gate GEMM");
-    e = swiglu::launch_gemm_store(A, W_fused, 1, up_ws, (int)M, (int)N, (int)K, s);
+    e = swiglu::launch_gemm_store(A, W_fused, 1, up_ws, (int)M, (int)N, (int)K,
+                                  make_ws(workspace, workspace_bytes, cus), s);
     if (e != hipSuccess) return launched(e, "ablation up GEMM");
     return launched(swiglu::launch_silu_mul(gate_ws, up_ws, Y, M * N, s), "ablation silu_mul");
 }

@@ -60,6 +60,19 @@ __device__ __forceinline__ float swap_adjacent_lanes(float v) {
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
 }
 
+// Per-lane choice by lane parity: even lanes get `even_v`, odd lanes `odd_v`
+// (v_cndmask against the constant odd-lane mask).  Written out so that the
+// compiler cannot turn a parity choice between two elements of one vector
+// into a variable-index extract, which it expands into a select chain over
+// the whole vector.
+__device__ __forceinline__ float by_lane_parity(float even_v, float odd_v) {
+    float r;
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3"
+        : "=v"(r)
+        : "v"(even_v), "v"(odd_v), "s"(0xAAAAAAAAAAAAAAAAull));
+    return r;
+}
+
 // SiLU(x) = x / (1 + e^{-x}) = x * rcp(1 + 2^{-x log2 e}) with the hardware
 // exp2 and reciprocal (about 1 ulp each in fp32).  Very negative x: the exp2
 // overflows to +inf, the reciprocal is 0 and the result is -0; large x:

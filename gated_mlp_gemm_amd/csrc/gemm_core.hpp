@@ -494,16 +494,13 @@ struct PingPong {
 template <class S>
 using PipelineFor = typename std::conditional<S::kPingPong, PingPong<S>, Pipeline<S>>::type;
 
-// Workgroup -> output tile.  Workgroups are dispatched round-robin over the
-// 8 XCDs (workgroup id mod 8); re-number them so that each XCD receives a
-// contiguous run of tile ids, then walk tiles in groups of `group_m` tile rows
-// so that tiles resident together share A rows and B columns in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_m, int &tm,
-                                            int &tn) {
-    const int bid = blockIdx.x;
-    const int nb = tiles_m * tiles_n;
-    const int per = nb / 8;
-    const int t = (bid < per * 8) ? (bid % 8) * per + bid / 8 : bid;
+// Tile order.  tile_coords() walks a tile index t over the tile grid in
+// groups of `group_m` tile rows (tiles close in t share A rows and B columns);
+// xcd_order() renumbers workgroup ids, which the hardware dispatches
+// round-robin over the 8 XCDs (id mod 8), so that each XCD receives a
+// contiguous run of indices and its L2 sees neighbouring tiles.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m,
+                                            int &tm, int &tn) {
     const int width = group_m * tiles_n;
     const int group = t / width;
     const int first_m = group * group_m;
@@ -511,6 +508,14 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_
     const int in_group = t % width;
     tm = first_m + in_group % rows_in_group;
     tn = in_group / rows_in_group;
+}
+__device__ __forceinline__ int xcd_order(int bid, int nb) {
+    const int per = nb / 8;
+    return (bid < per * 8) ? (bid % 8) * per + bid / 8 : bid;
+}
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_m, int &tm,
+                                            int &tn) {
+    tile_coords(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace swiglu

@@ -8,6 +8,7 @@
 
 #include "device.hpp"
 #include "gemm_core.hpp"
+#include "split_tail.hpp"
 
 namespace swiglu {
 
@@ -92,8 +93,24 @@ __device__ __forceinline__ int acc_row(int wm, int tm, int i, int lane) {
     return wm * S::kWaveM + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
+// Output stores of the epilogues go through a buffer resource that spans the
+// tile's valid rows of a row-major [M][ld] bf16 matrix.  A store whose offset
+// lies past those rows, or that carries kOutOfRange (the column is past the
+// end), is dropped by the hardware, so an epilogue needs neither a branch nor
+// a 64-bit address per element: one 32-bit lane offset per column group plus
+// a per-row term that is the same for all lanes.  With ld <= 2^22 and at most
+// 256 rows every offset stays below 2^32 (kOutOfRange + row term included).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(uint16_t *base, int m0, int rows,
+                                                           int ld) {
+    return make_rsrc(base + static_cast<int64_t>(m0) * ld,
+                     static_cast<uint32_t>(rows) * static_cast<uint32_t>(ld) * 2u);
+}
+__device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), 0, 0);
+}
+
 // ---------------------------------------------------------------------------
-// Variant I [gist: Method, Kernel-2]: one GEMM D = A . W_fused over a tile of
+// Variant I [gist: Method, Kernel-2]: one GEMM D = A . W_fused over tiles of
 // the [M, 2N] grid; the epilogue pairs adjacent accumulator columns
 // (D[m,2n], D[m,2n+1]) and stores SiLU(D[m,2n]) * D[m,2n+1].
 //
@@ -103,55 +120,156 @@ __device__ __forceinline__ int acc_row(int wm, int tm, int i, int lane) {
 // finishes registers 0..7 (it receives the partner's Up values), the odd lane
 // registers 8..15 (it receives Gate values); one DPP lane swap per output.
 // ---------------------------------------------------------------------------
-template <class S>
-__global__ __launch_bounds__(S::kThreads, 1) void fused_interleaved_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, uint16_t *__restrict__ Y,
-    int M, int N, int K, int tiles_m, int tiles_n) {
+struct PairMulEpilogue {
+    uint16_t *Y;
+    int M, N;
+
+    // Accumulator block (tm, tn) of thread tid (its lane must be tid % 64).
+    template <class S>
+    __device__ __forceinline__ void block(const f32x16 &a, int tm, int tn, int m0, int n0,
+                                          int tid) const {
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int wm = wave / S::WN, wn = wave % S::WN;
+        const bool odd = lane & 1;
+        const int rows_valid = min(S::BM, M - m0);
+        const int y0 = n0 / 2;                 // first Y column of the tile
+        const int ycols_valid = min(S::BN / 2, N - y0);
+        const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, N);
+        // even lanes finish accumulator registers 0..7, odd lanes 8..15, which
+        // sit 16 rows further down (acc_row with i = 8 + p)
+        const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, 0, odd ? 8 : 0, lane));
+        const int ycol = (wn * S::kWaveN + tn * 32 + (lane & 31)) >> 1;
+        const uint32_t voff =
+            ycol < ycols_valid
+                ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(y0 + ycol)) * 2u
+                : kOutOfRange;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const float lo = a[p], hi = a[8 + p];
+            const float recv = swap_adjacent_lanes(by_lane_parity(hi, lo));
+            const float gate = by_lane_parity(lo, recv);
+            const float up = by_lane_parity(recv, hi);
+            const uint32_t roff =
+                static_cast<uint32_t>(acc_row<S>(0, tm, p, 0)) * static_cast<uint32_t>(N) * 2u;
+            store_b16(r, voff + roff, to_bf16(silu(gate) * up));
+        }
+    }
+
+    template <class S>
+    __device__ __forceinline__ void apply(const f32x16 (&acc)[S::TM][S::TN], int m0, int n0,
+                                          int tid) const {
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < S::TN; ++tn) block<S>(acc[tm][tn], tm, tn, m0, n0, tid);
+    }
+};
+
+// Ablation GEMM epilogue: C = bf16(acc), so that Gate and Up are materialised
+// as an eager pipeline does [paper s1].
+struct StoreEpilogue {
+    uint16_t *C;
+    int M, N;
+
+    template <class S>
+    __device__ __forceinline__ void block(const f32x16 &a, int tm, int tn, int m0, int n0,
+                                          int tid) const {
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int wm = wave / S::WN, wn = wave % S::WN;
+        const int rows_valid = min(S::BM, M - m0);
+        const int cols_valid = min(S::BN, N - n0);
+        const __amdgpu_buffer_rsrc_t r = out_rsrc(C, m0, rows_valid, N);
+        const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, 0, 0, lane));
+        const int col = wn * S::kWaveN + tn * 32 + (lane & 31);
+        const uint32_t voff =
+            col < cols_valid
+                ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(n0 + col)) * 2u
+                : kOutOfRange;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t roff =
+                static_cast<uint32_t>(acc_row<S>(0, tm, i, 0)) * static_cast<uint32_t>(N) * 2u;
+            store_b16(r, voff + roff, to_bf16(a[i]));
+        }
+    }
+
+    template <class S>
+    __device__ __forceinline__ void apply(const f32x16 (&acc)[S::TM][S::TN], int m0, int n0,
+                                          int tid) const {
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < S::TN; ++tn) block<S>(acc[tm][tn], tm, tn, m0, n0, tid);
+    }
+};
+
+// One accumulator per tile: D = A . B^T over the tiles of `sch`, then `epi`.
+// Workgroup b < sch.dp runs tile b (XCD-ordered) whole and runs the epilogue;
+// with SPLIT, workgroup dp + j runs piece j % pieces of split tile
+// dp + j / pieces and stores its partial (split_tail.hpp), which
+// split_reduce_kernel finishes.  A workgroup runs one tile or piece: no loop.
+template <class S, class Epi, bool SPLIT>
+__global__ __launch_bounds__(S::kThreads, 1) void gemm_tiles_kernel(
+    const uint16_t *__restrict__ A, KMajor B, int M, int K, Epi epi, Schedule sch) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
 
-    int tm_, tn_;
-    tile_coords(tiles_m, tiles_n, 8, tm_, tn_);
-    const int m0 = tm_ * S::BM;
-    const int n0 = tn_ * S::BN;            // first W_fused column (packed row) of the tile
-    const int rows_valid = min(S::BM, M - m0);
-    const int nk = (K + S::BK - 1) / S::BK;
+    const int b = blockIdx.x;
+    int t, kb = 0, ke = sch.nk, j = 0;
+    const bool whole = !SPLIT || b < sch.dp;
+    if (whole) {
+        t = xcd_order(b, sch.dp);
+    } else {
+        j = b - sch.dp;
+        t = sch.dp + j / sch.pieces;
+        const int piece = j % sch.pieces;
+        kb = piece * sch.nk / sch.pieces;
+        ke = (piece + 1) * sch.nk / sch.pieces;
+    }
+    int tm, tn;
+    tile_coords(t, sch.tiles_m, sch.tiles_n, 8, tm, tn);
+    const int m0 = tm * S::BM;
+    const int n0 = tn * S::BN;
 
-    TileLoader<S> ld;
-    ld.init(KMajor{A, M, 1, 0}, m0, KMajor{Wf, 2 * N, 1, 0}, n0, K);
-    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, st); };
+    f32x16 acc[S::TM][S::TN];
     PipelineFor<S> pl;
     pl.init(lds);
-    f32x16 acc[S::TM][S::TN];
+    TileLoader<S> ld;
+    ld.init(KMajor{A, M, 1, 0}, m0, B, n0, K);
+    const int len = ke - kb;
+    // steps past the range load nothing (K step nk is past the end of K)
+    auto issue = [&](int s, SWIGLU_LDS char *st) { ld.issue(s < len ? kb + s : sch.nk, st); };
     zero_acc<S>(acc);
     pl.prologue(issue);
-    pl.run(issue, 0, nk, nk, acc);
+    pl.run(issue, 0, len, len, acc);
     pl.drain();
+    if (whole)
+        epi.template apply<S>(acc, m0, n0, threadIdx.x);
+    else
+        store_partial<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN, acc,
+                         threadIdx.x);
+}
 
-    // PairMul epilogue
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave / S::WN, wn = wave % S::WN;
-    const bool odd = lane & 1;
-    const int y0 = n0 / 2;                 // first Y column of the tile
-    const int ycols_valid = min(S::BN / 2, N - y0);
-#pragma unroll
-    for (int tm = 0; tm < S::TM; ++tm) {
-#pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn) {
-            const int ycol = (wn * S::kWaveN + tn * 32 + (lane & 31)) >> 1;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const float send = odd ? acc[tm][tn][p] : acc[tm][tn][8 + p];
-                const float recv = swap_adjacent_lanes(send);
-                const float gate = odd ? recv : acc[tm][tn][p];
-                const float up = odd ? acc[tm][tn][8 + p] : recv;
-                const int row = acc_row<S>(wm, tm, odd ? 8 + p : p, lane);
-                if (row < rows_valid && ycol < ycols_valid)
-                    Y[(int64_t)(m0 + row) * N + y0 + ycol] = to_bf16(silu(gate) * up);
-            }
-        }
-    }
+// The split tiles' epilogue: one wave per (split tile, GEMM wave, 32x32
+// accumulator block), four per workgroup.  The wave takes the registers of
+// the GEMM wave it stands for -- its lane l holds what GEMM thread
+// 64 w + l held, summed over the pieces -- so the epilogue's lane pairing
+// is the GEMM's.
+template <class S, class Epi>
+__global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch) {
+    constexpr int kBlocks = S::TM * S::TN;
+    constexpr int kPerTile = S::kWaves * kBlocks;
+    const int item = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+    const int i = item / kPerTile;                 // split tile
+    const int w = (item % kPerTile) / kBlocks;     // GEMM wave
+    const int blk = item % kBlocks;                // accumulator block tm * TN + tn
+    const int x = w * 64 + static_cast<int>(threadIdx.x & 63);
+    const f32x16 a = sum_pieces<S>(sch, i, blk, x);
+    int tm, tn;
+    tile_coords(sch.dp + i, sch.tiles_m, sch.tiles_n, 8, tm, tn);
+    epi.template block<S>(a, blk / S::TN, blk % S::TN, tm * S::BM, tn * S::BN, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -251,55 +369,6 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Ablation GEMM: C = bf16(A . B), the same mainloop with a plain store, so
-// that Gate and Up are materialised as an eager pipeline does [paper s1].
-// ---------------------------------------------------------------------------
-template <class S>
-__global__ __launch_bounds__(S::kThreads, 1) void gemm_store_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, int phase,
-    uint16_t *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
-    SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
-
-    int tm_, tn_;
-    tile_coords(tiles_m, tiles_n, 8, tm_, tn_);
-    const int m0 = tm_ * S::BM;
-    const int n0 = tn_ * S::BN;
-    const int rows_valid = min(S::BM, M - m0);
-    const int nk = (K + S::BK - 1) / S::BK;
-
-    // phase 0: Gate = A . W1 (even packed rows); phase 1: Up = A . W2 (odd rows)
-    TileLoader<S> ld;
-    ld.init(KMajor{A, M, 1, 0}, m0, KMajor{Wf, N, 2, phase}, n0, K);
-    auto issue = [&](int t, SWIGLU_LDS char *st) { ld.issue(t, st); };
-    PipelineFor<S> pl;
-    pl.init(lds);
-    f32x16 acc[S::TM][S::TN];
-    zero_acc<S>(acc);
-    pl.prologue(issue);
-    pl.run(issue, 0, nk, nk, acc);
-    pl.drain();
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave / S::WN, wn = wave % S::WN;
-    const int cols_valid = min(S::BN, N - n0);
-#pragma unroll
-    for (int tm = 0; tm < S::TM; ++tm) {
-#pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn) {
-            const int col = wn * S::kWaveN + tn * 32 + (lane & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = acc_row<S>(wm, tm, i, lane);
-                if (row < rows_valid && col < cols_valid)
-                    C[(int64_t)(m0 + row) * N + n0 + col] = to_bf16(acc[tm][tn][i]);
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Tile shapes and launchers
 // ---------------------------------------------------------------------------
 using ShapeWide = TileShape<256, 256, 32, 2, 4, 4>;    // I and ablation GEMM (ping-pong)
@@ -333,13 +402,58 @@ hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, in
     return hipGetLastError();
 }
 
+// Work schedule for a single-accumulator GEMM over an M x cols output (see
+// split_tail.hpp): all tiles whole unless the last round is partly idle, a
+// workspace is given and splitting the tail into s >= 2 pieces shortens it
+// by more than the reduction costs (reckoned as two K steps).
+template <class S>
+static Schedule make_schedule(int M, int cols, int K, const GemmWorkspace &ws) {
+    Schedule sch{};
+    sch.tiles_m = cdiv(M, S::BM);
+    sch.tiles_n = cdiv(cols, S::BN);
+    sch.nk = cdiv(K, S::BK);
+    const int64_t T = static_cast<int64_t>(sch.tiles_m) * sch.tiles_n;
+    sch.dp = static_cast<int>(T);
+    const int G = ws.cus;
+    if (ws.base == nullptr || G <= 0 || ws.bytes < workspace_bytes_for(G)) return sch;
+    const int64_t L = T % G;
+    if (L == 0) return sch;
+    const int pieces = static_cast<int>(min(static_cast<int64_t>(G) / L, static_cast<int64_t>(sch.nk)));
+    if (pieces < 2 || cdiv(sch.nk, pieces) + 2 >= sch.nk) return sch;
+    sch.dp = static_cast<int>(T - L);
+    sch.pieces = pieces;
+    sch.split_tiles = static_cast<int>(L);
+    sch.partials = reinterpret_cast<float *>(ws.base);
+    return sch;
+}
+
+template <class S, class Epi>
+static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int K, Epi epi,
+                              const GemmWorkspace &ws, hipStream_t stream) {
+    const Schedule sch = make_schedule<S>(M, cols, K, ws);
+    if (sch.pieces == 0) {
+        hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, false>), dim3(sch.dp), dim3(S::kThreads), 0,
+                           stream, A, B, M, K, epi, sch);
+        return hipGetLastError();
+    }
+    const int grid = sch.dp + sch.split_tiles * sch.pieces;
+    hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, true>), dim3(grid), dim3(S::kThreads), 0,
+                       stream, A, B, M, K, epi, sch);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // S::kWaves * TM * TN waves per split tile, four per workgroup
+    static_assert((S::kWaves * S::TM * S::TN) % 4 == 0, "whole workgroups per split tile");
+    const int rgrid = sch.split_tiles * (S::kWaves * S::TM * S::TN / 4);
+    hipLaunchKernelGGL((split_reduce_kernel<S, Epi>), dim3(rgrid), dim3(256), 0, stream, epi, sch);
+    return hipGetLastError();
+}
+
 hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
-                                    int N, int K, hipStream_t stream) {
-    if (M <= 128)
-        return launch_tiles<ShapeSmall>(fused_interleaved_kernel<ShapeSmall>, M, 2 * N, stream,
-                                        A, Wf, Y, M, N, K);
-    return launch_tiles<ShapeWide>(fused_interleaved_kernel<ShapeWide>, M, 2 * N, stream, A,
-                                   Wf, Y, M, N, K);
+                                    int N, int K, const GemmWorkspace &ws, hipStream_t stream) {
+    const KMajor B{Wf, 2 * N, 1, 0};
+    const PairMulEpilogue epi{Y, M, N};
+    if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, 2 * N, K, epi, ws, stream);
+    return launch_gemm<ShapeWide>(A, B, M, 2 * N, K, epi, ws, stream);
 }
 
 hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
@@ -352,13 +466,20 @@ hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16
 }
 
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
-                             int M, int N, int K, hipStream_t stream) {
-    if (M <= 128)
-        return launch_tiles<ShapeSmall>(gemm_store_kernel<ShapeSmall>, M, N, stream, A, Wf,
-                                        phase, C, M, N, K);
-    return launch_tiles<ShapeWide>(gemm_store_kernel<ShapeWide>, M, N, stream, A, Wf, phase, C,
-                                   M, N, K);
+                             int M, int N, int K, const GemmWorkspace &ws, hipStream_t stream) {
+    const KMajor B{Wf, N, 2, phase};
+    const StoreEpilogue epi{C, M, N};
+    if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, N, K, epi, ws, stream);
+    return launch_gemm<ShapeWide>(A, B, M, N, K, epi, ws, stream);
 }
+
+// One partial slot per CU (at most G pieces exist), sized for the largest
+// tile shape.
+uint64_t partials_bytes(int cus) {
+    return static_cast<uint64_t>(cus) * ShapeWide::BM * ShapeWide::BN * sizeof(float);
+}
+
+uint64_t workspace_bytes_for(int cus) { return partials_bytes(cus); }
 
 int64_t max_tiles(int64_t M, int64_t cols) {
     // the most workgroups any launcher above creates for an M x cols output

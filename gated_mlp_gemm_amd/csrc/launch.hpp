@@ -8,17 +8,29 @@
 
 namespace swiglu {
 
+// Caller-owned scratch for the split-tail schedule (may be empty: base == nullptr).
+struct GemmWorkspace {
+    void *base;
+    uint64_t bytes;
+    int cus;          // compute units of the device
+};
+// Scratch that lets the single-accumulator GEMMs split the tiles of a partial
+// last round along K (the same for every shape: one fp32 256 x 256 tile slot
+// per compute unit).
+uint64_t partials_bytes(int cus);
+uint64_t workspace_bytes_for(int cus);
+
 hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,
                        int64_t N, hipStream_t stream);
 hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,
                            hipStream_t stream);
 hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
-                                    int N, int K, hipStream_t stream);
+                                    int N, int K, const GemmWorkspace &ws, hipStream_t stream);
 hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
                                    int N, int K, hipStream_t stream);
 // phase 0: C = A . W1 (Gate columns of W_fused), phase 1: C = A . W2 (Up columns)
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
-                             int M, int N, int K, hipStream_t stream);
+                             int M, int N, int K, const GemmWorkspace &ws, hipStream_t stream);
 // Largest workgroup count any launcher uses for an M x cols output tile grid.
 int64_t max_tiles(int64_t M, int64_t cols);
 

@@ -1,0 +1,83 @@
+// Work schedule for the single-accumulator GEMM kernels: whole tiles for the
+// full rounds, the last partial round split along K.
+//
+// One tile per workgroup leaves CUs idle in the last round when the tile count
+// T is not a multiple of the CU count G: the M=2048, 2N=17920 output has 560
+// tiles of 256x256 for 256 CUs, 3 rounds for 2.19 rounds of work.  Here the
+// first R*G tiles (R = T / G full rounds) run whole, one per workgroup, and
+// each of the L = T mod G remaining tiles is cut into s = min(G / L, nk)
+// pieces of about nk / s K steps, one piece per workgroup: the tail round
+// takes nk / s steps instead of nk (for 560 tiles: 2 + 1/5 rounds).  Every
+// workgroup runs exactly one (tile, K range), so the GEMM kernel has no loop
+// over tiles and no more live registers than the one-tile kernel.
+//
+// A piece stores its fp32 partial accumulator in its own workspace slot and
+// ends.  A second, short kernel on the same stream then sums the s slots of
+// each split tile in piece order (so results are bitwise reproducible) and
+// runs the epilogue; it gives every 32x32 accumulator block of every split
+// tile its own wave, so the reduction is spread over the whole chip rather
+// than left to one workgroup per tile.  The stream order is the only
+// synchronisation: no counters, atomics or fences.
+//
+// Workspace (caller-owned device memory, no initialisation needed): G slots of
+// BM*BN floats, sized for the largest tile shape.
+#pragma once
+
+#include "gemm_core.hpp"
+
+namespace swiglu {
+
+struct Schedule {
+    int tiles_m, tiles_n;   // tile grid
+    int nk;                 // K steps per tile
+    int dp;                 // tiles [0, dp) run whole: workgroup b < dp runs one of them
+    int pieces;             // K pieces per split tile (0: no split tiles)
+    int split_tiles;        // tiles [dp, dp + split_tiles) are split
+    float *partials;        // one BM*BN slot per piece: slot j = piece j % pieces of split tile j / pieces
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// A partial tile is stored thread-major: float4 number i of GEMM thread x at
+// float4 index i * threads + x, so every access is a coalesced 16-byte one.
+// Float4 number i of a thread holds registers 4(i%4)..4(i%4)+3 of its
+// accumulator block i/4 (block = tm * TN + tn).
+template <class S>
+__device__ __forceinline__ void store_partial(float *slot, const f32x16 (&acc)[S::TM][S::TN],
+                                              int tid) {
+    f32x4 *dst = reinterpret_cast<f32x4 *>(slot);
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = (tm * S::TN + tn) * 4 + j;
+                dst[i * S::kThreads + tid] =
+                    f32x4{acc[tm][tn][4 * j], acc[tm][tn][4 * j + 1], acc[tm][tn][4 * j + 2],
+                          acc[tm][tn][4 * j + 3]};
+            }
+}
+
+// Accumulator block `blk` of GEMM thread x of split tile i: the sum, in
+// piece order, of the pieces' partials.
+template <class S>
+__device__ __forceinline__ f32x16 sum_pieces(const Schedule &sch, int i, int blk, int x) {
+    constexpr int64_t kSlot = static_cast<int64_t>(S::BM) * S::BN;
+    const float *first = sch.partials + static_cast<int64_t>(i) * sch.pieces * kSlot;
+    f32x16 a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t idx = static_cast<int64_t>(blk * 4 + j) * S::kThreads + x;
+        f32x4 v = reinterpret_cast<const f32x4 *>(first)[idx];
+        for (int p = 1; p < sch.pieces; ++p)
+            v += reinterpret_cast<const f32x4 *>(first + p * kSlot)[idx];
+        a[4 * j] = v.x;
+        a[4 * j + 1] = v.y;
+        a[4 * j + 2] = v.z;
+        a[4 * j + 3] = v.w;
+    }
+    return a;
+}
+
+}  // namespace swiglu

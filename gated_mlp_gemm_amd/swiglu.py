@@ -56,8 +56,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.swiglu_pack_weights.argtypes = [P, P, P, I64, I64, P]
-    lib.swiglu_fused_gemm.argtypes = [P, P, P, I64, I64, I64, I32, P]
-    lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+    U64 = ctypes.c_uint64
+    lib.swiglu_fused_gemm.argtypes = [P, P, P, I64, I64, I64, I32, P, U64, P]
+    lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, I64, I64, I64, P, U64, P]
+    lib.swiglu_workspace_size.argtypes = [I64, I64, I64, I32, ctypes.POINTER(U64)]
     lib.swiglu_silu_mul.argtypes = [P, P, P, I64, P]
     lib.swiglu_select_variant.argtypes = [I64, I64, I64]
     lib.swiglu_m_switch.argtypes = []
@@ -67,7 +69,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_last_error.argtypes = []
     lib.swiglu_last_error.restype = ctypes.c_char_p
     for name in ("swiglu_pack_weights", "swiglu_fused_gemm", "swiglu_unfused_ablation",
-                 "swiglu_silu_mul", "swiglu_select_variant"):
+                 "swiglu_silu_mul", "swiglu_select_variant", "swiglu_workspace_size"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -132,8 +134,34 @@ def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor,
     return W_fused
 
 
+def _ws(workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return None, 0
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def swiglu_workspace_size(M: int, N: int, K: int, variant="auto") -> int:
+    """Bytes of scratch that let a call split the tail round ('ablation' for the ablation)."""
+    v = -1 if variant == "ablation" else (VARIANTS[variant.lower()]
+                                          if isinstance(variant, str) else int(variant))
+    out = ctypes.c_uint64(0)
+    _check(load_library().swiglu_workspace_size(M, N, K, v, ctypes.byref(out)),
+           "swiglu_workspace_size")
+    return int(out.value)
+
+
+def make_workspace(M: int, N: int, K: int, variant="auto", device="cuda") -> Optional[torch.Tensor]:
+    """A device scratch tensor of swiglu_workspace_size() bytes (None if 0);
+    needs no initialisation and may be reused by later stream-ordered calls."""
+    n = swiglu_workspace_size(M, N, K, variant)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def swiglu_fused_gemm(A: torch.Tensor, W_fused: torch.Tensor,
-                      Y: Optional[torch.Tensor] = None, variant="auto") -> torch.Tensor:
+                      Y: Optional[torch.Tensor] = None, variant="auto",
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = bf16(SiLU(A.W1) * (A.W2)) from the packed weight; variant 'auto' | 's' | 'i'."""
     lib = load_library()
     v = VARIANTS[variant.lower()] if isinstance(variant, str) else int(variant)
@@ -145,7 +173,8 @@ def swiglu_fused_gemm(A: torch.Tensor, W_fused: torch.Tensor,
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _dev_tensor(Y, "Y", (M, N))
     with torch.cuda.device(A.device):
-        _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W_fused), _ptr(Y), M, N, K, v,
+        ws, wsb = _ws(workspace)
+        _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W_fused), _ptr(Y), M, N, K, v, ws, wsb,
                                      _stream(A.device)), "swiglu_fused_gemm")
     return Y
 
@@ -153,7 +182,8 @@ def swiglu_fused_gemm(A: torch.Tensor, W_fused: torch.Tensor,
 def swiglu_unfused_ablation(A: torch.Tensor, W_fused: torch.Tensor,
                             gate_ws: Optional[torch.Tensor] = None,
                             up_ws: Optional[torch.Tensor] = None,
-                            Y: Optional[torch.Tensor] = None
+                            Y: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None
                             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Two GEMMs + SiLU-mul from the packed weight; returns (Y, gate_ws, up_ws)."""
     lib = load_library()
@@ -168,8 +198,9 @@ def swiglu_unfused_ablation(A: torch.Tensor, W_fused: torch.Tensor,
         outs.append(_dev_tensor(t, name, (M, N)))
     gate_ws, up_ws, Y = outs
     with torch.cuda.device(A.device):
+        ws, wsb = _ws(workspace)
         _check(lib.swiglu_unfused_ablation(_ptr(A), _ptr(W_fused), _ptr(gate_ws), _ptr(up_ws),
-                                           _ptr(Y), M, N, K, _stream(A.device)),
+                                           _ptr(Y), M, N, K, ws, wsb, _stream(A.device)),
                "swiglu_unfused_ablation")
     return Y, gate_ws, up_ws
 

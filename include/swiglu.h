@@ -26,7 +26,7 @@
  *    nothing and returns a negative swiglu_status.  Preconditions:
  *      M >= 0, N >= 0, K >= 8;  K % 8 == 0 and N % 8 == 0 (each row is a
  *      whole number of 16-byte chunks);  M <= 2^31 - 1, K <= 2^21,
- *      N <= 2^23;
+ *      N <= 2^22;
  *      every pointer 16-byte aligned;  outputs do not overlap inputs or
  *      each other.
  *    M == 0 or N == 0 is an empty problem: SWIGLU_OK, nothing launched.
@@ -98,10 +98,20 @@ int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2,
  * variant SWIGLU_AUTO: whichever swiglu_select_variant(M, N, K) names.
  *
  * A: [M][K], W_fused: packed [2N][K], Y: [M][N]; device pointers.
+ *
+ * workspace / workspace_bytes: optional caller-owned device scratch
+ * (256-byte aligned, not shared by calls that may run concurrently; no
+ * initialisation needed, contents meaningless after the call).  With at least
+ * swiglu_workspace_size() bytes, variant I may split the output tiles of a
+ * partly idle last round of workgroups along K: every other tile runs whole,
+ * one per workgroup, and the pieces of a split tile leave fp32 partial tiles
+ * in the workspace that a second kernel on the same stream sums, in a fixed
+ * order (results stay bitwise reproducible), before the epilogue.  NULL or
+ * too small: every tile whole, one kernel.  Variant S does not use it.
  */
 int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
                       int64_t M, int64_t N, int64_t K, int variant,
-                      void *stream);
+                      void *workspace, uint64_t workspace_bytes, void *stream);
 
 /*
  * The unfused pipeline, kept as an ablation so the saved memory traffic can be
@@ -112,11 +122,25 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
  *     gate_ws = bf16(A.W1);  up_ws = bf16(A.W2);
  *     Y = bf16( SiLU(gate_ws) * up_ws )   (fp32 arithmetic, one rounding)
  * gate_ws, up_ws: caller-owned [M][N] device workspaces, written (their
- * contents are part of the result and may be inspected).
+ * contents are part of the result and may be inspected).  workspace /
+ * workspace_bytes: as for swiglu_fused_gemm (the two GEMMs use the same
+ * scheduler as variant I; size from swiglu_workspace_size(..., -1, ...)).
  */
+
+/*
+ * Bytes of `workspace` that let a call split the tail round: variant
+ * SWIGLU_VARIANT_I or SWIGLU_AUTO for swiglu_fused_gemm, -1 for
+ * swiglu_unfused_ablation (0 when nothing uses it, e.g. variant S, or for an
+ * empty problem).  Queries the current device's compute-unit count (a HIP
+ * call).  One fp32 256 x 256 tile per compute unit, whatever the shape:
+ * 64 MiB on MI355X.
+ */
+int swiglu_workspace_size(int64_t M, int64_t N, int64_t K, int variant,
+                          uint64_t *bytes);
 int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused,
                             uint16_t *gate_ws, uint16_t *up_ws, uint16_t *Y,
-                            int64_t M, int64_t N, int64_t K, void *stream);
+                            int64_t M, int64_t N, int64_t K, void *workspace,
+                            uint64_t workspace_bytes, void *stream);
 
 /*
  * The ablation's activation stage on its own: Y[i] = bf16(SiLU(gate[i]) *

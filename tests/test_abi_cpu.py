@@ -13,7 +13,7 @@ ERR_NULL, ERR_SHAPE, ERR_ALIGN = sw.SWIGLU_ERR_NULL, sw.SWIGLU_ERR_SHAPE, sw.SWI
 ERR_UNSUP, ERR_ALIAS = sw.SWIGLU_ERR_UNSUPPORTED, sw.SWIGLU_ERR_ALIAS
 
 # fake, 16-byte aligned, far apart "device" addresses (never dereferenced)
-A_, W1_, W2_, WF_, Y_, G_, U_ = (0x10_0000_0000 * (i + 1) for i in range(7))
+A_, W1_, W2_, WF_, Y_, G_, U_, WS_ = (0x10_0000_0000 * (i + 1) for i in range(8))
 
 
 @pytest.fixture(scope="module")
@@ -55,8 +55,8 @@ def test_dispatcher_thresholds(lib, monkeypatch):
     assert sw.swiglu_m_switch() == 2048
 
 
-def fused(lib, A=A_, WF=WF_, Y=Y_, M=256, N=256, K=256, v=2):
-    return lib.swiglu_fused_gemm(A, WF, Y, M, N, K, v, None)
+def fused(lib, A=A_, WF=WF_, Y=Y_, M=256, N=256, K=256, v=2, ws=None, wsb=0):
+    return lib.swiglu_fused_gemm(A, WF, Y, M, N, K, v, ws, wsb, None)
 
 
 def test_fused_validation(lib):
@@ -68,7 +68,7 @@ def test_fused_validation(lib):
     assert fused(lib, K=20) == ERR_SHAPE          # not a multiple of 8
     assert fused(lib, N=12) == ERR_SHAPE
     assert fused(lib, K=(1 << 21) + 8) == ERR_SHAPE
-    assert fused(lib, N=(1 << 23) + 8) == ERR_SHAPE
+    assert fused(lib, N=(1 << 22) + 8) == ERR_SHAPE
     assert fused(lib, M=1 << 31) == ERR_SHAPE
     # variant
     assert fused(lib, v=3) == ERR_UNSUP
@@ -86,13 +86,18 @@ def test_fused_validation(lib):
     assert fused(lib, Y=A_ + 1024) == ERR_ALIAS
     assert fused(lib, Y=WF_ + 4096, v=2) == ERR_ALIAS
     assert fused(lib, Y=WF_ + 2 * 256 * 256 * 2 - 16, v=1) == ERR_ALIAS
+    # workspace: 256-byte aligned, disjoint from the operands
+    assert fused(lib, ws=WS_ + 16, wsb=1 << 20) == ERR_ALIGN
+    assert fused(lib, ws=Y_ + 256, wsb=1 << 20) == ERR_ALIAS
+    assert fused(lib, ws=A_, wsb=1 << 20) == ERR_ALIAS
     assert "overlaps" in sw.swiglu_last_error()
 
 
 def test_empty_problems_succeed_without_pointers(lib):
-    assert lib.swiglu_fused_gemm(None, None, None, 0, 256, 64, 0, None) == 0
-    assert lib.swiglu_fused_gemm(None, None, None, 64, 0, 64, 0, None) == 0
-    assert lib.swiglu_unfused_ablation(None, None, None, None, None, 0, 64, 64, None) == 0
+    assert lib.swiglu_fused_gemm(None, None, None, 0, 256, 64, 0, None, 0, None) == 0
+    assert lib.swiglu_fused_gemm(None, None, None, 64, 0, 64, 0, None, 0, None) == 0
+    assert lib.swiglu_unfused_ablation(None, None, None, None, None, 0, 64, 64, None, 0,
+                                       None) == 0
     assert lib.swiglu_pack_weights(None, None, None, 0, 64, None) == 0
     assert lib.swiglu_pack_weights(None, None, None, 64, 0, None) == 0
     assert lib.swiglu_silu_mul(None, None, None, 0, None) == 0
@@ -117,7 +122,8 @@ def test_ablation_validation(lib):
 
     def call(**kw):
         a = {**ok, **kw}
-        return F(a["A"], a["WF"], a["G"], a["U"], a["Y"], 256, 256, 256, None)
+        return F(a["A"], a["WF"], a["G"], a["U"], a["Y"], 256, 256, 256, a.get("WS"),
+                 a.get("WSB", 0), None)
 
     assert call(G=None) == ERR_NULL
     assert call(U=None) == ERR_NULL
@@ -127,7 +133,19 @@ def test_ablation_validation(lib):
     assert call(Y=U_ + 16) == ERR_ALIAS
     assert call(G=WF_ + 64) == ERR_ALIAS         # output inside an input
     assert call(G=A_ + 64) == ERR_ALIAS
-    assert F(A_, WF_, G_, U_, Y_, 256, 20, 256, None) == ERR_SHAPE
+    assert call(WS=U_ + 512, WSB=1 << 20) == ERR_ALIAS
+    assert call(WS=WS_ + 8, WSB=1 << 20) == ERR_ALIGN
+    assert F(A_, WF_, G_, U_, Y_, 256, 20, 256, None, 0, None) == ERR_SHAPE
+
+
+def test_workspace_size_validation(lib):
+    import ctypes
+    out = ctypes.c_uint64(7)
+    assert lib.swiglu_workspace_size(256, 256, 256, 2, None) == ERR_NULL
+    assert lib.swiglu_workspace_size(256, 20, 256, 2, ctypes.byref(out)) == ERR_SHAPE
+    assert out.value == 0
+    assert lib.swiglu_workspace_size(256, 256, 256, 5, ctypes.byref(out)) == ERR_UNSUP
+    assert lib.swiglu_workspace_size(0, 256, 256, 2, ctypes.byref(out)) == 0 and out.value == 0
 
 
 def test_silu_mul_validation(lib):

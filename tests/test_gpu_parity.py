@@ -69,8 +69,30 @@ def assert_parity(y_bits, ref_bits, what: str):
     return rep
 
 
+_WS = {}
+
+
+def workspace_for(M, N, K, variant, dev):
+    """A workspace of the queried size, reused across calls and filled with
+    0xFF bytes (NaN as fp32) when allocated: the library needs no
+    initialisation, and a stale partial that leaked into a result would show."""
+    n = sw.swiglu_workspace_size(M, N, K, variant)
+    if n == 0:
+        return None
+    if _WS.get(dev) is None or _WS[dev].numel() < n:
+        _WS[dev] = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
+    return _WS[dev]
+
+
 def run_fused(A, Wf, variant):
-    Y = sw.swiglu_fused_gemm(A, Wf, variant=variant)
+    """variant 'i' | 's' | 'auto', with '+ws' appended to pass a workspace
+    (which lets variant I split the tiles of a partly idle last round)."""
+    ws = None
+    if variant.endswith("+ws"):
+        variant = variant[:-3]
+        M, K = A.shape
+        ws = workspace_for(M, Wf.shape[0] // 2, K, variant, A.device)
+    Y = sw.swiglu_fused_gemm(A, Wf, variant=variant, workspace=ws)
     torch.cuda.synchronize()
     return Y
 
@@ -98,7 +120,7 @@ SMALL = [(1, 8, 8), (5, 16, 24), (64, 64, 64), (128, 896, 520), (130, 200, 72),
 
 
 @pytest.mark.parametrize("M,K,N", SMALL)
-@pytest.mark.parametrize("variant", ["i", "s", "auto"])
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s", "auto", "auto+ws"])
 def test_small_shapes(dev, orc, M, K, N, variant):
     announce(f"fused {variant} M={M} K={K} N={N}")
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 31 + K * 7 + N)
@@ -116,7 +138,7 @@ def _pad(a, rows, cols):
     return out
 
 
-@pytest.mark.parametrize("variant", ["i", "s"])
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
 def test_hand_cases_padded(dev, orc, variant):
     """The hand-computed cases, zero-padded to legal shapes (K, N multiples of 8).
 
@@ -153,7 +175,7 @@ def test_saturating_gates(dev, orc):
     Wf = sw.swiglu_pack_weights(W1d, W2d)
     G = orc.matmul(inputs.bits(A), inputs.bits(W1))
     assert (G < -30).any() and (G > 30).any(), "inputs must reach the saturated regions"
-    for variant in ("i", "s"):
+    for variant in ("i", "i+ws", "s"):
         announce(f"saturating gates variant {variant}")
         Y = run_fused(Ad, Wf, variant)
         yb = bits_of(Y)
@@ -193,7 +215,7 @@ def _ref_samples(orc, d):
     return d["cache"]["ref_rows"], d["cache"]["ref_pts"]
 
 
-@pytest.mark.parametrize("variant", ["i", "s", "auto"])
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s", "auto+ws"])
 def test_workload_full_size(dev, orc, workload, variant):
     d = workload
     w = d["w"]
@@ -207,17 +229,18 @@ def test_workload_full_size(dev, orc, workload, variant):
     d["cache"][f"Y_{variant}"] = yb
 
 
-def test_workload_variants_agree(dev, workload):
-    """Over the whole output, I and S are each within 1 % of the truth, hence
-    within about 2 % of each other (plus the absolute floor twice)."""
+@pytest.mark.parametrize("pair", [("i", "s"), ("i+ws", "s"), ("i", "i+ws")])
+def test_workload_variants_agree(dev, workload, pair):
+    """Over the whole output, each path is within 1 % of the truth, hence the
+    two are within about 2 % of each other (plus the absolute floor twice)."""
     d = workload
-    yi, ys = d["cache"].get("Y_i"), d["cache"].get("Y_s")
-    if yi is None or ys is None:
+    ya, yb = (d["cache"].get(f"Y_{v}") for v in pair)
+    if ya is None or yb is None:
         pytest.skip("variant outputs not computed")
-    a, b = oracle_pkg.bf16_bits_to_f64(yi), oracle_pkg.bf16_bits_to_f64(ys)
+    a, b = oracle_pkg.bf16_bits_to_f64(ya), oracle_pkg.bf16_bits_to_f64(yb)
     bound = np.maximum(2e-3, 2.05e-2 * np.maximum(np.abs(a), np.abs(b)))
     bad = np.abs(a - b) > bound
-    assert not bad.any(), f"{int(bad.sum())} elements of I and S disagree on {d['w'].name}"
+    assert not bad.any(), f"{int(bad.sum())} elements of {pair} disagree on {d['w'].name}"
 
 
 def test_workload_pack(dev, orc, workload):
@@ -249,9 +272,12 @@ def _intermediate_within_bound(orc, a_bits, w_bits, got_bits, what):
     assert np.all(err <= bound), f"{what}: max err/bound {float((err / bound).max()):.3f}"
 
 
-def _check_ablation(orc, A, W1, W2, rows, dev, what):
+def _check_ablation(orc, A, W1, W2, rows, dev, what, use_ws=False):
     Ad = A.to(dev)
-    Y, g, u = sw.swiglu_unfused_ablation(Ad, sw.swiglu_pack_weights(W1.to(dev), W2.to(dev)))
+    M, K = A.shape
+    ws = workspace_for(M, W1.shape[1], K, "ablation", dev) if use_ws else None
+    Y, g, u = sw.swiglu_unfused_ablation(Ad, sw.swiglu_pack_weights(W1.to(dev), W2.to(dev)),
+                                         workspace=ws)
     torch.cuda.synchronize()
     sub = inputs.bits(A)[rows]
     hW1, hW2 = inputs.bits(W1), inputs.bits(W2)
@@ -272,18 +298,20 @@ def _check_ablation(orc, A, W1, W2, rows, dev, what):
 
 @pytest.mark.parametrize("M,K,N", [(5, 16, 24), (130, 200, 72), (257, 136, 264),
                                    (128, 896, 4864)])
-def test_ablation_small(dev, orc, M, K, N):
-    announce(f"ablation M={M} K={K} N={N}")
+@pytest.mark.parametrize("use_ws", [False, True], ids=["dp", "ws"])
+def test_ablation_small(dev, orc, M, K, N, use_ws):
+    announce(f"ablation M={M} K={K} N={N} workspace={use_ws}")
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=M + K + N)
-    _check_ablation(orc, A, W1, W2, np.arange(M), dev, f"ablation {M}x{K}x{N}")
+    _check_ablation(orc, A, W1, W2, np.arange(M), dev, f"ablation {M}x{K}x{N}", use_ws)
 
 
-def test_ablation_workload_rows(dev, orc):
+@pytest.mark.parametrize("use_ws", [False, True], ids=["dp", "ws"])
+def test_ablation_workload_rows(dev, orc, use_ws):
     w = inputs.WORKLOADS[1]
-    announce(f"ablation {w.name}")
+    announce(f"ablation {w.name} workspace={use_ws}")
     A, W1, W2 = inputs.workload_inputs(w)
     rows = np.array([0, 1, 777, w.M - 1])
-    _check_ablation(orc, A, W1, W2, rows, dev, f"ablation {w.name}")
+    _check_ablation(orc, A, W1, W2, rows, dev, f"ablation {w.name}", use_ws)
 
 
 def test_silu_mul_stage(dev, orc):
@@ -307,14 +335,80 @@ def test_determinism(dev):
     announce(f"determinism {w.name}")
     A, W1, W2 = (t.to(dev) for t in inputs.workload_inputs(w))
     Wf = sw.swiglu_pack_weights(W1, W2)
-    for variant in ("i", "s"):
+    for variant in ("i", "i+ws", "s"):
         y1 = run_fused(A, Wf, variant).clone()
         y2 = run_fused(A, Wf, variant)
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), variant
-    Y1, g1, u1 = sw.swiglu_unfused_ablation(A, Wf)
-    Y2, g2, u2 = sw.swiglu_unfused_ablation(A, Wf)
-    torch.cuda.synchronize()
-    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    ws = workspace_for(w.M, w.N, w.K, "ablation", dev)
+    for workspace in (None, ws):
+        Y1, g1, u1 = sw.swiglu_unfused_ablation(A, Wf, workspace=workspace)
+        Y1 = Y1.clone()
+        Y2, g2, u2 = sw.swiglu_unfused_ablation(A, Wf, workspace=workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+
+
+# (M, K, N) whose variant-I schedule splits tiles along K (256 CUs): every
+# tile split (32, 21, 36 pieces; 3 pieces with a K tail), whole tiles for a
+# full round plus split tail tiles, and the 128 x 64 tile shape of M <= 128
+SPLIT_TAIL = [(300, 1000, 136), (2048, 1536, 1032), (600, 4096, 392), (777, 520, 2056),
+              (100, 3000, 200), (3000, 2048, 3000), (70, 128, 520)]
+
+
+@pytest.mark.parametrize("M,K,N", SPLIT_TAIL)
+def test_split_tail_shapes(dev, orc, M, K, N):
+    announce(f"split tail M={M} K={K} N={N}")
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 3 + K * 5 + N)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    Wf = sw.swiglu_pack_weights(W1d, W2d)
+    Y = run_fused(Ad, Wf, "i+ws")
+    yb = bits_of(Y)
+    hA, hW1, hW2 = inputs.bits(A), inputs.bits(W1), inputs.bits(W2)
+    if M * N * K <= 2 ** 31:
+        assert_parity(yb, orc.swiglu(hA, hW1, hW2), f"split tail {M}x{K}x{N}")
+    else:
+        rng = np.random.default_rng(M + N + K)
+        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+        assert_parity(yb[rows], orc.swiglu_rows(hA, hW1, hW2, rows),
+                      f"split tail rows {M}x{K}x{N}")
+        pr, pc = rng.integers(0, M, 4000), rng.integers(0, N, 4000)
+        assert_parity(yb[pr, pc], orc.swiglu_points(hA, hW1, hW2, pr, pc),
+                      f"split tail points {M}x{K}x{N}")
+    # the one-kernel schedule agrees within the accuracy bound
+    yd = bits_of(run_fused(Ad, Wf, "i"))
+    a, b = oracle_pkg.bf16_bits_to_f64(yb), oracle_pkg.bf16_bits_to_f64(yd)
+    assert np.all(np.abs(a - b) <= np.maximum(2e-3, 2.05e-2 * np.maximum(np.abs(a), np.abs(b))))
+
+
+def test_workspace_reuse_sizes(dev, orc):
+    """One workspace across calls of different shapes, large then small then
+    large: counters left by a call never leak into the next."""
+    ws = None
+    for (M, K, N) in [(1030, 512, 1000), (260, 264, 136), (1030, 512, 1000), (70, 128, 520)]:
+        announce(f"workspace reuse M={M} K={K} N={N}")
+        A, W1, W2 = inputs.make_inputs(M, K, N, seed=M + 2 * K + 3 * N)
+        need = sw.swiglu_workspace_size(M, N, K, "i")
+        if ws is None:
+            ws = torch.empty(sw.swiglu_workspace_size(1030, 1000, 512, "i"), dtype=torch.uint8,
+                             device=dev)
+        assert ws.numel() >= need
+        Ad, Wf = A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+        Y = sw.swiglu_fused_gemm(Ad, Wf, variant="i", workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(bits_of(Y), orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2)),
+                      f"reuse {M}x{K}x{N}")
+
+
+def test_workspace_too_small_falls_back(dev, orc):
+    announce("workspace too small")
+    M, K, N = 300, 256, 264
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=5)
+    Ad, Wf = A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    small = torch.zeros(1024, dtype=torch.uint8, device=dev)
+    Y = sw.swiglu_fused_gemm(Ad, Wf, variant="i", workspace=small)
+    Yd = run_fused(Ad, Wf, "i")
+    assert torch.equal(Y.view(torch.int16), Yd.view(torch.int16))   # the same DP schedule
+    assert int(small.abs().sum().item()) == 0                          # untouched
 
 
 @pytest.mark.parametrize("M,expect", [(2047, "i"), (2048, "i"), (2049, "s")])
@@ -339,9 +433,12 @@ def test_non_default_stream(dev, orc):
         Wf = sw.swiglu_pack_weights(W1d, W2d)
         Yi = sw.swiglu_fused_gemm(Ad, Wf, variant="i")
         Ys = sw.swiglu_fused_gemm(Ad, Wf, variant="s")
+        ws = torch.empty(sw.swiglu_workspace_size(M, N, K, "i"), dtype=torch.uint8, device=dev)
+        Yk = sw.swiglu_fused_gemm(Ad, Wf, variant="i", workspace=ws)
     s.synchronize()
     assert_parity(bits_of(Yi), ref, "stream i")
     assert_parity(bits_of(Ys), ref, "stream s")
+    assert_parity(bits_of(Yk), ref, "stream i+ws")
 
 
 def test_empty_and_invalid_on_device(dev):

@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX]
                     [--variant auto|i|s] [--no-cpu-baseline]
+    python bench.py --sweep [--sweep-m 128,256,...]
 
 A step is one pass of the hot path over one batch of synthetic input: the
 fused call Y = SiLU(A.W1) (.) (A.W2) with the M-based dispatch (the weight
@@ -14,6 +15,11 @@ Prints ONE JSON line: TFLOP/s (4 M N K per step), the fraction of the bf16
 dense MFMA peak, the speedup over the unfused ablation (two GEMMs + SiLU-mul
 from the same mainloop, timed the same way), a roofline record for the fused
 kernel and the CPU oracle's throughput on a bounded sample.
+
+--sweep instead times variant I, variant S and the ablation over a range of M
+for each of the five K x N shapes of the workloads (inputs drawn on the
+device from the same distributions; the same rotation rule) and prints one
+JSON line per (shape, M): the data behind the M threshold of the dispatcher.
 """
 from __future__ import annotations
 
@@ -44,7 +50,75 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one device copy of known size (for HBM counter scaling)")
+    p.add_argument("--sweep", action="store_true",
+                   help="time I, S and the ablation over M for the five K x N shapes")
+    p.add_argument("--sweep-m", default="128,256,512,1024,2048,3072,4096,8192,16384")
     return p.parse_args()
+
+
+def sweep(args):
+    """Variant I vs S vs the ablation over M, per K x N shape (one JSON line each)."""
+    import torch
+
+    from gated_mlp_gemm_amd import inputs
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    sw.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    ms_list = [int(x) for x in args.sweep_m.split(",")]
+    shapes = sorted({(w.K, w.N) for w in inputs.WORKLOADS}, key=lambda kn: kn[0] * kn[1])
+    for K, N in shapes:
+        g = torch.Generator(device=dev)
+        g.manual_seed(K * 131 + N)
+        W1 = (torch.randn(K, N, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16)
+        W2 = (torch.randn(K, N, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16)
+        Wf = sw.swiglu_pack_weights(W1, W2)
+        del W1, W2
+        A_all = torch.randn(max(ms_list), K, device=dev, generator=g).to(torch.bfloat16)
+        ws = {v: sw.make_workspace(max(ms_list), N, K, v, dev) for v in ("i", "ablation")}
+        for M in ms_list:
+            step_bytes = 2 * (M * K + 2 * K * N + M * N)
+            R = max(1, -(-512 * 2 ** 20 // step_bytes))
+            A = A_all[:M]
+            copies = [(A, Wf)] + [(A.clone(), Wf.clone()) for _ in range(R - 1)]
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            G = torch.empty_like(Y)
+            U = torch.empty_like(Y)
+            calls = {
+                "i": lambda a, w: sw.swiglu_fused_gemm(a, w, Y=Y, variant="i", workspace=ws["i"]),
+                "s": lambda a, w: sw.swiglu_fused_gemm(a, w, Y=Y, variant="s"),
+                "ablation": lambda a, w: sw.swiglu_unfused_ablation(a, w, G, U, Y,
+                                                                    workspace=ws["ablation"]),
+            }
+            rec = {"K": K, "N": N, "M": M, "rotation_copies": R, "us": {}, "tflops": {}}
+            for name, fn in calls.items():
+                for r in range(3):
+                    fn(*copies[r % R])
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fn(*copies[0])
+                torch.cuda.synchronize()
+                est = max(time.perf_counter() - t0, 1e-6)
+                reps = int(min(100, max(5, 0.03 / est)))
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for r in range(reps):
+                    fn(*copies[r % R])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / reps * 1e3
+                rec["us"][name] = round(us, 2)
+                rec["tflops"][name] = round(4 * M * N * K / (us * 1e-6) / 1e12, 1)
+            rec["fastest_fused"] = min(("i", "s"), key=lambda v: rec["us"][v])
+            rec["speedup_i_vs_ablation"] = round(rec["us"]["ablation"] / rec["us"]["i"], 3)
+            rec["speedup_s_vs_ablation"] = round(rec["us"]["ablation"] / rec["us"]["s"], 3)
+            print(json.dumps(rec), flush=True)
+            del copies, Y, G, U
+        del Wf, A_all, ws
+        torch.cuda.empty_cache()
 
 
 def kernel_source_hash() -> str:
@@ -77,6 +151,9 @@ def main():
               "kernel here (a column split of N needs no communication; see the design "
               "notes); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
 
     import numpy as np
     import torch

@@ -162,7 +162,10 @@ struct PairMulEpilogue {
 #pragma unroll
         for (int tm = 0; tm < S::TM; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < S::TN; ++tn) block<S>(acc[tm][tn], tm, tn, m0, n0, tid);
+            for (int tn = 0; tn < S::TN; ++tn) {
+                block<S>(acc[tm][tn], tm, tn, m0, n0, tid);
+                __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
+            }
     }
 };
 
@@ -201,7 +204,10 @@ struct StoreEpilogue {
 #pragma unroll
         for (int tm = 0; tm < S::TM; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < S::TN; ++tn) block<S>(acc[tm][tn], tm, tn, m0, n0, tid);
+            for (int tn = 0; tn < S::TN; ++tn) {
+                block<S>(acc[tm][tn], tm, tn, m0, n0, tid);
+                __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
+            }
     }
 };
 
@@ -371,8 +377,15 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
 // ---------------------------------------------------------------------------
 // Tile shapes and launchers
 // ---------------------------------------------------------------------------
-using ShapeWide = TileShape<256, 256, 32, 2, 4, 4>;    // I and ablation GEMM (ping-pong)
-using ShapeSeq = TileShape<256, 128, 64, 4, 2, 3>;     // S: two 256x128 accumulators (ping-pong)
+// I and the ablation GEMMs: 4 waves, one per SIMD, each with a 128x128 block
+// (256 accumulator registers, which the compiler keeps in AGPRs), BK = 64 and
+// a two-stage ring (128 KiB of LDS).  S: 4 waves holding the Gate and the Up
+// accumulators of a 256x128 tile (2 x 128 registers), three stages (144 KiB).
+// Measured against the 8-wave ping-pong shapes (256x256x32, 4 stages for I;
+// 256x128x64, 3 stages for S) these are 10-16 % (I) and 5-9 % (S) faster on
+// M=2048..8192 outputs.
+using ShapeWide = TileShape<256, 256, 64, 2, 2, 2>;
+using ShapeSeq = TileShape<256, 128, 64, 2, 2, 3>;
 using ShapeSmall = TileShape<128, 64, 32, 2, 2, 4>;    // M <= 128: more tiles on the weights
 
 static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }

@@ -152,15 +152,18 @@ int swiglu_silu_mul(const uint16_t *gate, const uint16_t *up, uint16_t *Y,
 
 /*
  * The variant SWIGLU_AUTO runs for this shape: SWIGLU_VARIANT_I when
- * M <= swiglu_m_switch(), else SWIGLU_VARIANT_S (the pages aim the interleaved
- * kernel at small batches and the sequential one at large batches;
- * gist.science technical summary, Method, Kernel-1 and Kernel-2).  Host only,
- * no HIP call.  Returns SWIGLU_ERR_SHAPE for M < 0.
+ * M <= swiglu_m_switch(), else SWIGLU_VARIANT_S.  The pages aim the
+ * interleaved kernel at small batches and the sequential one at large batches
+ * (gist.science technical summary, Method, Kernel-1 and Kernel-2); on MI355X
+ * the interleaved kernel measured faster at every M (128 to 16384) of the five
+ * benchmark K x N shapes, so the built-in threshold is 2^31 - 1 (always I).
+ * Host only, no HIP call.  Returns SWIGLU_ERR_SHAPE for M < 0.
  */
 int swiglu_select_variant(int64_t M, int64_t N, int64_t K);
 
-/* The M threshold used by swiglu_select_variant (environment variable
- * SWIGLU_M_SWITCH overrides the built-in value when it parses as an integer). */
+/* The M threshold used by swiglu_select_variant: 2^31 - 1 unless the
+ * environment variable SWIGLU_M_SWITCH parses as an integer (e.g. 2048 for the
+ * pages' small/large-batch split), which then overrides it. */
 int64_t swiglu_m_switch(void);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */

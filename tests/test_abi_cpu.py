@@ -40,19 +40,22 @@ def test_status_strings(lib):
 
 
 def test_dispatcher_thresholds(lib, monkeypatch):
+    # built-in: variant I at every M (measured faster than S on MI355X)
     monkeypatch.delenv("SWIGLU_M_SWITCH", raising=False)
-    assert sw.swiglu_m_switch() == 2048
-    for M in (1, 128, 2047, 2048):
+    assert sw.swiglu_m_switch() == 2 ** 31 - 1
+    for M in (0, 1, 128, 2048, 2049, 8192, 2 ** 31 - 1):
         assert sw.swiglu_select_variant(M, 8960, 1536) == sw.SWIGLU_VARIANT_I
-    for M in (2049, 4096, 8192):
-        assert sw.swiglu_select_variant(M, 8960, 1536) == sw.SWIGLU_VARIANT_S
     assert lib.swiglu_select_variant(-1, 8, 8) == ERR_SHAPE
+    # the pages' small/large-batch split, set through the environment
+    monkeypatch.setenv("SWIGLU_M_SWITCH", "2048")
+    assert sw.swiglu_m_switch() == 2048
+    assert sw.swiglu_select_variant(2048) == sw.SWIGLU_VARIANT_I
+    assert sw.swiglu_select_variant(2049) == sw.SWIGLU_VARIANT_S
     monkeypatch.setenv("SWIGLU_M_SWITCH", "100")
-    assert sw.swiglu_m_switch() == 100
     assert sw.swiglu_select_variant(100) == sw.SWIGLU_VARIANT_I
     assert sw.swiglu_select_variant(101) == sw.SWIGLU_VARIANT_S
     monkeypatch.setenv("SWIGLU_M_SWITCH", "not-a-number")
-    assert sw.swiglu_m_switch() == 2048
+    assert sw.swiglu_m_switch() == 2 ** 31 - 1
 
 
 def fused(lib, A=A_, WF=WF_, Y=Y_, M=256, N=256, K=256, v=2, ws=None, wsb=0):

@@ -411,9 +411,13 @@ def test_workspace_too_small_falls_back(dev, orc):
     assert int(small.abs().sum().item()) == 0                          # untouched
 
 
-@pytest.mark.parametrize("M,expect", [(2047, "i"), (2048, "i"), (2049, "s")])
-def test_auto_dispatch_matches_named_variant(dev, M, expect, monkeypatch):
-    monkeypatch.delenv("SWIGLU_M_SWITCH", raising=False)
+@pytest.mark.parametrize("M,switch,expect", [(2047, None, "i"), (2049, None, "i"),
+                                             (2048, "2048", "i"), (2049, "2048", "s")])
+def test_auto_dispatch_matches_named_variant(dev, M, switch, expect, monkeypatch):
+    if switch is None:
+        monkeypatch.delenv("SWIGLU_M_SWITCH", raising=False)
+    else:
+        monkeypatch.setenv("SWIGLU_M_SWITCH", switch)
     announce(f"dispatch M={M}")
     A, W1, W2 = (t.to(dev) for t in inputs.make_inputs(M, 64, 64, seed=M))
     Wf = sw.swiglu_pack_weights(W1, W2)

@@ -90,11 +90,22 @@ int check_device(int *cus = nullptr) {
     return SWIGLU_OK;
 }
 
+// SWIGLU_I_TILE=256 or 128 forces the tile of variant I and the ablation
+// GEMMs above M = 128 (testing, measurement); anything else: the cost model.
+int tile_override() {
+    const char *s = std::getenv("SWIGLU_I_TILE");
+    if (s == nullptr) return 0;
+    if (std::strcmp(s, "256") == 0) return 256;
+    if (std::strcmp(s, "128") == 0) return 128;
+    return 0;
+}
+
 swiglu::GemmWorkspace make_ws(void *workspace, uint64_t bytes, int cus) {
     swiglu::GemmWorkspace ws{};
     ws.base = bytes > 0 ? workspace : nullptr;
     ws.bytes = workspace ? bytes : 0;
     ws.cus = cus;
+    ws.tile = tile_override();
     return ws;
 }
 

@@ -63,6 +63,9 @@ struct TileShape {
     static constexpr int kDmaPerStep = kDmaA + kDmaB;
     // 8 waves (two per SIMD) run the ping-pong schedule; 4 waves the plain one
     static constexpr bool kPingPong = (kWaves == 8);
+    // workgroups resident per CU that the kernel is built for: two when two
+    // fit the 160 KiB of LDS (the kernel then keeps to 256 registers a lane)
+    static constexpr int kOccupancy = (2 * kLdsBytes <= 160 * 1024) ? 2 : 1;
 
     static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");

@@ -10,6 +10,8 @@
 #include "gemm_core.hpp"
 #include "split_tail.hpp"
 
+#include <cmath>
+
 namespace swiglu {
 
 // ---------------------------------------------------------------------------
@@ -217,7 +219,7 @@ struct StoreEpilogue {
 // dp + j / pieces and stores its partial (split_tail.hpp), which
 // split_reduce_kernel finishes.  A workgroup runs one tile or piece: no loop.
 template <class S, class Epi, bool SPLIT>
-__global__ __launch_bounds__(S::kThreads, 1) void gemm_tiles_kernel(
+__global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
     const uint16_t *__restrict__ A, KMajor B, int M, int K, Epi epi, Schedule sch) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_tiles_kernel(
         ke = (piece + 1) * sch.nk / sch.pieces;
     }
     int tm, tn;
-    tile_coords(t, sch.tiles_m, sch.tiles_n, 8, tm, tn);
+    tile_coords(t, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
     const int m0 = tm * S::BM;
     const int n0 = tn * S::BN;
 
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch
     const int x = w * 64 + static_cast<int>(threadIdx.x & 63);
     const f32x16 a = sum_pieces<S>(sch, i, blk, x);
     int tm, tn;
-    tile_coords(sch.dp + i, sch.tiles_m, sch.tiles_n, 8, tm, tn);
+    tile_coords(sch.dp + i, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
     epi.template block<S>(a, blk / S::TN, blk % S::TN, tm * S::BM, tn * S::BN, x);
 }
 
@@ -385,6 +387,11 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
 // 256x128x64, 3 stages for S) these are 10-16 % (I) and 5-9 % (S) faster on
 // M=2048..8192 outputs.
 using ShapeWide = TileShape<256, 256, 64, 2, 2, 2>;
+// The alternative for I and the ablation GEMMs: 128x128x64 tiles, 4 waves of
+// 64x64, two stages (64 KiB), so two workgroups share a CU and one's prologue
+// and epilogue overlap the other's mainloop; four times the tiles also fill
+// the last round better.  Chosen per call by quad_tiles_faster().
+using ShapeQuad = TileShape<128, 128, 64, 2, 2, 2>;
 using ShapeSeq = TileShape<256, 128, 64, 2, 2, 3>;
 using ShapeSmall = TileShape<128, 64, 32, 2, 2, 4>;    // M <= 128: more tiles on the weights
 
@@ -415,24 +422,36 @@ hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, in
     return hipGetLastError();
 }
 
+// Rough time of one K step of a round of S tiles on MI355X (us): 2.1 for a
+// 256x256x64 step, scaled by tile volume and by the workgroups sharing a CU.
+// With the fixed cost of a split tail (the reduction kernel, its launch and
+// the pieces' partial traffic: about 25 us) it decides when splitting pays.
+template <class S>
+constexpr double step_us() {
+    return 2.1 * (static_cast<double>(S::BM) * S::BN * S::BK) / (256.0 * 256.0 * 64.0) *
+           S::kOccupancy;
+}
+constexpr double kSplitCostUs = 25.0;
+
 // Work schedule for a single-accumulator GEMM over an M x cols output (see
 // split_tail.hpp): all tiles whole unless the last round is partly idle, a
-// workspace is given and splitting the tail into s >= 2 pieces shortens it
-// by more than the reduction costs (reckoned as two K steps).
+// workspace is given and splitting the tail into s >= 2 pieces saves more
+// than the split costs.
 template <class S>
 static Schedule make_schedule(int M, int cols, int K, const GemmWorkspace &ws) {
     Schedule sch{};
     sch.tiles_m = cdiv(M, S::BM);
     sch.tiles_n = cdiv(cols, S::BN);
     sch.nk = cdiv(K, S::BK);
+    sch.group_m = 8;
     const int64_t T = static_cast<int64_t>(sch.tiles_m) * sch.tiles_n;
     sch.dp = static_cast<int>(T);
-    const int G = ws.cus;
-    if (ws.base == nullptr || G <= 0 || ws.bytes < workspace_bytes_for(G)) return sch;
+    const int G = ws.cus * S::kOccupancy;           // workgroup slots
+    if (ws.base == nullptr || G <= 0 || ws.bytes < workspace_bytes_for(ws.cus)) return sch;
     const int64_t L = T % G;
     if (L == 0) return sch;
     const int pieces = static_cast<int>(min(static_cast<int64_t>(G) / L, static_cast<int64_t>(sch.nk)));
-    if (pieces < 2 || cdiv(sch.nk, pieces) + 2 >= sch.nk) return sch;
+    if (pieces < 2 || (sch.nk - cdiv(sch.nk, pieces)) * step_us<S>() <= kSplitCostUs) return sch;
     sch.dp = static_cast<int>(T - L);
     sch.pieces = pieces;
     sch.split_tiles = static_cast<int>(L);
@@ -461,11 +480,41 @@ static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int 
     return hipGetLastError();
 }
 
+// Tile choice for an M x cols single-accumulator GEMM above M = 128: the
+// 128x128 two-per-CU tiles when they are predicted faster than the 256x256
+// tiles.  Each schedule's time is counted in rounds of its own tiles (a split
+// tail: 1/s of a round plus the split cost); a round of 256x256 tiles costs
+// r(K) rounds of 128x128 tiles, r measured on MI355X at 2.11 (K = 1536), 1.87
+// (K = 5120) and 1.79 (K = 8192) and taken as log-linear in K: the big tiles
+// gain on longer mainloops, the small ones hide prologue and epilogue better.
+template <class S>
+static double schedule_rounds(const Schedule &sch, int cus) {
+    const double G = static_cast<double>(cus) * S::kOccupancy;
+    const double full = sch.dp / G;
+    if (sch.pieces)
+        return full + 1.0 / sch.pieces + kSplitCostUs / (step_us<S>() * sch.nk);
+    return std::ceil(full);
+}
+
+static bool quad_tiles_faster(int M, int cols, int K, const GemmWorkspace &ws) {
+    if (ws.tile == 256) return false;
+    if (ws.tile == 128) return true;
+    if (ws.cus <= 0) return false;
+    const double rounds_wide =
+        schedule_rounds<ShapeWide>(make_schedule<ShapeWide>(M, cols, K, ws), ws.cus);
+    const double rounds_quad =
+        schedule_rounds<ShapeQuad>(make_schedule<ShapeQuad>(M, cols, K, ws), ws.cus);
+    const double r = 2.11 - 0.138 * std::log2(K / 1536.0);
+    return rounds_quad < rounds_wide * r;
+}
+
 hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
                                     int N, int K, const GemmWorkspace &ws, hipStream_t stream) {
     const KMajor B{Wf, 2 * N, 1, 0};
     const PairMulEpilogue epi{Y, M, N};
     if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, 2 * N, K, epi, ws, stream);
+    if (quad_tiles_faster(M, 2 * N, K, ws))
+        return launch_gemm<ShapeQuad>(A, B, M, 2 * N, K, epi, ws, stream);
     return launch_gemm<ShapeWide>(A, B, M, 2 * N, K, epi, ws, stream);
 }
 
@@ -483,11 +532,13 @@ hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, u
     const KMajor B{Wf, N, 2, phase};
     const StoreEpilogue epi{C, M, N};
     if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, N, K, epi, ws, stream);
+    if (quad_tiles_faster(M, N, K, ws)) return launch_gemm<ShapeQuad>(A, B, M, N, K, epi, ws, stream);
     return launch_gemm<ShapeWide>(A, B, M, N, K, epi, ws, stream);
 }
 
-// One partial slot per CU (at most G pieces exist), sized for the largest
-// tile shape.
+// One 256x256 fp32 slot per CU: a split schedule has at most one piece per
+// workgroup slot, and a CU holds one 256x256 workgroup or two of the smaller
+// shapes (whose slots are a quarter the size or less).
 uint64_t partials_bytes(int cus) {
     return static_cast<uint64_t>(cus) * ShapeWide::BM * ShapeWide::BN * sizeof(float);
 }

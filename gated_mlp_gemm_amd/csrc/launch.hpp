@@ -13,6 +13,7 @@ struct GemmWorkspace {
     void *base;
     uint64_t bytes;
     int cus;          // compute units of the device
+    int tile;         // variant I / ablation GEMM tile: 0 = by the cost model, 256 or 128 = forced
 };
 // Scratch that lets the single-accumulator GEMMs split the tiles of a partial
 // last round along K (the same for every shape: one fp32 256 x 256 tile slot

@@ -33,6 +33,7 @@ struct Schedule {
     int dp;                 // tiles [0, dp) run whole: workgroup b < dp runs one of them
     int pieces;             // K pieces per split tile (0: no split tiles)
     int split_tiles;        // tiles [dp, dp + split_tiles) are split
+    int group_m;            // tile order: groups of group_m tile rows (tile_coords)
     float *partials;        // one BM*BN slot per piece: slot j = piece j % pieces of split tile j / pieces
 };
 

@@ -35,6 +35,14 @@ def announce(msg: str):
     print(f"\n[case] {msg}", flush=True)
 
 
+@pytest.fixture(autouse=True)
+def _default_dispatch(monkeypatch):
+    """Every test starts from the built-in dispatch (tests that force a
+    variant threshold or a tile shape set the variable themselves)."""
+    monkeypatch.delenv("SWIGLU_M_SWITCH", raising=False)
+    monkeypatch.delenv("SWIGLU_I_TILE", raising=False)
+
+
 @pytest.fixture(scope="module")
 def orc():
     return oracle_pkg.load()
@@ -129,6 +137,20 @@ def test_small_shapes(dev, orc, M, K, N, variant):
     Wf = sw.swiglu_pack_weights(W1d, W2d)
     Y = run_fused(Ad, Wf, variant)
     assert_parity(bits_of(Y), ref, f"{variant} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(130, 200, 72), (257, 136, 264), (300, 1000, 136),
+                                   (513, 64, 1032), (700, 72, 392)])
+@pytest.mark.parametrize("tile", ["256", "128"])
+def test_small_shapes_forced_tile(dev, orc, M, K, N, tile, monkeypatch):
+    """Both tile shapes of variant I above M = 128, with and without workspace."""
+    monkeypatch.setenv("SWIGLU_I_TILE", tile)
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 31 + K * 7 + N)
+    ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
+    Ad, Wf = A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    for variant in ("i", "i+ws"):
+        announce(f"fused {variant} tile={tile} M={M} K={K} N={N}")
+        assert_parity(bits_of(run_fused(Ad, Wf, variant)), ref, f"{variant}@{tile} {M}x{K}x{N}")
 
 
 def _pad(a, rows, cols):
@@ -297,10 +319,17 @@ def _check_ablation(orc, A, W1, W2, rows, dev, what, use_ws=False):
 
 
 @pytest.mark.parametrize("M,K,N", [(5, 16, 24), (130, 200, 72), (257, 136, 264),
-                                   (128, 896, 4864)])
+                                   (128, 896, 4864), (600, 4096, 392)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["dp", "ws"])
-def test_ablation_small(dev, orc, M, K, N, use_ws):
-    announce(f"ablation M={M} K={K} N={N} workspace={use_ws}")
+@pytest.mark.parametrize("tile", [None, "256", "128"])
+def test_ablation_small(dev, orc, M, K, N, use_ws, tile, monkeypatch):
+    if tile is None:
+        monkeypatch.delenv("SWIGLU_I_TILE", raising=False)
+    else:
+        if M <= 128:
+            pytest.skip("one tile shape at M <= 128")
+        monkeypatch.setenv("SWIGLU_I_TILE", tile)
+    announce(f"ablation M={M} K={K} N={N} workspace={use_ws} tile={tile}")
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=M + K + N)
     _check_ablation(orc, A, W1, W2, np.arange(M), dev, f"ablation {M}x{K}x{N}", use_ws)
 
@@ -348,16 +377,22 @@ def test_determinism(dev):
         assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
 
 
-# (M, K, N) whose variant-I schedule splits tiles along K (256 CUs): every
-# tile split (32, 21, 36 pieces; 3 pieces with a K tail), whole tiles for a
-# full round plus split tail tiles, and the 128 x 64 tile shape of M <= 128
+# (M, K, N) for the two tile shapes above M = 128 (forced through
+# SWIGLU_I_TILE) and their schedules on 256 CUs: 256x256 tiles split 16, 3
+# and 21 ways, whole tiles for a full round plus split tail tiles (8 and 4
+# pieces), 128x128 tiles split 14 and 4 ways; tiles whole with K tails; and
+# 128x64 tiles (M <= 128) split 64 ways over a long K.
 SPLIT_TAIL = [(300, 1000, 136), (2048, 1536, 1032), (600, 4096, 392), (777, 520, 2056),
-              (100, 3000, 200), (3000, 2048, 3000), (70, 128, 520)]
+              (3000, 2048, 3000), (70, 128, 520), (128, 8192, 256)]
 
 
 @pytest.mark.parametrize("M,K,N", SPLIT_TAIL)
-def test_split_tail_shapes(dev, orc, M, K, N):
-    announce(f"split tail M={M} K={K} N={N}")
+@pytest.mark.parametrize("tile", ["256", "128"])
+def test_split_tail_shapes(dev, orc, M, K, N, tile, monkeypatch):
+    if M <= 128 and tile == "128":
+        pytest.skip("one tile shape at M <= 128")
+    monkeypatch.setenv("SWIGLU_I_TILE", tile)
+    announce(f"split tail M={M} K={K} N={N} tile={tile}")
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 3 + K * 5 + N)
     Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
     Wf = sw.swiglu_pack_weights(W1d, W2d)

@@ -248,10 +248,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    # variant I with a workspace is two launches (the GEMM, then the split-tail
-    # reduction); the record covers the whole fused call
-    kernel = ("gemm_tiles_kernel<256x256x64, PairMulEpilogue> + split_reduce_kernel"
-              if vname == "i" else "fused_sequential_kernel<256x128x64>")
+    # what the fused call launches (tile shape and schedule chosen by the
+    # library; with a split tail, two kernels: the record covers the call)
+    ws_used = scratch[args.variant]
+    kernel = sw.swiglu_describe_launch(M, N, K, args.variant,
+                                       0 if ws_used is None else ws_used.numel())
     workload = f"M={M},K={K},N={N}"
     roofline = {
         "bound": "mfma",

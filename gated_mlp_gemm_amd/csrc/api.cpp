@@ -193,6 +193,38 @@ int swiglu_workspace_size(int64_t M, int64_t N, int64_t K, int variant, uint64_t
     return ok();
 }
 
+int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
+                           uint64_t workspace_bytes, char *buf, uint64_t buf_bytes) {
+    if (!buf || buf_bytes == 0) return fail(SWIGLU_ERR_NULL, "buf is required");
+    buf[0] = '\0';
+    if (variant < -1 || variant > SWIGLU_VARIANT_I)
+        return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
+    int st = check_gemm_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0 || N == 0) {
+        std::snprintf(buf, buf_bytes, "nothing (empty problem)");
+        return ok();
+    }
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != SWIGLU_OK) return st;
+    // only the size of the workspace matters for the plan
+    const swiglu::GemmWorkspace ws =
+        make_ws(workspace_bytes ? reinterpret_cast<void *>(uintptr_t{256}) : nullptr,
+                workspace_bytes, cus);
+    const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
+    if (v == SWIGLU_VARIANT_S) {
+        swiglu::describe_fused_sequential((int)M, (int)N, buf, buf_bytes);
+    } else if (v == SWIGLU_VARIANT_I) {
+        swiglu::describe_gemm((int)M, (int)(2 * N), (int)K, ws, "PairMulEpilogue", buf, buf_bytes);
+    } else {
+        char g[256];
+        swiglu::describe_gemm((int)M, (int)N, (int)K, ws, "StoreEpilogue", g, sizeof g);
+        std::snprintf(buf, buf_bytes, "2 x %s + silu_mul_kernel", g);
+    }
+    return ok();
+}
+
 int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, int64_t M,
                       int64_t N, int64_t K, int variant, void *workspace,
                       uint64_t workspace_bytes, void *stream) {

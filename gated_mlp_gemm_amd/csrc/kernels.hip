@@ -11,6 +11,7 @@
 #include "split_tail.hpp"
 
 #include <cmath>
+#include <cstdio>
 
 namespace swiglu {
 
@@ -516,6 +517,41 @@ hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint1
     if (quad_tiles_faster(M, 2 * N, K, ws))
         return launch_gemm<ShapeQuad>(A, B, M, 2 * N, K, epi, ws, stream);
     return launch_gemm<ShapeWide>(A, B, M, 2 * N, K, epi, ws, stream);
+}
+
+// The kernels launch_fused_interleaved / launch_fused_sequential /
+// launch_gemm_store (one of the ablation's two GEMMs) would run, as text.
+template <class S>
+static int describe(const char *kernel, const char *epi, const Schedule &sch, char *buf,
+                    size_t n) {
+    if (sch.pieces)
+        return std::snprintf(buf, n,
+                             "%s<%dx%dx%d,%s> (%d whole tiles + %d tiles split %d ways along K)"
+                             " + split_reduce_kernel",
+                             kernel, S::BM, S::BN, S::BK, epi, sch.dp, sch.split_tiles,
+                             sch.pieces);
+    return std::snprintf(buf, n, "%s<%dx%dx%d,%s> (%d tiles)", kernel, S::BM, S::BN, S::BK,
+                         epi, sch.dp);
+}
+
+int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *epi, char *buf,
+                  size_t n) {
+    if (M <= 128)
+        return describe<ShapeSmall>("gemm_tiles_kernel", epi,
+                                    make_schedule<ShapeSmall>(M, cols, K, ws), buf, n);
+    if (quad_tiles_faster(M, cols, K, ws))
+        return describe<ShapeQuad>("gemm_tiles_kernel", epi,
+                                   make_schedule<ShapeQuad>(M, cols, K, ws), buf, n);
+    return describe<ShapeWide>("gemm_tiles_kernel", epi, make_schedule<ShapeWide>(M, cols, K, ws),
+                               buf, n);
+}
+
+int describe_fused_sequential(int M, int N, char *buf, size_t n) {
+    const bool small = M <= 128;
+    const int bm = small ? ShapeSmall::BM : ShapeSeq::BM, bn = small ? ShapeSmall::BN : ShapeSeq::BN;
+    const int bk = small ? ShapeSmall::BK : ShapeSeq::BK;
+    return std::snprintf(buf, n, "fused_sequential_kernel<%dx%dx%d> (%lld tiles)", bm, bn, bk,
+                         static_cast<long long>(cdiv(M, bm)) * cdiv(N, bn));
 }
 
 hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,

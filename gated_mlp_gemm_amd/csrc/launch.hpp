@@ -21,6 +21,12 @@ struct GemmWorkspace {
 uint64_t partials_bytes(int cus);
 uint64_t workspace_bytes_for(int cus);
 
+// Text naming the kernels (tile shape, schedule) a GEMM over an M x cols
+// output would launch (snprintf semantics).
+int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *epi, char *buf,
+                  size_t n);
+int describe_fused_sequential(int M, int N, char *buf, size_t n);
+
 hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,
                        int64_t N, hipStream_t stream);
 hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,

@@ -60,6 +60,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_fused_gemm.argtypes = [P, P, P, I64, I64, I64, I32, P, U64, P]
     lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, I64, I64, I64, P, U64, P]
     lib.swiglu_workspace_size.argtypes = [I64, I64, I64, I32, ctypes.POINTER(U64)]
+    lib.swiglu_describe_launch.argtypes = [I64, I64, I64, I32, U64, ctypes.c_char_p, U64]
     lib.swiglu_silu_mul.argtypes = [P, P, P, I64, P]
     lib.swiglu_select_variant.argtypes = [I64, I64, I64]
     lib.swiglu_m_switch.argtypes = []
@@ -69,7 +70,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_last_error.argtypes = []
     lib.swiglu_last_error.restype = ctypes.c_char_p
     for name in ("swiglu_pack_weights", "swiglu_fused_gemm", "swiglu_unfused_ablation",
-                 "swiglu_silu_mul", "swiglu_select_variant", "swiglu_workspace_size"):
+                 "swiglu_silu_mul", "swiglu_select_variant", "swiglu_workspace_size",
+                 "swiglu_describe_launch"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -150,6 +152,17 @@ def swiglu_workspace_size(M: int, N: int, K: int, variant="auto") -> int:
     _check(load_library().swiglu_workspace_size(M, N, K, v, ctypes.byref(out)),
            "swiglu_workspace_size")
     return int(out.value)
+
+
+def swiglu_describe_launch(M: int, N: int, K: int, variant="auto",
+                           workspace_bytes: int = 0) -> str:
+    """The kernels a call would launch ('ablation' for the unfused pipeline)."""
+    v = -1 if variant == "ablation" else (VARIANTS[variant.lower()]
+                                          if isinstance(variant, str) else int(variant))
+    buf = ctypes.create_string_buffer(512)
+    _check(load_library().swiglu_describe_launch(M, N, K, v, workspace_bytes, buf, len(buf)),
+           "swiglu_describe_launch")
+    return buf.value.decode()
 
 
 def make_workspace(M: int, N: int, K: int, variant="auto", device="cuda") -> Optional[torch.Tensor]:

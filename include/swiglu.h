@@ -143,6 +143,18 @@ int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused,
                             uint64_t workspace_bytes, void *stream);
 
 /*
+ * What a call would launch, as text (host only; queries the current device's
+ * compute-unit count): for swiglu_fused_gemm with `variant` (AUTO, S, I) or
+ * for swiglu_unfused_ablation (-1), given a workspace of `workspace_bytes`
+ * (0: none), the kernel names with their tile shapes and schedule, e.g.
+ * "gemm_tiles_kernel<128x128x64,PairMulEpilogue> (2240 tiles)".  Writes at
+ * most buf_bytes bytes including the terminating NUL (truncating).  Same
+ * shape validation as the calls it describes; SWIGLU_ERR_NULL without buf.
+ */
+int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
+                           uint64_t workspace_bytes, char *buf, uint64_t buf_bytes);
+
+/*
  * The ablation's activation stage on its own: Y[i] = bf16(SiLU(gate[i]) *
  * up[i]) for i < count, fp32 arithmetic, one rounding.  count % 8 == 0,
  * count >= 0; pointers 16-byte aligned, device.

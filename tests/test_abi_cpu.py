@@ -151,6 +151,19 @@ def test_workspace_size_validation(lib):
     assert lib.swiglu_workspace_size(0, 256, 256, 2, ctypes.byref(out)) == 0 and out.value == 0
 
 
+def test_describe_launch_validation(lib):
+    import ctypes
+    buf = ctypes.create_string_buffer(128)
+    assert lib.swiglu_describe_launch(256, 256, 256, 2, 0, None, 0) == ERR_NULL
+    assert lib.swiglu_describe_launch(256, 256, 256, 5, 0, buf, len(buf)) == ERR_UNSUP
+    assert lib.swiglu_describe_launch(256, 20, 256, 2, 0, buf, len(buf)) == ERR_SHAPE
+    assert lib.swiglu_describe_launch(0, 256, 256, 2, 0, buf, len(buf)) == 0
+    assert buf.value == b"nothing (empty problem)"
+    tiny = ctypes.create_string_buffer(8)                 # truncates, stays terminated
+    assert lib.swiglu_describe_launch(0, 256, 256, -1, 0, tiny, len(tiny)) == 0
+    assert tiny.value == b"nothing"
+
+
 def test_silu_mul_validation(lib):
     F = lib.swiglu_silu_mul
     assert F(G_, U_, Y_, 12, None) == ERR_SHAPE

@@ -480,6 +480,22 @@ def test_non_default_stream(dev, orc):
     assert_parity(bits_of(Yk), ref, "stream i+ws")
 
 
+def test_describe_launch(dev, monkeypatch):
+    """The launch description names the kernels the dispatch picks."""
+    ws = sw.swiglu_workspace_size(2048, 8960, 1536, "i")
+    d = sw.swiglu_describe_launch(2048, 8960, 1536, "auto", ws)
+    assert d.startswith("gemm_tiles_kernel<") and "PairMulEpilogue" in d
+    monkeypatch.setenv("SWIGLU_I_TILE", "256")
+    d = sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws)
+    assert "256x256x64" in d and "split 5 ways" in d and d.endswith("split_reduce_kernel")
+    assert "split" not in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
+    monkeypatch.setenv("SWIGLU_I_TILE", "128")
+    assert "128x128x64" in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
+    assert sw.swiglu_describe_launch(2048, 8960, 1536, "s").startswith("fused_sequential_kernel<")
+    assert sw.swiglu_describe_launch(2048, 8960, 1536, "ablation").startswith("2 x gemm_tiles")
+    assert "128x64x32" in sw.swiglu_describe_launch(128, 4864, 896, "i")
+
+
 def test_empty_and_invalid_on_device(dev):
     A = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
     W = torch.zeros((64, 64), dtype=torch.bfloat16, device=dev)

@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch
 // registers).
 // ---------------------------------------------------------------------------
 template <class S>
-__global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
+__global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, uint16_t *__restrict__ Y,
     int M, int N, int K, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
@@ -382,18 +382,19 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_kernel(
 // ---------------------------------------------------------------------------
 // I and the ablation GEMMs: 4 waves, one per SIMD, each with a 128x128 block
 // (256 accumulator registers, which the compiler keeps in AGPRs), BK = 64 and
-// a two-stage ring (128 KiB of LDS).  S: 4 waves holding the Gate and the Up
-// accumulators of a 256x128 tile (2 x 128 registers), three stages (144 KiB).
-// Measured against the 8-wave ping-pong shapes (256x256x32, 4 stages for I;
-// 256x128x64, 3 stages for S) these are 10-16 % (I) and 5-9 % (S) faster on
-// M=2048..8192 outputs.
+// a two-stage ring (128 KiB of LDS); measured 10-16 % faster than the 8-wave
+// ping-pong 256x256x32 shape on M=2048..8192 outputs.
 using ShapeWide = TileShape<256, 256, 64, 2, 2, 2>;
 // The alternative for I and the ablation GEMMs: 128x128x64 tiles, 4 waves of
 // 64x64, two stages (64 KiB), so two workgroups share a CU and one's prologue
 // and epilogue overlap the other's mainloop; four times the tiles also fill
 // the last round better.  Chosen per call by quad_tiles_faster().
 using ShapeQuad = TileShape<128, 128, 64, 2, 2, 2>;
-using ShapeSeq = TileShape<256, 128, 64, 2, 2, 3>;
+// S: 128x128 output tiles, 4 waves each holding 64x64 Gate and Up
+// accumulators, two stages (64 KiB), two workgroups per CU; measured against
+// 256x128x64 (one per CU, 3 stages): 34 % faster at M=2048 K=1536 N=8960, 7 %
+// at M=8192 K=5120 N=13824, equal at M=4096 K=8192 N=29568.
+using ShapeSeq = TileShape<128, 128, 64, 2, 2, 2>;
 using ShapeSmall = TileShape<128, 64, 32, 2, 2, 4>;    // M <= 128: more tiles on the weights
 
 static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }

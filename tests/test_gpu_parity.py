@@ -378,10 +378,10 @@ def test_determinism(dev):
 
 
 # (M, K, N) for the two tile shapes above M = 128 (forced through
-# SWIGLU_I_TILE) and their schedules on 256 CUs: 256x256 tiles split 16, 3
-# and 21 ways, whole tiles for a full round plus split tail tiles (8 and 4
-# pieces), 128x128 tiles split 14 and 4 ways; tiles whole with K tails; and
-# 128x64 tiles (M <= 128) split 64 ways over a long K.
+# SWIGLU_I_TILE) and their schedules on 256 CUs: split tails of 2 to 21
+# pieces, whole tiles for a full round plus split tail tiles, tiles whole
+# with K tails, and the 128x64 tiles of M <= 128 split 32 ways over a long K
+# (the exact schedule of each case is what swiglu_describe_launch reports).
 SPLIT_TAIL = [(300, 1000, 136), (2048, 1536, 1032), (600, 4096, 392), (777, 520, 2056),
               (3000, 2048, 3000), (70, 128, 520), (128, 8192, 256)]
 
@@ -493,7 +493,7 @@ def test_describe_launch(dev, monkeypatch):
     assert "128x128x64" in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
     assert sw.swiglu_describe_launch(2048, 8960, 1536, "s").startswith("fused_sequential_kernel<")
     assert sw.swiglu_describe_launch(2048, 8960, 1536, "ablation").startswith("2 x gemm_tiles")
-    assert "128x64x32" in sw.swiglu_describe_launch(128, 4864, 896, "i")
+    assert "128x64x64" in sw.swiglu_describe_launch(128, 4864, 896, "i")
 
 
 def test_empty_and_invalid_on_device(dev):

@@ -61,22 +61,43 @@ __device__ __forceinline__ void store_partial(float *slot, const f32x16 (&acc)[S
 }
 
 // Accumulator block `blk` of GEMM thread x of split tile i: the sum, in
-// piece order, of the pieces' partials.
+// piece order, of the pieces' partials.  The loads of up to four pieces are
+// issued together before any is added (a plain loop would wait out one memory
+// round trip per piece); the additions still run strictly in piece order, so
+// the result does not depend on the grouping.
 template <class S>
 __device__ __forceinline__ f32x16 sum_pieces(const Schedule &sch, int i, int blk, int x) {
-    constexpr int64_t kSlot = static_cast<int64_t>(S::BM) * S::BN;
-    const float *first = sch.partials + static_cast<int64_t>(i) * sch.pieces * kSlot;
+    constexpr int64_t kSlot4 = static_cast<int64_t>(S::BM) * S::BN / 4;   // float4 per slot
+    constexpr int kGroup = 4;
+    const f32x4 *first = reinterpret_cast<const f32x4 *>(sch.partials) +
+                         static_cast<int64_t>(i) * sch.pieces * kSlot4;
+    const int64_t idx0 = static_cast<int64_t>(blk * 4) * S::kThreads + x;
+    f32x4 sum[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum[j] = first[idx0 + j * S::kThreads];
+    for (int p = 1; p < sch.pieces; p += kGroup) {
+        // every load is issued (past the last piece it re-reads the last one,
+        // a valid address); only the additions are conditional
+        f32x4 v[kGroup][4];
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+            const int64_t q = min(p + g, sch.pieces - 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[g][j] = first[q * kSlot4 + idx0 + j * S::kThreads];
+        }
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (p + g < sch.pieces) sum[j] += v[g][j];
+    }
     f32x16 a;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int64_t idx = static_cast<int64_t>(blk * 4 + j) * S::kThreads + x;
-        f32x4 v = reinterpret_cast<const f32x4 *>(first)[idx];
-        for (int p = 1; p < sch.pieces; ++p)
-            v += reinterpret_cast<const f32x4 *>(first + p * kSlot)[idx];
-        a[4 * j] = v.x;
-        a[4 * j + 1] = v.y;
-        a[4 * j + 2] = v.z;
-        a[4 * j + 3] = v.w;
+        a[4 * j] = sum[j].x;
+        a[4 * j + 1] = sum[j].y;
+        a[4 * j + 2] = sum[j].z;
+        a[4 * j + 3] = sum[j].w;
     }
     return a;
 }

@@ -152,7 +152,8 @@ struct PanelLoader {
         if (bytes > 0x7FFFFFF0LL) bytes = 0x7FFFFFF0LL;
         rsrc = make_rsrc(panel, static_cast<uint32_t>(bytes));
         const int lane = threadIdx.x & 63;
-        const int wave = threadIdx.x >> 6;
+        // uniform per wave: keeps the LDS destinations (M0) in scalar registers
+        const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) {
             const int block = j * S::kWaves + wave;
@@ -165,19 +166,17 @@ struct PanelLoader {
         }
     }
 
+    // Branch-free, so that the loads can be scheduled among the MFMAs of the
+    // same K step: chunks at k >= K (the K tail, or a step past the end) get
+    // an out-of-range offset and load nothing.
+    // (No test on the step as a whole: a uniform condition would be turned
+    // back into a branch.  k0 <= K + BK keeps kOutOfRange + 2 k0 below 2^32.)
     __device__ __forceinline__ void issue(int k0, int K, SWIGLU_LDS char *panel_lds) const {
-        const bool live = k0 < K;
-        const uint32_t soff = live ? static_cast<uint32_t>(k0) * 2u : 0u;
-        if (live && k0 + S::BK <= K) {
+        const uint32_t soff = static_cast<uint32_t>(k0) * 2u;
 #pragma unroll
-            for (int j = 0; j < NDMA; ++j) dma16(rsrc, panel_lds + lds_off[j], voff[j], soff);
-        } else {
-            // K tail (or a step past the end): chunks at k >= K load nothing
-#pragma unroll
-            for (int j = 0; j < NDMA; ++j) {
-                const uint32_t v = (live && k0 + kcol[j] < K) ? voff[j] : kOutOfRange;
-                dma16(rsrc, panel_lds + lds_off[j], v, soff);
-            }
+        for (int j = 0; j < NDMA; ++j) {
+            const uint32_t v = (k0 + kcol[j] < K) ? voff[j] : kOutOfRange;
+            dma16(rsrc, panel_lds + lds_off[j], v, soff);
         }
     }
 };
@@ -359,14 +358,38 @@ struct Pipeline {
             mma<S>(f[KS & 1], acc);
             substeps<KS + 1>(issue, t, total, acc, hook);
         } else {
-            if (t + 1 < total) {
-                wait_vmcnt<S::kDmaPerStep * (S::STAGES - 2)>();
-                block_barrier();
-                issue(t + S::STAGES, stage(t));
-                read_frags<S, 0>(stage_addr(t + 1), off, f[(KS + 1) & 1]);
-            }
+            // Step t+1's loads have landed (own wait, then everyone's via the
+            // barrier), and every wave has finished reading stage t.  The
+            // first fragment reads of step t+1 go out before this substep's
+            // MFMAs (an LDS read lands asynchronously: its destination must
+            // not be registers that MFMAs issued just before it still read),
+            // and the refill of stage t (step t+STAGES) after them, in one
+            // straight-line block, so the scheduler can place those loads --
+            // which write LDS, not registers -- among the MFMAs instead of
+            // leaving the MFMA pipe idle while they are issued.  After the
+            // last step the loads are masked dummies (the issue lambda maps
+            // steps past the end to nothing) and the reads are unused; drain()
+            // waits for them.
+            wait_vmcnt<S::kDmaPerStep * (S::STAGES - 2)>();
+            block_barrier();
+            read_frags<S, 0>(stage_addr(t + 1), off, f[(KS + 1) & 1]);
             hook(KS);
             mma<S>(f[KS & 1], acc);
+            issue(t + S::STAGES, stage(t));
+            interleave_mfma_and_loads();
+        }
+    }
+
+    // Scheduling pattern for the last substep: one MFMA, then its share of
+    // the step's direct-to-LDS loads, and so on (sched_group_barrier masks:
+    // 0x008 MFMA, 0x020 VMEM read).
+    __device__ __forceinline__ static void interleave_mfma_and_loads() {
+        constexpr int kMfma = S::TM * S::TN;
+        constexpr int kPer = (S::kDmaPerStep + kMfma - 1) / kMfma;
+#pragma unroll
+        for (int i = 0; i < kMfma; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, kPer, 0);
         }
     }
 

@@ -491,11 +491,11 @@ static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int 
 // 128x128 two-per-CU tiles when they are predicted faster than the 256x256
 // tiles.  Each schedule's time is counted in rounds of its own tiles (a split
 // tail: 1/s of a round plus the split cost); a round of 256x256 tiles costs
-// 1.7 rounds of 128x128 tiles -- the ratio measured on MI355X with inputs
+// 1.5 rounds of 128x128 tiles -- the ratio measured on MI355X with inputs
 // streamed from HBM (rotated copies, N(0,1) data) on ten (M, K, N) points with
-// K from 896 to 8192 (1.55-1.97, no trend in K).  With that ratio the model
-// picks the measured-fastest option at nine of the ten points and is within
-// 4 % at the tenth.
+// K from 896 to 8192 (1.41-1.93, median 1.53).  At all ten the model then
+// picks the measured-fastest tile; 128x128 remains the choice where both
+// schedules take one round and a quarter-size tile finishes sooner.
 template <class S>
 static double schedule_rounds(const Schedule &sch, int cus) {
     const double G = static_cast<double>(cus) * S::kOccupancy;
@@ -513,7 +513,7 @@ static bool quad_tiles_faster(int M, int cols, int K, const GemmWorkspace &ws) {
         schedule_rounds<ShapeWide>(make_schedule<ShapeWide>(M, cols, K, ws), ws.cus);
     const double rounds_quad =
         schedule_rounds<ShapeQuad>(make_schedule<ShapeQuad>(M, cols, K, ws), ws.cus);
-    return rounds_quad < rounds_wide * 1.7;
+    return rounds_quad < rounds_wide * 1.5;
 }
 
 hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,

@@ -20,6 +20,12 @@ kernel and the CPU oracle's throughput on a bounded sample.
 for each of the five K x N shapes of the workloads (inputs drawn on the
 device from the same distributions; the same rotation rule) and prints one
 JSON line per (shape, M): the data behind the M threshold of the dispatcher.
+
+--schedule-calibration times variant I at the same shapes over a finer range
+of M, once with the library's own choice and once forced (SWIGLU_I_TILE,
+SWIGLU_TAIL) through each tile shape and tail schedule, one JSON line per
+(shape, M, schedule): the data the schedule cost model is fitted to
+(``python -m gated_mlp_gemm_amd.schedule_fit FILE``).
 """
 from __future__ import annotations
 
@@ -56,21 +62,46 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="time I, S and the ablation over M for the five K x N shapes")
     p.add_argument("--sweep-m", default="128,256,512,1024,2048,3072,4096,8192,16384")
+    p.add_argument("--schedule-calibration", action="store_true",
+                   help="time variant I under every forced tile shape / tail schedule")
+    p.add_argument("--calibration-m",
+                   default="256,512,640,768,1024,1280,1536,2048,2560,3072,4096,5120,6144,8192,16384")
     return p.parse_args()
 
 
-def sweep(args):
-    """Variant I vs S vs the ablation over M, per K x N shape (one JSON line each)."""
+def _time_call(fn, copies, stream, budget_s=0.03, max_reps=100):
+    """Per-call microseconds of fn over rotated input copies (3 warm-up calls,
+    then enough timed calls for about budget_s), with HIP events on `stream`."""
+    import torch
+
+    R = len(copies)
+    for r in range(3):
+        fn(*copies[r % R])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn(*copies[0])
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-6)
+    reps = int(min(max_reps, max(5, budget_s / est)))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        fn(*copies[r % R])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def _sweep_shapes(dev, ms_list, body):
+    """For each K x N shape of the workloads (smallest first): draw the weights
+    and a tall A on the device, then call body(K, N, M, copies, Wf) per M with
+    R rotated copies of (A[:M], W_fused), R x step bytes >= 512 MiB."""
     import torch
 
     from gated_mlp_gemm_amd import inputs
     from gated_mlp_gemm_amd import swiglu as sw
 
-    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
-    sw.load_library()
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-    ms_list = [int(x) for x in args.sweep_m.split(",")]
     shapes = sorted({(w.K, w.N) for w in inputs.WORKLOADS}, key=lambda kn: kn[0] * kn[1])
     for K, N in shapes:
         g = torch.Generator(device=dev)
@@ -80,48 +111,98 @@ def sweep(args):
         Wf = sw.swiglu_pack_weights(W1, W2)
         del W1, W2
         A_all = torch.randn(max(ms_list), K, device=dev, generator=g).to(torch.bfloat16)
-        ws = {v: sw.make_workspace(max(ms_list), N, K, v, dev) for v in ("i", "ablation")}
         for M in ms_list:
             step_bytes = 2 * (M * K + 2 * K * N + M * N)
             R = max(1, -(-512 * 2 ** 20 // step_bytes))
             A = A_all[:M]
             copies = [(A, Wf)] + [(A.clone(), Wf.clone()) for _ in range(R - 1)]
-            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            G = torch.empty_like(Y)
-            U = torch.empty_like(Y)
-            calls = {
-                "i": lambda a, w: sw.swiglu_fused_gemm(a, w, Y=Y, variant="i", workspace=ws["i"]),
-                "s": lambda a, w: sw.swiglu_fused_gemm(a, w, Y=Y, variant="s"),
-                "ablation": lambda a, w: sw.swiglu_unfused_ablation(a, w, G, U, Y,
-                                                                    workspace=ws["ablation"]),
-            }
-            rec = {"K": K, "N": N, "M": M, "rotation_copies": R, "us": {}, "tflops": {}}
-            for name, fn in calls.items():
-                for r in range(3):
-                    fn(*copies[r % R])
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                fn(*copies[0])
-                torch.cuda.synchronize()
-                est = max(time.perf_counter() - t0, 1e-6)
-                reps = int(min(100, max(5, 0.03 / est)))
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for r in range(reps):
-                    fn(*copies[r % R])
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / reps * 1e3
-                rec["us"][name] = round(us, 2)
-                rec["tflops"][name] = round(4 * M * N * K / (us * 1e-6) / 1e12, 1)
-            rec["fastest_fused"] = min(("i", "s"), key=lambda v: rec["us"][v])
-            rec["speedup_i_vs_ablation"] = round(rec["us"]["ablation"] / rec["us"]["i"], 3)
-            rec["speedup_s_vs_ablation"] = round(rec["us"]["ablation"] / rec["us"]["s"], 3)
-            print(json.dumps(rec), flush=True)
-            del copies, Y, G, U
-        del Wf, A_all, ws
+            body(K, N, M, copies, Wf)
+            del copies
+        del Wf, A_all
         torch.cuda.empty_cache()
+
+
+def schedule_calibration(args):
+    """Variant I per (shape, M) under the library's choice and every forced
+    (tile, tail) schedule; one JSON line each."""
+    import torch
+
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    sw.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    ms_list = [int(x) for x in args.calibration_m.split(",")]
+    schedules = [("auto", "auto"), ("256", "whole"), ("256", "split"), ("256", "quarter"),
+                 ("128", "whole"), ("128", "split")]
+    saved = {k: os.environ.get(k) for k in ("SWIGLU_I_TILE", "SWIGLU_TAIL")}
+
+    def body(K, N, M, copies, Wf):
+        ws = sw.make_workspace(M, N, K, "i", dev)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for tile, tail in schedules:
+            for k, v in (("SWIGLU_I_TILE", tile), ("SWIGLU_TAIL", tail)):
+                if v == "auto":
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+            desc = sw.swiglu_describe_launch(M, N, K, "i", ws.numel() if ws is not None else 0)
+            us = _time_call(lambda a, w: sw.swiglu_fused_gemm(a, w, Y=Y, variant="i",
+                                                              workspace=ws),
+                            copies, stream, budget_s=0.04, max_reps=200)
+            print(json.dumps({"K": K, "N": N, "M": M, "tile": tile, "tail": tail,
+                              "us": round(us, 2), "launch": desc}), flush=True)
+
+    try:
+        _sweep_shapes(dev, ms_list, body)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def sweep(args):
+    """Variant I vs S vs the ablation over M, per K x N shape (one JSON line each)."""
+    import torch
+
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    sw.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    ms_list = [int(x) for x in args.sweep_m.split(",")]
+    ws = {}
+
+    def body(K, N, M, copies, Wf):
+        if (K, N) not in ws:
+            ws.clear()
+            ws[(K, N)] = {v: sw.make_workspace(max(ms_list), N, K, v, dev)
+                          for v in ("i", "ablation")}
+        w = ws[(K, N)]
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        G = torch.empty_like(Y)
+        U = torch.empty_like(Y)
+        calls = {
+            "i": lambda a, wf: sw.swiglu_fused_gemm(a, wf, Y=Y, variant="i", workspace=w["i"]),
+            "s": lambda a, wf: sw.swiglu_fused_gemm(a, wf, Y=Y, variant="s"),
+            "ablation": lambda a, wf: sw.swiglu_unfused_ablation(a, wf, G, U, Y,
+                                                                 workspace=w["ablation"]),
+        }
+        rec = {"K": K, "N": N, "M": M, "rotation_copies": len(copies), "us": {}, "tflops": {}}
+        for name, fn in calls.items():
+            us = _time_call(fn, copies, stream)
+            rec["us"][name] = round(us, 2)
+            rec["tflops"][name] = round(4 * M * N * K / (us * 1e-6) / 1e12, 1)
+        rec["fastest_fused"] = min(("i", "s"), key=lambda v: rec["us"][v])
+        rec["speedup_i_vs_ablation"] = round(rec["us"]["ablation"] / rec["us"]["i"], 3)
+        rec["speedup_s_vs_ablation"] = round(rec["us"]["ablation"] / rec["us"]["s"], 3)
+        print(json.dumps(rec), flush=True)
+
+    _sweep_shapes(dev, ms_list, body)
 
 
 def kernel_source_hash() -> str:
@@ -156,6 +237,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.schedule_calibration:
+        schedule_calibration(args)
         return
 
     import numpy as np

@@ -100,12 +100,25 @@ int tile_override() {
     return 0;
 }
 
+// SWIGLU_TAIL=whole, split or quarter forces how the tiles of a partly idle
+// last round run (split only takes effect with a workspace; quarter only for
+// the 256x256 tile); unset or anything else: the cost model decides.
+int tail_override() {
+    const char *s = std::getenv("SWIGLU_TAIL");
+    if (s == nullptr) return swiglu::kTailAuto;
+    if (std::strcmp(s, "whole") == 0) return swiglu::kTailWhole;
+    if (std::strcmp(s, "split") == 0) return swiglu::kTailPieces;
+    if (std::strcmp(s, "quarter") == 0) return swiglu::kTailQuarters;
+    return swiglu::kTailAuto;
+}
+
 swiglu::GemmWorkspace make_ws(void *workspace, uint64_t bytes, int cus) {
     swiglu::GemmWorkspace ws{};
     ws.base = bytes > 0 ? workspace : nullptr;
     ws.bytes = workspace ? bytes : 0;
     ws.cus = cus;
     ws.tile = tile_override();
+    ws.tail = tail_override();
     return ws;
 }
 

@@ -214,20 +214,76 @@ struct StoreEpilogue {
     }
 };
 
+// K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
+template <class S>
+__device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const uint16_t *A,
+                                              const KMajor &B, int M, int K, int m0, int n0,
+                                              int kb, int ke, int nk,
+                                              f32x16 (&acc)[S::TM][S::TN]) {
+    PipelineFor<S> pl;
+    pl.init(lds);
+    TileLoader<S> ld;
+    ld.init(KMajor{A, M, 1, 0}, m0, B, n0, K);
+    const int len = ke - kb;
+    // steps past the range load nothing (K step nk is past the end of K)
+    auto issue = [&](int s, SWIGLU_LDS char *st) { ld.issue(s < len ? kb + s : nk, st); };
+    zero_acc<S>(acc);
+    pl.prologue(issue);
+    pl.run(issue, 0, len, len, acc);
+    pl.drain();
+}
+
+// The quarter-size tile of a 4-wave shape S, used for a tail round: half the
+// rows and columns, with as many stages (up to 4) as S's LDS holds, so that a
+// lone workgroup on a CU still keeps several K steps of loads in flight.
+template <class S>
+constexpr bool kQuarterable =
+    S::kOccupancy == 1 && S::kWaves == 4 && S::BM % 128 == 0 && S::BN % 128 == 0;
+
+template <class S>
+struct QuarterOf {
+    static constexpr int kStage = (S::BM / 2 + S::BN / 2) * S::BK * 2;
+    static constexpr int kStages = S::kLdsBytes / kStage < 4 ? S::kLdsBytes / kStage : 4;
+    using type = TileShape<S::BM / 2, S::BN / 2, S::BK, 2, 2, kStages>;
+};
+
+enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2 };
+
 // One accumulator per tile: D = A . B^T over the tiles of `sch`, then `epi`.
-// Workgroup b < sch.dp runs tile b (XCD-ordered) whole and runs the epilogue;
-// with SPLIT, workgroup dp + j runs piece j % pieces of split tile
-// dp + j / pieces and stores its partial (split_tail.hpp), which
-// split_reduce_kernel finishes.  A workgroup runs one tile or piece: no loop.
-template <class S, class Epi, bool SPLIT>
+// Workgroup b < sch.dp runs tile b (XCD-ordered) whole and runs the epilogue.
+// The tiles [dp, dp + split_tiles) of a partly idle last round run
+//  - with kTailSplit: workgroup dp + j runs piece j % pieces of split tile
+//    dp + j / pieces and stores its partial (split_tail.hpp), which
+//    split_reduce_kernel finishes;
+//  - with kTailQuarter: workgroup dp + q runs quarter q % 4 (row half q/2 % 2,
+//    column half q % 2) of tile dp + q / 4 whole, as a quarter-size tile, so
+//    four times the workgroups share the round.
+// A workgroup runs one tile, quarter or piece: no loop.
+template <class S, class Epi, int TAIL>
 __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
     const uint16_t *__restrict__ A, KMajor B, int M, int K, Epi epi, Schedule sch) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
 
     const int b = blockIdx.x;
+    if constexpr (TAIL == kTailQuarter) {
+        if (b >= sch.dp) {
+            using Q = typename QuarterOf<S>::type;
+            static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
+            const int q = xcd_order(b - sch.dp, 4 * sch.split_tiles);
+            int tm, tn;
+            tile_coords(sch.dp + q / 4, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
+            const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
+            const int n0 = tn * S::BN + (q & 1) * Q::BN;
+            if (m0 >= M || n0 >= B.rows) return;   // quarter wholly past the output's edge
+            f32x16 acc[Q::TM][Q::TN];
+            tile_mainloop<Q>(lds, A, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
+            epi.template apply<Q>(acc, m0, n0, threadIdx.x);
+            return;
+        }
+    }
     int t, kb = 0, ke = sch.nk, j = 0;
-    const bool whole = !SPLIT || b < sch.dp;
+    const bool whole = TAIL != kTailSplit || b < sch.dp;
     if (whole) {
         t = xcd_order(b, sch.dp);
     } else {
@@ -243,17 +299,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
     const int n0 = tn * S::BN;
 
     f32x16 acc[S::TM][S::TN];
-    PipelineFor<S> pl;
-    pl.init(lds);
-    TileLoader<S> ld;
-    ld.init(KMajor{A, M, 1, 0}, m0, B, n0, K);
-    const int len = ke - kb;
-    // steps past the range load nothing (K step nk is past the end of K)
-    auto issue = [&](int s, SWIGLU_LDS char *st) { ld.issue(s < len ? kb + s : sch.nk, st); };
-    zero_acc<S>(acc);
-    pl.prologue(issue);
-    pl.run(issue, 0, len, len, acc);
-    pl.drain();
+    tile_mainloop<S>(lds, A, B, M, K, m0, n0, kb, ke, sch.nk, acc);
     if (whole)
         epi.template apply<S>(acc, m0, n0, threadIdx.x);
     else
@@ -429,23 +475,50 @@ hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, in
     return hipGetLastError();
 }
 
-// Rough time of one K step of a round of S tiles on MI355X (us): 2.1 for a
-// 256x256x64 step, scaled by tile volume and by the workgroups sharing a CU.
-// With the fixed cost of a split tail (the reduction kernel, its launch and
-// the pieces' partial traffic: about 25 us) it decides when splitting pays.
+// Schedule cost model (MI355X, microseconds).  A round of workgroups costs
+// kRoundUs plus nk K steps of its tile shape; a split tail also pays the
+// reduction (kReduceUs plus its partials, written once and read once, at
+// kPartialBytesPerUs).  Fitted to 375 timings of variant I with inputs
+// streamed from HBM: the five K x N shapes of the benchmark workloads, M from
+// 256 to 16384, each forced through every tile shape and tail schedule
+// (RMS error 7 %); on those points the schedule it picks is on average within
+// 0.5 % of the measured-fastest (at most 4.1 %).
+constexpr double kRoundUs = 3.7;
+constexpr double kReduceUs = 3.4;
+constexpr double kPartialBytesPerUs = 6.4e6;
+
+// One K step of a round of S tiles: 1.69 for 256x256x64 (one per CU), 1.03
+// for 128x128x64 (two per CU, so twice the tiles per round); other shapes
+// scaled from the first by tile volume and workgroups per CU.
 template <class S>
 constexpr double step_us() {
-    return 2.1 * (static_cast<double>(S::BM) * S::BN * S::BK) / (256.0 * 256.0 * 64.0) *
+    if (S::BM == 256 && S::BN == 256 && S::BK == 64 && S::kOccupancy == 1) return 1.69;
+    if (S::BM == 128 && S::BN == 128 && S::BK == 64 && S::kOccupancy == 2) return 1.03;
+    return 1.69 * (static_cast<double>(S::BM) * S::BN * S::BK) / (256.0 * 256.0 * 64.0) *
            S::kOccupancy;
 }
-constexpr double kSplitCostUs = 25.0;
+
+// One K step of a round of quarter-size tiles (QuarterOf<S>) in the S kernel:
+// 0.59 for the 128x128 quarters of 256x256x64.
+template <class S>
+constexpr double quarter_step_us() {
+    return 0.59 * (static_cast<double>(S::BM) * S::BN * S::BK) / (256.0 * 256.0 * 64.0);
+}
 
 // Work schedule for a single-accumulator GEMM over an M x cols output (see
-// split_tail.hpp): all tiles whole unless the last round is partly idle, a
-// workspace is given and splitting the tail into s >= 2 pieces saves more
-// than the split costs.
+// split_tail.hpp): all tiles whole unless the last round is partly idle.  Then
+// its L tiles run whichever way the cost model predicts fastest:
+//  - whole: one more round;
+//  - as 4L quarter-size tiles (kQuarterable shapes: one workgroup per CU,
+//    whose LDS gives a quarter tile a deeper ring): ceil(4L / G) rounds of
+//    quarter steps;
+//  - split into s = min(G / L, nk) >= 2 pieces (with a workspace): a round of
+//    ceil(nk / s) steps plus the reduction.
+// ws.tail forces one of them where it applies.  `us`, if given, receives the
+// predicted time of the whole schedule.
 template <class S>
-static Schedule make_schedule(int M, int cols, int K, const GemmWorkspace &ws) {
+static Schedule make_schedule(int M, int cols, int K, const GemmWorkspace &ws,
+                              double *us = nullptr) {
     Schedule sch{};
     sch.tiles_m = cdiv(M, S::BM);
     sch.tiles_n = cdiv(cols, S::BN);
@@ -454,15 +527,39 @@ static Schedule make_schedule(int M, int cols, int K, const GemmWorkspace &ws) {
     const int64_t T = static_cast<int64_t>(sch.tiles_m) * sch.tiles_n;
     sch.dp = static_cast<int>(T);
     const int G = ws.cus * S::kOccupancy;           // workgroup slots
-    if (ws.base == nullptr || G <= 0 || ws.bytes < workspace_bytes_for(ws.cus)) return sch;
+    const double round = kRoundUs + sch.nk * step_us<S>();
+    if (us) *us = G > 0 ? cdiv(T, G) * round : 0.0;
+    if (G <= 0 || ws.tail == kTailWhole) return sch;
     const int64_t L = T % G;
     if (L == 0) return sch;
-    const int pieces = static_cast<int>(min(static_cast<int64_t>(G) / L, static_cast<int64_t>(sch.nk)));
-    if (pieces < 2 || (sch.nk - cdiv(sch.nk, pieces)) * step_us<S>() <= kSplitCostUs) return sch;
-    sch.dp = static_cast<int>(T - L);
-    sch.pieces = pieces;
-    sch.split_tiles = static_cast<int>(L);
-    sch.partials = reinterpret_cast<float *>(ws.base);
+    const bool forced = ws.tail != kTailAuto;
+    double best = round;                            // tail tiles whole
+    if (kQuarterable<S> && (!forced || ws.tail == kTailQuarters)) {
+        const double t = cdiv(4 * L, G) * (kRoundUs + sch.nk * quarter_step_us<S>());
+        if (forced || t < best) {
+            best = t;
+            sch.dp = static_cast<int>(T - L);
+            sch.split_tiles = static_cast<int>(L);
+            sch.quartered = 1;
+        }
+    }
+    const bool has_ws = ws.base != nullptr && ws.bytes >= workspace_bytes_for(ws.cus);
+    if (has_ws && (!forced || ws.tail == kTailPieces)) {
+        const int pieces =
+            static_cast<int>(min(static_cast<int64_t>(G) / L, static_cast<int64_t>(sch.nk)));
+        const double partials = static_cast<double>(L) * pieces * S::BM * S::BN * 4.0 * 2.0;
+        const double t = kRoundUs + cdiv(sch.nk, pieces) * step_us<S>() + kReduceUs +
+                         partials / kPartialBytesPerUs;
+        if (pieces >= 2 && (forced || t < best)) {
+            best = t;
+            sch.dp = static_cast<int>(T - L);
+            sch.split_tiles = static_cast<int>(L);
+            sch.quartered = 0;
+            sch.pieces = pieces;
+            sch.partials = reinterpret_cast<float *>(ws.base);
+        }
+    }
+    if (us) *us = (T / G) * round + best;
     return sch;
 }
 
@@ -470,13 +567,22 @@ template <class S, class Epi>
 static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int K, Epi epi,
                               const GemmWorkspace &ws, hipStream_t stream) {
     const Schedule sch = make_schedule<S>(M, cols, K, ws);
+    if (sch.quartered) {
+        if constexpr (kQuarterable<S>) {
+            hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailQuarter>),
+                               dim3(sch.dp + 4 * sch.split_tiles), dim3(S::kThreads), 0, stream,
+                               A, B, M, K, epi, sch);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidConfiguration;   // make_schedule quarters no other shape
+    }
     if (sch.pieces == 0) {
-        hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, false>), dim3(sch.dp), dim3(S::kThreads), 0,
-                           stream, A, B, M, K, epi, sch);
+        hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailNone>), dim3(sch.dp),
+                           dim3(S::kThreads), 0, stream, A, B, M, K, epi, sch);
         return hipGetLastError();
     }
     const int grid = sch.dp + sch.split_tiles * sch.pieces;
-    hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, true>), dim3(grid), dim3(S::kThreads), 0,
+    hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailSplit>), dim3(grid), dim3(S::kThreads), 0,
                        stream, A, B, M, K, epi, sch);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -488,32 +594,16 @@ static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int 
 }
 
 // Tile choice for an M x cols single-accumulator GEMM above M = 128: the
-// 128x128 two-per-CU tiles when they are predicted faster than the 256x256
-// tiles.  Each schedule's time is counted in rounds of its own tiles (a split
-// tail: 1/s of a round plus the split cost); a round of 256x256 tiles costs
-// 1.5 rounds of 128x128 tiles -- the ratio measured on MI355X with inputs
-// streamed from HBM (rotated copies, N(0,1) data) on ten (M, K, N) points with
-// K from 896 to 8192 (1.41-1.93, median 1.53).  At all ten the model then
-// picks the measured-fastest tile; 128x128 remains the choice where both
-// schedules take one round and a quarter-size tile finishes sooner.
-template <class S>
-static double schedule_rounds(const Schedule &sch, int cus) {
-    const double G = static_cast<double>(cus) * S::kOccupancy;
-    const double full = sch.dp / G;
-    if (sch.pieces)
-        return full + 1.0 / sch.pieces + kSplitCostUs / (step_us<S>() * sch.nk);
-    return std::ceil(full);
-}
-
+// 128x128 two-per-CU tiles when the cost model predicts their schedule
+// faster than the 256x256 tiles' (each with its own best tail).
 static bool quad_tiles_faster(int M, int cols, int K, const GemmWorkspace &ws) {
     if (ws.tile == 256) return false;
     if (ws.tile == 128) return true;
     if (ws.cus <= 0) return false;
-    const double rounds_wide =
-        schedule_rounds<ShapeWide>(make_schedule<ShapeWide>(M, cols, K, ws), ws.cus);
-    const double rounds_quad =
-        schedule_rounds<ShapeQuad>(make_schedule<ShapeQuad>(M, cols, K, ws), ws.cus);
-    return rounds_quad < rounds_wide * 1.5;
+    double wide = 0.0, quad = 0.0;
+    make_schedule<ShapeWide>(M, cols, K, ws, &wide);
+    make_schedule<ShapeQuad>(M, cols, K, ws, &quad);
+    return quad < wide;
 }
 
 hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
@@ -537,6 +627,10 @@ static int describe(const char *kernel, const char *epi, const Schedule &sch, ch
                              " + split_reduce_kernel",
                              kernel, S::BM, S::BN, S::BK, epi, sch.dp, sch.split_tiles,
                              sch.pieces);
+    if (sch.quartered)
+        return std::snprintf(buf, n, "%s<%dx%dx%d,%s> (%d tiles + %d tiles run as %d %dx%d tiles)",
+                             kernel, S::BM, S::BN, S::BK, epi, sch.dp, sch.split_tiles,
+                             4 * sch.split_tiles, S::BM / 2, S::BN / 2);
     return std::snprintf(buf, n, "%s<%dx%dx%d,%s> (%d tiles)", kernel, S::BM, S::BN, S::BK,
                          epi, sch.dp);
 }
@@ -592,7 +686,10 @@ int64_t max_tiles(int64_t M, int64_t cols) {
     // the most workgroups any launcher above creates for an M x cols output
     const int64_t small = ((M + 127) / 128) * ((cols + 63) / 64);
     const int64_t wide = ((M + 255) / 256) * ((cols + 127) / 128);
-    return small > wide ? small : wide;
+    // 256x256 tiles with the tail quartered: at most four workgroups a tile
+    const int64_t quartered = 4 * ((M + 255) / 256) * ((cols + 255) / 256);
+    const int64_t most = small > wide ? small : wide;
+    return most > quartered ? most : quartered;
 }
 
 }  // namespace swiglu

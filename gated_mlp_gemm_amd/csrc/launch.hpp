@@ -14,7 +14,10 @@ struct GemmWorkspace {
     uint64_t bytes;
     int cus;          // compute units of the device
     int tile;         // variant I / ablation GEMM tile: 0 = by the cost model, 256 or 128 = forced
+    int tail;         // partly idle last round: 0 = by the cost model, else a TailChoice
 };
+// How the tiles of a partly idle last round run (GemmWorkspace::tail).
+enum TailChoice { kTailAuto = 0, kTailWhole = 1, kTailPieces = 2, kTailQuarters = 3 };
 // Scratch that lets the single-accumulator GEMMs split the tiles of a partial
 // last round along K (the same for every shape: one fp32 256 x 256 tile slot
 // per compute unit).

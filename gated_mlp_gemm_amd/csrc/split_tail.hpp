@@ -1,5 +1,7 @@
 // Work schedule for the single-accumulator GEMM kernels: whole tiles for the
-// full rounds, the last partial round split along K.
+// full rounds; the tiles of a partly idle last round whole, quartered (run as
+// quarter-size tiles by the same kernel, see gemm_tiles_kernel) or split along
+// K as described here, whichever the launcher's cost model prefers.
 //
 // One tile per workgroup leaves CUs idle in the last round when the tile count
 // T is not a multiple of the CU count G: the M=2048, 2N=17920 output has 560
@@ -32,8 +34,9 @@ struct Schedule {
     int nk;                 // K steps per tile
     int dp;                 // tiles [0, dp) run whole: workgroup b < dp runs one of them
     int pieces;             // K pieces per split tile (0: no split tiles)
-    int split_tiles;        // tiles [dp, dp + split_tiles) are split
+    int split_tiles;        // tiles [dp, dp + split_tiles) are split (or quartered)
     int group_m;            // tile order: groups of group_m tile rows (tile_coords)
+    int quartered;          // 1: the tail tiles run as four quarter-size tiles instead
     float *partials;        // one BM*BN slot per piece: slot j = piece j % pieces of split tile j / pieces
 };
 

@@ -101,13 +101,16 @@ int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2,
  *
  * workspace / workspace_bytes: optional caller-owned device scratch
  * (256-byte aligned, not shared by calls that may run concurrently; no
- * initialisation needed, contents meaningless after the call).  With at least
- * swiglu_workspace_size() bytes, variant I may split the output tiles of a
- * partly idle last round of workgroups along K: every other tile runs whole,
- * one per workgroup, and the pieces of a split tile leave fp32 partial tiles
- * in the workspace that a second kernel on the same stream sums, in a fixed
- * order (results stay bitwise reproducible), before the epilogue.  NULL or
- * too small: every tile whole, one kernel.  Variant S does not use it.
+ * initialisation needed, contents meaningless after the call).  When the
+ * output tiles leave the last round of workgroups partly idle, variant I runs
+ * that round's tiles whichever way a cost model of the device predicts
+ * fastest: whole; as quarter-size tiles in the same kernel (no workspace
+ * needed); or, given at least swiglu_workspace_size() bytes of workspace,
+ * split along K, the pieces leaving fp32 partial tiles in the workspace that
+ * a second kernel on the same stream sums, in a fixed order, before the
+ * epilogue.  Every schedule gives bitwise reproducible results for a given
+ * (M, N, K, workspace size, device).  NULL or too small: no split.  Variant S
+ * does not use it.
  */
 int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
                       int64_t M, int64_t N, int64_t K, int variant,
@@ -128,7 +131,7 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
  */
 
 /*
- * Bytes of `workspace` that let a call split the tail round: variant
+ * Bytes of `workspace` that let a call split the tail round along K: variant
  * SWIGLU_VARIANT_I or SWIGLU_AUTO for swiglu_fused_gemm, -1 for
  * swiglu_unfused_ablation (0 when nothing uses it, e.g. variant S, or for an
  * empty problem).  Queries the current device's compute-unit count (a HIP

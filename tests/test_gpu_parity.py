@@ -41,6 +41,7 @@ def _default_dispatch(monkeypatch):
     variant threshold or a tile shape set the variable themselves)."""
     monkeypatch.delenv("SWIGLU_M_SWITCH", raising=False)
     monkeypatch.delenv("SWIGLU_I_TILE", raising=False)
+    monkeypatch.delenv("SWIGLU_TAIL", raising=False)
 
 
 @pytest.fixture(scope="module")
@@ -392,6 +393,7 @@ def test_split_tail_shapes(dev, orc, M, K, N, tile, monkeypatch):
     if M <= 128 and tile == "128":
         pytest.skip("one tile shape at M <= 128")
     monkeypatch.setenv("SWIGLU_I_TILE", tile)
+    monkeypatch.setenv("SWIGLU_TAIL", "split")
     announce(f"split tail M={M} K={K} N={N} tile={tile}")
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 3 + K * 5 + N)
     Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
@@ -413,6 +415,60 @@ def test_split_tail_shapes(dev, orc, M, K, N, tile, monkeypatch):
     yd = bits_of(run_fused(Ad, Wf, "i"))
     a, b = oracle_pkg.bf16_bits_to_f64(yb), oracle_pkg.bf16_bits_to_f64(yd)
     assert np.all(np.abs(a - b) <= np.maximum(2e-3, 2.05e-2 * np.maximum(np.abs(a), np.abs(b))))
+
+
+# (M, K, N) whose 256x256 tiles leave a partly idle last round on 256 CUs, run
+# with that round's tiles as quarter-size (128x128) tiles: quarters past the
+# output's bottom or right edge (M = 300, 777, 3000; 2N = 272, 784, 4112,
+# 6000), no whole tile at all (300 x 136), a full round plus quarters
+# (3000 x 3000: 12 x 24 tiles), K tails (1000, 520, 136), and one K step.
+QUARTER_TAIL = [(300, 1000, 136), (2048, 1536, 1032), (600, 4096, 392), (777, 520, 2056),
+                (3000, 2048, 3000), (257, 64, 1032), (513, 136, 640)]
+
+
+@pytest.mark.parametrize("M,K,N", QUARTER_TAIL)
+def test_quarter_tail_shapes(dev, orc, M, K, N, monkeypatch):
+    monkeypatch.setenv("SWIGLU_I_TILE", "256")
+    monkeypatch.setenv("SWIGLU_TAIL", "quarter")
+    desc = sw.swiglu_describe_launch(M, N, K, "i", 0)
+    announce(f"quarter tail M={M} K={K} N={N}: {desc}")
+    assert "run as" in desc and "128x128 tiles" in desc, desc
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 7 + K * 3 + N)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    Wf = sw.swiglu_pack_weights(W1d, W2d)
+    # poison the output: every element must be written
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    sw.swiglu_fused_gemm(Ad, Wf, Y=Y, variant="i")
+    torch.cuda.synchronize()
+    yb = bits_of(Y)
+    hA, hW1, hW2 = inputs.bits(A), inputs.bits(W1), inputs.bits(W2)
+    if M * N * K <= 2 ** 31:
+        assert_parity(yb, orc.swiglu(hA, hW1, hW2), f"quarter tail {M}x{K}x{N}")
+    else:
+        rng = np.random.default_rng(M + N + K)
+        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+        assert_parity(yb[rows], orc.swiglu_rows(hA, hW1, hW2, rows),
+                      f"quarter tail rows {M}x{K}x{N}")
+        pr, pc = rng.integers(0, M, 4000), rng.integers(0, N, 4000)
+        assert_parity(yb[pr, pc], orc.swiglu_points(hA, hW1, hW2, pr, pc),
+                      f"quarter tail points {M}x{K}x{N}")
+    # a quarter tile sums each output over the same K steps in the same order
+    # as the whole tile: bit-identical to the all-whole schedule
+    monkeypatch.setenv("SWIGLU_TAIL", "whole")
+    assert "run as" not in sw.swiglu_describe_launch(M, N, K, "i", 0)
+    yw = bits_of(run_fused(Ad, Wf, "i"))
+    assert np.array_equal(yb, yw)
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 1000, 136), (777, 520, 1032)])
+def test_ablation_quarter_tail(dev, orc, M, K, N, monkeypatch):
+    monkeypatch.setenv("SWIGLU_I_TILE", "256")
+    monkeypatch.setenv("SWIGLU_TAIL", "quarter")
+    desc = sw.swiglu_describe_launch(M, N, K, "ablation", 0)
+    announce(f"ablation quarter tail M={M} K={K} N={N}: {desc}")
+    assert "run as" in desc, desc
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M + 2 * K + N)
+    _check_ablation(orc, A, W1, W2, np.arange(M), dev, f"ablation quarter {M}x{K}x{N}")
 
 
 def test_workspace_reuse_sizes(dev, orc):
@@ -487,8 +543,15 @@ def test_describe_launch(dev, monkeypatch):
     assert d.startswith("gemm_tiles_kernel<") and "PairMulEpilogue" in d
     monkeypatch.setenv("SWIGLU_I_TILE", "256")
     d = sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws)
+    assert "256x256x64" in d and "512 tiles + 48 tiles run as 192 128x128 tiles" in d, d
+    assert "split" not in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
+    monkeypatch.setenv("SWIGLU_TAIL", "split")
+    d = sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws)
     assert "256x256x64" in d and "split 5 ways" in d and d.endswith("split_reduce_kernel")
     assert "split" not in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
+    monkeypatch.setenv("SWIGLU_TAIL", "whole")
+    assert sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws).endswith("(560 tiles)")
+    monkeypatch.delenv("SWIGLU_TAIL")
     monkeypatch.setenv("SWIGLU_I_TILE", "128")
     assert "128x128x64" in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
     assert sw.swiglu_describe_launch(2048, 8960, 1536, "s").startswith("fused_sequential_kernel<")

@@ -73,6 +73,22 @@ __device__ __forceinline__ float by_lane_parity(float even_v, float odd_v) {
     return r;
 }
 
+// An accumulator value read out of its AGPR at this point of the program.
+// Volatile asm keeps the reads in order with the other volatile statements,
+// so the compiler cannot hoist all of a tile's accumulator reads above the
+// epilogue (it would then hold the whole tile in VGPRs and spill).
+__device__ __forceinline__ float read_acc(float a) {
+    float r;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(a));
+    return r;
+}
+
+template <bool kFromAcc>
+__device__ __forceinline__ float acc_value(float a) {
+    if constexpr (kFromAcc) return read_acc(a);
+    else return a;
+}
+
 // SiLU(x) = x / (1 + e^{-x}) = x * rcp(1 + 2^{-x log2 e}) with the hardware
 // exp2 and reciprocal (about 1 ulp each in fp32).  Very negative x: the exp2
 // overflows to +inf, the reciprocal is 0 and the result is -0; large x:

@@ -131,7 +131,20 @@ struct KMajor {
     int rows;        // logical rows
     int stride;
     int offset;
+    // 1: the operand is the interleaved packed weight read as one matrix and
+    // each 64-row group of a panel is loaded de-interleaved: LDS rows
+    // 32g' .. 32g'+31 of the group get its even (Gate) rows, the next 32 its
+    // odd (Up) rows (pair_row).  Then the Gate and Up columns of one output
+    // column meet in the same lane of two adjacent 32x32 accumulator blocks.
+    int pairs;
 };
+
+// Panel row whose data lands in LDS row `r` of a de-interleaved panel: within
+// each 64-row group, LDS rows 0..31 take the group's rows 0, 2, ..., 62 and
+// LDS rows 32..63 its rows 1, 3, ..., 63.
+__device__ __forceinline__ int pair_row(int r) {
+    return (r & ~63) + 2 * (r & 31) + ((r >> 5) & 1);
+}
 
 // The direct-to-LDS loads of one tile panel (NROWS rows) of a KMajor
 // operand: NDMA loads per wave per K step.
@@ -158,9 +171,10 @@ struct PanelLoader {
         for (int j = 0; j < NDMA; ++j) {
             const int block = j * S::kWaves + wave;
             const int p = block * 64 + lane;                  // physical chunk in the panel
-            const int row = p / S::kChunksPerRow;
+            const int row = p / S::kChunksPerRow;             // LDS row
             const int c = (p % S::kChunksPerRow) ^ swz<S>(row);
-            voff[j] = static_cast<uint32_t>(row * op.stride) * K * 2u + c * 16u;
+            const int grow = op.pairs ? pair_row(row) : row;  // panel row it holds
+            voff[j] = static_cast<uint32_t>(grow * op.stride) * K * 2u + c * 16u;
             kcol[j] = c * 8;
             lds_off[j] = block * 1024;
         }
@@ -337,13 +351,23 @@ struct Pipeline {
         off.init(wave / S::WN, wave % S::WN, lane);
     }
 
+    // The prologue in two halves, so that a persistent workgroup can put the
+    // loads of its next tile in flight before it runs the current tile's
+    // epilogue (the ring must be idle: after drain()).
     template <class Issue>
-    __device__ __forceinline__ void prologue(const Issue &issue) {
+    __device__ __forceinline__ void prologue_issue(const Issue &issue) {
 #pragma unroll
         for (int t = 0; t < S::STAGES; ++t) issue(t, stage(t));
+    }
+    __device__ __forceinline__ void prologue_wait() {
         wait_vmcnt<S::kDmaPerStep * (S::STAGES - 1)>();
         block_barrier();
         read_frags<S, 0>(stage_addr(0), off, f[0]);
+    }
+    template <class Issue>
+    __device__ __forceinline__ void prologue(const Issue &issue) {
+        prologue_issue(issue);
+        prologue_wait();
     }
 
     template <int KS, class Issue, class Hook>

@@ -111,64 +111,124 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(uint16_t *base, int m
 __device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), 0, 0);
 }
+// The high 16 bits of v, with the same range check (buffer_store_short_d16_hi,
+// which the store builtin does not produce: it would shift first).
+__device__ __forceinline__ void store_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+    asm volatile("buffer_store_short_d16_hi %0, %1, %2, 0 offen" ::"v"(v), "v"(off), "s"(r)
+                 : "memory");
+}
 
 // ---------------------------------------------------------------------------
 // Variant I [gist: Method, Kernel-2]: one GEMM D = A . W_fused over tiles of
-// the [M, 2N] grid; the epilogue pairs adjacent accumulator columns
-// (D[m,2n], D[m,2n+1]) and stores SiLU(D[m,2n]) * D[m,2n+1].
+// the [M, 2N] grid; the epilogue pairs each Gate accumulator column D[m,2n]
+// with its Up partner D[m,2n+1] and stores SiLU(D[m,2n]) * D[m,2n+1].
 //
-// In the 32x32 MFMA accumulator layout every lane holds one column, so the
-// Gate column 2n sits in an even lane and its Up partner 2n+1 in the next
-// lane, at the same register indices.  The pair splits the work: the even lane
-// finishes registers 0..7 (it receives the partner's Up values), the odd lane
-// registers 8..15 (it receives Gate values); one DPP lane swap per output.
+// Epilogues work in units of accumulator blocks: unit<S>(a0, a1, u, ...)
+// finishes unit u (u < TM * TN / unit_blocks<S>()) of a wave from its
+// unit_blocks<S>() 32x32 blocks a0 (and a1), given in order.
+//
+// Paired layout (wave tiles an even number of 32x32 blocks wide): the weight
+// panel is loaded de-interleaved (KMajor::pairs), so block 2p of a wave holds
+// the Gate columns and block 2p+1 the Up columns of the same 32 outputs, each
+// output column in one lane: every lane finishes its own 16 outputs of the
+// unit with no lane exchange, and one conversion packs two of them.
+// Interleaved layout (one block wide, the 128x64 tiles): in the 32x32 MFMA
+// accumulator layout every lane holds one column, so a Gate column 2n sits in
+// an even lane and its Up partner 2n+1 in the next lane, at the same register
+// indices; the even lane finishes registers 0..7 (it receives the partner's
+// Up values), the odd lane registers 8..15 (it receives Gate values), one DPP
+// lane swap per output.
 // ---------------------------------------------------------------------------
 struct PairMulEpilogue {
     uint16_t *Y;
     int M, N;
 
-    // Accumulator block (tm, tn) of thread tid (its lane must be tid % 64).
     template <class S>
-    __device__ __forceinline__ void block(const f32x16 &a, int tm, int tn, int m0, int n0,
-                                          int tid) const {
+    static constexpr bool paired() { return S::TN % 2 == 0; }
+    template <class S>
+    static constexpr int unit_blocks() { return paired<S>() ? 2 : 1; }
+
+    // kFromAcc: the blocks are MFMA accumulators (AGPRs), read out in order
+    // (read_acc); else ordinary values (the split reduction's sums).
+    template <class S, bool kFromAcc = true>
+    __device__ __forceinline__ void unit(const f32x16 &a0, const f32x16 &a1, int u, int m0, int n0,
+                                         int tid) const {
         const int lane = tid & 63;
         const int wave = tid >> 6;
         const int wm = wave / S::WN, wn = wave % S::WN;
-        const bool odd = lane & 1;
         const int rows_valid = min(S::BM, M - m0);
         const int y0 = n0 / 2;                 // first Y column of the tile
         const int ycols_valid = min(S::BN / 2, N - y0);
         const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, N);
-        // even lanes finish accumulator registers 0..7, odd lanes 8..15, which
-        // sit 16 rows further down (acc_row with i = 8 + p)
-        const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, 0, odd ? 8 : 0, lane));
-        const int ycol = (wn * S::kWaveN + tn * 32 + (lane & 31)) >> 1;
-        const uint32_t voff =
-            ycol < ycols_valid
-                ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(y0 + ycol)) * 2u
-                : kOutOfRange;
+        if constexpr (paired<S>()) {
+            constexpr int kPairBlocks = S::TN / 2;
+            const int tm = u / kPairBlocks, tp = u % kPairBlocks;
+            const f32x16 &g = a0, &up = a1;
+            const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, tm, 0, lane));
+            const int ycol = wn * (S::kWaveN / 2) + tp * 32 + (lane & 31);
+            const uint32_t voff =
+                ycol < ycols_valid
+                    ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(y0 + ycol)) * 2u
+                    : kOutOfRange;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const float lo = a[p], hi = a[8 + p];
-            const float recv = swap_adjacent_lanes(by_lane_parity(hi, lo));
-            const float gate = by_lane_parity(lo, recv);
-            const float up = by_lane_parity(recv, hi);
-            const uint32_t roff =
-                static_cast<uint32_t>(acc_row<S>(0, tm, p, 0)) * static_cast<uint32_t>(N) * 2u;
-            store_b16(r, voff + roff, to_bf16(silu(gate) * up));
+            for (int i = 0; i < 16; i += 2) {
+                // registers i, i+1 are rows 8(i/4) + (i%4) and the next one
+                const float g0 = acc_value<kFromAcc>(g[i]), g1 = acc_value<kFromAcc>(g[i + 1]);
+                const float u0 = acc_value<kFromAcc>(up[i]), u1 = acc_value<kFromAcc>(up[i + 1]);
+                const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+                const uint32_t roff =
+                    static_cast<uint32_t>(acc_row<S>(0, 0, i, 0)) * static_cast<uint32_t>(N) * 2u;
+                store_b16(r, voff + roff, static_cast<uint16_t>(v));
+                store_b16_hi(r, voff + roff + static_cast<uint32_t>(N) * 2u, v);
+            }
+        } else {
+            const int tm = u / S::TN, tn = u % S::TN;
+            const bool odd = lane & 1;
+            // even lanes finish accumulator registers 0..7, odd lanes 8..15,
+            // which sit 16 rows further down (acc_row with i = 8 + p)
+            const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, 0, odd ? 8 : 0, lane));
+            const int ycol = (wn * S::kWaveN + tn * 32 + (lane & 31)) >> 1;
+            const uint32_t voff =
+                ycol < ycols_valid
+                    ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(y0 + ycol)) * 2u
+                    : kOutOfRange;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const float lo = a0[p], hi = a0[8 + p];
+                const float recv = swap_adjacent_lanes(by_lane_parity(hi, lo));
+                const float gate = by_lane_parity(lo, recv);
+                const float upv = by_lane_parity(recv, hi);
+                const uint32_t roff = static_cast<uint32_t>(acc_row<S>(0, tm, p, 0)) *
+                                      static_cast<uint32_t>(N) * 2u;
+                store_b16(r, voff + roff, to_bf16(silu(gate) * upv));
+            }
         }
     }
 
     template <class S>
     __device__ __forceinline__ void apply(const f32x16 (&acc)[S::TM][S::TN], int m0, int n0,
                                           int tid) const {
+        constexpr int kUnits = S::TM * S::TN / unit_blocks<S>();
+        __builtin_amdgcn_sched_barrier(0);   // nothing of the epilogue moves into the mainloop
 #pragma unroll
-        for (int tm = 0; tm < S::TM; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < S::TN; ++tn) {
-                block<S>(acc[tm][tn], tm, tn, m0, n0, tid);
-                __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
+        for (int u = 0; u < kUnits; ++u) {
+            if constexpr (paired<S>()) {
+                const int tm = u / (S::TN / 2), tp = u % (S::TN / 2);
+                unit<S>(acc[tm][2 * tp], acc[tm][2 * tp + 1], u, m0, n0, tid);
+            } else {
+                unit<S>(acc[u / S::TN][u % S::TN], acc[u / S::TN][u % S::TN], u, m0, n0, tid);
             }
+            __builtin_amdgcn_sched_barrier(0);   // one unit's temporaries live at a time
+        }
+    }
+
+    // Accumulator block of unit u's k-th block (index tm * TN + tn).
+    template <class S>
+    __device__ __forceinline__ static int unit_block(int u, int k) {
+        if constexpr (paired<S>())
+            return (u / (S::TN / 2)) * S::TN + 2 * (u % (S::TN / 2)) + k;
+        else
+            return u;
     }
 };
 
@@ -178,7 +238,7 @@ struct StoreEpilogue {
     uint16_t *C;
     int M, N;
 
-    template <class S>
+    template <class S, bool kFromAcc = true>
     __device__ __forceinline__ void block(const f32x16 &a, int tm, int tn, int m0, int n0,
                                           int tid) const {
         const int lane = tid & 63;
@@ -197,7 +257,7 @@ struct StoreEpilogue {
         for (int i = 0; i < 16; ++i) {
             const uint32_t roff =
                 static_cast<uint32_t>(acc_row<S>(0, tm, i, 0)) * static_cast<uint32_t>(N) * 2u;
-            store_b16(r, voff + roff, to_bf16(a[i]));
+            store_b16(r, voff + roff, to_bf16(acc_value<kFromAcc>(a[i])));
         }
     }
 
@@ -212,6 +272,18 @@ struct StoreEpilogue {
                 __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
             }
     }
+
+    template <class S>
+    static constexpr bool paired() { return false; }
+    template <class S>
+    static constexpr int unit_blocks() { return 1; }
+    template <class S, bool kFromAcc = true>
+    __device__ __forceinline__ void unit(const f32x16 &a0, const f32x16 &, int u, int m0, int n0,
+                                         int tid) const {
+        block<S, kFromAcc>(a0, u / S::TN, u % S::TN, m0, n0, tid);
+    }
+    template <class S>
+    __device__ __forceinline__ static int unit_block(int u, int) { return u; }
 };
 
 // K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
@@ -250,81 +322,109 @@ struct QuarterOf {
 enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2 };
 
 // One accumulator per tile: D = A . B^T over the tiles of `sch`, then `epi`.
-// Workgroup b < sch.dp runs tile b (XCD-ordered) whole and runs the epilogue.
-// The tiles [dp, dp + split_tiles) of a partly idle last round run
-//  - with kTailSplit: workgroup dp + j runs piece j % pieces of split tile
-//    dp + j / pieces and stores its partial (split_tail.hpp), which
-//    split_reduce_kernel finishes;
-//  - with kTailQuarter: workgroup dp + q runs quarter q % 4 (row half q/2 % 2,
-//    column half q % 2) of tile dp + q / 4 whole, as a quarter-size tile, so
-//    four times the workgroups share the round.
-// A workgroup runs one tile, quarter or piece: no loop.
+// Persistent: workgroup b runs whole tiles b, b + grid, ... below sch.dp
+// (XCD-ordered), one after the other; before the epilogue of each it puts the
+// first K steps of its next tile in flight, so their load latency hides behind
+// the epilogue and no workgroup launch sits between tiles.  Then it takes its
+// share of the tiles [dp, dp + split_tiles) of a partly idle last round:
+//  - with kTailSplit: work item j (j = b, b + grid, ...) is piece j % pieces
+//    of split tile dp + j / pieces, which stores its partial (split_tail.hpp)
+//    for split_reduce_kernel to finish;
+//  - with kTailQuarter: work item q is quarter q % 4 (row half q/2 % 2, column
+//    half q % 2) of tile dp + q / 4, run whole as a quarter-size tile.
 template <class S, class Epi, int TAIL>
 __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
     const uint16_t *__restrict__ A, KMajor B, int M, int K, Epi epi, Schedule sch) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
-
     const int b = blockIdx.x;
+    const int grid = sch.grid;
+    const KMajor Ak{A, M, 1, 0};
+
+    if (b < sch.dp) {
+        PipelineFor<S> pl;
+        pl.init(lds);
+        TileLoader<S> ld;
+        int j = b, tm, tn;
+        tile_coords(xcd_order(j, sch.dp), sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
+        ld.init(Ak, tm * S::BM, B, tn * S::BN, K);
+        const int nk = sch.nk;
+        // steps past the end load nothing (K step nk is past the end of K)
+        auto issue = [&](int s, SWIGLU_LDS char *st) { ld.issue(s < nk ? s : nk, st); };
+        pl.prologue_issue(issue);
+        for (; j < sch.dp; j += grid) {
+            f32x16 acc[S::TM][S::TN];
+            zero_acc<S>(acc);
+            pl.prologue_wait();
+            pl.run(issue, 0, nk, nk, acc);
+            pl.drain();
+            const int m0 = tm * S::BM, n0 = tn * S::BN;
+            if (j + grid < sch.dp) {
+                tile_coords(xcd_order(j + grid, sch.dp), sch.tiles_m, sch.tiles_n, sch.group_m, tm,
+                            tn);
+                ld.init(Ak, tm * S::BM, B, tn * S::BN, K);
+                pl.prologue_issue(issue);
+            }
+            epi.template apply<S>(acc, m0, n0, threadIdx.x);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
     if constexpr (TAIL == kTailQuarter) {
-        if (b >= sch.dp) {
-            using Q = typename QuarterOf<S>::type;
-            static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
-            const int q = xcd_order(b - sch.dp, 4 * sch.split_tiles);
+        using Q = typename QuarterOf<S>::type;
+        static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
+        const int nq = 4 * sch.split_tiles;
+        for (int i = b; i < nq; i += grid) {
+            const int q = xcd_order(i, nq);
             int tm, tn;
             tile_coords(sch.dp + q / 4, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
             const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
             const int n0 = tn * S::BN + (q & 1) * Q::BN;
-            if (m0 >= M || n0 >= B.rows) return;   // quarter wholly past the output's edge
+            if (m0 >= M || n0 >= B.rows) continue;   // quarter wholly past the output's edge
             f32x16 acc[Q::TM][Q::TN];
             tile_mainloop<Q>(lds, A, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
             epi.template apply<Q>(acc, m0, n0, threadIdx.x);
-            return;
+        }
+    } else if constexpr (TAIL == kTailSplit) {
+        const int np = sch.split_tiles * sch.pieces;
+        for (int j = b; j < np; j += grid) {
+            const int t = sch.dp + j / sch.pieces;
+            const int piece = j % sch.pieces;
+            const int kb = piece * sch.nk / sch.pieces;
+            const int ke = (piece + 1) * sch.nk / sch.pieces;
+            int tm, tn;
+            tile_coords(t, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
+            f32x16 acc[S::TM][S::TN];
+            tile_mainloop<S>(lds, A, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
+            store_partial<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN, acc,
+                             threadIdx.x);
         }
     }
-    int t, kb = 0, ke = sch.nk, j = 0;
-    const bool whole = TAIL != kTailSplit || b < sch.dp;
-    if (whole) {
-        t = xcd_order(b, sch.dp);
-    } else {
-        j = b - sch.dp;
-        t = sch.dp + j / sch.pieces;
-        const int piece = j % sch.pieces;
-        kb = piece * sch.nk / sch.pieces;
-        ke = (piece + 1) * sch.nk / sch.pieces;
-    }
-    int tm, tn;
-    tile_coords(t, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
-    const int m0 = tm * S::BM;
-    const int n0 = tn * S::BN;
-
-    f32x16 acc[S::TM][S::TN];
-    tile_mainloop<S>(lds, A, B, M, K, m0, n0, kb, ke, sch.nk, acc);
-    if (whole)
-        epi.template apply<S>(acc, m0, n0, threadIdx.x);
-    else
-        store_partial<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN, acc,
-                         threadIdx.x);
 }
 
-// The split tiles' epilogue: one wave per (split tile, GEMM wave, 32x32
-// accumulator block), four per workgroup.  The wave takes the registers of
-// the GEMM wave it stands for -- its lane l holds what GEMM thread
-// 64 w + l held, summed over the pieces -- so the epilogue's lane pairing
-// is the GEMM's.
+// The split tiles' epilogue: one wave per (split tile, GEMM wave, epilogue
+// unit), four per workgroup.  The wave takes the registers of the GEMM wave it
+// stands for -- its lane l holds what GEMM thread 64 w + l held, summed over
+// the pieces -- so the epilogue's lane layout is the GEMM's.
 template <class S, class Epi>
 __global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch) {
-    constexpr int kBlocks = S::TM * S::TN;
-    constexpr int kPerTile = S::kWaves * kBlocks;
-    const int item = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+    constexpr int kUnitBlocks = Epi::template unit_blocks<S>();
+    constexpr int kUnits = S::TM * S::TN / kUnitBlocks;
+    constexpr int kPerTile = S::kWaves * kUnits;
+    // uniform per wave (scalar registers: the output resource derived from it
+    // must be scalar)
+    const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int i = item / kPerTile;                 // split tile
-    const int w = (item % kPerTile) / kBlocks;     // GEMM wave
-    const int blk = item % kBlocks;                // accumulator block tm * TN + tn
+    const int w = (item % kPerTile) / kUnits;      // GEMM wave
+    const int u = item % kUnits;                   // epilogue unit
     const int x = w * 64 + static_cast<int>(threadIdx.x & 63);
-    const f32x16 a = sum_pieces<S>(sch, i, blk, x);
+    f32x16 a[kUnitBlocks];
+#pragma unroll
+    for (int k = 0; k < kUnitBlocks; ++k)
+        a[k] = sum_pieces<S>(sch, i, Epi::template unit_block<S>(u, k), x);
     int tm, tn;
     tile_coords(sch.dp + i, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
-    epi.template block<S>(a, blk / S::TN, blk % S::TN, tm * S::BM, tn * S::BN, x);
+    epi.template unit<S, false>(a[0], a[kUnitBlocks - 1], u, tm * S::BM, tn * S::BN, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -563,32 +663,45 @@ static Schedule make_schedule(int M, int cols, int K, const GemmWorkspace &ws,
     return sch;
 }
 
+// Workgroups of a persistent launch of `sch`: one per slot, or fewer when
+// there is less work (unknown slot count: one per whole tile).
+template <class S>
+static int launch_grid(const Schedule &sch, int cus) {
+    const int64_t tail = sch.quartered ? 4LL * sch.split_tiles
+                                       : static_cast<int64_t>(sch.split_tiles) * sch.pieces;
+    const int64_t work = sch.dp > tail ? sch.dp : tail;
+    const int64_t G = static_cast<int64_t>(cus) * S::kOccupancy;
+    return static_cast<int>(G > 0 && G < work ? G : work);
+}
+
 template <class S, class Epi>
 static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int K, Epi epi,
                               const GemmWorkspace &ws, hipStream_t stream) {
-    const Schedule sch = make_schedule<S>(M, cols, K, ws);
+    Schedule sch = make_schedule<S>(M, cols, K, ws);
+    sch.grid = launch_grid<S>(sch, ws.cus);
+    B.pairs = Epi::template paired<S>() ? 1 : 0;   // de-interleaved weight panels
+    if (sch.grid <= 0) return hipSuccess;
     if (sch.quartered) {
         if constexpr (kQuarterable<S>) {
-            hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailQuarter>),
-                               dim3(sch.dp + 4 * sch.split_tiles), dim3(S::kThreads), 0, stream,
-                               A, B, M, K, epi, sch);
+            hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailQuarter>), dim3(sch.grid),
+                               dim3(S::kThreads), 0, stream, A, B, M, K, epi, sch);
             return hipGetLastError();
         }
         return hipErrorInvalidConfiguration;   // make_schedule quarters no other shape
     }
     if (sch.pieces == 0) {
-        hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailNone>), dim3(sch.dp),
+        hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailNone>), dim3(sch.grid),
                            dim3(S::kThreads), 0, stream, A, B, M, K, epi, sch);
         return hipGetLastError();
     }
-    const int grid = sch.dp + sch.split_tiles * sch.pieces;
-    hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailSplit>), dim3(grid), dim3(S::kThreads), 0,
-                       stream, A, B, M, K, epi, sch);
+    hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailSplit>), dim3(sch.grid), dim3(S::kThreads),
+                       0, stream, A, B, M, K, epi, sch);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // S::kWaves * TM * TN waves per split tile, four per workgroup
-    static_assert((S::kWaves * S::TM * S::TN) % 4 == 0, "whole workgroups per split tile");
-    const int rgrid = sch.split_tiles * (S::kWaves * S::TM * S::TN / 4);
+    // S::kWaves * (epilogue units per wave) waves per split tile, four per workgroup
+    constexpr int kWavesPerTile = S::kWaves * S::TM * S::TN / Epi::template unit_blocks<S>();
+    static_assert(kWavesPerTile % 4 == 0, "whole workgroups per split tile");
+    const int rgrid = sch.split_tiles * (kWavesPerTile / 4);
     hipLaunchKernelGGL((split_reduce_kernel<S, Epi>), dim3(rgrid), dim3(256), 0, stream, epi, sch);
     return hipGetLastError();
 }
@@ -619,32 +732,35 @@ hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint1
 // The kernels launch_fused_interleaved / launch_fused_sequential /
 // launch_gemm_store (one of the ablation's two GEMMs) would run, as text.
 template <class S>
-static int describe(const char *kernel, const char *epi, const Schedule &sch, char *buf,
-                    size_t n) {
+static int describe(const char *kernel, const char *epi, const Schedule &sch, int cus,
+                    char *buf, size_t n) {
+    const int wgs = launch_grid<S>(sch, cus);
     if (sch.pieces)
         return std::snprintf(buf, n,
-                             "%s<%dx%dx%d,%s> (%d whole tiles + %d tiles split %d ways along K)"
-                             " + split_reduce_kernel",
+                             "%s<%dx%dx%d,%s> (%d whole tiles + %d tiles split %d ways along K;"
+                             " %d workgroups) + split_reduce_kernel",
                              kernel, S::BM, S::BN, S::BK, epi, sch.dp, sch.split_tiles,
-                             sch.pieces);
+                             sch.pieces, wgs);
     if (sch.quartered)
-        return std::snprintf(buf, n, "%s<%dx%dx%d,%s> (%d tiles + %d tiles run as %d %dx%d tiles)",
+        return std::snprintf(buf, n,
+                             "%s<%dx%dx%d,%s> (%d tiles + %d tiles run as %d %dx%d tiles;"
+                             " %d workgroups)",
                              kernel, S::BM, S::BN, S::BK, epi, sch.dp, sch.split_tiles,
-                             4 * sch.split_tiles, S::BM / 2, S::BN / 2);
-    return std::snprintf(buf, n, "%s<%dx%dx%d,%s> (%d tiles)", kernel, S::BM, S::BN, S::BK,
-                         epi, sch.dp);
+                             4 * sch.split_tiles, S::BM / 2, S::BN / 2, wgs);
+    return std::snprintf(buf, n, "%s<%dx%dx%d,%s> (%d tiles; %d workgroups)", kernel, S::BM,
+                         S::BN, S::BK, epi, sch.dp, wgs);
 }
 
 int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *epi, char *buf,
                   size_t n) {
     if (M <= 128)
         return describe<ShapeSmall>("gemm_tiles_kernel", epi,
-                                    make_schedule<ShapeSmall>(M, cols, K, ws), buf, n);
+                                    make_schedule<ShapeSmall>(M, cols, K, ws), ws.cus, buf, n);
     if (quad_tiles_faster(M, cols, K, ws))
         return describe<ShapeQuad>("gemm_tiles_kernel", epi,
-                                   make_schedule<ShapeQuad>(M, cols, K, ws), buf, n);
+                                   make_schedule<ShapeQuad>(M, cols, K, ws), ws.cus, buf, n);
     return describe<ShapeWide>("gemm_tiles_kernel", epi, make_schedule<ShapeWide>(M, cols, K, ws),
-                               buf, n);
+                               ws.cus, buf, n);
 }
 
 int describe_fused_sequential(int M, int N, char *buf, size_t n) {

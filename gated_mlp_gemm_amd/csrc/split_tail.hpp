@@ -37,6 +37,7 @@ struct Schedule {
     int split_tiles;        // tiles [dp, dp + split_tiles) are split (or quartered)
     int group_m;            // tile order: groups of group_m tile rows (tile_coords)
     int quartered;          // 1: the tail tiles run as four quarter-size tiles instead
+    int grid;               // workgroups launched (each loops over its share of the work)
     float *partials;        // one BM*BN slot per piece: slot j = piece j % pieces of split tile j / pieces
 };
 

@@ -150,9 +150,11 @@ int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused,
  * compute-unit count): for swiglu_fused_gemm with `variant` (AUTO, S, I) or
  * for swiglu_unfused_ablation (-1), given a workspace of `workspace_bytes`
  * (0: none), the kernel names with their tile shapes and schedule, e.g.
- * "gemm_tiles_kernel<128x128x64,PairMulEpilogue> (2240 tiles)".  Writes at
- * most buf_bytes bytes including the terminating NUL (truncating).  Same
- * shape validation as the calls it describes; SWIGLU_ERR_NULL without buf.
+ * "gemm_tiles_kernel<128x128x64,PairMulEpilogue> (2240 tiles; 512 workgroups)"
+ * (the GEMM kernels are persistent: each workgroup loops over its share of
+ * the tiles).  Writes at most buf_bytes bytes including the terminating NUL
+ * (truncating).  Same shape validation as the calls it describes;
+ * SWIGLU_ERR_NULL without buf.
  */
 int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
                            uint64_t workspace_bytes, char *buf, uint64_t buf_bytes);

@@ -543,14 +543,14 @@ def test_describe_launch(dev, monkeypatch):
     assert d.startswith("gemm_tiles_kernel<") and "PairMulEpilogue" in d
     monkeypatch.setenv("SWIGLU_I_TILE", "256")
     d = sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws)
-    assert "256x256x64" in d and "512 tiles + 48 tiles run as 192 128x128 tiles" in d, d
+    assert "256x256x64" in d and "512 tiles + 48 tiles run as 192 128x128 tiles; 256 workgroups" in d, d
     assert "split" not in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
     monkeypatch.setenv("SWIGLU_TAIL", "split")
     d = sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws)
     assert "256x256x64" in d and "split 5 ways" in d and d.endswith("split_reduce_kernel")
     assert "split" not in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
     monkeypatch.setenv("SWIGLU_TAIL", "whole")
-    assert sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws).endswith("(560 tiles)")
+    assert sw.swiglu_describe_launch(2048, 8960, 1536, "i", ws).endswith("(560 tiles; 256 workgroups)")
     monkeypatch.delenv("SWIGLU_TAIL")
     monkeypatch.setenv("SWIGLU_I_TILE", "128")
     assert "128x128x64" in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)

@@ -214,15 +214,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_record(path: str, workload: str):
+def traffic_record(variant: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    table_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(table_path):
         return None
-    with open(path) as f:
+    with open(table_path) as f:
         table = json.load(f)
-    rec = table.get(f"{path}|{workload}")
+    rec = table.get(f"{variant}|{workload}")
     if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")

@@ -83,6 +83,10 @@ class Oracle:
         lib.swo_swiglu_materialised.argtypes = [_U16P, _U16P, _U16P, i64,
                                                 i64, i64, nu16, nu16, nu16]
         lib.swo_silu_mul.argtypes = [_U16P, _U16P, i64, _U16P]
+        lib.swo_pack_nk.argtypes = [_U16P, _U16P, _U16P, i64, i64]
+        lib.swo_down_proj.argtypes = [_U16P, _U16P, i64, i64, i64, nf64, _U16P]
+        lib.swo_gated_mlp.argtypes = [_U16P, _U16P, _U16P, _U16P, i64, i64,
+                                      i64, _U16P, _U16P]
         lib.swo_num_threads.restype = ctypes.c_int
         self._lib = lib
         self.path = path
@@ -176,6 +180,37 @@ class Oracle:
         Wf = np.empty((K, 2 * N), dtype=np.uint16)
         self._lib.swo_pack(W1, W2, Wf, K, N)
         return Wf
+
+    def pack_nk(self, W1t, W2t):
+        """W_fused [K, 2N] from linear-layer weights W1t, W2t [N, K]."""
+        W1t, W2t = self._u16(W1t), self._u16(W2t)
+        N, K = W1t.shape
+        assert W2t.shape == (N, K)
+        Wf = np.empty((K, 2 * N), dtype=np.uint16)
+        self._lib.swo_pack_nk(W1t, W2t, Wf, K, N)
+        return Wf
+
+    def down_proj(self, H, W3, want_f64: bool = False):
+        """Out = bf16(H . W3); H [M, N], W3 [N, D]; returns [M, D] (and o64)."""
+        H, W3 = self._u16(H), self._u16(W3)
+        M, N = H.shape
+        N2, D = W3.shape
+        assert N == N2
+        out = np.empty((M, D), dtype=np.uint16)
+        o64 = np.empty((M, D), dtype=np.float64) if want_f64 else None
+        self._lib.swo_down_proj(H, W3, M, N, D, o64, out)
+        return (out, o64) if want_f64 else out
+
+    def gated_mlp(self, A, W1, W2, W3):
+        """MLP block: returns (H [M, N], Out [M, K]) bf16 patterns."""
+        A, W1, W2, W3 = (self._u16(x) for x in (A, W1, W2, W3))
+        M, K = A.shape
+        N = W1.shape[1]
+        assert W1.shape == (K, N) and W2.shape == (K, N) and W3.shape == (N, K)
+        h = np.empty((M, N), dtype=np.uint16)
+        out = np.empty((M, K), dtype=np.uint16)
+        self._lib.swo_gated_mlp(A, W1, W2, W3, M, N, K, h, out)
+        return h, out
 
     def swiglu_materialised(self, A, W1, W2):
         """Unfused pipeline: returns (gate_bf16, up_bf16, y_bf16)."""

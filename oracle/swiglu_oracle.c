@@ -35,6 +35,18 @@
  * SiLU(D[m,2n]) * D[m,2n+1].  It is provided separately so that the
  * invariant "interleaved == separate, bit for bit" can be tested.
  *
+ * Weights in the layout of a linear layer ([N][K]: one row per output
+ * feature, i.e. W1 and W2 transposed) pack into the same W_fused; the
+ * packer for them is written out separately and pinned against slicing.
+ *
+ * The gated MLP block whose execution time the SwiGLU share is measured
+ * against [paper s1, Figure 1: SwiGLU activation and materialisation as a
+ * fraction of total MLP time] ends with the down projection back to the
+ * model width: Out = Y . W3 with W3 in R^{N x K}.  The pages name the MLP
+ * block but print no formula for it; the plain reading is that Y, a bf16
+ * tensor like every activation here, is the input of one more GEMM:
+ *   Out[m,d] = bf16( sum_n Y_bf16[m,n] W3[n,d] ), double, n ascending.
+ *
  * The materialised form rounds Gate and Up to bf16 before the activation,
  * as the unfused eager pipeline does [paper s1: two full intermediate tensors
  * are materialised in HBM between the GEMM and activation stages]; it pins
@@ -47,7 +59,10 @@
  * patterns and against torch's independent float->bf16 cast; SiLU closed
  * forms and the identity SiLU(x) - SiLU(-x) = x; hand-computed 2x3x2 cases;
  * dot products against numpy float64 matmul; the interleave invariant; the
- * pack against numpy slicing.  Planted-mistake builds (PLANT_* macros below,
+ * pack against numpy slicing; the linear-layer packer against slicing of the
+ * transposes; the down projection against numpy float64 matmul, the
+ * identity weight and a hand case whose result changes sign if Y is not
+ * rounded to bf16 first.  Planted-mistake builds (PLANT_* macros below,
  * compiled only by the tests) show that each plausible slip fails a pin.
  */
 #include <math.h>
@@ -333,6 +348,81 @@ void swo_silu_mul(const uint16_t *g, const uint16_t *u, int64_t count,
                          swo_bf16_to_double(u[i]);
         ybf[i] = swo_double_to_bf16(y);
     }
+}
+
+/*
+ * Packer for weights in a linear layer's layout: W1t and W2t are [N][K]
+ * (row n holds column n of W1, resp. W2).  The output is the same W_fused
+ * [K, 2N] as swo_pack:  W_fused[k, 2n] = W1t[n, k],  W_fused[k, 2n+1] =
+ * W2t[n, k]  [gist: Kernel-2].
+ */
+void swo_pack_nk(const uint16_t *W1t, const uint16_t *W2t, uint16_t *Wf,
+                 int64_t K, int64_t N)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t n = 0; n < N; ++n) {
+#ifdef PLANT_PACK_NK_UNTRANSPOSED   /* reads [N][K] as if it were [K][N]  */
+            Wf[k * 2 * N + 2 * n] = W1t[k * N + n];
+            Wf[k * 2 * N + 2 * n + 1] = W2t[k * N + n];
+#else
+            Wf[k * 2 * N + 2 * n] = W1t[n * K + k];
+            Wf[k * 2 * N + 2 * n + 1] = W2t[n * K + k];
+#endif
+        }
+    }
+}
+
+/*
+ * Down projection of the MLP block: Out[m, d] = bf16( sum_n H[m, n] W3[n, d] )
+ * for H [M][N] and W3 [N][D] (D is the model width, K of the gated GEMM),
+ * double, n ascending, one rounding.  out64 (unrounded) may be NULL.
+ */
+void swo_down_proj(const uint16_t *H, const uint16_t *W3, int64_t M, int64_t N,
+                   int64_t D, double *out64, uint16_t *outbf)
+{
+    #pragma omp parallel
+    {
+        double *o = (double *)malloc((size_t)D * sizeof(double));
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m) {
+            row_times_matrix(H + m * N, W3, N, D, o);
+            for (int64_t d = 0; d < D; ++d) {
+                if (out64) out64[m * D + d] = o[d];
+                outbf[m * D + d] = swo_double_to_bf16(o[d]);
+            }
+        }
+        free(o);
+    }
+}
+
+/*
+ * The gated MLP block [paper s1]: H = bf16(SiLU(A.W1) * (A.W2)) as in
+ * swo_swiglu_separate, then Out = bf16(H . W3) with W3 [N][K] (the output
+ * has the model width K of the input).  hbf (the bf16 H, [M][N]) is
+ * written; the down projection reads H as rounded.
+ */
+void swo_gated_mlp(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
+                   const uint16_t *W3, int64_t M, int64_t N, int64_t K,
+                   uint16_t *hbf, uint16_t *outbf)
+{
+#ifdef PLANT_MLP_UNROUNDED_H        /* feeds the unrounded product onward   */
+    double *h64 = (double *)malloc((size_t)(M * N) * sizeof(double));
+    swo_swiglu_separate(A, W1, W2, M, N, K, h64, hbf);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t d = 0; d < K; ++d) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                s += h64[m * N + n] * swo_bf16_to_double(W3[n * K + d]);
+            outbf[m * K + d] = swo_double_to_bf16(s);
+        }
+    }
+    free(h64);
+#else
+    swo_swiglu_separate(A, W1, W2, M, N, K, NULL, hbf);
+    swo_down_proj(hbf, W3, M, N, K, NULL, outbf);
+#endif
 }
 
 /* Threads the OpenMP runtime will use for a parallel region. */

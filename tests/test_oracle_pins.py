@@ -289,6 +289,75 @@ def check_pack(orc):
         assert np.array_equal(Wf[:, 0::2], W1) and np.array_equal(Wf[:, 1::2], W2)
 
 
+def check_pack_nk(orc):
+    rng = np.random.default_rng(6)
+    for K, N in [(1, 1), (8, 3), (24, 136), (40, 16)]:
+        W1t = rng.integers(0, 2 ** 16, size=(N, K), dtype=np.uint16)
+        W2t = rng.integers(0, 2 ** 16, size=(N, K), dtype=np.uint16)
+        Wf = orc.pack_nk(W1t, W2t)
+        assert Wf.shape == (K, 2 * N)
+        # column 2n of W_fused is row n of W1t, column 2n+1 row n of W2t
+        assert np.array_equal(Wf[:, 0::2], W1t.T) and np.array_equal(Wf[:, 1::2], W2t.T)
+
+
+def _mlp_hand_cases():
+    with open(os.path.join(HERE, "golden", "mlp_hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _rational_bits(table):
+    out = np.empty((len(table), len(table[0])), dtype=np.uint16)
+    for (i, j), _ in np.ndenumerate(out):
+        v, negzero = parse_rational(table[i][j])
+        out[i, j] = 0x8000 if negzero else brute_bf16(v)
+    return out
+
+
+def check_mlp_hand_cases(orc):
+    for case in _mlp_hand_cases():
+        H = [[parse_rational(v)[0] for v in row] for row in case["H_bf16"]]
+        W3 = [[Fraction(v) for v in row] for row in case["W3"]]
+        M, N, D = len(H), len(W3), len(W3[0])
+        want = _rational_bits(case["out_bf16"])
+        # independent brute force: exact rational sums, exact nearest-even search
+        for m in range(M):
+            for d in range(D):
+                o = sum(H[m][n] * W3[n][d] for n in range(N))
+                assert o == parse_rational(case["out_exact"][m][d])[0], (case["name"], m, d)
+                assert brute_bf16(o) == want[m, d], (case["name"], m, d)
+        h_bits = _rational_bits(case["H_bf16"])
+        w3_bits = to_bits(case["W3"])
+        assert np.array_equal(orc.down_proj(h_bits, w3_bits), want), case["name"]
+        h, out = orc.gated_mlp(to_bits(case["A"]), to_bits(case["W1"]), to_bits(case["W2"]),
+                               w3_bits)
+        assert np.array_equal(h, h_bits), case["name"]
+        assert np.array_equal(out, want), (case["name"], out, want)
+
+
+def check_down_proj_vs_numpy(orc):
+    for seed in range(16):
+        H, W3, _ = _random_case(40 + seed)          # H [M,K'], W3 [K',N']: any bf16 pair
+        h, w = bits_to_f64(H), bits_to_f64(W3)
+        out, o64 = orc.down_proj(H, W3, want_f64=True)
+        bound = 1e-12 * (np.abs(h) @ np.abs(w)) + 1e-300
+        assert np.all(np.abs(o64 - h @ w) <= bound), seed
+        for (m, d), v in np.ndenumerate(o64):
+            b = brute_bf16(Fraction(float(v))) if v != 0 else (0x8000 if math.copysign(1, v) < 0 else 0)
+            assert out[m, d] == b, (seed, m, d)
+
+
+def check_mlp_identity_down(orc):
+    # W3 = I (model width K = N): the block's output is its bf16 SwiGLU output
+    for seed, (M, N) in enumerate([(3, 8), (17, 40)]):
+        A = inputs.bits(inputs.random_bf16((M, N), 500 + seed))
+        W1 = inputs.bits(inputs.random_bf16((N, N), 600 + seed, 1 / math.sqrt(N)))
+        W2 = inputs.bits(inputs.random_bf16((N, N), 700 + seed, 1 / math.sqrt(N)))
+        eye = to_bits(np.eye(N))
+        h, out = orc.gated_mlp(A, W1, W2, eye)
+        assert np.array_equal(h, orc.swiglu(A, W1, W2))
+        assert np.array_equal(out, h)
+
+
 CHECKS = [
     check_rounding_patterns,
     check_rounding_vs_torch,
@@ -299,6 +368,10 @@ CHECKS = [
     check_pipeline_vs_numpy,
     check_interleave_invariant,
     check_pack,
+    check_pack_nk,
+    check_mlp_hand_cases,
+    check_down_proj_vs_numpy,
+    check_mlp_identity_down,
 ]
 
 
@@ -369,6 +442,8 @@ MUTANTS = [
     "PLANT_TRANSPOSED_UP",
     "PLANT_ROUND_TOWARD_ZERO",
     "PLANT_PACK_UP_EVEN",
+    "PLANT_PACK_NK_UNTRANSPOSED",
+    "PLANT_MLP_UNROUNDED_H",
 ]
 
 

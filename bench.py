@@ -21,6 +21,10 @@ for each of the five K x N shapes of the workloads (inputs drawn on the
 device from the same distributions; the same rotation rule) and prints one
 JSON line per (shape, M): the data behind the M threshold of the dispatcher.
 
+--mlp times the gated MLP block (the fused SwiGLU GEMM, then the down
+projection back to the model width) against the unfused pipeline followed by
+the same down projection, on the five workloads: one JSON line each.
+
 --schedule-calibration times variant I at the same shapes over a finer range
 of M, once with the library's own choice and once forced (SWIGLU_I_TILE,
 SWIGLU_TAIL) through each tile shape and tail schedule, one JSON line per
@@ -62,6 +66,10 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="time I, S and the ablation over M for the five K x N shapes")
     p.add_argument("--sweep-m", default="128,256,512,1024,2048,3072,4096,8192,16384")
+    p.add_argument("--mlp", action="store_true",
+                   help="time the gated MLP block (SwiGLU + down projection), fused vs "
+                        "unfused, on the five workloads")
+    p.add_argument("--mlp-workloads", default="0,1,2,3,4")
     p.add_argument("--schedule-calibration", action="store_true",
                    help="time variant I under every forced tile shape / tail schedule")
     p.add_argument("--calibration-m",
@@ -164,6 +172,85 @@ def schedule_calibration(args):
                 os.environ[k] = v
 
 
+def mlp_blocks(args):
+    """The gated MLP block per workload (one JSON line each): the fused SwiGLU
+    GEMM followed by the down projection Out = H . W3 (W3 in R^{N x K}), against
+    the unfused pipeline (two GEMMs materialising Gate and Up, the SiLU-mul
+    kernel) followed by the same down projection; plus each stage alone.  The
+    share of the unfused block spent in the activation kernel, and the share
+    the fusion removes, are the MI355X counterparts of the paper's Figure 1
+    (SwiGLU and its materialisation as a fraction of MLP time)."""
+    import torch
+
+    from gated_mlp_gemm_amd import inputs
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    sw.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for idx in (int(x) for x in args.mlp_workloads.split(",")):
+        w = inputs.WORKLOADS[idx]
+        M, K, N = w.M, w.K, w.N
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed)
+        # the workload's distributions, drawn on the device (same recipe as
+        # the parity tests' generator, different stream of numbers)
+        A = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+        W1 = (torch.randn(K, N, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16)
+        W2 = (torch.randn(K, N, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16)
+        Wf = sw.swiglu_pack_weights(W1, W2)
+        del W1, W2
+        W3t = (torch.randn(K, N, device=dev, generator=g) / N ** 0.5).to(torch.bfloat16)
+        in_bytes = 2 * (M * K + 2 * K * N + K * N)
+        R = max(1, -(-512 * 2 ** 20 // in_bytes))
+        copies = []
+        for r in range(R):
+            a, wf, w3 = (A, Wf, W3t) if r == 0 else (A.clone(), Wf.clone(), W3t.clone())
+            bufs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+            out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+            copies.append((a, wf, w3, bufs[0], bufs[1], bufs[2], out))
+        ws = sw.make_workspace(M, N, K, "ablation", dev)
+        torch.cuda.synchronize()
+
+        def unfused(a, wf, w3, h, gt, up, out):
+            sw.swiglu_unfused_ablation(a, wf, gate_ws=gt, up_ws=up, Y=h, workspace=ws)
+            sw.swiglu_down_proj(h, w3, Out=out, workspace=ws)
+
+        calls = {
+            "fused_swiglu": lambda a, wf, w3, h, gt, up, out:
+                sw.swiglu_fused_gemm(a, wf, Y=h, variant="auto", workspace=ws),
+            "ablation_swiglu": lambda a, wf, w3, h, gt, up, out:
+                sw.swiglu_unfused_ablation(a, wf, gate_ws=gt, up_ws=up, Y=h, workspace=ws),
+            "silu_mul": lambda a, wf, w3, h, gt, up, out: sw.swiglu_silu_mul(gt, up, Y=h),
+            "down_proj": lambda a, wf, w3, h, gt, up, out:
+                sw.swiglu_down_proj(h, w3, Out=out, workspace=ws),
+            "mlp_fused": lambda a, wf, w3, h, gt, up, out:
+                sw.swiglu_gated_mlp(a, wf, w3, H=h, Out=out, variant="auto", workspace=ws),
+            "mlp_unfused": unfused,
+        }
+        us = {}
+        for name, fn in calls.items():
+            us[name] = round(_time_call(fn, copies, stream, budget_s=0.25, max_reps=2000), 2)
+        mlp_flops = 6 * M * N * K
+        rec = {
+            "workload": f"gated MLP block M={M} K={K} N={N} (seed {w.seed})",
+            "M": M, "K": K, "N": N, "rotation_copies": R, "us": us,
+            "down_proj_launch": sw.swiglu_describe_launch(M, N, K, "down_proj",
+                                                          0 if ws is None else ws.numel()),
+            "down_proj_tflops": round(2 * M * N * K / (us["down_proj"] * 1e-6) / 1e12, 1),
+            "mlp_tflops_fused": round(mlp_flops / (us["mlp_fused"] * 1e-6) / 1e12, 1),
+            "mlp_tflops_unfused": round(mlp_flops / (us["mlp_unfused"] * 1e-6) / 1e12, 1),
+            "mlp_speedup_fused_vs_unfused": round(us["mlp_unfused"] / us["mlp_fused"], 3),
+            "activation_share_of_unfused_mlp": round(us["silu_mul"] / us["mlp_unfused"], 4),
+            "fusion_saving_share_of_unfused_mlp":
+                round((us["mlp_unfused"] - us["mlp_fused"]) / us["mlp_unfused"], 4),
+        }
+        print(json.dumps(rec), flush=True)
+        del copies, A, Wf, W3t, ws
+        torch.cuda.empty_cache()
+
+
 def sweep(args):
     """Variant I vs S vs the ablation over M, per K x N shape (one JSON line each)."""
     import torch
@@ -232,11 +319,14 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the fused SwiGLU GEMM is a single-device "
-              "kernel here (a column split of N needs no communication; see the design "
-              "notes); --gpus must be 1", file=sys.stderr)
+              "kernel here (a column split of N needs no communication, so each GPU would "
+              "run this same call on its share of the columns); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.mlp:
+        mlp_blocks(args)
         return
     if args.schedule_calibration:
         schedule_calibration(args)

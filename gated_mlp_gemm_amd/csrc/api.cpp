@@ -63,6 +63,22 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
     return SWIGLU_OK;
 }
 
+// The down projection Out [M][D] = H [M][N] . W3 reduces over N: N is its
+// K-like dimension (multiple of 8, at most 2^21) and D its column count.
+int check_down_shape(int64_t M, int64_t N, int64_t D) {
+    if (M < 0 || D < 0) return fail(SWIGLU_ERR_SHAPE, "negative size M=%lld D=%lld", (long long)M, (long long)D);
+    if (N < 8) return fail(SWIGLU_ERR_SHAPE, "N=%lld must be >= 8", (long long)N);
+    if (N % 8 != 0 || D % 8 != 0)
+        return fail(SWIGLU_ERR_SHAPE, "N=%lld and D=%lld must be multiples of 8", (long long)N, (long long)D);
+    if (M > kMaxM || N > kMaxK || D > kMaxN)
+        return fail(SWIGLU_ERR_SHAPE, "size beyond limits (M<=2^31-1, N<=2^21, D<=2^22)");
+    if (swiglu::max_tiles(M, D) > 2147483647) return fail(SWIGLU_ERR_SHAPE, "tile grid too large");
+    return SWIGLU_OK;
+}
+
+// swiglu_describe_launch's code for the down projection of the gated MLP.
+constexpr int kDescribeDownProj = -2;
+
 // Per-device cache: state 1 = gfx950, -1 = other architecture, 0 = not yet
 // queried; and the device's compute-unit count (sizes the split-tail schedule).
 std::mutex g_dev_mutex;
@@ -210,9 +226,9 @@ int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
                            uint64_t workspace_bytes, char *buf, uint64_t buf_bytes) {
     if (!buf || buf_bytes == 0) return fail(SWIGLU_ERR_NULL, "buf is required");
     buf[0] = '\0';
-    if (variant < -1 || variant > SWIGLU_VARIANT_I)
+    if (variant < kDescribeDownProj || variant > SWIGLU_VARIANT_I)
         return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
-    int st = check_gemm_shape(M, N, K);
+    int st = variant == kDescribeDownProj ? check_down_shape(M, N, K) : check_gemm_shape(M, N, K);
     if (st != SWIGLU_OK) return st;
     if (M == 0 || N == 0) {
         std::snprintf(buf, buf_bytes, "nothing (empty problem)");
@@ -226,7 +242,9 @@ int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
         make_ws(workspace_bytes ? reinterpret_cast<void *>(uintptr_t{256}) : nullptr,
                 workspace_bytes, cus);
     const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
-    if (v == SWIGLU_VARIANT_S) {
+    if (v == kDescribeDownProj) {
+        swiglu::describe_gemm((int)M, (int)K, (int)N, ws, "StoreEpilogue", buf, buf_bytes);
+    } else if (v == SWIGLU_VARIANT_S) {
         swiglu::describe_fused_sequential((int)M, (int)N, buf, buf_bytes);
     } else if (v == SWIGLU_VARIANT_I) {
         swiglu::describe_gemm((int)M, (int)(2 * N), (int)K, ws, "PairMulEpilogue", buf, buf_bytes);
@@ -331,4 +349,99 @@ int swiglu_silu_mul(const uint16_t *gate, const uint16_t *up, uint16_t *Y, int64
     return launched(swiglu::launch_silu_mul(gate, up, Y, count, (hipStream_t)stream), "silu_mul");
 }
 
-}  // extern "C"
+int swiglu_pack_weights_nk(const uint16_t *W1t, const uint16_t *W2t, uint16_t *W_fused,
+                           int64_t K, int64_t N, void *stream) {
+    if (K < 0 || N < 0) return fail(SWIGLU_ERR_SHAPE, "negative size");
+    // K is the row length of all three arrays
+    if (K % 8 != 0) return fail(SWIGLU_ERR_SHAPE, "K=%lld must be a multiple of 8", (long long)K);
+    if (K > kMaxK || N > kMaxN) return fail(SWIGLU_ERR_SHAPE, "size beyond limits");
+    if (K == 0 || N == 0) return ok();
+    if (!W1t || !W2t || !W_fused) return fail(SWIGLU_ERR_NULL, "W1t, W2t and W_fused are required");
+    if (!aligned16(W1t) || !aligned16(W2t) || !aligned16(W_fused))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t wbytes = K * N * 2;
+    if (overlap(W_fused, 2 * wbytes, W1t, wbytes) || overlap(W_fused, 2 * wbytes, W2t, wbytes))
+        return fail(SWIGLU_ERR_ALIAS, "W_fused overlaps W1t or W2t");
+    int st = check_device();
+    if (st != SWIGLU_OK) return st;
+    return launched(swiglu::launch_pack_nk(W1t, W2t, W_fused, K, N, (hipStream_t)stream),
+                    "pack_nk");
+}
+
+int swiglu_down_proj(const uint16_t *H, const uint16_t *W3t, uint16_t *Out, int64_t M, int64_t N,
+                     int64_t D, void *workspace, uint64_t workspace_bytes, void *stream) {
+    int st = check_down_shape(M, N, D);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0 || D == 0) return ok();
+    if (!H || !W3t || !Out) return fail(SWIGLU_ERR_NULL, "H, W3t and Out are required");
+    if (!aligned16(H) || !aligned16(W3t) || !aligned16(Out))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t hbytes = M * N * 2, wbytes = D * N * 2, obytes = M * D * 2;
+    if (overlap(Out, obytes, H, hbytes) || overlap(Out, obytes, W3t, wbytes))
+        return fail(SWIGLU_ERR_ALIAS, "Out overlaps an input");
+    st = check_workspace(workspace, workspace_bytes);
+    if (st != SWIGLU_OK) return st;
+    if (workspace && workspace_bytes > 0 &&
+        (overlap(workspace, (int64_t)workspace_bytes, H, hbytes) ||
+         overlap(workspace, (int64_t)workspace_bytes, W3t, wbytes) ||
+         overlap(workspace, (int64_t)workspace_bytes, Out, obytes)))
+        return fail(SWIGLU_ERR_ALIAS, "workspace overlaps an operand");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != SWIGLU_OK) return st;
+    return launched(swiglu::launch_down_proj(H, W3t, Out, (int)M, (int)N, (int)D,
+                                             make_ws(workspace, workspace_bytes, cus),
+                                             (hipStream_t)stream),
+                    "down projection");
+}
+
+int swiglu_gated_mlp(const uint16_t *A, const uint16_t *W_fused, const uint16_t *W3t,
+                     uint16_t *H, uint16_t *Out, int64_t M, int64_t N, int64_t K, int variant,
+                     void *workspace, uint64_t workspace_bytes, void *stream) {
+    if (variant != SWIGLU_AUTO && variant != SWIGLU_VARIANT_S && variant != SWIGLU_VARIANT_I)
+        return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
+    int st = check_gemm_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    st = check_down_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return ok();   // N >= 8 and K >= 8 here (both are reduction lengths)
+    const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
+    if (!A || !W_fused || !W3t || !H || !Out)
+        return fail(SWIGLU_ERR_NULL, "A, W_fused, W3t, H and Out are required");
+    if (!aligned16(A) || !aligned16(W_fused) || !aligned16(W3t) || !aligned16(H) ||
+        !aligned16(Out))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t abytes = M * K * 2, wbytes = 2 * K * N * 2, w3bytes = K * N * 2;
+    const int64_t hbytes = M * N * 2, obytes = M * K * 2;
+    const void *ins[3] = {A, W_fused, W3t};
+    const int64_t inb[3] = {abytes, wbytes, w3bytes};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(H, hbytes, ins[i], inb[i]) || overlap(Out, obytes, ins[i], inb[i]))
+            return fail(SWIGLU_ERR_ALIAS, "an output overlaps an input");
+    if (overlap(H, hbytes, Out, obytes)) return fail(SWIGLU_ERR_ALIAS, "H overlaps Out");
+    st = check_workspace(workspace, workspace_bytes);
+    if (st != SWIGLU_OK) return st;
+    if (workspace && workspace_bytes > 0) {
+        for (int i = 0; i < 3; ++i)
+            if (overlap(workspace, (int64_t)workspace_bytes, ins[i], inb[i]))
+                return fail(SWIGLU_ERR_ALIAS, "workspace overlaps an operand");
+        if (overlap(workspace, (int64_t)workspace_bytes, H, hbytes) ||
+            overlap(workspace, (int64_t)workspace_bytes, Out, obytes))
+            return fail(SWIGLU_ERR_ALIAS, "workspace overlaps an operand");
+    }
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != SWIGLU_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    const swiglu::GemmWorkspace ws = make_ws(workspace, workspace_bytes, cus);
+    // the two launches run in stream order, so they may share the workspace
+    hipError_t e = v == SWIGLU_VARIANT_I
+                       ? swiglu::launch_fused_interleaved(A, W_fused, H, (int)M, (int)N, (int)K,
+                                                          ws, s)
+                       : swiglu::launch_fused_sequential(A, W_fused, H, (int)M, (int)N, (int)K, s);
+    if (e != hipSuccess) return launched(e, "gated MLP: fused SwiGLU");
+    return launched(swiglu::launch_down_proj(H, W3t, Out, (int)M, (int)N, (int)K, ws, s),
+                    "gated MLP: down projection");
+}
+
+}  // extern "C\"

@@ -61,6 +61,26 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Weight packer for weights in a linear layer's layout, W1t and W2t [N][K]
+// (row n holds column n of W1, resp. W2): the packed [2N][K] array takes row
+// n of W1t as its row 2n and row n of W2t as its row 2n+1 [gist: Method,
+// Kernel-2], so the pack is a row interleave: every thread copies one 16-byte
+// chunk, coalesced on both sides (grid-stride).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_nk_kernel(const uint16_t *__restrict__ W1t,
+                                                      const uint16_t *__restrict__ W2t,
+                                                      uint16_t *__restrict__ Wf,
+                                                      int64_t chunks_per_row, int64_t nchunks) {
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t orow = c / chunks_per_row, kc = c - orow * chunks_per_row;
+        const uint16_t *src = (orow & 1) ? W2t : W1t;
+        const u32x4 v = gload16(src + ((orow >> 1) * chunks_per_row + kc) * 8);
+        gstore16(Wf + c * 8, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Ablation activation stage: Y = bf16(SiLU(gate) * up), fp32 arithmetic,
 // one rounding.  HBM-bound: 8 elements (three 16-byte accesses) per thread
 // per iteration, grid-stride.
@@ -566,6 +586,16 @@ hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int
     return hipGetLastError();
 }
 
+hipError_t launch_pack_nk(const uint16_t *W1t, const uint16_t *W2t, uint16_t *Wf, int64_t K,
+                          int64_t N, hipStream_t stream) {
+    const int64_t per_row = K / 8, chunks = 2 * N * per_row;
+    const int64_t blocks = (chunks + 255) / 256;
+    const int grid = static_cast<int>(blocks < 65536 ? blocks : 65536);
+    hipLaunchKernelGGL(pack_nk_kernel, dim3(grid), dim3(256), 0, stream, W1t, W2t, Wf, per_row,
+                       chunks);
+    return hipGetLastError();
+}
+
 hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,
                            hipStream_t stream) {
     const int64_t chunks = count / 8;
@@ -780,13 +810,26 @@ hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16
                                   N, K);
 }
 
+// C [M][cols] = bf16(A . B^T) for a K-contiguous operand B of `cols` logical
+// rows: the ablation's GEMMs and the down projection.
+static hipError_t launch_store_gemm(const uint16_t *A, const KMajor &B, uint16_t *C, int M,
+                                    int cols, int K, const GemmWorkspace &ws,
+                                    hipStream_t stream) {
+    const StoreEpilogue epi{C, M, cols};
+    if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, cols, K, epi, ws, stream);
+    if (quad_tiles_faster(M, cols, K, ws))
+        return launch_gemm<ShapeQuad>(A, B, M, cols, K, epi, ws, stream);
+    return launch_gemm<ShapeWide>(A, B, M, cols, K, epi, ws, stream);
+}
+
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
                              int M, int N, int K, const GemmWorkspace &ws, hipStream_t stream) {
-    const KMajor B{Wf, N, 2, phase};
-    const StoreEpilogue epi{C, M, N};
-    if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, N, K, epi, ws, stream);
-    if (quad_tiles_faster(M, N, K, ws)) return launch_gemm<ShapeQuad>(A, B, M, N, K, epi, ws, stream);
-    return launch_gemm<ShapeWide>(A, B, M, N, K, epi, ws, stream);
+    return launch_store_gemm(A, KMajor{Wf, N, 2, phase}, C, M, N, K, ws, stream);
+}
+
+hipError_t launch_down_proj(const uint16_t *H, const uint16_t *W3t, uint16_t *Out, int M, int N,
+                            int D, const GemmWorkspace &ws, hipStream_t stream) {
+    return launch_store_gemm(H, KMajor{W3t, D, 1, 0}, Out, M, D, N, ws, stream);
 }
 
 // One 256x256 fp32 slot per CU: a split schedule has at most one piece per

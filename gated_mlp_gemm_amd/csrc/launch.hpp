@@ -32,6 +32,9 @@ int describe_fused_sequential(int M, int N, char *buf, size_t n);
 
 hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,
                        int64_t N, hipStream_t stream);
+// Linear-layer-layout weights W1t, W2t [N][K] -> packed [2N][K] (row interleave).
+hipError_t launch_pack_nk(const uint16_t *W1t, const uint16_t *W2t, uint16_t *Wf, int64_t K,
+                          int64_t N, hipStream_t stream);
 hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,
                            hipStream_t stream);
 hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
@@ -41,6 +44,9 @@ hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16
 // phase 0: C = A . W1 (Gate columns of W_fused), phase 1: C = A . W2 (Up columns)
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
                              int M, int N, int K, const GemmWorkspace &ws, hipStream_t stream);
+// Out [M][D] = bf16(H [M][N] . W3), W3 given K-contiguous as W3t [D][N].
+hipError_t launch_down_proj(const uint16_t *H, const uint16_t *W3t, uint16_t *Out, int M, int N,
+                            int D, const GemmWorkspace &ws, hipStream_t stream);
 // Largest workgroup count any launcher uses for an M x cols output tile grid.
 int64_t max_tiles(int64_t M, int64_t cols);
 

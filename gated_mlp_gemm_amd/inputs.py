@@ -67,6 +67,23 @@ def make_inputs(M: int, K: int, N: int, seed: int,
     return A, W1, W2
 
 
+def make_mlp_inputs(M: int, K: int, N: int, seed: int):
+    """A, W1, W2 exactly as make_inputs(M, K, N, seed), then the down
+    projection's weight W3 [N, K] drawn next from the same generator:
+    float32 standard normals divided by sqrt(N) (its fan-in), rounded to
+    bf16.  So W3 ~ N(0, 1/N) and every output of the block has the variance
+    of one SwiGLU output (about 0.35)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    A = torch.randn(M, K, dtype=torch.float32, generator=g).to(torch.bfloat16)
+    root_k = math.sqrt(K) if K > 0 else 1.0
+    W1 = (torch.randn(K, N, dtype=torch.float32, generator=g) / root_k).to(torch.bfloat16)
+    W2 = (torch.randn(K, N, dtype=torch.float32, generator=g) / root_k).to(torch.bfloat16)
+    root_n = math.sqrt(N) if N > 0 else 1.0
+    W3 = (torch.randn(N, K, dtype=torch.float32, generator=g) / root_n).to(torch.bfloat16)
+    return A, W1, W2, W3
+
+
 def workload_inputs(w: Workload):
     return make_inputs(w.M, w.K, w.N, w.seed)
 

@@ -62,6 +62,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_workspace_size.argtypes = [I64, I64, I64, I32, ctypes.POINTER(U64)]
     lib.swiglu_describe_launch.argtypes = [I64, I64, I64, I32, U64, ctypes.c_char_p, U64]
     lib.swiglu_silu_mul.argtypes = [P, P, P, I64, P]
+    lib.swiglu_pack_weights_nk.argtypes = [P, P, P, I64, I64, P]
+    lib.swiglu_down_proj.argtypes = [P, P, P, I64, I64, I64, P, U64, P]
+    lib.swiglu_gated_mlp.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, U64, P]
     lib.swiglu_select_variant.argtypes = [I64, I64, I64]
     lib.swiglu_m_switch.argtypes = []
     lib.swiglu_m_switch.restype = I64
@@ -71,7 +74,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_last_error.restype = ctypes.c_char_p
     for name in ("swiglu_pack_weights", "swiglu_fused_gemm", "swiglu_unfused_ablation",
                  "swiglu_silu_mul", "swiglu_select_variant", "swiglu_workspace_size",
-                 "swiglu_describe_launch"):
+                 "swiglu_describe_launch", "swiglu_pack_weights_nk", "swiglu_down_proj",
+                 "swiglu_gated_mlp"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -136,6 +140,23 @@ def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor,
     return W_fused
 
 
+def swiglu_pack_weights_nk(W1t: torch.Tensor, W2t: torch.Tensor,
+                           W_fused: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pack linear-layer-layout weights W1t, W2t [N, K] (W1, W2 transposed)
+    into the same [2N, K] W_fused storage as swiglu_pack_weights."""
+    lib = load_library()
+    N, K = W1t.shape
+    _dev_tensor(W1t, "W1t", (N, K))
+    _dev_tensor(W2t, "W2t", (N, K))
+    if W_fused is None:
+        W_fused = torch.empty((2 * N, K), dtype=torch.bfloat16, device=W1t.device)
+    _dev_tensor(W_fused, "W_fused", (2 * N, K))
+    with torch.cuda.device(W1t.device):
+        _check(lib.swiglu_pack_weights_nk(_ptr(W1t), _ptr(W2t), _ptr(W_fused), K, N,
+                                          _stream(W1t.device)), "swiglu_pack_weights_nk")
+    return W_fused
+
+
 def _ws(workspace: Optional[torch.Tensor]):
     if workspace is None:
         return None, 0
@@ -144,10 +165,23 @@ def _ws(workspace: Optional[torch.Tensor]):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
+# swiglu_describe_launch / swiglu_workspace_size codes beyond the variants
+_CALL_CODES = {"ablation": -1, "down_proj": -2}
+
+
+def _call_code(variant) -> int:
+    if isinstance(variant, str):
+        v = variant.lower()
+        return _CALL_CODES[v] if v in _CALL_CODES else VARIANTS[v]
+    return int(variant)
+
+
 def swiglu_workspace_size(M: int, N: int, K: int, variant="auto") -> int:
-    """Bytes of scratch that let a call split the tail round ('ablation' for the ablation)."""
-    v = -1 if variant == "ablation" else (VARIANTS[variant.lower()]
-                                          if isinstance(variant, str) else int(variant))
+    """Bytes of scratch that let a call split the tail round ('ablation' for the
+    ablation; the down projection and the gated MLP use the ablation's size)."""
+    v = _call_code(variant)
+    if v == -2:
+        v = -1
     out = ctypes.c_uint64(0)
     _check(load_library().swiglu_workspace_size(M, N, K, v, ctypes.byref(out)),
            "swiglu_workspace_size")
@@ -156,9 +190,9 @@ def swiglu_workspace_size(M: int, N: int, K: int, variant="auto") -> int:
 
 def swiglu_describe_launch(M: int, N: int, K: int, variant="auto",
                            workspace_bytes: int = 0) -> str:
-    """The kernels a call would launch ('ablation' for the unfused pipeline)."""
-    v = -1 if variant == "ablation" else (VARIANTS[variant.lower()]
-                                          if isinstance(variant, str) else int(variant))
+    """The kernels a call would launch ('ablation' for the unfused pipeline,
+    'down_proj' for the gated MLP's down projection over (M, N, K))."""
+    v = _call_code(variant)
     buf = ctypes.create_string_buffer(512)
     _check(load_library().swiglu_describe_launch(M, N, K, v, workspace_bytes, buf, len(buf)),
            "swiglu_describe_launch")
@@ -216,6 +250,49 @@ def swiglu_unfused_ablation(A: torch.Tensor, W_fused: torch.Tensor,
                                            _ptr(Y), M, N, K, ws, wsb, _stream(A.device)),
                "swiglu_unfused_ablation")
     return Y, gate_ws, up_ws
+
+
+def swiglu_down_proj(H: torch.Tensor, W3t: torch.Tensor, Out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Out [M, D] = bf16(H . W3) for H [M, N] and W3t = W3^T stored [D, N]."""
+    lib = load_library()
+    M, N = H.shape
+    D = W3t.shape[0]
+    _dev_tensor(H, "H", (M, N))
+    _dev_tensor(W3t, "W3t", (D, N))
+    if Out is None:
+        Out = torch.empty((M, D), dtype=torch.bfloat16, device=H.device)
+    _dev_tensor(Out, "Out", (M, D))
+    with torch.cuda.device(H.device):
+        ws, wsb = _ws(workspace)
+        _check(lib.swiglu_down_proj(_ptr(H), _ptr(W3t), _ptr(Out), M, N, D, ws, wsb,
+                                    _stream(H.device)), "swiglu_down_proj")
+    return Out
+
+
+def swiglu_gated_mlp(A: torch.Tensor, W_fused: torch.Tensor, W3t: torch.Tensor,
+                     H: Optional[torch.Tensor] = None, Out: Optional[torch.Tensor] = None,
+                     variant="auto", workspace: Optional[torch.Tensor] = None
+                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The gated MLP block: H = fused SwiGLU GEMM, Out = bf16(H . W3); returns (Out, H)."""
+    lib = load_library()
+    v = VARIANTS[variant.lower()] if isinstance(variant, str) else int(variant)
+    M, K = A.shape
+    N = W_fused.shape[0] // 2
+    _dev_tensor(A, "A", (M, K))
+    _dev_tensor(W_fused, "W_fused", (2 * N, K))
+    _dev_tensor(W3t, "W3t", (K, N))
+    if H is None:
+        H = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if Out is None:
+        Out = torch.empty((M, K), dtype=torch.bfloat16, device=A.device)
+    _dev_tensor(H, "H", (M, N))
+    _dev_tensor(Out, "Out", (M, K))
+    with torch.cuda.device(A.device):
+        ws, wsb = _ws(workspace)
+        _check(lib.swiglu_gated_mlp(_ptr(A), _ptr(W_fused), _ptr(W3t), _ptr(H), _ptr(Out),
+                                    M, N, K, v, ws, wsb, _stream(A.device)), "swiglu_gated_mlp")
+    return Out, H
 
 
 def swiglu_silu_mul(gate: torch.Tensor, up: torch.Tensor,

@@ -146,9 +146,70 @@ int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused,
                             uint64_t workspace_bytes, void *stream);
 
 /*
+ * Packer for weights in a linear layer's layout (one row per output feature,
+ * as a framework's gate and up projection layers store them): W1t and W2t
+ * are [N][K] row-major, W1t[n][k] = W1[k][n] and W2t[n][k] = W2[k][n].
+ * Writes the same packed W_fused as swiglu_pack_weights [gist.science
+ * technical summary, Method, Kernel-2]: row 2n of the [2N][K] array is row n
+ * of W1t, row 2n+1 is row n of W2t (a row interleave, bit-exact).
+ * W1t, W2t: device, read only; W_fused: 2N*K elements, device, written.
+ * K % 8 == 0 (the row length of all three arrays; N is unrestricted),
+ * K <= 2^21, N <= 2^22, pointers 16-byte aligned, no overlap between the
+ * output and the inputs.  K == 0 or N == 0 is an empty problem.
+ */
+int swiglu_pack_weights_nk(const uint16_t *W1t, const uint16_t *W2t,
+                           uint16_t *W_fused, int64_t K, int64_t N,
+                           void *stream);
+
+/*
+ * The down projection that closes the gated MLP block, Out = bf16(H . W3)
+ * with H [M][N] (the SwiGLU output) and W3 in R^{N x D} (D is the model
+ * width, K of the gated GEMM).  The paper measures the SwiGLU stage as a
+ * share of the whole MLP block's time (paper text, section 1 Introduction,
+ * Figure 1); the block's last GEMM is this one.
+ *
+ * H: [M][N] row-major device; W3t: W3 stored K-contiguous, i.e. the
+ * row-major [D][N] array with W3t[d][n] = W3[n][d] (a linear layer's weight
+ * layout); Out: [M][D] row-major device, written.  fp32 accumulation, one
+ * round-to-nearest-even.  Preconditions: M >= 0, D >= 0, N >= 8; N % 8 == 0
+ * and D % 8 == 0; N <= 2^21, D <= 2^22; pointers 16-byte aligned; Out
+ * overlaps no input.  M == 0 or D == 0: SWIGLU_OK, nothing launched.
+ * workspace / workspace_bytes: as for swiglu_fused_gemm (the same scheduler;
+ * size from swiglu_workspace_size(M, N, D, -1, ...)): with few output tiles
+ * (e.g. a narrow model width at small M) it lets the call split the tiles
+ * along N so that every compute unit works.
+ */
+int swiglu_down_proj(const uint16_t *H, const uint16_t *W3t, uint16_t *Out,
+                     int64_t M, int64_t N, int64_t D, void *workspace,
+                     uint64_t workspace_bytes, void *stream);
+
+/*
+ * The gated MLP block (paper text, section 1 Introduction: Gate = A x W1,
+ * Up = A x W2, Y = SiLU(Gate) (.) Up; Figure 1: the MLP block the SwiGLU
+ * stage is a share of), with its down projection back to the model width K:
+ *     H = swiglu_fused_gemm(A, W_fused, variant)      (bf16, [M][N])
+ *     Out = bf16(H . W3)                               ([M][K])
+ * Two stream-ordered launches (the fused SwiGLU GEMM, then the down
+ * projection); Gate and Up never reach device memory, H does (the down
+ * projection reduces over all N columns of a row, which span many tiles).
+ * A [M][K], W_fused packed [2N][K], W3t [K][N] (W3 in R^{N x K} stored
+ * K-contiguous), H [M][N] (caller-owned, written: the block's intermediate),
+ * Out [M][K]; all device.  Preconditions: those of swiglu_fused_gemm and of
+ * swiglu_down_proj with D = K; H and Out overlap no input and not each other.
+ * M == 0: SWIGLU_OK, nothing launched.  workspace: as for swiglu_fused_gemm,
+ * shared by the two launches (stream order).
+ */
+int swiglu_gated_mlp(const uint16_t *A, const uint16_t *W_fused,
+                     const uint16_t *W3t, uint16_t *H, uint16_t *Out,
+                     int64_t M, int64_t N, int64_t K, int variant,
+                     void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
  * What a call would launch, as text (host only; queries the current device's
  * compute-unit count): for swiglu_fused_gemm with `variant` (AUTO, S, I) or
- * for swiglu_unfused_ablation (-1), given a workspace of `workspace_bytes`
+ * for swiglu_unfused_ablation (-1), for the down projection of
+ * swiglu_gated_mlp over (M, N, K) (-2: an M x K output reducing over N),
+ * given a workspace of `workspace_bytes`
  * (0: none), the kernel names with their tile shapes and schedule, e.g.
  * "gemm_tiles_kernel<128x128x64,PairMulEpilogue> (2240 tiles; 512 workgroups)"
  * (the GEMM kernels are persistent: each workgroup loops over its share of

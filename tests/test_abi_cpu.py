@@ -171,3 +171,69 @@ def test_silu_mul_validation(lib):
     assert F(None, U_, Y_, 8, None) == ERR_NULL
     assert F(G_, U_ + 2, Y_, 8, None) == ERR_ALIGN
     assert F(G_, U_, G_ + 16, 64, None) == ERR_ALIAS
+
+
+def test_pack_nk_validation(lib):
+    P = lib.swiglu_pack_weights_nk
+    assert P(W1_, W2_, WF_, -8, 8, None) == ERR_SHAPE
+    assert P(W1_, W2_, WF_, 12, 8, None) == ERR_SHAPE     # K is every row's length
+    assert P(W1_, W2_, WF_, 1 << 22, 8, None) == ERR_SHAPE
+    assert P(None, None, None, 0, 8, None) == 0           # empty
+    assert P(None, None, None, 8, 0, None) == 0
+    assert P(None, W2_, WF_, 8, 8, None) == ERR_NULL
+    assert P(W1_, W2_ + 8, WF_, 8, 8, None) == ERR_ALIGN
+    assert P(W1_, W2_, W2_ + 64, 8, 8, None) == ERR_ALIAS
+
+
+H_, W3_, O_ = A_ + 0x1_0000_0000, W1_ + 0x1_0000_0000, Y_ + 0x1_0000_0000
+
+
+def test_down_proj_validation(lib):
+    F = lib.swiglu_down_proj
+
+    def call(H=H_, W3=W3_, O=O_, M=256, N=256, D=256, WS=None, WSB=0):
+        return F(H, W3, O, M, N, D, WS, WSB, None)
+
+    assert call(M=-1) == ERR_SHAPE
+    assert call(N=0) == ERR_SHAPE                        # N is the reduction length
+    assert call(N=12) == ERR_SHAPE
+    assert call(D=20) == ERR_SHAPE
+    assert call(N=1 << 22) == ERR_SHAPE
+    assert call(M=0, H=None, W3=None, O=None) == 0      # empty
+    assert call(D=0, H=None, W3=None, O=None) == 0
+    assert call(W3=None) == ERR_NULL
+    assert call(O=O_ + 2) == ERR_ALIGN
+    assert call(O=H_ + 64) == ERR_ALIAS
+    assert call(O=W3_ + 64) == ERR_ALIAS
+    assert call(WS=O_ + 256, WSB=1 << 20) == ERR_ALIAS
+    assert call(WS=WS_ + 16, WSB=1 << 20) == ERR_ALIGN
+
+
+def test_gated_mlp_validation(lib):
+    F = lib.swiglu_gated_mlp
+
+    def call(A=A_, WF=WF_, W3=W3_, H=H_, O=O_, M=256, N=256, K=256, v=2, WS=None, WSB=0):
+        return F(A, WF, W3, H, O, M, N, K, v, WS, WSB, None)
+
+    assert call(v=7) == ERR_UNSUP
+    assert call(K=4) == ERR_SHAPE
+    assert call(N=0) == ERR_SHAPE                        # the down projection reduces over N
+    assert call(N=20) == ERR_SHAPE
+    assert call(M=0, A=None, WF=None, W3=None, H=None, O=None) == 0
+    for name in ("A", "WF", "W3", "H", "O"):
+        assert call(**{name: None}) == ERR_NULL, name
+    assert call(H=H_ + 8) == ERR_ALIGN
+    assert call(H=A_ + 64) == ERR_ALIAS                  # intermediate inside an input
+    assert call(O=W3_ + 64) == ERR_ALIAS
+    assert call(O=H_ + 64) == ERR_ALIAS                  # output overlaps the intermediate
+    assert call(WS=H_ + 256, WSB=1 << 20) == ERR_ALIAS
+    assert call(WS=WS_ + 16, WSB=1 << 20) == ERR_ALIGN
+
+
+def test_describe_down_proj_validation(lib):
+    import ctypes
+    buf = ctypes.create_string_buffer(128)
+    assert lib.swiglu_describe_launch(256, 256, 256, -3, 0, buf, len(buf)) == ERR_UNSUP
+    assert lib.swiglu_describe_launch(256, 4, 256, -2, 0, buf, len(buf)) == ERR_SHAPE
+    assert lib.swiglu_describe_launch(0, 256, 256, -2, 0, buf, len(buf)) == 0
+    assert buf.value == b"nothing (empty problem)"

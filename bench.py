@@ -34,7 +34,6 @@ SWIGLU_TAIL) through each tile shape and tail schedule, one JSON line per
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -61,6 +60,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--no-warm", action="store_true",
+                   help="skip the warm (single cache-resident copy) loop (counter passes)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one device copy of known size (for HBM counter scaling)")
     p.add_argument("--sweep", action="store_true",
@@ -293,12 +294,8 @@ def sweep(args):
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_mlp_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
+    from gated_mlp_gemm_amd.counters import kernel_source_hash as h
+    return h()
 
 
 def traffic_record(variant: str, workload: str):
@@ -408,9 +405,11 @@ def main():
     ams, _ = timed(ablation_step, args.steps, args.warmup)
     per["ablation"] = {"ms": ams, "tflops": flops / (ams * 1e-3) / 1e12}
     # warm (one copy, cache-resident where it fits) for context
-    wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, Wf, Y=outs[0], variant=args.variant,
-                                                  workspace=scratch[args.variant]),
-                   args.steps, args.warmup)
+    wms = None
+    if not args.no_warm:
+        wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, Wf, Y=outs[0], variant=args.variant,
+                                                      workspace=scratch[args.variant]),
+                       args.steps, args.warmup)
     for k, v in per.items():
         print(f"[bench] {k}: {v['ms'] * 1e3:.1f} us, {v['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
@@ -496,8 +495,8 @@ def main():
         "speedup_vs_ablation": round(per["ablation"]["ms"] / ms, 4),
         "per_variant": {k: {"ms": round(v["ms"], 5), "tflops": round(v["tflops"], 2)}
                         for k, v in per.items()},
-        "warm_single_copy": {"ms": round(wms, 5),
-                             "tflops": round(flops / (wms * 1e-3) / 1e12, 2)},
+        "warm_single_copy": None if wms is None else {
+            "ms": round(wms, 5), "tflops": round(flops / (wms * 1e-3) / 1e12, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

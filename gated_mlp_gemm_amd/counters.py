@@ -1,0 +1,137 @@
+"""HBM traffic per call from rocprofv3 counter passes.
+
+    python -m gated_mlp_gemm_amd.counters FETCH_DIR WRITE_DIR \
+        [--workload M=2048,K=1536,N=8960] [--out profiles/traffic.json]
+
+FETCH_DIR and WRITE_DIR hold the CSV output of two rocprofv3 runs of the same
+command, one counter each (rocprofv3 collects what one pass allows):
+
+    rocprofv3 --pmc FETCH_SIZE -f csv -d FETCH_DIR -o bench -- \
+        python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-warm --copy-calibration
+    rocprofv3 --pmc WRITE_SIZE -f csv -d WRITE_DIR -o bench -- (the same)
+
+Both counters report KiB per dispatch.  Each is scaled by what it reads for
+the plain 256 MiB device copy that ``--copy-calibration`` runs last (the copy
+moves exactly 262144 KiB each way), and each path's kernels are summed with
+their launches per call.  The entries record the hash of the kernel sources
+they were taken on; the bench reports a figure only while the sources still
+hash the same.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+from typing import Dict, List
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COPY_KIB = 256 * 1024
+
+# the kernels each bench path launches per call: (substrings every matching
+# kernel name contains, launches per call).  A partly idle last round may add
+# a split_reduce_kernel of the same epilogue, one per GEMM launch.
+PATHS = {
+    "i": [(("gemm_tiles_kernel", "PairMulEpilogue"), 1),
+          (("split_reduce_kernel", "PairMulEpilogue"), 1)],
+    "s": [(("fused_sequential_kernel",), 1)],
+    "ablation": [(("gemm_tiles_kernel", "StoreEpilogue"), 2),
+                 (("split_reduce_kernel", "StoreEpilogue"), 2),
+                 (("silu_mul_kernel",), 1)],
+}
+
+
+def kernel_source_hash() -> str:
+    """Hash of every file under csrc/ (name and bytes), 16 hex digits."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter(directory: str, counter: str) -> Dict[str, List[float]]:
+    """Kernel name -> the counter's values, in dispatch order."""
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                 float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {directory}")
+    out: Dict[str, List[float]] = {}
+    for _, name, value in sorted(rows):
+        out.setdefault(name, []).append(value)
+    return out
+
+
+def copy_scale(values: Dict[str, List[float]]) -> float:
+    """262144 KiB over the reading of the last device-copy dispatch."""
+    copies = [v for name, vs in values.items() if "copyBuffer" in name for v in vs]
+    if not copies:
+        raise SystemExit("no device-copy dispatch found (run the bench with --copy-calibration)")
+    return COPY_KIB / copies[-1]
+
+
+def path_records(fetch: Dict[str, List[float]], write: Dict[str, List[float]],
+                 source_hash: str) -> Dict[str, dict]:
+    fs, ws = copy_scale(fetch), copy_scale(write)
+    recs = {}
+    for path, kernels in PATHS.items():
+        names, launches, f_raw, w_raw = [], [], [], []
+        for parts, per_call in kernels:
+            for name in fetch:
+                if all(p in name for p in parts) and name in write and name not in names:
+                    names.append(name)
+                    launches.append(per_call)
+                    f_raw.append(round(statistics.median(fetch[name]), 1))
+                    w_raw.append(round(statistics.median(write[name]), 1))
+        if not names:
+            continue
+        kib = sum(n * (f * fs + w * ws) for n, f, w in zip(launches, f_raw, w_raw))
+        recs[path] = {
+            "kernel_source_hash": source_hash,
+            "kernels": names,
+            "launches_per_call": launches,
+            "fetch_kib_raw": f_raw,
+            "write_kib_raw": w_raw,
+            "fetch_scale": round(fs, 4),
+            "write_scale": round(ws, 4),
+            "hbm_bytes_per_launch": int(round(kib * 1024)),
+        }
+    return recs
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    p.add_argument("fetch_dir")
+    p.add_argument("write_dir")
+    p.add_argument("--workload", default="M=2048,K=1536,N=8960")
+    p.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    a = p.parse_args(argv)
+    recs = path_records(read_counter(a.fetch_dir, "FETCH_SIZE"),
+                        read_counter(a.write_dir, "WRITE_SIZE"), kernel_source_hash())
+    table = {}
+    if os.path.exists(a.out):
+        with open(a.out) as f:
+            table = json.load(f)
+    for path, rec in recs.items():
+        table[f"{path}|{a.workload}"] = rec
+    with open(a.out, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    for path, rec in recs.items():
+        print(f"{path}: {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per call "
+              f"({', '.join(rec['kernels'])})")
+
+
+if __name__ == "__main__":
+    main()

@@ -87,6 +87,14 @@ class Oracle:
         lib.swo_down_proj.argtypes = [_U16P, _U16P, i64, i64, i64, nf64, _U16P]
         lib.swo_gated_mlp.argtypes = [_U16P, _U16P, _U16P, _U16P, i64, i64,
                                       i64, _U16P, _U16P]
+        _U8P = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+        lib.swo_fp8_to_double.argtypes = [ctypes.c_uint8]
+        lib.swo_fp8_to_double.restype = ctypes.c_double
+        lib.swo_double_to_fp8.argtypes = [ctypes.c_double]
+        lib.swo_double_to_fp8.restype = ctypes.c_uint8
+        lib.swo_quantize_fp8.argtypes = [_U16P, i64, ctypes.c_int, _U8P]
+        lib.swo_swiglu_fp8_rows.argtypes = [_U8P, _U8P, i64, i64, _nullable(_I64P), i64,
+                                            ctypes.c_int, ctypes.c_int, nf64, nu16]
         lib.swo_num_threads.restype = ctypes.c_int
         self._lib = lib
         self.path = path
@@ -211,6 +219,40 @@ class Oracle:
         out = np.empty((M, K), dtype=np.uint16)
         self._lib.swo_gated_mlp(A, W1, W2, W3, M, N, K, h, out)
         return h, out
+
+    # -- FP8 (E4M3) inputs ------------------------------------------------
+    def fp8_to_double(self, code: int) -> float:
+        return self._lib.swo_fp8_to_double(int(code))
+
+    def double_to_fp8(self, x: float) -> int:
+        return int(self._lib.swo_double_to_fp8(float(x)))
+
+    def quantize_fp8(self, x, scale_exp: int):
+        """fp8(x * 2^-scale_exp) codes (uint8) for bf16 patterns x."""
+        x = self._u16(x)
+        q = np.empty(x.shape, dtype=np.uint8)
+        self._lib.swo_quantize_fp8(x.reshape(-1), x.size, int(scale_exp), q.reshape(-1))
+        return q
+
+    def swiglu_fp8(self, A8, WfT8, a_exp: int, w_exp: int, rows=None,
+                   want_f64: bool = False):
+        """Fused SwiGLU on FP8 codes: A8 [M,K] uint8, WfT8 [2N,K] uint8
+        (W_fused stored by columns); all rows, or the listed ones."""
+        A8 = np.ascontiguousarray(A8, dtype=np.uint8)
+        WfT8 = np.ascontiguousarray(WfT8, dtype=np.uint8)
+        M, K = A8.shape
+        assert WfT8.shape[1] == K and WfT8.shape[0] % 2 == 0
+        N = WfT8.shape[0] // 2
+        if rows is None:
+            rws, n = None, M
+        else:
+            rws = np.ascontiguousarray(rows, dtype=np.int64)
+            assert rws.size == 0 or (rws.min() >= 0 and rws.max() < M)
+            n = rws.size
+        y = np.empty((n, N), dtype=np.uint16)
+        y64 = np.empty((n, N), dtype=np.float64) if want_f64 else None
+        self._lib.swo_swiglu_fp8_rows(A8, WfT8, N, K, rws, n, int(a_exp), int(w_exp), y64, y)
+        return (y, y64) if want_f64 else y
 
     def swiglu_materialised(self, A, W1, W2):
         """Unfused pipeline: returns (gate_bf16, up_bf16, y_bf16)."""

@@ -62,7 +62,10 @@
  * pack against numpy slicing; the linear-layer packer against slicing of the
  * transposes; the down projection against numpy float64 matmul, the
  * identity weight and a hand case whose result changes sign if Y is not
- * rounded to bf16 first.  Planted-mistake builds (PLANT_* macros below,
+ * rounded to bf16 first; the FP8 decoder against torch's float8_e4m3fn for
+ * all 256 codes, the FP8 rounding against torch's cast and a brute-force
+ * nearest search, and the FP8 GEMM against the bf16 oracle on inputs exact
+ * in both formats (with and without scales).  Planted-mistake builds (PLANT_* macros below,
  * compiled only by the tests) show that each plausible slip fails a pin.
  */
 #include <math.h>
@@ -423,6 +426,117 @@ void swo_gated_mlp(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
     swo_swiglu_separate(A, W1, W2, M, N, K, NULL, hbf);
     swo_down_proj(hbf, W3, M, N, K, NULL, outbf);
 #endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 inputs (the pages' motivation: quantisation to FP8 makes the GEMMs    */
+/* cheaper, so materialisation costs relatively more [paper s1]).            */
+/*                                                                           */
+/* Format: OCP FP8 E4M3 -- 1 sign bit, 4 exponent bits with bias 7, 3        */
+/* mantissa bits, subnormals at exponent 0 (m/8 * 2^-6), no infinities,      */
+/* S.1111.111 is NaN, largest finite value 448.  Scaling: one power of two   */
+/* per tensor, A ~= 2^a_exp * A8 and W_fused ~= 2^w_exp * W8, so Gate =      */
+/* 2^(a_exp+w_exp) * (A8 . W1_8) and likewise Up.                             */
+/* ------------------------------------------------------------------------ */
+
+#ifdef PLANT_FP8_BIAS8              /* the exponent bias of the FNUZ variant */
+#define FP8_BIAS 8
+#else
+#define FP8_BIAS 7
+#endif
+
+double swo_fp8_to_double(uint8_t q)
+{
+    const int e = (q >> 3) & 15, m = q & 7;
+    double v;
+    if (e == 15 && m == 7) {
+        v = NAN;
+    } else if (e == 0) {
+        v = ldexp((double)m, 1 - FP8_BIAS - 3);        /* (m/8) 2^(1-bias)     */
+    } else {
+        v = ldexp(8.0 + m, e - FP8_BIAS - 3);          /* (1 + m/8) 2^(e-bias) */
+    }
+    return (q & 0x80) ? -v : v;
+}
+
+/*
+ * Round a double to the nearest E4M3 value, ties to even; finite values
+ * beyond the largest (448), and infinities, saturate to +-448; NaN -> 0x7F.
+ * For |x| in [2^e, 2^(e+1)) with e >= -6 the spacing is 2^(e-3); below 2^-6
+ * it stays at the subnormal quantum 2^-9.
+ */
+uint8_t swo_double_to_fp8(double x)
+{
+    if (isnan(x)) return 0x7F;
+    const uint8_t s = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (isinf(a) || a > 448.0) return (uint8_t)(s | 0x7E);
+    if (a == 0.0) return s;
+    int ex;
+    (void)frexp(a, &ex);                      /* a in [2^(ex-1), 2^ex)      */
+    int e = ex - 1;
+    if (e < -6) e = -6;
+    const double q = ldexp(1.0, e - 3);
+    double r = nearbyint(a / q) * q;          /* exact scaling, RNE         */
+    if (r > 448.0) r = 448.0;                 /* 480 is not a finite value  */
+    if (r == 0.0) return s;
+    int er;
+    (void)frexp(r, &er);
+    er -= 1;                                  /* r in [2^er, 2^(er+1))      */
+    if (er < -6) return (uint8_t)(s | (uint8_t)(r / ldexp(1.0, -9)));
+    const int m = (int)(r / ldexp(1.0, er - 3)) - 8;
+    return (uint8_t)(s | (uint8_t)(((er + 7) << 3) | m));
+}
+
+/* q[i] = fp8(x[i] * 2^-scale_exp) for bf16 x (the scaling is exact). */
+void swo_quantize_fp8(const uint16_t *x, int64_t count, int scale_exp,
+                      uint8_t *q)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        q[i] = swo_double_to_fp8(ldexp(swo_bf16_to_double(x[i]), -scale_exp));
+    }
+}
+
+/*
+ * The fused SwiGLU GEMM on FP8 inputs, for a list of rows (rows == NULL:
+ * rows 0..nrows-1): A8 [M][K]; WfT8 is W_fused stored by columns, [2N][K]
+ * (row 2n = Gate column n, row 2n+1 = Up column n [gist: Kernel-2]).
+ *   g = 2^(a_exp+w_exp) sum_k A8[m,k] WfT8[2n,k],  u likewise with 2n+1
+ * (each product of two FP8 values is exact in double; k ascending), then
+ * y = SiLU(g) u and one rounding to bf16.  Outputs by list position.
+ */
+void swo_swiglu_fp8_rows(const uint8_t *A8, const uint8_t *WfT8, int64_t N,
+                         int64_t K, const int64_t *rows, int64_t nrows,
+                         int a_exp, int w_exp, double *y64, uint16_t *ybf)
+{
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = swo_fp8_to_double((uint8_t)c);
+    #pragma omp parallel
+    {
+        double *a = (double *)malloc((size_t)K * sizeof(double));
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t m = rows ? rows[i] : i;
+            for (int64_t k = 0; k < K; ++k) a[k] = table[A8[m * K + k]];
+            for (int64_t n = 0; n < N; ++n) {
+                const uint8_t *wg = WfT8 + (2 * n) * K;
+                const uint8_t *wu = WfT8 + (2 * n + 1) * K;
+                double g = 0.0, u = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    g += a[k] * table[wg[k]];
+                    u += a[k] * table[wu[k]];
+                }
+                g = ldexp(g, a_exp + w_exp);
+#ifndef PLANT_FP8_SCALE_ONCE        /* leaves Up unscaled                  */
+                u = ldexp(u, a_exp + w_exp);
+#endif
+                gate_up_to_y(g, u, y64 ? y64 + i * N + n : NULL,
+                             ybf ? ybf + i * N + n : NULL);
+            }
+        }
+        free(a);
+    }
 }
 
 /* Threads the OpenMP runtime will use for a parallel region. */

@@ -358,6 +358,125 @@ def check_mlp_identity_down(orc):
         assert np.array_equal(out, h)
 
 
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) inputs
+# ---------------------------------------------------------------------------
+def _torch_fp8_values():
+    """All 256 E4M3 codes decoded by torch's own float8_e4m3fn (independent)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+
+
+def _fp8_brute(x: Fraction) -> int:
+    """Nearest finite E4M3 code by exhaustive search (ties: even code), with
+    saturation to +-448; independent of the oracle's rounding."""
+    vals = _torch_fp8_values()
+    neg = x < 0
+    a = -x if neg else x
+    best, best_d = None, None
+    for c in range(0x7F):                       # 0x00..0x7E: the finite non-negative codes
+        d = abs(Fraction(float(vals[c])) - a)
+        if best is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    if a > 448:
+        best = 0x7E
+    return best | (0x80 if neg else 0)
+
+
+def check_fp8_decode_vs_torch(orc):
+    want = _torch_fp8_values()
+    got = np.array([orc.fp8_to_double(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def check_fp8_rounding(orc):
+    vals = _torch_fp8_values()
+    # every finite code round-trips
+    for c in range(256):
+        if not math.isnan(vals[c]):
+            assert orc.double_to_fp8(vals[c]) == c, hex(c)
+    # saturation, NaN, ties to even, subnormal ties
+    cases = [(448.5, 0x7E), (479.99, 0x7E), (1e6, 0x7E), (-1e6, 0xFE), (math.inf, 0x7E),
+             (-math.inf, 0xFE), (1.0625, 0x38), (1.1875, 0x3A), (2.0 ** -10, 0x00),
+             (3 * 2.0 ** -10, 0x02), (-(2.0 ** -10), 0x80), (2.0 ** -6 - 2.0 ** -10, 0x08)]
+    for x, code in cases:
+        assert orc.double_to_fp8(x) == code, (x, hex(code))
+    assert orc.double_to_fp8(math.nan) == 0x7F
+    # torch's float32 -> float8_e4m3fn cast (round to nearest even) inside the range
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(2000) * s for s in (0.01, 1.0, 60.0)])
+    x = x[np.abs(x) < 440].astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.double_to_fp8(float(v)) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def check_fp8_quantize_brute_force(orc):
+    rng = np.random.default_rng(10)
+    for exp in (-6, 0, 3):
+        x = inputs.bits(inputs.random_bf16((160,), 900 + exp, 2.0 ** (exp + 3)))
+        x[:4] = [0x0000, 0x8000, 0x7F80, 0x4480]          # +0, -0, +inf, 1024
+        q = orc.quantize_fp8(x, exp)
+        for xb, qc in zip(x, q):
+            v = bits_to_f64(np.uint16(xb))
+            if math.isinf(v):
+                want = 0x7E if v > 0 else 0xFE
+            elif v == 0:
+                want = 0x80 if math.copysign(1, v) < 0 else 0x00
+            else:
+                want = _fp8_brute(Fraction(float(v)) * Fraction(2) ** (-exp))
+            assert qc == want, (hex(xb), exp, hex(qc), hex(want))
+
+
+def _fp8_exact_case(seed, M, K, N, lo=-8, hi=8):
+    """Integers in [lo, hi]: exact in E4M3 and in bf16."""
+    rng = np.random.default_rng(seed)
+    A = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
+    W1 = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float32) / 16
+    W2 = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float32) / 16
+    return A, W1, W2
+
+
+def check_fp8_gemm_reduces_to_bf16(orc):
+    # inputs exact in both formats: the FP8 GEMM equals the (pinned) bf16 oracle
+    for seed, (M, K, N), (ea, ew) in [(0, (3, 16, 8), (0, 0)), (1, (9, 40, 24), (2, -3)),
+                                      (2, (17, 64, 16), (-1, -4))]:
+        A, W1, W2 = _fp8_exact_case(seed, M, K, N)
+        # the FP8 codes hold the unscaled integers; the bf16 inputs the scaled values
+        A8 = orc.quantize_fp8(to_bits(A), 0)
+        WfT8 = orc.quantize_fp8(np.ascontiguousarray(orc.pack(to_bits(W1), to_bits(W2)).T), 0)
+        ref = orc.swiglu(to_bits(A * 2.0 ** ea), to_bits(W1 * 2.0 ** ew), to_bits(W2 * 2.0 ** ew))
+        got = orc.swiglu_fp8(A8, WfT8, ea, ew)
+        assert np.array_equal(got, ref), (seed, ea, ew)
+
+
+def check_fp8_gemm_vs_numpy(orc):
+    rng = np.random.default_rng(11)
+    vals = _torch_fp8_values()
+    finite = np.flatnonzero(~np.isnan(vals)).astype(np.uint8)
+    for M, K, N, ea, ew in [(4, 16, 8, -6, -8), (13, 48, 24, 0, -5)]:
+        A8 = rng.choice(finite, size=(M, K))
+        WfT8 = rng.choice(finite, size=(2 * N, K))
+        a, w = vals[A8], vals[WfT8]
+        D = a @ w.T * 2.0 ** (ea + ew)
+        G, U = D[:, 0::2], D[:, 1::2]
+        with np.errstate(over="ignore"):           # exp(-G) -> inf gives SiLU -> -0
+            want = G / (1.0 + np.exp(-G)) * U
+        _, y64 = orc.swiglu_fp8(A8, WfT8, ea, ew, want_f64=True)
+        scale = (np.abs(a) @ np.abs(w.T))[:, 0::2] * (np.abs(a) @ np.abs(w.T))[:, 1::2]
+        scale = scale * 2.0 ** (2 * (ea + ew)) + 1e-300
+        with np.errstate(over="ignore"):
+            assert np.all(np.abs(y64 - want) <= 1e-12 * scale + 1e-300)
+    # the row list selects rows of the full result
+    A8 = rng.choice(finite, size=(7, 32))
+    WfT8 = rng.choice(finite, size=(16, 32))
+    full = orc.swiglu_fp8(A8, WfT8, -4, -6)
+    assert np.array_equal(orc.swiglu_fp8(A8, WfT8, -4, -6, rows=[6, 0, 3]), full[[6, 0, 3]])
+
+
 CHECKS = [
     check_rounding_patterns,
     check_rounding_vs_torch,
@@ -372,6 +491,11 @@ CHECKS = [
     check_mlp_hand_cases,
     check_down_proj_vs_numpy,
     check_mlp_identity_down,
+    check_fp8_decode_vs_torch,
+    check_fp8_rounding,
+    check_fp8_quantize_brute_force,
+    check_fp8_gemm_reduces_to_bf16,
+    check_fp8_gemm_vs_numpy,
 ]
 
 
@@ -444,6 +568,8 @@ MUTANTS = [
     "PLANT_PACK_UP_EVEN",
     "PLANT_PACK_NK_UNTRANSPOSED",
     "PLANT_MLP_UNROUNDED_H",
+    "PLANT_FP8_BIAS8",
+    "PLANT_FP8_SCALE_ONCE",
 ]
 
 

@@ -25,6 +25,9 @@ JSON line per (shape, M): the data behind the M threshold of the dispatcher.
 projection back to the model width) against the unfused pipeline followed by
 the same down projection, on the five workloads: one JSON line each.
 
+--fp8 times the fused GEMM (variant I) on FP8 E4M3 operands against the same
+call on bf16, on the five workloads: one JSON line each.
+
 --schedule-calibration times variant I at the same shapes over a finer range
 of M, once with the library's own choice and once forced (SWIGLU_I_TILE,
 SWIGLU_TAIL) through each tile shape and tail schedule, one JSON line per
@@ -44,6 +47,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 METRIC = "fused SwiGLU-GEMM TFLOP/s + % bf16 MFMA peak; speedup vs unfused ablation"
 
 
@@ -71,6 +75,9 @@ def parse():
                    help="time the gated MLP block (SwiGLU + down projection), fused vs "
                         "unfused, on the five workloads")
     p.add_argument("--mlp-workloads", default="0,1,2,3,4")
+    p.add_argument("--fp8", action="store_true",
+                   help="time the fused GEMM on FP8 (E4M3) operands against bf16, five workloads")
+    p.add_argument("--fp8-workloads", default="0,1,2,3,4")
     p.add_argument("--schedule-calibration", action="store_true",
                    help="time variant I under every forced tile shape / tail schedule")
     p.add_argument("--calibration-m",
@@ -252,6 +259,64 @@ def mlp_blocks(args):
         torch.cuda.empty_cache()
 
 
+def fp8_compare(args):
+    """The fused GEMM (variant I) on FP8 E4M3 operands against the same call on
+    bf16, per workload (one JSON line each).  The operands are quantized once,
+    untimed (power-of-two tensor scales from the absolute maxima), like the
+    weight pack; the timed call is the fused GEMM alone."""
+    import torch
+
+    from gated_mlp_gemm_amd import inputs
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    sw.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for idx in (int(x) for x in args.fp8_workloads.split(",")):
+        w = inputs.WORKLOADS[idx]
+        M, K, N = w.M, w.K, w.N
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed)
+        A = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+        W1 = (torch.randn(K, N, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16)
+        W2 = (torch.randn(K, N, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16)
+        Wf = sw.swiglu_pack_weights(W1, W2)
+        del W1, W2
+        a_exp = sw.swiglu_fp8_scale_exp(float(A.float().abs().max()))
+        w_exp = sw.swiglu_fp8_scale_exp(float(Wf.float().abs().max()))
+        A8 = sw.swiglu_quantize_fp8(A, a_exp)
+        W8 = sw.swiglu_quantize_fp8(Wf, w_exp)
+        step16 = 2 * (M * K + 2 * K * N + M * N)
+        R = max(1, -(-512 * 2 ** 20 // step16))
+        bf = [(A, Wf)] + [(A.clone(), Wf.clone()) for _ in range(R - 1)]
+        f8 = [(A8, W8)] + [(A8.clone(), W8.clone()) for _ in range(R - 1)]
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = sw.make_workspace(M, N, K, "i", dev)
+        torch.cuda.synchronize()
+        us16 = _time_call(lambda a, wf: sw.swiglu_fused_gemm(a, wf, Y=Y, variant="auto",
+                                                             workspace=ws),
+                          bf, stream, budget_s=0.25, max_reps=2000)
+        us8 = _time_call(lambda a, wf: sw.swiglu_fused_gemm_fp8(a, wf, a_exp, w_exp, Y=Y,
+                                                                workspace=ws),
+                         f8, stream, budget_s=0.25, max_reps=2000)
+        flops = 4 * M * N * K
+        t8 = flops / (us8 * 1e-6) / 1e12
+        rec = {
+            "workload": f"fused SwiGLU GEMM M={M} K={K} N={N} (seed {w.seed})",
+            "M": M, "K": K, "N": N, "rotation_copies": R, "a_exp": a_exp, "w_exp": w_exp,
+            "us": {"bf16": round(us16, 2), "fp8": round(us8, 2)},
+            "tflops": {"bf16": round(flops / (us16 * 1e-6) / 1e12, 1), "fp8": round(t8, 1)},
+            "fp8_pct_of_fp8_peak": round(100 * t8 / PEAK_FP8_TFLOPS, 2),
+            "fp8_speedup_vs_bf16": round(us16 / us8, 3),
+            "fp8_launch": sw.swiglu_describe_launch(M, N, K, "fp8",
+                                                    0 if ws is None else ws.numel()),
+        }
+        print(json.dumps(rec), flush=True)
+        del bf, f8, A, Wf, A8, W8, ws
+        torch.cuda.empty_cache()
+
+
 def sweep(args):
     """Variant I vs S vs the ablation over M, per K x N shape (one JSON line each)."""
     import torch
@@ -324,6 +389,9 @@ def main():
         return
     if args.mlp:
         mlp_blocks(args)
+        return
+    if args.fp8:
+        fp8_compare(args)
         return
     if args.schedule_calibration:
         schedule_calibration(args)

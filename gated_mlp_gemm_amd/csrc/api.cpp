@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <atomic>
 #include <mutex>
@@ -76,8 +77,10 @@ int check_down_shape(int64_t M, int64_t N, int64_t D) {
     return SWIGLU_OK;
 }
 
-// swiglu_describe_launch's code for the down projection of the gated MLP.
+// swiglu_describe_launch's codes for the down projection of the gated MLP
+// and for the FP8 fused call.
 constexpr int kDescribeDownProj = -2;
+constexpr int kDescribeFp8 = -3;
 
 // Per-device cache: state 1 = gfx950, -1 = other architecture, 0 = not yet
 // queried; and the device's compute-unit count (sizes the split-tail schedule).
@@ -226,7 +229,7 @@ int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
                            uint64_t workspace_bytes, char *buf, uint64_t buf_bytes) {
     if (!buf || buf_bytes == 0) return fail(SWIGLU_ERR_NULL, "buf is required");
     buf[0] = '\0';
-    if (variant < kDescribeDownProj || variant > SWIGLU_VARIANT_I)
+    if (variant < kDescribeFp8 || variant > SWIGLU_VARIANT_I)
         return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
     int st = variant == kDescribeDownProj ? check_down_shape(M, N, K) : check_gemm_shape(M, N, K);
     if (st != SWIGLU_OK) return st;
@@ -242,7 +245,9 @@ int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
         make_ws(workspace_bytes ? reinterpret_cast<void *>(uintptr_t{256}) : nullptr,
                 workspace_bytes, cus);
     const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
-    if (v == kDescribeDownProj) {
+    if (v == kDescribeFp8) {
+        swiglu::describe_gemm_fp8((int)M, (int)(2 * N), (int)K, ws, buf, buf_bytes);
+    } else if (v == kDescribeDownProj) {
         swiglu::describe_gemm((int)M, (int)K, (int)N, ws, "StoreEpilogue", buf, buf_bytes);
     } else if (v == SWIGLU_VARIANT_S) {
         swiglu::describe_fused_sequential((int)M, (int)N, buf, buf_bytes);
@@ -444,4 +449,63 @@ int swiglu_gated_mlp(const uint16_t *A, const uint16_t *W_fused, const uint16_t 
                     "gated MLP: down projection");
 }
 
-}  // extern "C\"
+int swiglu_fp8_scale_exp(double amax) {
+    if (!(amax > 0.0) || amax > 3.5e38) return 0;   // zero, negative, NaN or beyond float
+    int e = -126;
+    while (e < 126 && std::ldexp(amax, -e) > 448.0) ++e;   // smallest e: amax 2^-e <= 448
+    return e;
+}
+
+int swiglu_quantize_fp8(const uint16_t *X, uint8_t *Q, int64_t count, int scale_exp,
+                        void *stream) {
+    if (count < 0 || count % 16 != 0)
+        return fail(SWIGLU_ERR_SHAPE, "count=%lld must be a non-negative multiple of 16",
+                    (long long)count);
+    if (scale_exp < -126 || scale_exp > 126)
+        return fail(SWIGLU_ERR_SHAPE, "scale_exp=%d outside [-126, 126]", scale_exp);
+    if (count == 0) return ok();
+    if (!X || !Q) return fail(SWIGLU_ERR_NULL, "X and Q are required");
+    if (!aligned16(X) || !aligned16(Q))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    if (overlap(Q, count, X, 2 * count)) return fail(SWIGLU_ERR_ALIAS, "Q overlaps X");
+    int st = check_device();
+    if (st != SWIGLU_OK) return st;
+    return launched(swiglu::launch_quantize_fp8(X, Q, count, scale_exp, (hipStream_t)stream),
+                    "quantize_fp8");
+}
+
+int swiglu_fused_gemm_fp8(const uint8_t *A8, const uint8_t *W_fused8, uint16_t *Y, int64_t M,
+                          int64_t N, int64_t K, int a_exp, int w_exp, void *workspace,
+                          uint64_t workspace_bytes, void *stream) {
+    int st = check_gemm_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    if (K % 16 != 0) return fail(SWIGLU_ERR_SHAPE, "K=%lld must be a multiple of 16", (long long)K);
+    if (a_exp < -126 || a_exp > 126 || w_exp < -126 || w_exp > 126 || a_exp + w_exp < -126 ||
+        a_exp + w_exp > 126)
+        return fail(SWIGLU_ERR_SHAPE, "scale exponents out of range (a_exp + w_exp in [-126, 126])");
+    if (M == 0 || N == 0) return ok();
+    if (!A8 || !W_fused8 || !Y) return fail(SWIGLU_ERR_NULL, "A8, W_fused8 and Y are required");
+    if (!aligned16(A8) || !aligned16(W_fused8) || !aligned16(Y))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t abytes = M * K, ybytes = M * N * 2, wbytes = 2 * K * N;
+    if (overlap(Y, ybytes, A8, abytes) || overlap(Y, ybytes, W_fused8, wbytes))
+        return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
+    st = check_workspace(workspace, workspace_bytes);
+    if (st != SWIGLU_OK) return st;
+    if (workspace && workspace_bytes > 0 &&
+        (overlap(workspace, (int64_t)workspace_bytes, A8, abytes) ||
+         overlap(workspace, (int64_t)workspace_bytes, W_fused8, wbytes) ||
+         overlap(workspace, (int64_t)workspace_bytes, Y, ybytes)))
+        return fail(SWIGLU_ERR_ALIAS, "workspace overlaps an operand");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != SWIGLU_OK) return st;
+    const float scale = std::ldexp(1.0f, a_exp + w_exp);
+    return launched(swiglu::launch_fused_interleaved_fp8(A8, W_fused8, Y, (int)M, (int)N, (int)K,
+                                                         scale,
+                                                         make_ws(workspace, workspace_bytes, cus),
+                                                         (hipStream_t)stream),
+                    "fused interleaved fp8");
+}
+
+}  // extern "C"

@@ -29,6 +29,20 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// FP8 E4M3 x FP8 E4M3 -> fp32, 32x32 outputs, 64 k (v_mfma_f32_32x32x64_f8f6f4;
+// format code 0 = E4M3 for both operands, no block scales).  Each operand is
+// 32 bytes per lane, given as two 16-byte chunks (low chunk first).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(const u32x4 &a0, const u32x4 &a1,
+                                                    const u32x4 &b0, const u32x4 &b1,
+                                                    const f32x16 &c) {
+    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                     (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // 16-byte LDS read (ds_read_b128).
 __device__ __forceinline__ u32x4 lds_read16(const SWIGLU_LDS char *p) {
     return *reinterpret_cast<const SWIGLU_LDS u32x4 *>(p);

@@ -40,19 +40,27 @@
 
 namespace swiglu {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+// EB is the operand element size in bytes: 2 for bf16 (v_mfma_f32_32x32x16_bf16,
+// 16 k per MFMA, one 16-byte chunk per lane and operand), 1 for FP8 E4M3
+// (v_mfma_f32_32x32x64_f8f6f4, 64 k per MFMA, two chunks per lane).  A K step
+// of BK elements moves BK * EB bytes per tile row either way.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int EB_ = 2>
 struct TileShape {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int STAGES = STAGES_;
+    static constexpr int EB = EB_;
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kWaveM = BM / WM;
     static constexpr int kWaveN = BN / WN;
     static constexpr int TM = kWaveM / 32;          // 32x32 MFMA blocks per wave (M)
     static constexpr int TN = kWaveN / 32;          // 32x32 MFMA blocks per wave (N)
-    static constexpr int kKSub = BK / 16;           // MFMA k-substeps per K step
-    static constexpr int kChunksPerRow = BK / 8;    // 16-byte chunks per tile row
-    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kMfmaK = EB == 2 ? 16 : 64;   // k per MFMA
+    static constexpr int kKSub = BK / kMfmaK;       // MFMA k-substeps per K step
+    static constexpr int kFragChunks = kMfmaK * EB / 32;   // 16-byte chunks per lane and operand
+    static constexpr int kElemsPerChunk = 16 / EB;
+    static constexpr int kChunksPerRow = BK * EB / 16;   // 16-byte chunks per tile row
+    static constexpr int kRowBytes = BK * EB;
     static constexpr int kABytes = BM * kRowBytes;
     static constexpr int kBBytes = BN * kRowBytes;
     static constexpr int kStageBytes = kABytes + kBBytes;
@@ -68,7 +76,9 @@ struct TileShape {
     static constexpr int kOccupancy = (2 * kLdsBytes <= 160 * 1024) ? 2 : 1;
 
     static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(EB == 2 || EB == 1, "bf16 or FP8 operands");
+    static_assert(EB == 2 ? (BK == 32 || BK == 64) : BK == 128,
+                  "BK: 32 or 64 bf16 elements, or 128 FP8 elements");
     static_assert(kABytes % (kThreads * 16) == 0 && kDmaA >= 1, "A tile must split evenly");
     static_assert(kBBytes % (kThreads * 16) == 0 && kDmaB >= 1, "B tile must split evenly");
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup is 160 KiB");
@@ -127,7 +137,7 @@ __device__ __forceinline__ void block_barrier() {
 // a row-major [rows*stride][K] matrix.  (stride 2 selects the Gate (offset 0)
 // or Up (offset 1) columns of the interleaved packed weight.)
 struct KMajor {
-    const uint16_t *base;
+    const void *base;   // elements of the tile shape's size (bf16 or FP8)
     int rows;        // logical rows
     int stride;
     int offset;
@@ -159,8 +169,8 @@ struct PanelLoader {
     __device__ __forceinline__ void init(const KMajor &op, int r0, int K) {
         const int64_t phys0 = static_cast<int64_t>(r0) * op.stride + op.offset;
         const int64_t phys_end = static_cast<int64_t>(op.rows) * op.stride;  // past the matrix
-        const uint16_t *panel = op.base + phys0 * K;
-        int64_t bytes = (phys_end - phys0) * K * 2;
+        const char *panel = static_cast<const char *>(op.base) + phys0 * K * S::EB;
+        int64_t bytes = (phys_end - phys0) * K * S::EB;
         if (bytes < 0) bytes = 0;
         if (bytes > 0x7FFFFFF0LL) bytes = 0x7FFFFFF0LL;
         rsrc = make_rsrc(panel, static_cast<uint32_t>(bytes));
@@ -174,8 +184,8 @@ struct PanelLoader {
             const int row = p / S::kChunksPerRow;             // LDS row
             const int c = (p % S::kChunksPerRow) ^ swz<S>(row);
             const int grow = op.pairs ? pair_row(row) : row;  // panel row it holds
-            voff[j] = static_cast<uint32_t>(grow * op.stride) * K * 2u + c * 16u;
-            kcol[j] = c * 8;
+            voff[j] = static_cast<uint32_t>(grow * op.stride) * K * S::EB + c * 16u;
+            kcol[j] = c * S::kElemsPerChunk;
             lds_off[j] = block * 1024;
         }
     }
@@ -186,7 +196,7 @@ struct PanelLoader {
     // (No test on the step as a whole: a uniform condition would be turned
     // back into a branch.  k0 <= K + BK keeps kOutOfRange + 2 k0 below 2^32.)
     __device__ __forceinline__ void issue(int k0, int K, SWIGLU_LDS char *panel_lds) const {
-        const uint32_t soff = static_cast<uint32_t>(k0) * 2u;
+        const uint32_t soff = static_cast<uint32_t>(k0) * S::EB;
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) {
             const uint32_t v = (k0 + kcol[j] < K) ? voff[j] : kOutOfRange;
@@ -222,11 +232,12 @@ struct TileLoader {
     }
 };
 
-// Fragment registers of one k-substep: raw 16-byte MFMA operands.
+// Fragment registers of one k-substep: raw MFMA operands, kFragChunks
+// 16-byte chunks per block.
 template <class S>
 struct Frags {
-    u32x4 a[S::TM];
-    u32x4 b[S::TN];
+    u32x4 a[S::TM][S::kFragChunks];
+    u32x4 b[S::TN][S::kFragChunks];
 };
 
 // LDS reads issued as inline assembly.  The compiler neither tracks their
@@ -242,38 +253,46 @@ __device__ __forceinline__ u32x4 asm_read_b128(uint32_t addr) {
 }
 
 // Per-lane LDS byte offsets of the fragment reads, relative to a stage base,
-// one per k-substep for each operand (the swizzle mixes the substep into the
-// address); 32-row blocks tm / tn are +32 rows (the swizzle has period 32).
+// one per k-substep and 16-byte chunk for each operand (the swizzle mixes the
+// chunk index into the address); 32-row blocks tm / tn are +32 rows (the
+// swizzle has period 32).  Lane l (half h = l / 32) takes the kFragChunks
+// consecutive chunks starting at chunk kFragChunks * (2 KS + h) of its row:
+// for bf16 the 8 k of its MFMA operand; for FP8 32 consecutive k.  The same
+// lane-to-k assignment serves both operands, so whatever order the FP8 MFMA
+// gives those k within a lane, the products pair A and B at equal k.
 template <class S>
 struct FragOffsets {
-    uint32_t a[S::kKSub];
-    uint32_t b[S::kKSub];
+    uint32_t a[S::kKSub][S::kFragChunks];
+    uint32_t b[S::kKSub][S::kFragChunks];
 
     __device__ __forceinline__ void init(int wm, int wn, int lane) {
         const int h = lane >> 5;
         const int ra = wm * S::kWaveM + (lane & 31);
         const int rb = wn * S::kWaveN + (lane & 31);
 #pragma unroll
-        for (int ks = 0; ks < S::kKSub; ++ks) {
-            a[ks] = static_cast<uint32_t>(ra * S::kRowBytes + (((ks * 2 + h) ^ swz<S>(ra)) * 16));
-            b[ks] = static_cast<uint32_t>(S::kABytes + rb * S::kRowBytes +
-                                          (((ks * 2 + h) ^ swz<S>(rb)) * 16));
-        }
+        for (int ks = 0; ks < S::kKSub; ++ks)
+#pragma unroll
+            for (int j = 0; j < S::kFragChunks; ++j) {
+                const int c = (ks * 2 + h) * S::kFragChunks + j;
+                a[ks][j] = static_cast<uint32_t>(ra * S::kRowBytes + ((c ^ swz<S>(ra)) * 16));
+                b[ks][j] = static_cast<uint32_t>(S::kABytes + rb * S::kRowBytes +
+                                                 ((c ^ swz<S>(rb)) * 16));
+            }
     }
 };
 
 template <class S, int I>
-__device__ __forceinline__ void read_a_blocks(uint32_t p, Frags<S> &f) {
+__device__ __forceinline__ void read_a_blocks(uint32_t p, Frags<S> &f, int j) {
     if constexpr (I < S::TM) {
-        f.a[I] = asm_read_b128<I * 32 * S::kRowBytes>(p);
-        read_a_blocks<S, I + 1>(p, f);
+        f.a[I][j] = asm_read_b128<I * 32 * S::kRowBytes>(p);
+        read_a_blocks<S, I + 1>(p, f, j);
     }
 }
 template <class S, int I>
-__device__ __forceinline__ void read_b_blocks(uint32_t p, Frags<S> &f) {
+__device__ __forceinline__ void read_b_blocks(uint32_t p, Frags<S> &f, int j) {
     if constexpr (I < S::TN) {
-        f.b[I] = asm_read_b128<I * 32 * S::kRowBytes>(p);
-        read_b_blocks<S, I + 1>(p, f);
+        f.b[I][j] = asm_read_b128<I * 32 * S::kRowBytes>(p);
+        read_b_blocks<S, I + 1>(p, f, j);
     }
 }
 
@@ -281,8 +300,11 @@ __device__ __forceinline__ void read_b_blocks(uint32_t p, Frags<S> &f) {
 template <class S, int KS>
 __device__ __forceinline__ void read_frags(uint32_t stage, const FragOffsets<S> &o,
                                            Frags<S> &f) {
-    read_a_blocks<S, 0>(stage + o.a[KS], f);
-    read_b_blocks<S, 0>(stage + o.b[KS], f);
+#pragma unroll
+    for (int j = 0; j < S::kFragChunks; ++j) {
+        read_a_blocks<S, 0>(stage + o.a[KS][j], f, j);
+        read_b_blocks<S, 0>(stage + o.b[KS][j], f, j);
+    }
 }
 
 // Wait until every fragment read issued so far has landed, and make the
@@ -293,9 +315,12 @@ template <class S>
 __device__ __forceinline__ void wait_frags(Frags<S> &f) {
     asm volatile("s_waitcnt lgkmcnt(0)");
 #pragma unroll
-    for (int tm = 0; tm < S::TM; ++tm) asm volatile("" : "+v"(f.a[tm]));
+    for (int j = 0; j < S::kFragChunks; ++j) {
 #pragma unroll
-    for (int tn = 0; tn < S::TN; ++tn) asm volatile("" : "+v"(f.b[tn]));
+        for (int tm = 0; tm < S::TM; ++tm) asm volatile("" : "+v"(f.a[tm][j]));
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn) asm volatile("" : "+v"(f.b[tn][j]));
+    }
 }
 
 template <class S>
@@ -303,9 +328,14 @@ __device__ __forceinline__ void mma(const Frags<S> &f, f32x16 (&acc)[S::TM][S::T
 #pragma unroll
     for (int tm = 0; tm < S::TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn)
-            acc[tm][tn] = mfma_32x32x16(__builtin_bit_cast(bf16x8, f.a[tm]),
-                                        __builtin_bit_cast(bf16x8, f.b[tn]), acc[tm][tn]);
+        for (int tn = 0; tn < S::TN; ++tn) {
+            if constexpr (S::EB == 2)
+                acc[tm][tn] = mfma_32x32x16(__builtin_bit_cast(bf16x8, f.a[tm][0]),
+                                            __builtin_bit_cast(bf16x8, f.b[tn][0]), acc[tm][tn]);
+            else
+                acc[tm][tn] = mfma_32x32x64_fp8(f.a[tm][0], f.a[tm][1], f.b[tn][0], f.b[tn][1],
+                                                acc[tm][tn]);
+        }
 }
 
 template <class S>

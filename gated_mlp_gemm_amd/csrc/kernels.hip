@@ -109,6 +109,52 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t *__restric
 }
 
 // ---------------------------------------------------------------------------
+// FP8 quantizer: q = E4M3(x * 2^-scale_exp) for bf16 x, round to nearest even,
+// finite values beyond 448 (and infinities) saturated to +-448, NaN -> 0x7F.
+// The scaling is exact in fp32 (a power of two); values below 2^-6 round on
+// the subnormal grid of spacing 2^-9.  16 values (32 bytes in, 16 out) per
+// thread per iteration, grid-stride.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fp8_e4m3_rne_sat(float v) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = __builtin_fabsf(v);
+    if (a != a) return 0x7Fu;                                   // NaN
+    if (a >= 464.0f) return sign | 0x7Eu;                       // rounds past 448: saturate
+    if (a < 0.015625f) {                                        // below 2^-6: multiples of 2^-9
+        const uint32_t m = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // 0..8, exact
+        return sign | m;                                        // m = 8 is 2^-6 (code 0x08)
+    }
+    // normal: keep 3 of the 23 fraction bits, round to nearest even on the rest
+    const uint32_t ab = bits & 0x7FFFFFFFu;
+    const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);
+    const uint32_t e = (r >> 23) - 127u + 7u;                   // 1..15 (a < 464)
+    const uint32_t code = (e << 3) | ((r >> 20) & 7u);
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t *__restrict__ x,
+                                                           uint8_t *__restrict__ q,
+                                                           float inv_scale, int64_t nchunks) {
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const u32x4 lo = gload16(x + c * 16);
+        const u32x4 hi = gload16(x + c * 16 + 8);
+        u32x4 out;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const u32x4 &src = d < 2 ? lo : hi;
+            const uint32_t w0 = src[(d & 1) * 2], w1 = src[(d & 1) * 2 + 1];
+            out[d] = fp8_e4m3_rne_sat(bf16_lo(w0) * inv_scale) |
+                     (fp8_e4m3_rne_sat(bf16_hi(w0) * inv_scale) << 8) |
+                     (fp8_e4m3_rne_sat(bf16_lo(w1) * inv_scale) << 16) |
+                     (fp8_e4m3_rne_sat(bf16_hi(w1) * inv_scale) << 24);
+        }
+        *reinterpret_cast<u32x4 *>(q + c * 16) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Accumulator geometry: row of register i of 32x32 block (tm) for this lane.
 // ---------------------------------------------------------------------------
 template <class S>
@@ -159,9 +205,18 @@ __device__ __forceinline__ void store_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t 
 // Up values), the odd lane registers 8..15 (it receives Gate values), one DPP
 // lane swap per output.
 // ---------------------------------------------------------------------------
-struct PairMulEpilogue {
+// kScaled: the accumulators hold D / scale (FP8 operands with power-of-two
+// tensor scales), so Gate and Up are scale * D before the activation.
+template <bool kScaled>
+struct PairMulEpilogueT {
     uint16_t *Y;
     int M, N;
+    float scale;   // used only when kScaled
+
+    __device__ __forceinline__ float scaled(float x) const {
+        if constexpr (kScaled) return x * scale;
+        else return x;
+    }
 
     template <class S>
     static constexpr bool paired() { return S::TN % 2 == 0; }
@@ -193,8 +248,10 @@ struct PairMulEpilogue {
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
                 // registers i, i+1 are rows 8(i/4) + (i%4) and the next one
-                const float g0 = acc_value<kFromAcc>(g[i]), g1 = acc_value<kFromAcc>(g[i + 1]);
-                const float u0 = acc_value<kFromAcc>(up[i]), u1 = acc_value<kFromAcc>(up[i + 1]);
+                const float g0 = scaled(acc_value<kFromAcc>(g[i]));
+                const float g1 = scaled(acc_value<kFromAcc>(g[i + 1]));
+                const float u0 = scaled(acc_value<kFromAcc>(up[i]));
+                const float u1 = scaled(acc_value<kFromAcc>(up[i + 1]));
                 const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
                 const uint32_t roff =
                     static_cast<uint32_t>(acc_row<S>(0, 0, i, 0)) * static_cast<uint32_t>(N) * 2u;
@@ -216,8 +273,8 @@ struct PairMulEpilogue {
             for (int p = 0; p < 8; ++p) {
                 const float lo = a0[p], hi = a0[8 + p];
                 const float recv = swap_adjacent_lanes(by_lane_parity(hi, lo));
-                const float gate = by_lane_parity(lo, recv);
-                const float upv = by_lane_parity(recv, hi);
+                const float gate = scaled(by_lane_parity(lo, recv));
+                const float upv = scaled(by_lane_parity(recv, hi));
                 const uint32_t roff = static_cast<uint32_t>(acc_row<S>(0, tm, p, 0)) *
                                       static_cast<uint32_t>(N) * 2u;
                 store_b16(r, voff + roff, to_bf16(silu(gate) * upv));
@@ -251,6 +308,9 @@ struct PairMulEpilogue {
             return u;
     }
 };
+
+using PairMulEpilogue = PairMulEpilogueT<false>;
+using PairMulEpilogueFp8 = PairMulEpilogueT<true>;
 
 // Ablation GEMM epilogue: C = bf16(acc), so that Gate and Up are materialised
 // as an eager pipeline does [paper s1].
@@ -308,7 +368,7 @@ struct StoreEpilogue {
 
 // K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
 template <class S>
-__device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const uint16_t *A,
+__device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const void *A,
                                               const KMajor &B, int M, int K, int m0, int n0,
                                               int kb, int ke, int nk,
                                               f32x16 (&acc)[S::TM][S::TN]) {
@@ -334,9 +394,9 @@ constexpr bool kQuarterable =
 
 template <class S>
 struct QuarterOf {
-    static constexpr int kStage = (S::BM / 2 + S::BN / 2) * S::BK * 2;
+    static constexpr int kStage = (S::BM / 2 + S::BN / 2) * S::kRowBytes;
     static constexpr int kStages = S::kLdsBytes / kStage < 4 ? S::kLdsBytes / kStage : 4;
-    using type = TileShape<S::BM / 2, S::BN / 2, S::BK, 2, 2, kStages>;
+    using type = TileShape<S::BM / 2, S::BN / 2, S::BK, 2, 2, kStages, S::EB>;
 };
 
 enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2 };
@@ -354,7 +414,7 @@ enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2 };
 //    half q % 2) of tile dp + q / 4, run whole as a quarter-size tile.
 template <class S, class Epi, int TAIL>
 __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
-    const uint16_t *__restrict__ A, KMajor B, int M, int K, Epi epi, Schedule sch) {
+    const void *__restrict__ A, KMajor B, int M, int K, Epi epi, Schedule sch) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
     const int b = blockIdx.x;
@@ -567,6 +627,12 @@ using ShapeSeq = TileShape<128, 128, 64, 2, 2, 2>;
 // 128x64x32 x 4 stages: 21 % faster at M=128 K=896 N=4864, 24-29 % on K =
 // 5120..8192 (up to 4.2 TB/s of weights).
 using ShapeSmall = TileShape<128, 64, 64, 2, 2, 4>;
+// Variant I on FP8 operands: the same three shapes with K steps of 128 FP8
+// values, so every tile row of a stage is 128 bytes and the LDS rings, load
+// counts and swizzles are those of the bf16 shapes.
+using ShapeWide8 = TileShape<256, 256, 128, 2, 2, 2, 1>;
+using ShapeQuad8 = TileShape<128, 128, 128, 2, 2, 2, 1>;
+using ShapeSmall8 = TileShape<128, 64, 128, 2, 2, 4, 1>;
 
 static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
@@ -596,6 +662,17 @@ hipError_t launch_pack_nk(const uint16_t *W1t, const uint16_t *W2t, uint16_t *Wf
     return hipGetLastError();
 }
 
+hipError_t launch_quantize_fp8(const uint16_t *x, uint8_t *q, int64_t count, int scale_exp,
+                               hipStream_t stream) {
+    const int64_t chunks = count / 16;
+    const int64_t blocks = (chunks + 255) / 256;
+    const int grid = static_cast<int>(blocks < 65536 ? blocks : 65536);
+    const float inv_scale = std::ldexp(1.0f, -scale_exp);
+    hipLaunchKernelGGL(quantize_fp8_kernel, dim3(grid), dim3(256), 0, stream, x, q, inv_scale,
+                       chunks);
+    return hipGetLastError();
+}
+
 hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,
                            hipStream_t stream) {
     const int64_t chunks = count / 8;
@@ -620,11 +697,14 @@ constexpr double kPartialBytesPerUs = 6.4e6;
 // One K step of a round of S tiles: 1.69 for 256x256x64 (one per CU), 1.03
 // for 128x128x64 (two per CU, so twice the tiles per round); other shapes
 // scaled from the first by tile volume and workgroups per CU.
+// (Per K step of 128-byte tile rows: an FP8 step of 128 k takes the MFMA
+// cycles and the load bytes of a bf16 step of 64 k.)
 template <class S>
 constexpr double step_us() {
-    if (S::BM == 256 && S::BN == 256 && S::BK == 64 && S::kOccupancy == 1) return 1.69;
-    if (S::BM == 128 && S::BN == 128 && S::BK == 64 && S::kOccupancy == 2) return 1.03;
-    return 1.69 * (static_cast<double>(S::BM) * S::BN * S::BK) / (256.0 * 256.0 * 64.0) *
+    constexpr int kRow = S::kRowBytes;
+    if (S::BM == 256 && S::BN == 256 && kRow == 128 && S::kOccupancy == 1) return 1.69;
+    if (S::BM == 128 && S::BN == 128 && kRow == 128 && S::kOccupancy == 2) return 1.03;
+    return 1.69 * (static_cast<double>(S::BM) * S::BN * kRow) / (256.0 * 256.0 * 128.0) *
            S::kOccupancy;
 }
 
@@ -632,7 +712,7 @@ constexpr double step_us() {
 // 0.59 for the 128x128 quarters of 256x256x64.
 template <class S>
 constexpr double quarter_step_us() {
-    return 0.59 * (static_cast<double>(S::BM) * S::BN * S::BK) / (256.0 * 256.0 * 64.0);
+    return 0.59 * (static_cast<double>(S::BM) * S::BN * S::kRowBytes) / (256.0 * 256.0 * 128.0);
 }
 
 // Work schedule for a single-accumulator GEMM over an M x cols output (see
@@ -705,7 +785,7 @@ static int launch_grid(const Schedule &sch, int cus) {
 }
 
 template <class S, class Epi>
-static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int K, Epi epi,
+static hipError_t launch_gemm(const void *A, KMajor B, int M, int cols, int K, Epi epi,
                               const GemmWorkspace &ws, hipStream_t stream) {
     Schedule sch = make_schedule<S>(M, cols, K, ws);
     sch.grid = launch_grid<S>(sch, ws.cus);
@@ -739,13 +819,14 @@ static hipError_t launch_gemm(const uint16_t *A, KMajor B, int M, int cols, int 
 // Tile choice for an M x cols single-accumulator GEMM above M = 128: the
 // 128x128 two-per-CU tiles when the cost model predicts their schedule
 // faster than the 256x256 tiles' (each with its own best tail).
+template <class Wide = ShapeWide, class Quad = ShapeQuad>
 static bool quad_tiles_faster(int M, int cols, int K, const GemmWorkspace &ws) {
     if (ws.tile == 256) return false;
     if (ws.tile == 128) return true;
     if (ws.cus <= 0) return false;
     double wide = 0.0, quad = 0.0;
-    make_schedule<ShapeWide>(M, cols, K, ws, &wide);
-    make_schedule<ShapeQuad>(M, cols, K, ws, &quad);
+    make_schedule<Wide>(M, cols, K, ws, &wide);
+    make_schedule<Quad>(M, cols, K, ws, &quad);
     return quad < wide;
 }
 
@@ -799,6 +880,32 @@ int describe_fused_sequential(int M, int N, char *buf, size_t n) {
     const int bk = small ? ShapeSmall::BK : ShapeSeq::BK;
     return std::snprintf(buf, n, "fused_sequential_kernel<%dx%dx%d> (%lld tiles)", bm, bn, bk,
                          static_cast<long long>(cdiv(M, bm)) * cdiv(N, bn));
+}
+
+// Variant I on FP8 operands: the same GEMM over W_fused with K steps of 128
+// FP8 values (128-byte tile rows, as bf16's 64), the f8f6f4 MFMA, and the
+// paired epilogue scaling Gate and Up by 2^(a_exp + w_exp) before SiLU.
+hipError_t launch_fused_interleaved_fp8(const uint8_t *A8, const uint8_t *Wf8, uint16_t *Y,
+                                        int M, int N, int K, float scale,
+                                        const GemmWorkspace &ws, hipStream_t stream) {
+    const KMajor B{Wf8, 2 * N, 1, 0};
+    const PairMulEpilogueFp8 epi{Y, M, N, scale};
+    if (M <= 128) return launch_gemm<ShapeSmall8>(A8, B, M, 2 * N, K, epi, ws, stream);
+    if (quad_tiles_faster<ShapeWide8, ShapeQuad8>(M, 2 * N, K, ws))
+        return launch_gemm<ShapeQuad8>(A8, B, M, 2 * N, K, epi, ws, stream);
+    return launch_gemm<ShapeWide8>(A8, B, M, 2 * N, K, epi, ws, stream);
+}
+
+int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf, size_t n) {
+    const char *epi = "PairMulEpilogueFp8";
+    if (M <= 128)
+        return describe<ShapeSmall8>("gemm_tiles_kernel", epi,
+                                     make_schedule<ShapeSmall8>(M, cols, K, ws), ws.cus, buf, n);
+    if (quad_tiles_faster<ShapeWide8, ShapeQuad8>(M, cols, K, ws))
+        return describe<ShapeQuad8>("gemm_tiles_kernel", epi,
+                                    make_schedule<ShapeQuad8>(M, cols, K, ws), ws.cus, buf, n);
+    return describe<ShapeWide8>("gemm_tiles_kernel", epi,
+                                make_schedule<ShapeWide8>(M, cols, K, ws), ws.cus, buf, n);
 }
 
 hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,

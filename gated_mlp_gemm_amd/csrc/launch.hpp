@@ -47,6 +47,14 @@ hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, u
 // Out [M][D] = bf16(H [M][N] . W3), W3 given K-contiguous as W3t [D][N].
 hipError_t launch_down_proj(const uint16_t *H, const uint16_t *W3t, uint16_t *Out, int M, int N,
                             int D, const GemmWorkspace &ws, hipStream_t stream);
+// FP8 (E4M3) path: q = fp8(x * 2^-scale_exp); variant I on FP8 operands with
+// the epilogue scaling Gate and Up by `scale` (= 2^(a_exp + w_exp)).
+hipError_t launch_quantize_fp8(const uint16_t *x, uint8_t *q, int64_t count, int scale_exp,
+                               hipStream_t stream);
+hipError_t launch_fused_interleaved_fp8(const uint8_t *A8, const uint8_t *Wf8, uint16_t *Y,
+                                        int M, int N, int K, float scale,
+                                        const GemmWorkspace &ws, hipStream_t stream);
+int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf, size_t n);
 // Largest workgroup count any launcher uses for an M x cols output tile grid.
 int64_t max_tiles(int64_t M, int64_t cols);
 

@@ -65,6 +65,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_pack_weights_nk.argtypes = [P, P, P, I64, I64, P]
     lib.swiglu_down_proj.argtypes = [P, P, P, I64, I64, I64, P, U64, P]
     lib.swiglu_gated_mlp.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, U64, P]
+    lib.swiglu_fp8_scale_exp.argtypes = [ctypes.c_double]
+    lib.swiglu_quantize_fp8.argtypes = [P, P, I64, I32, P]
+    lib.swiglu_fused_gemm_fp8.argtypes = [P, P, P, I64, I64, I64, I32, I32, P, U64, P]
     lib.swiglu_select_variant.argtypes = [I64, I64, I64]
     lib.swiglu_m_switch.argtypes = []
     lib.swiglu_m_switch.restype = I64
@@ -75,7 +78,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     for name in ("swiglu_pack_weights", "swiglu_fused_gemm", "swiglu_unfused_ablation",
                  "swiglu_silu_mul", "swiglu_select_variant", "swiglu_workspace_size",
                  "swiglu_describe_launch", "swiglu_pack_weights_nk", "swiglu_down_proj",
-                 "swiglu_gated_mlp"):
+                 "swiglu_gated_mlp", "swiglu_fp8_scale_exp", "swiglu_quantize_fp8",
+                 "swiglu_fused_gemm_fp8"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -104,6 +108,21 @@ def _dev_tensor(t: torch.Tensor, name: str, shape) -> torch.Tensor:
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _dev_bytes(t: torch.Tensor, name: str, shape) -> torch.Tensor:
+    """A contiguous uint8 device tensor (FP8 E4M3 codes) of the given shape."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must hold FP8 codes as uint8, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
     if not t.is_contiguous():
@@ -166,7 +185,7 @@ def _ws(workspace: Optional[torch.Tensor]):
 
 
 # swiglu_describe_launch / swiglu_workspace_size codes beyond the variants
-_CALL_CODES = {"ablation": -1, "down_proj": -2}
+_CALL_CODES = {"ablation": -1, "down_proj": -2, "fp8": -3}
 
 
 def _call_code(variant) -> int:
@@ -182,6 +201,8 @@ def swiglu_workspace_size(M: int, N: int, K: int, variant="auto") -> int:
     v = _call_code(variant)
     if v == -2:
         v = -1
+    elif v == -3:
+        v = SWIGLU_VARIANT_I   # the FP8 call uses variant I's workspace
     out = ctypes.c_uint64(0)
     _check(load_library().swiglu_workspace_size(M, N, K, v, ctypes.byref(out)),
            "swiglu_workspace_size")
@@ -306,6 +327,46 @@ def swiglu_silu_mul(gate: torch.Tensor, up: torch.Tensor,
     with torch.cuda.device(gate.device):
         _check(lib.swiglu_silu_mul(_ptr(gate), _ptr(up), _ptr(Y), gate.numel(),
                                    _stream(gate.device)), "swiglu_silu_mul")
+    return Y
+
+
+def swiglu_fp8_scale_exp(amax: float) -> int:
+    """Smallest e with amax * 2^-e <= 448 (the largest E4M3 value)."""
+    return int(load_library().swiglu_fp8_scale_exp(float(amax)))
+
+
+def swiglu_quantize_fp8(X: torch.Tensor, scale_exp: int,
+                        Q: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """E4M3 codes of X * 2^-scale_exp (uint8, the shape of X)."""
+    lib = load_library()
+    _dev_tensor(X, "X", X.shape)
+    if Q is None:
+        Q = torch.empty(X.shape, dtype=torch.uint8, device=X.device)
+    _dev_bytes(Q, "Q", X.shape)
+    with torch.cuda.device(X.device):
+        _check(lib.swiglu_quantize_fp8(_ptr(X), _ptr(Q), X.numel(), int(scale_exp),
+                                       _stream(X.device)), "swiglu_quantize_fp8")
+    return Q
+
+
+def swiglu_fused_gemm_fp8(A8: torch.Tensor, W_fused8: torch.Tensor, a_exp: int, w_exp: int,
+                          Y: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = bf16(SiLU(2^(a+w) A8.W1_8) * (2^(a+w) A8.W2_8)): variant I on FP8 codes
+    (A8 [M, K], W_fused8 [2N, K], both uint8)."""
+    lib = load_library()
+    M, K = A8.shape
+    N = W_fused8.shape[0] // 2
+    _dev_bytes(A8, "A8", (M, K))
+    _dev_bytes(W_fused8, "W_fused8", (2 * N, K))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A8.device)
+    _dev_tensor(Y, "Y", (M, N))
+    with torch.cuda.device(A8.device):
+        ws, wsb = _ws(workspace)
+        _check(lib.swiglu_fused_gemm_fp8(_ptr(A8), _ptr(W_fused8), _ptr(Y), M, N, K, int(a_exp),
+                                         int(w_exp), ws, wsb, _stream(A8.device)),
+               "swiglu_fused_gemm_fp8")
     return Y
 
 

@@ -205,10 +205,46 @@ int swiglu_gated_mlp(const uint16_t *A, const uint16_t *W_fused,
                      void *workspace, uint64_t workspace_bytes, void *stream);
 
 /*
+ * FP8 inputs.  The pages' motivation is that quantisation (FP8, INT4) makes
+ * the GEMMs cheaper, so the materialisation the fusion removes costs
+ * relatively more (paper text, section 1 Introduction).  Format: OCP FP8 E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ * S.1111.111 is NaN; largest finite 448), one byte per value.  Scaling: one
+ * power of two per tensor, A = 2^a_exp * A8 and W_fused = 2^w_exp * W8.
+ *
+ * swiglu_fp8_scale_exp: the smallest exponent e with amax * 2^-e <= 448
+ * (host only; 0 for amax <= 0, NaN or beyond the float range).
+ *
+ * swiglu_quantize_fp8: Q[i] = E4M3(X[i] * 2^-scale_exp) for bf16 X, round to
+ * nearest even, finite values beyond 448 and infinities saturated to +-448,
+ * NaN -> 0x7F (bit-exact).  X: count bf16 values, Q: count bytes, device;
+ * count % 16 == 0, -126 <= scale_exp <= 126, pointers 16-byte aligned, Q does
+ * not overlap X.  Quantising the packed weight (swiglu_pack_weights output,
+ * count = 2N*K) gives W_fused8; quantising A gives A8.
+ *
+ * swiglu_fused_gemm_fp8: variant I on FP8 operands,
+ *     Y = bf16( SiLU(2^(a_exp+w_exp) A8.W1_8) * (2^(a_exp+w_exp) A8.W2_8) )
+ * with A8 [M][K] and W_fused8 packed [2N][K] (the layout of
+ * swiglu_pack_weights, one byte per value); fp32 accumulation of exact FP8
+ * products, the scales applied to Gate and Up in fp32 before the activation,
+ * one rounding to bf16.  Preconditions: those of swiglu_fused_gemm, and K %
+ * 16 == 0 (16-byte rows); a_exp, w_exp and a_exp + w_exp in [-126, 126].
+ * workspace: as for swiglu_fused_gemm (same size).
+ */
+int swiglu_fp8_scale_exp(double amax);
+int swiglu_quantize_fp8(const uint16_t *X, uint8_t *Q, int64_t count,
+                        int scale_exp, void *stream);
+int swiglu_fused_gemm_fp8(const uint8_t *A8, const uint8_t *W_fused8,
+                          uint16_t *Y, int64_t M, int64_t N, int64_t K,
+                          int a_exp, int w_exp, void *workspace,
+                          uint64_t workspace_bytes, void *stream);
+
+/*
  * What a call would launch, as text (host only; queries the current device's
  * compute-unit count): for swiglu_fused_gemm with `variant` (AUTO, S, I) or
  * for swiglu_unfused_ablation (-1), for the down projection of
  * swiglu_gated_mlp over (M, N, K) (-2: an M x K output reducing over N),
+ * for swiglu_fused_gemm_fp8 (-3),
  * given a workspace of `workspace_bytes`
  * (0: none), the kernel names with their tile shapes and schedule, e.g.
  * "gemm_tiles_kernel<128x128x64,PairMulEpilogue> (2240 tiles; 512 workgroups)"

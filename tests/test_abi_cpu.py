@@ -233,7 +233,48 @@ def test_gated_mlp_validation(lib):
 def test_describe_down_proj_validation(lib):
     import ctypes
     buf = ctypes.create_string_buffer(128)
-    assert lib.swiglu_describe_launch(256, 256, 256, -3, 0, buf, len(buf)) == ERR_UNSUP
+    assert lib.swiglu_describe_launch(256, 256, 256, -4, 0, buf, len(buf)) == ERR_UNSUP
     assert lib.swiglu_describe_launch(256, 4, 256, -2, 0, buf, len(buf)) == ERR_SHAPE
     assert lib.swiglu_describe_launch(0, 256, 256, -2, 0, buf, len(buf)) == 0
     assert buf.value == b"nothing (empty problem)"
+
+
+def test_fp8_scale_exp(lib):
+    f = sw.swiglu_fp8_scale_exp
+    assert f(448.0) == 0 and f(448.1) == 1 and f(224.0) == -1 and f(896.0) == 1
+    assert f(5.0) == -6                      # 5 * 64 = 320 <= 448, 5 * 128 > 448
+    for amax in (1e-30, 0.37, 3.0, 1000.0, 3e38):
+        e = f(amax)
+        assert amax * 2.0 ** -e <= 448.0 < amax * 2.0 ** -(e - 1)
+    assert f(0.0) == 0 and f(-1.0) == 0 and f(float("nan")) == 0
+
+
+A8_, W8_ = A_ + 0x2_0000_0000, WF_ + 0x2_0000_0000
+
+
+def test_fp8_validation(lib):
+    Qz = lib.swiglu_quantize_fp8
+    assert Qz(G_, U_, 24, 0, None) == ERR_SHAPE          # count % 16
+    assert Qz(G_, U_, 32, 127, None) == ERR_SHAPE
+    assert Qz(None, None, 0, 0, None) == 0
+    assert Qz(None, U_, 32, 0, None) == ERR_NULL
+    assert Qz(G_ + 8, U_, 32, 0, None) == ERR_ALIGN
+    assert Qz(G_, G_ + 32, 32, 0, None) == ERR_ALIAS
+    F = lib.swiglu_fused_gemm_fp8
+
+    def call(A=A8_, W=W8_, Y=Y_, M=256, N=256, K=256, ea=-6, ew=-8, WS=None, WSB=0):
+        return F(A, W, Y, M, N, K, ea, ew, WS, WSB, None)
+
+    assert call(K=24) == ERR_SHAPE                         # FP8 rows are 16-byte multiples
+    assert call(N=12) == ERR_SHAPE
+    assert call(ea=100, ew=100) == ERR_SHAPE
+    assert call(ea=-127) == ERR_SHAPE
+    assert call(M=0, A=None, W=None, Y=None) == 0
+    assert call(W=None) == ERR_NULL
+    assert call(Y=Y_ + 4) == ERR_ALIGN
+    assert call(Y=W8_ + 64) == ERR_ALIAS
+    assert call(WS=Y_ + 256, WSB=1 << 20) == ERR_ALIAS
+    import ctypes
+    buf = ctypes.create_string_buffer(64)
+    assert lib.swiglu_describe_launch(0, 256, 256, -3, 0, buf, len(buf)) == 0
+    assert lib.swiglu_describe_launch(256, 256, 256, -4, 0, buf, len(buf)) == ERR_UNSUP

@@ -315,6 +315,11 @@ def fp8_compare(args):
         print(json.dumps(rec), flush=True)
         del bf, f8, A, Wf, A8, W8, ws
         torch.cuda.empty_cache()
+    if args.copy_calibration:
+        # one plain device copy of known size, for scaling HBM byte counters
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
 
 
 def sweep(args):

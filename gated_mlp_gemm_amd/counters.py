@@ -10,6 +10,9 @@ command, one counter each (rocprofv3 collects what one pass allows):
         python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-warm --copy-calibration
     rocprofv3 --pmc WRITE_SIZE -f csv -d WRITE_DIR -o bench -- (the same)
 
+(or of ``bench.py --fp8 --fp8-workloads 1 --copy-calibration`` with
+``--paths fp8`` for the FP8 kernel).
+
 Both counters report KiB per dispatch.  Each is scaled by what it reads for
 the plain 256 MiB device copy that ``--copy-calibration`` runs last (the copy
 moves exactly 262144 KiB each way), and each path's kernels are summed with
@@ -36,8 +39,10 @@ COPY_KIB = 256 * 1024
 # kernel name contains, launches per call).  A partly idle last round may add
 # a split_reduce_kernel of the same epilogue, one per GEMM launch.
 PATHS = {
-    "i": [(("gemm_tiles_kernel", "PairMulEpilogue"), 1),
-          (("split_reduce_kernel", "PairMulEpilogue"), 1)],
+    "i": [(("gemm_tiles_kernel", "PairMulEpilogueT<false>"), 1),
+          (("split_reduce_kernel", "PairMulEpilogueT<false>"), 1)],
+    "fp8": [(("gemm_tiles_kernel", "PairMulEpilogueT<true>"), 1),
+            (("split_reduce_kernel", "PairMulEpilogueT<true>"), 1)],
     "s": [(("fused_sequential_kernel",), 1)],
     "ablation": [(("gemm_tiles_kernel", "StoreEpilogue"), 2),
                  (("split_reduce_kernel", "StoreEpilogue"), 2),
@@ -116,9 +121,13 @@ def main(argv=None):
     p.add_argument("write_dir")
     p.add_argument("--workload", default="M=2048,K=1536,N=8960")
     p.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    p.add_argument("--paths", default=",".join(PATHS),
+                   help="which paths of the run to record (default: all found)")
     a = p.parse_args(argv)
     recs = path_records(read_counter(a.fetch_dir, "FETCH_SIZE"),
                         read_counter(a.write_dir, "WRITE_SIZE"), kernel_source_hash())
+    keep = set(a.paths.split(","))
+    recs = {k: v for k, v in recs.items() if k in keep}
     table = {}
     if os.path.exists(a.out):
         with open(a.out) as f:

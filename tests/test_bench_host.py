@@ -39,7 +39,7 @@ def _write_csv(directory, counter, rows):
 def test_counter_table_from_synthetic_passes(tmp_path):
     from gated_mlp_gemm_amd import counters
 
-    gemm_i = "gemm_tiles_kernel<TileShape<256, 256, 64, 2, 2, 2>, PairMulEpilogue, 2>"
+    gemm_i = "gemm_tiles_kernel<TileShape<256, 256, 64, 2, 2, 2>, PairMulEpilogueT<false>, 2>"
     gemm_s = "gemm_tiles_kernel<TileShape<256, 256, 64, 2, 2, 2>, StoreEpilogue, 2>"
     copy = "__amd_rocclr_copyBuffer"
     # the copy reads half of what it moves on the fetch counter (scale 2)

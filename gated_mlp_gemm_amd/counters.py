@@ -34,6 +34,7 @@ from typing import Dict, List
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 COPY_KIB = 256 * 1024
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
 
 # the kernels each bench path launches per call: (substrings every matching
 # kernel name contains, launches per call).  A partly idle last round may add
@@ -115,6 +116,54 @@ def path_records(fetch: Dict[str, List[float]], write: Dict[str, List[float]],
     return recs
 
 
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void swiglu::", "").replace("swiglu::", "")
+
+
+def kernel_table(mfma_dir: str, fetch: Dict[str, List[float]],
+                 write: Dict[str, List[float]]) -> List[dict]:
+    """Per kernel of a run: median duration and mean clock / MFMA busy from a
+    `--kernel-trace --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES` pass
+    (first dispatch of each kernel dropped), and median HBM bytes from the
+    FETCH_SIZE / WRITE_SIZE passes of the same command (copy-scaled).
+    Clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / those cycles."""
+    durs = {}
+    for path in glob.glob(os.path.join(mfma_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                durs[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    per: Dict[str, Dict[str, float]] = {}
+    names: Dict[str, str] = {}
+    for path in glob.glob(os.path.join(mfma_dir, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                per.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    groups: Dict[str, List[tuple]] = {}
+    for d in sorted(per, key=int):
+        c, name = per[d], names[d]
+        if d not in durs or "GRBM_GUI_ACTIVE" not in c or durs[d] <= 0:
+            continue
+        cycles = c["GRBM_GUI_ACTIVE"] / 8.0
+        groups.setdefault(name, []).append(
+            (durs[d], cycles / durs[d], c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024.0 / cycles))
+    fs, ws = copy_scale(fetch), copy_scale(write)
+    rows = []
+    for name, vals in groups.items():
+        if "swiglu::" not in name or name not in fetch or name not in write:
+            continue   # only the library's kernels
+        vals = vals[1:] if len(vals) > 1 else vals
+        dur = statistics.median(v[0] for v in vals)
+        hbm = (statistics.median(fetch[name]) * fs + statistics.median(write[name]) * ws) * 1024
+        rows.append({"kernel": _short(name), "dispatches": len(vals), "us": dur * 1e6,
+                     "clock_ghz": statistics.mean(v[1] for v in vals) / 1e9,
+                     "mfma_busy": statistics.mean(v[2] for v in vals),
+                     "hbm_mb": hbm / 1e6, "hbm_gbs": hbm / dur / 1e9})
+    return rows
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("fetch_dir")
@@ -123,7 +172,22 @@ def main(argv=None):
     p.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     p.add_argument("--paths", default=",".join(PATHS),
                    help="which paths of the run to record (default: all found)")
+    p.add_argument("--mfma", default=None, metavar="DIR",
+                   help="also print a per-kernel table (duration, clock, MFMA busy, HBM GB/s) "
+                        "from a --kernel-trace --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES "
+                        "pass of the same command; writes nothing")
     a = p.parse_args(argv)
+    if a.mfma:
+        fetch = read_counter(a.fetch_dir, "FETCH_SIZE")
+        write = read_counter(a.write_dir, "WRITE_SIZE")
+        print("| kernel | dispatches | median µs | clock GHz | MFMA busy | HBM MB | HBM GB/s "
+              "| % of 8 TB/s |")
+        print("|---|---|---|---|---|---|---|---|")
+        for r in kernel_table(a.mfma, fetch, write):
+            print(f"| {r['kernel']} | {r['dispatches']} | {r['us']:.2f} | {r['clock_ghz']:.2f} | "
+                  f"{100 * r['mfma_busy']:.1f} % | {r['hbm_mb']:.1f} | {r['hbm_gbs']:.0f} | "
+                  f"{100 * r['hbm_gbs'] / PEAK_HBM_GBS:.0f} % |")
+        return
     recs = path_records(read_counter(a.fetch_dir, "FETCH_SIZE"),
                         read_counter(a.write_dir, "WRITE_SIZE"), kernel_source_hash())
     keep = set(a.paths.split(","))

@@ -14,7 +14,9 @@ the 256 MB Infinity Cache cannot hold the working set across steps.
 Prints ONE JSON line: TFLOP/s (4 M N K per step), the fraction of the bf16
 dense MFMA peak, the speedup over the unfused ablation (two GEMMs + SiLU-mul
 from the same mainloop, timed the same way), a roofline record for the fused
-kernel and the CPU oracle's throughput on a bounded sample.
+kernel, the CPU oracle's throughput on a bounded sample, and for context the
+same call on FP8 E4M3 operands (`fp8`: operands quantized beforehand, and
+with the activation quantized inside each step).
 
 --sweep instead times variant I, variant S and the ablation over a range of M
 for each of the five K x N shapes of the workloads (inputs drawn on the
@@ -64,6 +66,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--no-fp8", action="store_true",
+                   help="skip the FP8 context timing of the default line")
     p.add_argument("--no-warm", action="store_true",
                    help="skip the warm (single cache-resident copy) loop (counter passes)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -289,16 +293,17 @@ def fp8_compare(args):
         W8 = sw.swiglu_quantize_fp8(Wf, w_exp)
         step16 = 2 * (M * K + 2 * K * N + M * N)
         R = max(1, -(-512 * 2 ** 20 // step16))
-        bf = [(A, Wf)] + [(A.clone(), Wf.clone()) for _ in range(R - 1)]
-        f8 = [(A8, W8)] + [(A8.clone(), W8.clone()) for _ in range(R - 1)]
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        # inputs and outputs rotate together, as in the default line
+        Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        bf = [(A, Wf, Ys[0])] + [(A.clone(), Wf.clone(), Ys[r]) for r in range(1, R)]
+        f8 = [(A8, W8, Ys[0])] + [(A8.clone(), W8.clone(), Ys[r]) for r in range(1, R)]
         ws = sw.make_workspace(M, N, K, "i", dev)
         torch.cuda.synchronize()
-        us16 = _time_call(lambda a, wf: sw.swiglu_fused_gemm(a, wf, Y=Y, variant="auto",
-                                                             workspace=ws),
-                          bf, stream, budget_s=0.25, max_reps=2000)
-        us8 = _time_call(lambda a, wf: sw.swiglu_fused_gemm_fp8(a, wf, a_exp, w_exp, Y=Y,
+        us16 = _time_call(lambda a, wf, y: sw.swiglu_fused_gemm(a, wf, Y=y, variant="auto",
                                                                 workspace=ws),
+                          bf, stream, budget_s=0.25, max_reps=2000)
+        us8 = _time_call(lambda a, wf, y: sw.swiglu_fused_gemm_fp8(a, wf, a_exp, w_exp, Y=y,
+                                                                   workspace=ws),
                          f8, stream, budget_s=0.25, max_reps=2000)
         flops = 4 * M * N * K
         t8 = flops / (us8 * 1e-6) / 1e12
@@ -313,7 +318,7 @@ def fp8_compare(args):
                                                     0 if ws is None else ws.numel()),
         }
         print(json.dumps(rec), flush=True)
-        del bf, f8, A, Wf, A8, W8, ws
+        del bf, f8, Ys, A, Wf, A8, W8, ws
         torch.cuda.empty_cache()
     if args.copy_calibration:
         # one plain device copy of known size, for scaling HBM byte counters
@@ -487,6 +492,39 @@ def main():
         print(f"[bench] {k}: {v['ms'] * 1e3:.1f} us, {v['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
 
+    # context, not the headline: the same call on FP8 E4M3 operands (power-of-two
+    # tensor scales from the absolute maxima), with the operands quantized
+    # beforehand, and with the activation quantized inside each timed step
+    fp8 = None
+    if not args.no_fp8:
+        a_exp = sw.swiglu_fp8_scale_exp(float(A.float().abs().max()))
+        w_exp = sw.swiglu_fp8_scale_exp(float(Wf.float().abs().max()))
+        copies8 = [(sw.swiglu_quantize_fp8(a, a_exp), sw.swiglu_quantize_fp8(wf, w_exp))
+                   for a, wf in copies]
+        torch.cuda.synchronize()
+
+        def fp8_step(s, quantize_a):
+            a8, w8 = copies8[s % R]
+            if quantize_a:
+                sw.swiglu_quantize_fp8(copies[s % R][0], a_exp, Q=a8)
+            sw.swiglu_fused_gemm_fp8(a8, w8, a_exp, w_exp, Y=outs[s % R], workspace=scratch["i"])
+
+        ms8, _ = timed(lambda s: fp8_step(s, False), args.steps, args.warmup)
+        msq, _ = timed(lambda s: fp8_step(s, True), args.steps, args.warmup)
+        t8 = flops / (ms8 * 1e-3) / 1e12
+        fp8 = {
+            "ms": round(ms8, 5), "tflops": round(t8, 2),
+            "pct_fp8_peak": round(100 * t8 / PEAK_FP8_TFLOPS, 2),
+            "speedup_vs_bf16": round(ms / ms8, 4),
+            "ms_with_activation_quantize": round(msq, 5),
+            "a_exp": a_exp, "w_exp": w_exp,
+            "kernel": sw.swiglu_describe_launch(M, N, K, "fp8", scratch["i"].numel()
+                                                if scratch["i"] is not None else 0),
+        }
+        print(f"[bench] fp8: {ms8 * 1e3:.1f} us, {t8:.1f} TFLOP/s "
+              f"({msq * 1e3:.1f} us with A quantized per step)", file=sys.stderr, flush=True)
+        del copies8
+
     if args.copy_calibration:
         # one plain device copy of known size, for scaling HBM byte counters
         src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -571,6 +609,7 @@ def main():
         "warm_single_copy": None if wms is None else {
             "ms": round(wms, 5), "tflops": round(flops / (wms * 1e-3) / 1e12, 2)},
         "roofline": roofline,
+        "fp8": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

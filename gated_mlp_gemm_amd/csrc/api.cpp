@@ -261,19 +261,28 @@ int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
     return ok();
 }
 
-int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, int64_t M,
-                      int64_t N, int64_t K, int variant, void *workspace,
-                      uint64_t workspace_bytes, void *stream) {
+int swiglu_fused_gemm_strided(const uint16_t *A, int64_t lda, const uint16_t *W_fused,
+                              uint16_t *Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                              int variant, void *workspace, uint64_t workspace_bytes,
+                              void *stream) {
     if (variant != SWIGLU_AUTO && variant != SWIGLU_VARIANT_S && variant != SWIGLU_VARIANT_I)
         return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
     int st = check_gemm_shape(M, N, K);
     if (st != SWIGLU_OK) return st;
+    if (lda < K || lda % 8 != 0 || lda > kMaxK)
+        return fail(SWIGLU_ERR_SHAPE, "lda=%lld must be a multiple of 8 in [K, 2^21]",
+                    (long long)lda);
+    if (ldy < N || ldy > kMaxN)
+        return fail(SWIGLU_ERR_SHAPE, "ldy=%lld must lie in [N, 2^22]", (long long)ldy);
     if (M == 0 || N == 0) return ok();
     const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
     if (!A || !W_fused || !Y) return fail(SWIGLU_ERR_NULL, "A, W_fused and Y are required");
     if (!aligned16(A) || !aligned16(W_fused) || !aligned16(Y))
         return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
-    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = 2 * K * N * 2;
+    // the memory spans of the strided views (conservative: rows interleaved
+    // with another operand's count as overlapping)
+    const int64_t abytes = ((M - 1) * lda + K) * 2, ybytes = ((M - 1) * ldy + N) * 2;
+    const int64_t wbytes = 2 * K * N * 2;
     if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W_fused, wbytes))
         return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
     st = check_workspace(workspace, workspace_bytes);
@@ -288,12 +297,23 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, i
     if (st != SWIGLU_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
     if (v == SWIGLU_VARIANT_I)
-        return launched(swiglu::launch_fused_interleaved(A, W_fused, Y, (int)M, (int)N, (int)K,
+        return launched(swiglu::launch_fused_interleaved(A, (int)lda, W_fused, Y, (int)ldy,
+                                                         (int)M, (int)N, (int)K,
                                                          make_ws(workspace, workspace_bytes, cus),
                                                          s),
                         "fused interleaved");
-    return launched(swiglu::launch_fused_sequential(A, W_fused, Y, (int)M, (int)N, (int)K, s),
+    return launched(swiglu::launch_fused_sequential(A, (int)lda, W_fused, Y, (int)ldy, (int)M,
+                                                    (int)N, (int)K, s),
                     "fused sequential");
+}
+
+int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, int64_t M,
+                      int64_t N, int64_t K, int variant, void *workspace,
+                      uint64_t workspace_bytes, void *stream) {
+    // contiguous rows: lda = K, ldy = N (validated by the strided entry point
+    // after the shape check, so the shape errors are reported first)
+    return swiglu_fused_gemm_strided(A, K, W_fused, Y, N, M, N, K, variant, workspace,
+                                     workspace_bytes, stream);
 }
 
 int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused, uint16_t *gate_ws,
@@ -441,9 +461,10 @@ int swiglu_gated_mlp(const uint16_t *A, const uint16_t *W_fused, const uint16_t 
     const swiglu::GemmWorkspace ws = make_ws(workspace, workspace_bytes, cus);
     // the two launches run in stream order, so they may share the workspace
     hipError_t e = v == SWIGLU_VARIANT_I
-                       ? swiglu::launch_fused_interleaved(A, W_fused, H, (int)M, (int)N, (int)K,
-                                                          ws, s)
-                       : swiglu::launch_fused_sequential(A, W_fused, H, (int)M, (int)N, (int)K, s);
+                       ? swiglu::launch_fused_interleaved(A, (int)K, W_fused, H, (int)N, (int)M,
+                                                          (int)N, (int)K, ws, s)
+                       : swiglu::launch_fused_sequential(A, (int)K, W_fused, H, (int)N, (int)M,
+                                                         (int)N, (int)K, s);
     if (e != hipSuccess) return launched(e, "gated MLP: fused SwiGLU");
     return launched(swiglu::launch_down_proj(H, W3t, Out, (int)M, (int)N, (int)K, ws, s),
                     "gated MLP: down projection");

@@ -134,7 +134,8 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 // A K-contiguous operand: logical row r is physical row r*stride + offset of
-// a row-major [rows*stride][K] matrix.  (stride 2 selects the Gate (offset 0)
+// a row-major [rows*stride][K] matrix whose rows are ld elements apart (ld = 0:
+// K, the rows are contiguous).  (stride 2 selects the Gate (offset 0)
 // or Up (offset 1) columns of the interleaved packed weight.)
 struct KMajor {
     const void *base;   // elements of the tile shape's size (bf16 or FP8)
@@ -147,6 +148,9 @@ struct KMajor {
     // odd (Up) rows (pair_row).  Then the Gate and Up columns of one output
     // column meet in the same lane of two adjacent 32x32 accumulator blocks.
     int pairs;
+    // Elements from one physical row to the next (a row-strided view); 0: K
+    // (contiguous rows).
+    int ld;
 };
 
 // Panel row whose data lands in LDS row `r` of a de-interleaved panel: within
@@ -169,8 +173,10 @@ struct PanelLoader {
     __device__ __forceinline__ void init(const KMajor &op, int r0, int K) {
         const int64_t phys0 = static_cast<int64_t>(r0) * op.stride + op.offset;
         const int64_t phys_end = static_cast<int64_t>(op.rows) * op.stride;  // past the matrix
-        const char *panel = static_cast<const char *>(op.base) + phys0 * K * S::EB;
-        int64_t bytes = (phys_end - phys0) * K * S::EB;
+        const int64_t pitch = op.ld > 0 ? op.ld : K;      // elements per physical row
+        const char *panel = static_cast<const char *>(op.base) + phys0 * pitch * S::EB;
+        // (past the last row's K elements nothing is read: those chunks are masked)
+        int64_t bytes = (phys_end - phys0) * pitch * S::EB;
         if (bytes < 0) bytes = 0;
         if (bytes > 0x7FFFFFF0LL) bytes = 0x7FFFFFF0LL;
         rsrc = make_rsrc(panel, static_cast<uint32_t>(bytes));
@@ -184,7 +190,8 @@ struct PanelLoader {
             const int row = p / S::kChunksPerRow;             // LDS row
             const int c = (p % S::kChunksPerRow) ^ swz<S>(row);
             const int grow = op.pairs ? pair_row(row) : row;  // panel row it holds
-            voff[j] = static_cast<uint32_t>(grow * op.stride) * K * S::EB + c * 16u;
+            voff[j] = static_cast<uint32_t>(grow * op.stride) * static_cast<uint32_t>(pitch) * S::EB +
+                      c * 16u;
             kcol[j] = c * S::kElemsPerChunk;
             lds_off[j] = block * 1024;
         }

@@ -224,6 +224,7 @@ template <bool kScaled>
 struct PairMulEpilogueT {
     uint16_t *Y;
     int M, N;
+    int ldy;       // elements from one row of Y to the next (>= N)
     float scale;   // used only when kScaled
 
     __device__ __forceinline__ float scaled(float x) const {
@@ -247,7 +248,7 @@ struct PairMulEpilogueT {
         const int rows_valid = min(S::BM, M - m0);
         const int y0 = n0 / 2;                 // first Y column of the tile
         const int ycols_valid = min(S::BN / 2, N - y0);
-        const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, N);
+        const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, ldy);
         if constexpr (paired<S>()) {
             constexpr int kPairBlocks = S::TN / 2;
             const int tm = u / kPairBlocks, tp = u % kPairBlocks;
@@ -256,7 +257,7 @@ struct PairMulEpilogueT {
             const int ycol = wn * (S::kWaveN / 2) + tp * 32 + (lane & 31);
             const uint32_t voff =
                 ycol < ycols_valid
-                    ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(y0 + ycol)) * 2u
+                    ? (lrow * static_cast<uint32_t>(ldy) + static_cast<uint32_t>(y0 + ycol)) * 2u
                     : kOutOfRange;
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
@@ -267,9 +268,9 @@ struct PairMulEpilogueT {
                 const float u1 = scaled(acc_value<kFromAcc>(up[i + 1]));
                 const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
                 const uint32_t roff =
-                    static_cast<uint32_t>(acc_row<S>(0, 0, i, 0)) * static_cast<uint32_t>(N) * 2u;
+                    static_cast<uint32_t>(acc_row<S>(0, 0, i, 0)) * static_cast<uint32_t>(ldy) * 2u;
                 store_y_b16(r, voff + roff, static_cast<uint16_t>(v));
-                store_y_b16_hi(r, voff + roff + static_cast<uint32_t>(N) * 2u, v);
+                store_y_b16_hi(r, voff + roff + static_cast<uint32_t>(ldy) * 2u, v);
             }
         } else {
             const int tm = u / S::TN, tn = u % S::TN;
@@ -280,7 +281,7 @@ struct PairMulEpilogueT {
             const int ycol = (wn * S::kWaveN + tn * 32 + (lane & 31)) >> 1;
             const uint32_t voff =
                 ycol < ycols_valid
-                    ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(y0 + ycol)) * 2u
+                    ? (lrow * static_cast<uint32_t>(ldy) + static_cast<uint32_t>(y0 + ycol)) * 2u
                     : kOutOfRange;
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
@@ -289,7 +290,7 @@ struct PairMulEpilogueT {
                 const float gate = scaled(by_lane_parity(lo, recv));
                 const float upv = scaled(by_lane_parity(recv, hi));
                 const uint32_t roff = static_cast<uint32_t>(acc_row<S>(0, tm, p, 0)) *
-                                      static_cast<uint32_t>(N) * 2u;
+                                      static_cast<uint32_t>(ldy) * 2u;
                 store_y_b16(r, voff + roff, to_bf16(silu(gate) * upv));
             }
         }
@@ -381,14 +382,14 @@ struct StoreEpilogue {
 
 // K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
 template <class S>
-__device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const void *A,
+__device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor &A,
                                               const KMajor &B, int M, int K, int m0, int n0,
                                               int kb, int ke, int nk,
                                               f32x16 (&acc)[S::TM][S::TN]) {
     PipelineFor<S> pl;
     pl.init(lds);
     TileLoader<S> ld;
-    ld.init(KMajor{A, M, 1, 0}, m0, B, n0, K);
+    ld.init(A, m0, B, n0, K);
     const int len = ke - kb;
     // steps past the range load nothing (K step nk is past the end of K)
     auto issue = [&](int s, SWIGLU_LDS char *st) { ld.issue(s < len ? kb + s : nk, st); };
@@ -427,12 +428,11 @@ enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2 };
 //    half q % 2) of tile dp + q / 4, run whole as a quarter-size tile.
 template <class S, class Epi, int TAIL>
 __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
-    const void *__restrict__ A, KMajor B, int M, int K, Epi epi, Schedule sch) {
+    KMajor Ak, KMajor B, int M, int K, Epi epi, Schedule sch) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
     const int b = blockIdx.x;
     const int grid = sch.grid;
-    const KMajor Ak{A, M, 1, 0};
 
     if (b < sch.dp) {
         PipelineFor<S> pl;
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             const int n0 = tn * S::BN + (q & 1) * Q::BN;
             if (m0 >= M || n0 >= B.rows) continue;   // quarter wholly past the output's edge
             f32x16 acc[Q::TM][Q::TN];
-            tile_mainloop<Q>(lds, A, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
+            tile_mainloop<Q>(lds, Ak, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
             epi.template apply<Q>(acc, m0, n0, threadIdx.x);
         }
     } else if constexpr (TAIL == kTailSplit) {
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             int tm, tn;
             tile_coords(t, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
             f32x16 acc[S::TM][S::TN];
-            tile_mainloop<S>(lds, A, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
+            tile_mainloop<S>(lds, Ak, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
             store_partial<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN, acc,
                              threadIdx.x);
         }
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch
 template <class S>
 __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, uint16_t *__restrict__ Y,
-    int M, int N, int K, int tiles_m, int tiles_n) {
+    int M, int N, int K, int lda, int ldy, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
 
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
     // Gate columns of W_fused (even packed rows), steps [nk, 2nk) against the
     // Up columns (odd packed rows); the loads run ahead across the boundary.
     TileLoader<S> ld;
-    ld.init(KMajor{A, M, 1, 0}, m0, KMajor{Wf, N, 2, 0}, n0, K);
+    ld.init(KMajor{A, M, 1, 0, 0, lda}, m0, KMajor{Wf, N, 2, 0}, n0, K);
     PanelLoader<S, S::BN, S::kDmaB> up;
     up.init(KMajor{Wf, N, 2, 1}, n0, K);
     auto issue = [&](int t, SWIGLU_LDS char *st) {
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
             for (int i = 0; i < 16; ++i) {
                 const int row = acc_row<S>(wm, tm, i, lane);
                 if (row < rows_valid && col < cols_valid)
-                    Y[(int64_t)(m0 + row) * N + n0 + col] = to_bf16(g[tm][tn][i] * u[tm][tn][i]);
+                    Y[(int64_t)(m0 + row) * ldy + n0 + col] = to_bf16(g[tm][tn][i] * u[tm][tn][i]);
             }
         }
     }
@@ -798,7 +798,7 @@ static int launch_grid(const Schedule &sch, int cus) {
 }
 
 template <class S, class Epi>
-static hipError_t launch_gemm(const void *A, KMajor B, int M, int cols, int K, Epi epi,
+static hipError_t launch_gemm(KMajor A, KMajor B, int M, int cols, int K, Epi epi,
                               const GemmWorkspace &ws, hipStream_t stream) {
     Schedule sch = make_schedule<S>(M, cols, K, ws);
     sch.grid = launch_grid<S>(sch, ws.cus);
@@ -843,14 +843,16 @@ static bool quad_tiles_faster(int M, int cols, int K, const GemmWorkspace &ws) {
     return quad < wide;
 }
 
-hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
-                                    int N, int K, const GemmWorkspace &ws, hipStream_t stream) {
+hipError_t launch_fused_interleaved(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
+                                    int ldy, int M, int N, int K, const GemmWorkspace &ws,
+                                    hipStream_t stream) {
+    const KMajor Ak{A, M, 1, 0, 0, lda};
     const KMajor B{Wf, 2 * N, 1, 0};
-    const PairMulEpilogue epi{Y, M, N};
-    if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, 2 * N, K, epi, ws, stream);
+    const PairMulEpilogue epi{Y, M, N, ldy, 1.0f};
+    if (M <= 128) return launch_gemm<ShapeSmall>(Ak, B, M, 2 * N, K, epi, ws, stream);
     if (quad_tiles_faster(M, 2 * N, K, ws))
-        return launch_gemm<ShapeQuad>(A, B, M, 2 * N, K, epi, ws, stream);
-    return launch_gemm<ShapeWide>(A, B, M, 2 * N, K, epi, ws, stream);
+        return launch_gemm<ShapeQuad>(Ak, B, M, 2 * N, K, epi, ws, stream);
+    return launch_gemm<ShapeWide>(Ak, B, M, 2 * N, K, epi, ws, stream);
 }
 
 // The kernels launch_fused_interleaved / launch_fused_sequential /
@@ -901,12 +903,13 @@ int describe_fused_sequential(int M, int N, char *buf, size_t n) {
 hipError_t launch_fused_interleaved_fp8(const uint8_t *A8, const uint8_t *Wf8, uint16_t *Y,
                                         int M, int N, int K, float scale,
                                         const GemmWorkspace &ws, hipStream_t stream) {
+    const KMajor Ak{A8, M, 1, 0};
     const KMajor B{Wf8, 2 * N, 1, 0};
-    const PairMulEpilogueFp8 epi{Y, M, N, scale};
-    if (M <= 128) return launch_gemm<ShapeSmall8>(A8, B, M, 2 * N, K, epi, ws, stream);
+    const PairMulEpilogueFp8 epi{Y, M, N, N, scale};
+    if (M <= 128) return launch_gemm<ShapeSmall8>(Ak, B, M, 2 * N, K, epi, ws, stream);
     if (quad_tiles_faster<ShapeWide8, ShapeQuad8>(M, 2 * N, K, ws))
-        return launch_gemm<ShapeQuad8>(A8, B, M, 2 * N, K, epi, ws, stream);
-    return launch_gemm<ShapeWide8>(A8, B, M, 2 * N, K, epi, ws, stream);
+        return launch_gemm<ShapeQuad8>(Ak, B, M, 2 * N, K, epi, ws, stream);
+    return launch_gemm<ShapeWide8>(Ak, B, M, 2 * N, K, epi, ws, stream);
 }
 
 int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf, size_t n) {
@@ -921,13 +924,13 @@ int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf
                                 make_schedule<ShapeWide8>(M, cols, K, ws), ws.cus, buf, n);
 }
 
-hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
-                                   int N, int K, hipStream_t stream) {
+hipError_t launch_fused_sequential(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
+                                   int ldy, int M, int N, int K, hipStream_t stream) {
     if (M <= 128)
         return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, A, Wf,
-                                        Y, M, N, K);
+                                        Y, M, N, K, lda, ldy);
     return launch_tiles<ShapeSeq>(fused_sequential_kernel<ShapeSeq>, M, N, stream, A, Wf, Y, M,
-                                  N, K);
+                                  N, K, lda, ldy);
 }
 
 // C [M][cols] = bf16(A . B^T) for a K-contiguous operand B of `cols` logical
@@ -935,11 +938,12 @@ hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16
 static hipError_t launch_store_gemm(const uint16_t *A, const KMajor &B, uint16_t *C, int M,
                                     int cols, int K, const GemmWorkspace &ws,
                                     hipStream_t stream) {
+    const KMajor Ak{A, M, 1, 0};
     const StoreEpilogue epi{C, M, cols};
-    if (M <= 128) return launch_gemm<ShapeSmall>(A, B, M, cols, K, epi, ws, stream);
+    if (M <= 128) return launch_gemm<ShapeSmall>(Ak, B, M, cols, K, epi, ws, stream);
     if (quad_tiles_faster(M, cols, K, ws))
-        return launch_gemm<ShapeQuad>(A, B, M, cols, K, epi, ws, stream);
-    return launch_gemm<ShapeWide>(A, B, M, cols, K, epi, ws, stream);
+        return launch_gemm<ShapeQuad>(Ak, B, M, cols, K, epi, ws, stream);
+    return launch_gemm<ShapeWide>(Ak, B, M, cols, K, epi, ws, stream);
 }
 
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,

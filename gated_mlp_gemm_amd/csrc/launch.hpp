@@ -37,10 +37,12 @@ hipError_t launch_pack_nk(const uint16_t *W1t, const uint16_t *W2t, uint16_t *Wf
                           int64_t N, hipStream_t stream);
 hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, int64_t count,
                            hipStream_t stream);
-hipError_t launch_fused_interleaved(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
-                                    int N, int K, const GemmWorkspace &ws, hipStream_t stream);
-hipError_t launch_fused_sequential(const uint16_t *A, const uint16_t *Wf, uint16_t *Y, int M,
-                                   int N, int K, hipStream_t stream);
+// lda / ldy: elements from one row of A / Y to the next (K / N when contiguous).
+hipError_t launch_fused_interleaved(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
+                                    int ldy, int M, int N, int K, const GemmWorkspace &ws,
+                                    hipStream_t stream);
+hipError_t launch_fused_sequential(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
+                                   int ldy, int M, int N, int K, hipStream_t stream);
 // phase 0: C = A . W1 (Gate columns of W_fused), phase 1: C = A . W2 (Up columns)
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
                              int M, int N, int K, const GemmWorkspace &ws, hipStream_t stream);

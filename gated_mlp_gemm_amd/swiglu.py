@@ -59,6 +59,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     U64 = ctypes.c_uint64
     lib.swiglu_fused_gemm.argtypes = [P, P, P, I64, I64, I64, I32, P, U64, P]
     lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, I64, I64, I64, P, U64, P]
+    lib.swiglu_fused_gemm_strided.argtypes = [P, I64, P, P, I64, I64, I64, I64, I32, P, U64, P]
     lib.swiglu_workspace_size.argtypes = [I64, I64, I64, I32, ctypes.POINTER(U64)]
     lib.swiglu_describe_launch.argtypes = [I64, I64, I64, I32, U64, ctypes.c_char_p, U64]
     lib.swiglu_silu_mul.argtypes = [P, P, P, I64, P]
@@ -79,7 +80,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                  "swiglu_silu_mul", "swiglu_select_variant", "swiglu_workspace_size",
                  "swiglu_describe_launch", "swiglu_pack_weights_nk", "swiglu_down_proj",
                  "swiglu_gated_mlp", "swiglu_fp8_scale_exp", "swiglu_quantize_fp8",
-                 "swiglu_fused_gemm_fp8"):
+                 "swiglu_fused_gemm_fp8", "swiglu_fused_gemm_strided"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -244,6 +245,42 @@ def swiglu_fused_gemm(A: torch.Tensor, W_fused: torch.Tensor,
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W_fused), _ptr(Y), M, N, K, v, ws, wsb,
                                      _stream(A.device)), "swiglu_fused_gemm")
+    return Y
+
+
+def _dev_rows(t: torch.Tensor, name: str, shape) -> int:
+    """A bf16 device matrix whose rows are contiguous (stride 1 along a row);
+    returns the row pitch in elements."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dim() != 2 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError(f"{name} must have contiguous rows")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def swiglu_fused_gemm_strided(A: torch.Tensor, W_fused: torch.Tensor, Y: torch.Tensor,
+                              variant="auto",
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """swiglu_fused_gemm on row-strided views: A [M, K] and Y [M, N] may be
+    column slices of wider tensors (their row strides are passed as lda / ldy)."""
+    lib = load_library()
+    v = VARIANTS[variant.lower()] if isinstance(variant, str) else int(variant)
+    M, K = A.shape
+    N = W_fused.shape[0] // 2
+    lda = _dev_rows(A, "A", (M, K))
+    ldy = _dev_rows(Y, "Y", (M, N))
+    _dev_tensor(W_fused, "W_fused", (2 * N, K))
+    with torch.cuda.device(A.device):
+        ws, wsb = _ws(workspace)
+        _check(lib.swiglu_fused_gemm_strided(_ptr(A), lda, _ptr(W_fused), _ptr(Y), ldy, M, N, K,
+                                             v, ws, wsb, _stream(A.device)),
+               "swiglu_fused_gemm_strided")
     return Y
 
 

@@ -117,6 +117,23 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
                       void *workspace, uint64_t workspace_bytes, void *stream);
 
 /*
+ * swiglu_fused_gemm on row-strided views of A and Y, for activations and
+ * outputs that are slices of wider tensors (rows of A are lda elements apart,
+ * rows of Y ldy elements apart; the packed weight stays contiguous).  Same
+ * computation, variants, workspace and preconditions as swiglu_fused_gemm,
+ * plus: K <= lda <= 2^21 with lda % 8 == 0 (16-byte aligned rows), and
+ * N <= ldy <= 2^22.  Only the M x K elements of A and the M x N elements of Y
+ * are accessed; Y's elements between rows are left untouched.  Overlap is
+ * judged on the spans [A, A + (M-1)*lda + K) and [Y, Y + (M-1)*ldy + N), so
+ * views that interleave rows of one allocation are rejected as overlapping.
+ * swiglu_fused_gemm(A, W, Y, M, N, K, ...) is this call with lda = K, ldy = N.
+ */
+int swiglu_fused_gemm_strided(const uint16_t *A, int64_t lda, const uint16_t *W_fused,
+                              uint16_t *Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                              int variant, void *workspace, uint64_t workspace_bytes,
+                              void *stream);
+
+/*
  * The unfused pipeline, kept as an ablation so the saved memory traffic can be
  * measured (paper text, section 1: the unfused form materialises two full
  * intermediate tensors, Gate and Up, between the GEMM and activation stages).

@@ -278,3 +278,22 @@ def test_fp8_validation(lib):
     buf = ctypes.create_string_buffer(64)
     assert lib.swiglu_describe_launch(0, 256, 256, -3, 0, buf, len(buf)) == 0
     assert lib.swiglu_describe_launch(256, 256, 256, -4, 0, buf, len(buf)) == ERR_UNSUP
+
+
+def test_strided_validation(lib):
+    F = lib.swiglu_fused_gemm_strided
+
+    def call(A=A_, lda=256, W=WF_, Y=Y_, ldy=256, M=256, N=256, K=256, v=2):
+        return F(A, lda, W, Y, ldy, M, N, K, v, None, 0, None)
+
+    assert call(lda=248) == ERR_SHAPE                     # lda < K
+    assert call(lda=260) == ERR_SHAPE                     # rows not 16-byte aligned
+    assert call(lda=1 << 22) == ERR_SHAPE
+    assert call(ldy=200) == ERR_SHAPE                     # ldy < N
+    assert call(ldy=(1 << 22) + 8) == ERR_SHAPE
+    assert call(M=0, A=None, W=None, Y=None) == 0
+    assert call(Y=None) == ERR_NULL
+    # Y inside A's strided span (rows of A are 4096 elements apart)
+    assert call(lda=4096, Y=A_ + 2 * 304) == ERR_ALIAS
+    # contiguous call = strided with lda = K, ldy = N: same errors
+    assert lib.swiglu_fused_gemm(A_, WF_, A_ + 64, 256, 256, 256, 2, None, 0, None) == ERR_ALIAS

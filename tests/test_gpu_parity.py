@@ -567,3 +567,40 @@ def test_empty_and_invalid_on_device(dev):
     with pytest.raises(sw.SwigluError):      # K = 20 is not a multiple of 8
         sw.swiglu_fused_gemm(torch.empty((8, 20), dtype=torch.bfloat16, device=dev),
                              torch.empty((128, 20), dtype=torch.bfloat16, device=dev))
+
+
+# ---------------------------------------------------------------------------
+# row-strided views of A and Y (swiglu_fused_gemm_strided)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(1, 16, 8), (130, 200, 72), (300, 1000, 136),
+                                   (513, 64, 1032), (2048, 1536, 8960)])
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
+def test_strided_views(dev, orc, M, K, N, variant):
+    """A is columns [8, 8+K) of an [M, K+24] matrix whose other columns hold
+    1e4 (reading them would wreck the result); Y is columns [16, 16+N) of an
+    [M, N+40] buffer of sentinels, which must be untouched outside the view."""
+    announce(f"strided {variant} M={M} K={K} N={N}")
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 13 + K * 3 + N)
+    Abig = torch.full((M, K + 24), 1e4, dtype=torch.bfloat16, device=dev)
+    Abig[:, 8:8 + K] = A.to(dev)
+    Av = Abig[:, 8:8 + K]
+    sentinel = 0x7F7F                                    # a large finite bf16 pattern
+    Ybig = torch.full((M, N + 40), 0, dtype=torch.int16, device=dev)
+    Ybig.fill_(sentinel)
+    Ybig = Ybig.view(torch.bfloat16)
+    Yv = Ybig[:, 16:16 + N]
+    Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    v = variant.split("+")[0]
+    ws = workspace_for(M, N, K, v, dev) if variant.endswith("+ws") else None
+    sw.swiglu_fused_gemm_strided(Av, Wf, Yv, variant=v, workspace=ws)
+    torch.cuda.synchronize()
+    big = bits_of(Ybig)
+    outside = np.concatenate([big[:, :16].ravel(), big[:, 16 + N:].ravel()])
+    assert np.all(outside == sentinel), "stores outside the Y view"
+    yb = np.ascontiguousarray(big[:, 16:16 + N])
+    hA, hW1, hW2 = inputs.bits(A), inputs.bits(W1), inputs.bits(W2)
+    if M * N * K > 1e9:
+        rows = np.array([0, 1, M // 2, M - 1])
+        assert_parity(yb[rows], orc.swiglu_rows(hA, hW1, hW2, rows), f"strided {variant} rows")
+    else:
+        assert_parity(yb, orc.swiglu(hA, hW1, hW2), f"strided {variant} {M}x{K}x{N}")

@@ -110,7 +110,8 @@ int check_device(int *cus = nullptr) {
 }
 
 // SWIGLU_I_TILE=256 or 128 forces the tile of variant I and the ablation
-// GEMMs above M = 128 (testing, measurement); anything else: the cost model.
+// GEMMs above M = 128, and variant I's 128x64 (256) or 128x128 (128) tiles at
+// M <= 128 (testing, measurement); anything else: the cost model / rule.
 int tile_override() {
     const char *s = std::getenv("SWIGLU_I_TILE");
     if (s == nullptr) return 0;
@@ -252,7 +253,8 @@ int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
     } else if (v == SWIGLU_VARIANT_S) {
         swiglu::describe_fused_sequential((int)M, (int)N, buf, buf_bytes);
     } else if (v == SWIGLU_VARIANT_I) {
-        swiglu::describe_gemm((int)M, (int)(2 * N), (int)K, ws, "PairMulEpilogue", buf, buf_bytes);
+        swiglu::describe_gemm((int)M, (int)(2 * N), (int)K, ws, "PairMulEpilogue", buf, buf_bytes,
+                              true);
     } else {
         char g[256];
         swiglu::describe_gemm((int)M, (int)N, (int)K, ws, "StoreEpilogue", g, sizeof g);

@@ -843,13 +843,39 @@ static bool quad_tiles_faster(int M, int cols, int K, const GemmWorkspace &ws) {
     return quad < wide;
 }
 
+// Variant I at M <= 128 streams the packed weight once, so its time follows
+// the rows of W_fused the busiest compute unit has to stream: 64 per round
+// of 128x64 tiles (one workgroup per CU), or 128 per resident 128x128 tile
+// (two share a CU).  The 128x128 tiles are taken when M > 64 and they put no
+// more rows on any CU (fewer workgroups, one round).  Measured at M = 128:
+// 6-10 % faster on (K, N) = (1536, 8960), (5120, 13824), (8192, 29568), where
+// the 128x64 tiles need a second (or fourth) round; the rule keeps 128x64 on
+// (896, 4864) and (3584, 18944), where 128x128 tiles ran 64 % and 5 % slower;
+// at M <= 64 the 128x64 tiles were as fast or faster on all five shapes.
+// The FP8 path applies the same rule (there the 128x128 tiles also gain 10-19 %
+// on the first and last of those three shapes; on (3584, 18944) they would be
+// 10 % faster but the rule keeps 128x64).
+// SWIGLU_I_TILE=128 / 256 forces the 128x128 / 128x64 tiles here.
+static bool small_m_quad_tiles(int M, int cols, const GemmWorkspace &ws) {
+    if (ws.tile == 128) return true;
+    if (ws.tile == 256 || M <= 64 || ws.cus <= 0) return false;
+    const int64_t small = cdiv(cols, ShapeSmall::BN), quad = cdiv(cols, ShapeQuad::BN);
+    const int64_t rows_small = 64 * ((small + ws.cus - 1) / ws.cus);
+    const int64_t rows_quad = 128 * ((quad + ws.cus - 1) / ws.cus);
+    return rows_quad <= rows_small;
+}
+
 hipError_t launch_fused_interleaved(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
                                     int ldy, int M, int N, int K, const GemmWorkspace &ws,
                                     hipStream_t stream) {
     const KMajor Ak{A, M, 1, 0, 0, lda};
     const KMajor B{Wf, 2 * N, 1, 0};
     const PairMulEpilogue epi{Y, M, N, ldy, 1.0f};
-    if (M <= 128) return launch_gemm<ShapeSmall>(Ak, B, M, 2 * N, K, epi, ws, stream);
+    if (M <= 128) {
+        if (small_m_quad_tiles(M, 2 * N, ws))
+            return launch_gemm<ShapeQuad>(Ak, B, M, 2 * N, K, epi, ws, stream);
+        return launch_gemm<ShapeSmall>(Ak, B, M, 2 * N, K, epi, ws, stream);
+    }
     if (quad_tiles_faster(M, 2 * N, K, ws))
         return launch_gemm<ShapeQuad>(Ak, B, M, 2 * N, K, epi, ws, stream);
     return launch_gemm<ShapeWide>(Ak, B, M, 2 * N, K, epi, ws, stream);
@@ -878,7 +904,10 @@ static int describe(const char *kernel, const char *epi, const Schedule &sch, in
 }
 
 int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *epi, char *buf,
-                  size_t n) {
+                  size_t n, bool fused_i) {
+    if (M <= 128 && fused_i && small_m_quad_tiles(M, cols, ws))
+        return describe<ShapeQuad>("gemm_tiles_kernel", epi,
+                                   make_schedule<ShapeQuad>(M, cols, K, ws), ws.cus, buf, n);
     if (M <= 128)
         return describe<ShapeSmall>("gemm_tiles_kernel", epi,
                                     make_schedule<ShapeSmall>(M, cols, K, ws), ws.cus, buf, n);
@@ -906,7 +935,11 @@ hipError_t launch_fused_interleaved_fp8(const uint8_t *A8, const uint8_t *Wf8, u
     const KMajor Ak{A8, M, 1, 0};
     const KMajor B{Wf8, 2 * N, 1, 0};
     const PairMulEpilogueFp8 epi{Y, M, N, N, scale};
-    if (M <= 128) return launch_gemm<ShapeSmall8>(Ak, B, M, 2 * N, K, epi, ws, stream);
+    if (M <= 128) {
+        if (small_m_quad_tiles(M, 2 * N, ws))
+            return launch_gemm<ShapeQuad8>(Ak, B, M, 2 * N, K, epi, ws, stream);
+        return launch_gemm<ShapeSmall8>(Ak, B, M, 2 * N, K, epi, ws, stream);
+    }
     if (quad_tiles_faster<ShapeWide8, ShapeQuad8>(M, 2 * N, K, ws))
         return launch_gemm<ShapeQuad8>(Ak, B, M, 2 * N, K, epi, ws, stream);
     return launch_gemm<ShapeWide8>(Ak, B, M, 2 * N, K, epi, ws, stream);
@@ -914,6 +947,9 @@ hipError_t launch_fused_interleaved_fp8(const uint8_t *A8, const uint8_t *Wf8, u
 
 int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf, size_t n) {
     const char *epi = "PairMulEpilogueFp8";
+    if (M <= 128 && small_m_quad_tiles(M, cols, ws))
+        return describe<ShapeQuad8>("gemm_tiles_kernel", epi,
+                                    make_schedule<ShapeQuad8>(M, cols, K, ws), ws.cus, buf, n);
     if (M <= 128)
         return describe<ShapeSmall8>("gemm_tiles_kernel", epi,
                                      make_schedule<ShapeSmall8>(M, cols, K, ws), ws.cus, buf, n);

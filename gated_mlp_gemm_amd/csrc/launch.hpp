@@ -26,8 +26,10 @@ uint64_t workspace_bytes_for(int cus);
 
 // Text naming the kernels (tile shape, schedule) a GEMM over an M x cols
 // output would launch (snprintf semantics).
+// fused_i: the variant-I GEMM (its M <= 128 tile choice differs from the
+// ablation's and the down projection's).
 int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *epi, char *buf,
-                  size_t n);
+                  size_t n, bool fused_i = false);
 int describe_fused_sequential(int M, int N, char *buf, size_t n);
 
 hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,

@@ -556,7 +556,16 @@ def test_describe_launch(dev, monkeypatch):
     assert "128x128x64" in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
     assert sw.swiglu_describe_launch(2048, 8960, 1536, "s").startswith("fused_sequential_kernel<")
     assert sw.swiglu_describe_launch(2048, 8960, 1536, "ablation").startswith("2 x gemm_tiles")
-    assert "128x64x64" in sw.swiglu_describe_launch(128, 4864, 896, "i")
+    assert "128x128x64" in sw.swiglu_describe_launch(128, 4864, 896, "i")    # forced at M <= 128
+    monkeypatch.setenv("SWIGLU_I_TILE", "256")
+    assert "128x64x64" in sw.swiglu_describe_launch(128, 8960, 1536, "i")    # forced at M <= 128
+    monkeypatch.delenv("SWIGLU_I_TILE")
+    # M <= 128: 128x128 tiles where they put no more weight rows on a CU (M > 64)
+    assert "128x64x64" in sw.swiglu_describe_launch(128, 4864, 896, "i")     # 152 vs 76 tiles
+    assert "128x128x64" in sw.swiglu_describe_launch(128, 8960, 1536, "i")   # 280 vs 140 tiles
+    assert "128x64x64" in sw.swiglu_describe_launch(64, 8960, 1536, "i")
+    assert "128x64x64" in sw.swiglu_describe_launch(128, 18944, 3584, "i")   # 592 vs 296 tiles
+    assert "128x128x128" in sw.swiglu_describe_launch(128, 8960, 1536, "fp8")
 
 
 def test_empty_and_invalid_on_device(dev):
@@ -604,3 +613,15 @@ def test_strided_views(dev, orc, M, K, N, variant):
         assert_parity(yb[rows], orc.swiglu_rows(hA, hW1, hW2, rows), f"strided {variant} rows")
     else:
         assert_parity(yb, orc.swiglu(hA, hW1, hW2), f"strided {variant} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(100, 136, 8960), (128, 64, 13824)])
+@pytest.mark.parametrize("variant", ["i", "i+ws", "auto"])
+def test_small_m_quad_tiles(dev, orc, M, K, N, variant):
+    """M <= 128 shapes for which variant I takes 128x128 tiles (two per CU)."""
+    assert "128x128x64" in sw.swiglu_describe_launch(M, N, K, "i")
+    announce(f"small-M 128x128 {variant} M={M} K={K} N={N}")
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 7 + N)
+    ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
+    Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    assert_parity(bits_of(run_fused(A.to(dev), Wf, variant)), ref, f"{variant} {M}x{K}x{N}")

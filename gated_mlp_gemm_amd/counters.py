@@ -51,13 +51,40 @@ PATHS = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++/HIP source with comments removed and whitespace runs collapsed, so
+    that edits to comments alone leave the hash unchanged.  String literals
+    are kept (a '//' inside one is not a comment)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':                                    # string literal
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of every file under csrc/ (name and bytes), 16 hex digits."""
+    """Hash of the code (comments and whitespace aside) of every file under
+    csrc/, with the file names; 16 hex digits."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -41,8 +41,8 @@ constexpr int64_t kMaxN = int64_t(1) << 22;
 // Built-in M threshold of the dispatcher: every M.  On MI355X variant I was
 // faster than variant S at 44 of 45 measured (M, K, N) points -- M from 128 to
 // 16384 on each of the five K x N shapes of the workloads, by 10-20 % at large
-// M -- and within 2 % at the other, so AUTO runs I unless SWIGLU_M_SWITCH
-// sets a smaller threshold.
+// M -- and within 1-8 % (run to run) at the other (M = 128, K = 1536, N =
+// 8960), so AUTO runs I unless SWIGLU_M_SWITCH sets a smaller threshold.
 constexpr int64_t kDefaultMSwitch = kMaxM;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

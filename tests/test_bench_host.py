@@ -62,3 +62,16 @@ def test_counter_table_from_synthetic_passes(tmp_path):
     assert ab["hbm_bytes_per_launch"] == (2 * (50 * 2 + 40) + (30 * 2 + 20)) * 1024
     assert "s|M=8,K=8,N=8" not in table                        # no sequential kernel ran
     assert i["kernel_source_hash"] == counters.kernel_source_hash()
+
+
+def test_source_hash_ignores_comments_only():
+    from gated_mlp_gemm_amd import counters
+
+    a = 'int f(int x) { return x + 1; }  // one\n/* block\n comment */\nconst char *s = "//x";\n'
+    b = '// header\nint f(int x)\n{\n    return x + 1;   /* inline */\n}\nconst char *s = "//x";\n'
+    c = 'int f(int x) { return x + 2; }\nconst char *s = "//x";\n'
+    d = 'int f(int x) { return x + 1; }\nconst char *s = "//y";\n'
+    assert counters._code_only(a) == counters._code_only(b)
+    assert counters._code_only(a) != counters._code_only(c)
+    assert counters._code_only(a) != counters._code_only(d)     # strings are code
+    assert counters._code_only('char q[] = "a\\\\"b"; int z;') == 'char q[] = "a\\\\"b"; int z;'

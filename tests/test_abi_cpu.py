@@ -297,3 +297,17 @@ def test_strided_validation(lib):
     assert call(lda=4096, Y=A_ + 2 * 304) == ERR_ALIAS
     # contiguous call = strided with lda = K, ldy = N: same errors
     assert lib.swiglu_fused_gemm(A_, WF_, A_ + 64, 256, 256, 256, 2, None, 0, None) == ERR_ALIAS
+
+
+def test_plain_c_client(tmp_path, lib):
+    """The header compiles as C11 and a C program links the library and gets
+    the documented statuses back (host-only and validation paths: no GPU)."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(sw.LIBRARY)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(root, "include"), os.path.join(root, "tests", "c", "abi_check.c"),
+                    "-o", str(exe), "-L", libdir, "-lswiglu", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr

@@ -169,8 +169,8 @@ def test_mlp_hand_case_padded(dev, orc):
         assert np.array_equal(bits_of(Out), out_ref)
 
 
-MLP_SMALL = [(1, 8, 8), (5, 16, 24), (130, 200, 72), (257, 136, 264), (300, 1000, 136),
-             (513, 64, 1032)]
+MLP_SMALL = [(1, 8, 8), (5, 16, 24), (100, 64, 8960), (130, 200, 72), (257, 136, 264),
+             (300, 1000, 136), (513, 64, 1032)]
 
 
 @pytest.mark.parametrize("M,K,N", MLP_SMALL)

@@ -164,3 +164,22 @@ def test_fp8_workload_rows(dev, orc, w):
     yb = inputs.bits(Y.cpu())
     assert_parity(yb[rows], ref, f"fp8 rows {w.name}")
     assert np.isfinite(oracle_pkg.bf16_bits_to_f64(yb)).all()
+
+
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 700)), int(rng.integers(1, 70)) * 16, int(rng.integers(1, 140)) * 8)
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("M,K,N", _random_shapes(2025, 8))
+def test_fp8_random_shapes(dev, orc, M, K, N):
+    announce(f"fp8 random shape M={M} K={K} N={N}")
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=3 * M + K + 11 * N)
+    A8, W8, hA8, hWT8, ea, ew = prepare(orc, dev, A, W1, W2)
+    assert np.array_equal(A8.cpu().numpy(), hA8) and np.array_equal(W8.cpu().numpy(), hWT8)
+    ref = orc.swiglu_fp8(hA8, hWT8, ea, ew)
+    for ws in (None, sw.make_workspace(M, N, K, "fp8", dev)):
+        Y = sw.swiglu_fused_gemm_fp8(A8, W8, ea, ew, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(inputs.bits(Y.cpu()), ref, f"fp8 {M}x{K}x{N} ws={ws is not None}")

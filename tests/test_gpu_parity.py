@@ -625,3 +625,28 @@ def test_small_m_quad_tiles(dev, orc, M, K, N, variant):
     ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
     Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
     assert_parity(bits_of(run_fused(A.to(dev), Wf, variant)), ref, f"{variant} {M}x{K}x{N}")
+
+
+# ---------------------------------------------------------------------------
+# seeded random ragged shapes (deterministic; whole outputs against the oracle)
+# ---------------------------------------------------------------------------
+def _random_shapes(seed, count, k_mult):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(count):
+        M = int(rng.integers(1, 700))
+        K = int(rng.integers(1, 1100 // k_mult + 1)) * k_mult
+        N = int(rng.integers(1, 140)) * 8
+        shapes.append((M, K, N))
+    return shapes
+
+
+@pytest.mark.parametrize("M,K,N", _random_shapes(2024, 12, 8))
+def test_random_shapes(dev, orc, M, K, N):
+    announce(f"random shape M={M} K={K} N={N}")
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M + 7 * K + 13 * N)
+    ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
+    Ad = A.to(dev)
+    Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    for variant in ("i", "i+ws", "s"):
+        assert_parity(bits_of(run_fused(Ad, Wf, variant)), ref, f"{variant} {M}x{K}x{N}")

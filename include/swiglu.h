@@ -14,7 +14,9 @@
  *  - Every matrix is bf16, passed as its 16-bit patterns (uint16_t), dense
  *    and contiguous: A [M][K], W1 and W2 [K][N], Y / gate_ws / up_ws [M][N]
  *    row-major; the packed weight W_fused (K x 2N) column-major, i.e. a
- *    row-major [2N][K] array whose row c is column c of W_fused.
+ *    row-major [2N][K] array whose row c is column c of W_fused.  Exceptions
+ *    are stated by the calls they concern: the FP8 calls take one-byte E4M3
+ *    codes (uint8_t), swiglu_fused_gemm_strided takes row-strided A and Y.
  *  - Every matrix pointer is a DEVICE pointer, allocated and owned by the
  *    caller.  The library allocates, frees and retains nothing: no pointer is
  *    kept past the call.
@@ -30,9 +32,10 @@
  *      every pointer 16-byte aligned;  outputs do not overlap inputs or
  *      each other.
  *    M == 0 or N == 0 is an empty problem: SWIGLU_OK, nothing launched.
- *  - Outputs are computed with fp32 accumulation of bf16 products and one
- *    round-to-nearest-even to bf16 at the end; the accumulation order is not
- *    specified (results of different variants need not be bitwise equal).
+ *  - Outputs are computed with fp32 accumulation of bf16 (or FP8) products
+ *    and one round-to-nearest-even to bf16 at the end; the accumulation order
+ *    is not specified (results of different variants need not be bitwise
+ *    equal).
  *  - Calls are re-entrant; the only global state is a per-device cache of
  *    the device's architecture.
  *  - The code object targets gfx950 only: on another device every launching
@@ -134,6 +137,18 @@ int swiglu_fused_gemm_strided(const uint16_t *A, int64_t lda, const uint16_t *W_
                               void *stream);
 
 /*
+ * Bytes of `workspace` that let a call split the tail round along K: variant
+ * SWIGLU_VARIANT_I or SWIGLU_AUTO for swiglu_fused_gemm, -1 for
+ * swiglu_unfused_ablation, swiglu_down_proj and swiglu_gated_mlp (0 when
+ * nothing uses it, e.g. variant S, or for an empty problem; the FP8 call uses
+ * variant I's size).  Queries the current device's compute-unit count (a HIP
+ * call).  One fp32 256 x 256 tile per compute unit, whatever the shape:
+ * 64 MiB on MI355X.
+ */
+int swiglu_workspace_size(int64_t M, int64_t N, int64_t K, int variant,
+                          uint64_t *bytes);
+
+/*
  * The unfused pipeline, kept as an ablation so the saved memory traffic can be
  * measured (paper text, section 1: the unfused form materialises two full
  * intermediate tensors, Gate and Up, between the GEMM and activation stages).
@@ -146,17 +161,6 @@ int swiglu_fused_gemm_strided(const uint16_t *A, int64_t lda, const uint16_t *W_
  * workspace_bytes: as for swiglu_fused_gemm (the two GEMMs use the same
  * scheduler as variant I; size from swiglu_workspace_size(..., -1, ...)).
  */
-
-/*
- * Bytes of `workspace` that let a call split the tail round along K: variant
- * SWIGLU_VARIANT_I or SWIGLU_AUTO for swiglu_fused_gemm, -1 for
- * swiglu_unfused_ablation (0 when nothing uses it, e.g. variant S, or for an
- * empty problem).  Queries the current device's compute-unit count (a HIP
- * call).  One fp32 256 x 256 tile per compute unit, whatever the shape:
- * 64 MiB on MI355X.
- */
-int swiglu_workspace_size(int64_t M, int64_t N, int64_t K, int variant,
-                          uint64_t *bytes);
 int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused,
                             uint16_t *gate_ws, uint16_t *up_ws, uint16_t *Y,
                             int64_t M, int64_t N, int64_t K, void *workspace,

@@ -264,8 +264,8 @@ def mlp_blocks(args):
 
 
 def fp8_compare(args):
-    """The fused GEMM (variant I) on FP8 E4M3 operands against the same call on
-    bf16, per workload (one JSON line each).  The operands are quantized once,
+    """The fused GEMM (AUTO, i.e. variant I) on FP8 E4M3 operands against the
+    same call on bf16, and variant S on FP8, per workload (one JSON line each).  The operands are quantized once,
     untimed (power-of-two tensor scales from the absolute maxima), like the
     weight pack; the timed call is the fused GEMM alone."""
     import torch
@@ -305,13 +305,17 @@ def fp8_compare(args):
         us8 = _time_call(lambda a, wf, y: sw.swiglu_fused_gemm_fp8(a, wf, a_exp, w_exp, Y=y,
                                                                    workspace=ws),
                          f8, stream, budget_s=0.25, max_reps=2000)
+        us8s = _time_call(lambda a, wf, y: sw.swiglu_fused_gemm_fp8(a, wf, a_exp, w_exp, Y=y,
+                                                                    variant="s"),
+                          f8, stream, budget_s=0.25, max_reps=2000)
         flops = 4 * M * N * K
         t8 = flops / (us8 * 1e-6) / 1e12
         rec = {
             "workload": f"fused SwiGLU GEMM M={M} K={K} N={N} (seed {w.seed})",
             "M": M, "K": K, "N": N, "rotation_copies": R, "a_exp": a_exp, "w_exp": w_exp,
-            "us": {"bf16": round(us16, 2), "fp8": round(us8, 2)},
-            "tflops": {"bf16": round(flops / (us16 * 1e-6) / 1e12, 1), "fp8": round(t8, 1)},
+            "us": {"bf16": round(us16, 2), "fp8": round(us8, 2), "fp8_s": round(us8s, 2)},
+            "tflops": {"bf16": round(flops / (us16 * 1e-6) / 1e12, 1), "fp8": round(t8, 1),
+                       "fp8_s": round(flops / (us8s * 1e-6) / 1e12, 1)},
             "fp8_pct_of_fp8_peak": round(100 * t8 / PEAK_FP8_TFLOPS, 2),
             "fp8_speedup_vs_bf16": round(us16 / us8, 3),
             "fp8_launch": sw.swiglu_describe_launch(M, N, K, "fp8",

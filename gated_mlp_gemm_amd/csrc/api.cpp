@@ -498,8 +498,10 @@ int swiglu_quantize_fp8(const uint16_t *X, uint8_t *Q, int64_t count, int scale_
 }
 
 int swiglu_fused_gemm_fp8(const uint8_t *A8, const uint8_t *W_fused8, uint16_t *Y, int64_t M,
-                          int64_t N, int64_t K, int a_exp, int w_exp, void *workspace,
-                          uint64_t workspace_bytes, void *stream) {
+                          int64_t N, int64_t K, int a_exp, int w_exp, int variant,
+                          void *workspace, uint64_t workspace_bytes, void *stream) {
+    if (variant != SWIGLU_AUTO && variant != SWIGLU_VARIANT_S && variant != SWIGLU_VARIANT_I)
+        return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
     int st = check_gemm_shape(M, N, K);
     if (st != SWIGLU_OK) return st;
     if (K % 16 != 0) return fail(SWIGLU_ERR_SHAPE, "K=%lld must be a multiple of 16", (long long)K);
@@ -524,6 +526,11 @@ int swiglu_fused_gemm_fp8(const uint8_t *A8, const uint8_t *W_fused8, uint16_t *
     st = check_device(&cus);
     if (st != SWIGLU_OK) return st;
     const float scale = std::ldexp(1.0f, a_exp + w_exp);
+    const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
+    if (v == SWIGLU_VARIANT_S)
+        return launched(swiglu::launch_fused_sequential_fp8(A8, W_fused8, Y, (int)M, (int)N,
+                                                            (int)K, scale, (hipStream_t)stream),
+                        "fused sequential fp8");
     return launched(swiglu::launch_fused_interleaved_fp8(A8, W_fused8, Y, (int)M, (int)N, (int)K,
                                                          scale,
                                                          make_ws(workspace, workspace_bytes, cus),

@@ -531,9 +531,13 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch
 // registers).
 // ---------------------------------------------------------------------------
 template <class S>
+//
+// On FP8 operands (S::EB == 1) the accumulators hold D / scale: Gate and Up
+// are scaled by `scale` (= 2^(a_exp + w_exp)) before SiLU and the product.
 __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wf, uint16_t *__restrict__ Y,
-    int M, int N, int K, int lda, int ldy, int tiles_m, int tiles_n) {
+    const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y,
+    int M, int N, int K, int lda, int ldy, float scale, int tiles_m, int tiles_n) {
+    constexpr bool kScaled = S::EB == 1;
     __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
 
@@ -580,8 +584,11 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
                 const int b = j * S::kKSub + ks;
                 if (b < kBlocks) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        g[b / S::TN][b % S::TN][i] = silu(g[b / S::TN][b % S::TN][i]);
+                    for (int i = 0; i < 16; ++i) {
+                        float x = g[b / S::TN][b % S::TN][i];
+                        if constexpr (kScaled) x *= scale;
+                        g[b / S::TN][b % S::TN][i] = silu(x);
+                    }
                 }
             });
         }
@@ -591,8 +598,11 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
     for (int b = 0; b < kBlocks; ++b) {
         if (b >= nk * S::kKSub) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                g[b / S::TN][b % S::TN][i] = silu(g[b / S::TN][b % S::TN][i]);
+            for (int i = 0; i < 16; ++i) {
+                float x = g[b / S::TN][b % S::TN][i];
+                if constexpr (kScaled) x *= scale;
+                g[b / S::TN][b % S::TN][i] = silu(x);
+            }
         }
     }
     // rest of the Up loop
@@ -609,8 +619,11 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = acc_row<S>(wm, tm, i, lane);
-                if (row < rows_valid && col < cols_valid)
-                    Y[(int64_t)(m0 + row) * ldy + n0 + col] = to_bf16(g[tm][tn][i] * u[tm][tn][i]);
+                if (row < rows_valid && col < cols_valid) {
+                    float up = u[tm][tn][i];
+                    if constexpr (kScaled) up *= scale;
+                    Y[(int64_t)(m0 + row) * ldy + n0 + col] = to_bf16(g[tm][tn][i] * up);
+                }
             }
         }
     }
@@ -646,6 +659,7 @@ using ShapeSmall = TileShape<128, 64, 64, 2, 2, 4>;
 using ShapeWide8 = TileShape<256, 256, 128, 2, 2, 2, 1>;
 using ShapeQuad8 = TileShape<128, 128, 128, 2, 2, 2, 1>;
 using ShapeSmall8 = TileShape<128, 64, 128, 2, 2, 4, 1>;
+using ShapeSeq8 = TileShape<128, 128, 128, 2, 2, 2, 1>;
 
 static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
@@ -962,11 +976,23 @@ int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf
 
 hipError_t launch_fused_sequential(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
                                    int ldy, int M, int N, int K, hipStream_t stream) {
+    const void *a = A, *w = Wf;
     if (M <= 128)
-        return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, A, Wf,
-                                        Y, M, N, K, lda, ldy);
-    return launch_tiles<ShapeSeq>(fused_sequential_kernel<ShapeSeq>, M, N, stream, A, Wf, Y, M,
-                                  N, K, lda, ldy);
+        return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, a, w,
+                                        Y, M, N, K, lda, ldy, 1.0f);
+    return launch_tiles<ShapeSeq>(fused_sequential_kernel<ShapeSeq>, M, N, stream, a, w, Y, M,
+                                  N, K, lda, ldy, 1.0f);
+}
+
+// Variant S on FP8 operands: the same kernel with K steps of 128 FP8 values.
+hipError_t launch_fused_sequential_fp8(const uint8_t *A8, const uint8_t *Wf8, uint16_t *Y, int M,
+                                       int N, int K, float scale, hipStream_t stream) {
+    const void *a = A8, *w = Wf8;
+    if (M <= 128)
+        return launch_tiles<ShapeSmall8>(fused_sequential_kernel<ShapeSmall8>, M, N, stream, a, w,
+                                         Y, M, N, K, K, N, scale);
+    return launch_tiles<ShapeSeq8>(fused_sequential_kernel<ShapeSeq8>, M, N, stream, a, w, Y, M,
+                                   N, K, K, N, scale);
 }
 
 // C [M][cols] = bf16(A . B^T) for a K-contiguous operand B of `cols` logical

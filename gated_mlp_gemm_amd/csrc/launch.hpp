@@ -58,6 +58,8 @@ hipError_t launch_quantize_fp8(const uint16_t *x, uint8_t *q, int64_t count, int
 hipError_t launch_fused_interleaved_fp8(const uint8_t *A8, const uint8_t *Wf8, uint16_t *Y,
                                         int M, int N, int K, float scale,
                                         const GemmWorkspace &ws, hipStream_t stream);
+hipError_t launch_fused_sequential_fp8(const uint8_t *A8, const uint8_t *Wf8, uint16_t *Y, int M,
+                                       int N, int K, float scale, hipStream_t stream);
 int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf, size_t n);
 // Largest workgroup count any launcher uses for an M x cols output tile grid.
 int64_t max_tiles(int64_t M, int64_t cols);

@@ -68,7 +68,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_gated_mlp.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, U64, P]
     lib.swiglu_fp8_scale_exp.argtypes = [ctypes.c_double]
     lib.swiglu_quantize_fp8.argtypes = [P, P, I64, I32, P]
-    lib.swiglu_fused_gemm_fp8.argtypes = [P, P, P, I64, I64, I64, I32, I32, P, U64, P]
+    lib.swiglu_fused_gemm_fp8.argtypes = [P, P, P, I64, I64, I64, I32, I32, I32, P, U64, P]
     lib.swiglu_select_variant.argtypes = [I64, I64, I64]
     lib.swiglu_m_switch.argtypes = []
     lib.swiglu_m_switch.restype = I64
@@ -387,11 +387,12 @@ def swiglu_quantize_fp8(X: torch.Tensor, scale_exp: int,
 
 
 def swiglu_fused_gemm_fp8(A8: torch.Tensor, W_fused8: torch.Tensor, a_exp: int, w_exp: int,
-                          Y: Optional[torch.Tensor] = None,
+                          Y: Optional[torch.Tensor] = None, variant="auto",
                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = bf16(SiLU(2^(a+w) A8.W1_8) * (2^(a+w) A8.W2_8)): variant I on FP8 codes
-    (A8 [M, K], W_fused8 [2N, K], both uint8)."""
+    """Y = bf16(SiLU(2^(a+w) A8.W1_8) * (2^(a+w) A8.W2_8)) on FP8 codes (A8 [M, K],
+    W_fused8 [2N, K], both uint8); variant 'auto' | 's' | 'i'."""
     lib = load_library()
+    v = VARIANTS[variant.lower()] if isinstance(variant, str) else int(variant)
     M, K = A8.shape
     N = W_fused8.shape[0] // 2
     _dev_bytes(A8, "A8", (M, K))
@@ -402,7 +403,7 @@ def swiglu_fused_gemm_fp8(A8: torch.Tensor, W_fused8: torch.Tensor, a_exp: int, 
     with torch.cuda.device(A8.device):
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_fused_gemm_fp8(_ptr(A8), _ptr(W_fused8), _ptr(Y), M, N, K, int(a_exp),
-                                         int(w_exp), ws, wsb, _stream(A8.device)),
+                                         int(w_exp), v, ws, wsb, _stream(A8.device)),
                "swiglu_fused_gemm_fp8")
     return Y
 

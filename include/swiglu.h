@@ -243,21 +243,23 @@ int swiglu_gated_mlp(const uint16_t *A, const uint16_t *W_fused,
  * not overlap X.  Quantising the packed weight (swiglu_pack_weights output,
  * count = 2N*K) gives W_fused8; quantising A gives A8.
  *
- * swiglu_fused_gemm_fp8: variant I on FP8 operands,
+ * swiglu_fused_gemm_fp8: the fused SwiGLU GEMM on FP8 operands,
  *     Y = bf16( SiLU(2^(a_exp+w_exp) A8.W1_8) * (2^(a_exp+w_exp) A8.W2_8) )
  * with A8 [M][K] and W_fused8 packed [2N][K] (the layout of
  * swiglu_pack_weights, one byte per value); fp32 accumulation of exact FP8
  * products, the scales applied to Gate and Up in fp32 before the activation,
- * one rounding to bf16.  Preconditions: those of swiglu_fused_gemm, and K %
- * 16 == 0 (16-byte rows); a_exp, w_exp and a_exp + w_exp in [-126, 126].
- * workspace: as for swiglu_fused_gemm (same size).
+ * one rounding to bf16.  `variant`: SWIGLU_VARIANT_I, SWIGLU_VARIANT_S or
+ * SWIGLU_AUTO (swiglu_select_variant), as for swiglu_fused_gemm.
+ * Preconditions: those of swiglu_fused_gemm, and K % 16 == 0 (16-byte rows);
+ * a_exp, w_exp and a_exp + w_exp in [-126, 126].  workspace: as for
+ * swiglu_fused_gemm (variant I's size; variant S does not use it).
  */
 int swiglu_fp8_scale_exp(double amax);
 int swiglu_quantize_fp8(const uint16_t *X, uint8_t *Q, int64_t count,
                         int scale_exp, void *stream);
 int swiglu_fused_gemm_fp8(const uint8_t *A8, const uint8_t *W_fused8,
                           uint16_t *Y, int64_t M, int64_t N, int64_t K,
-                          int a_exp, int w_exp, void *workspace,
+                          int a_exp, int w_exp, int variant, void *workspace,
                           uint64_t workspace_bytes, void *stream);
 
 /*

@@ -42,7 +42,9 @@ int main(void) {
           SWIGLU_ERR_ALIAS);
     CHECK(swiglu_quantize_fp8(A, (uint8_t *)Y, 24, 0, NULL) == SWIGLU_ERR_SHAPE);
     CHECK(swiglu_fused_gemm_fp8((const uint8_t *)A, (const uint8_t *)W, Y, 256, 256, 24, 0, 0,
-                                NULL, 0, NULL) == SWIGLU_ERR_SHAPE);
+                                SWIGLU_AUTO, NULL, 0, NULL) == SWIGLU_ERR_SHAPE);
+    CHECK(swiglu_fused_gemm_fp8((const uint8_t *)A, (const uint8_t *)W, Y, 256, 256, 256, 0, 0, 9,
+                                NULL, 0, NULL) == SWIGLU_ERR_UNSUPPORTED);
     CHECK(swiglu_silu_mul(A, A, Y, 12, NULL) == SWIGLU_ERR_SHAPE);
     /* empty problems succeed without touching anything */
     CHECK(swiglu_fused_gemm(NULL, NULL, NULL, 0, 256, 256, SWIGLU_AUTO, NULL, 0, NULL) == SWIGLU_OK);

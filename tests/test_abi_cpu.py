@@ -262,8 +262,10 @@ def test_fp8_validation(lib):
     assert Qz(G_, G_ + 32, 32, 0, None) == ERR_ALIAS
     F = lib.swiglu_fused_gemm_fp8
 
-    def call(A=A8_, W=W8_, Y=Y_, M=256, N=256, K=256, ea=-6, ew=-8, WS=None, WSB=0):
-        return F(A, W, Y, M, N, K, ea, ew, WS, WSB, None)
+    def call(A=A8_, W=W8_, Y=Y_, M=256, N=256, K=256, ea=-6, ew=-8, v=2, WS=None, WSB=0):
+        return F(A, W, Y, M, N, K, ea, ew, v, WS, WSB, None)
+
+    assert call(v=5) == ERR_UNSUP
 
     assert call(K=24) == ERR_SHAPE                         # FP8 rows are 16-byte multiples
     assert call(N=12) == ERR_SHAPE

@@ -1,7 +1,7 @@
 """Parity of the FP8 (E4M3) path's HIP kernels with the CPU oracle (needs an MI355X).
 
 The product path quantizes on the device (swiglu_quantize_fp8 of A and of the
-packed weight) and runs variant I on the codes (swiglu_fused_gemm_fp8); the
+packed weight) and runs variant I or S on the codes (swiglu_fused_gemm_fp8); the
 oracle quantizes the same seeded bf16 inputs on the CPU with its own
 quantizer.  The codes must agree bit for bit; Y must meet the bar of the bf16
 path, |y_gpu - y_ref| <= max(1e-3, 1e-2 |y_ref|), against the oracle's fused
@@ -100,18 +100,19 @@ SMALL = [(1, 16, 8), (5, 32, 24), (64, 128, 64), (128, 896, 520), (100, 144, 896
 
 
 @pytest.mark.parametrize("M,K,N", SMALL)
-@pytest.mark.parametrize("use_ws", [False, True], ids=["nows", "ws"])
-def test_fp8_small_shapes(dev, orc, M, K, N, use_ws):
-    announce(f"fused fp8 M={M} K={K} N={N} ws={use_ws}")
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
+def test_fp8_small_shapes(dev, orc, M, K, N, variant):
+    announce(f"fused fp8 {variant} M={M} K={K} N={N}")
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=M * 29 + K * 5 + N)
     A8, W8, hA8, hWT8, ea, ew = prepare(orc, dev, A, W1, W2)
     assert np.array_equal(A8.cpu().numpy(), hA8)
     assert np.array_equal(W8.cpu().numpy(), hWT8)
     ref = orc.swiglu_fp8(hA8, hWT8, ea, ew)
-    ws = sw.make_workspace(M, N, K, "fp8", dev) if use_ws else None
-    Y = sw.swiglu_fused_gemm_fp8(A8, W8, ea, ew, workspace=ws)
+    v = variant.split("+")[0]
+    ws = sw.make_workspace(M, N, K, "fp8", dev) if variant.endswith("+ws") else None
+    Y = sw.swiglu_fused_gemm_fp8(A8, W8, ea, ew, variant=v, workspace=ws)
     torch.cuda.synchronize()
-    assert_parity(inputs.bits(Y.cpu()), ref, f"fp8 {M}x{K}x{N} ws={use_ws}")
+    assert_parity(inputs.bits(Y.cpu()), ref, f"fp8 {variant} {M}x{K}x{N}")
 
 
 @pytest.mark.parametrize("tile", ["256", "128"])
@@ -154,16 +155,17 @@ def test_fp8_workload_rows(dev, orc, w):
     assert np.array_equal(A8.cpu().numpy(), hA8)
     assert np.array_equal(W8.cpu().numpy(), hWT8)
     ws = sw.make_workspace(w.M, w.N, w.K, "fp8", dev)
-    announce(f"fused fp8 {w.name} a_exp={ea} w_exp={ew}")
-    Y = sw.swiglu_fused_gemm_fp8(A8, W8, ea, ew, workspace=ws)
-    torch.cuda.synchronize()
     rng = np.random.default_rng(3000 + w.seed)
     rows = np.unique(np.concatenate([[0, w.M - 1], rng.integers(0, w.M, 3)]))
     announce(f"oracle rows {list(rows)} {w.name}")
     ref = orc.swiglu_fp8(hA8, hWT8, ea, ew, rows=rows)
-    yb = inputs.bits(Y.cpu())
-    assert_parity(yb[rows], ref, f"fp8 rows {w.name}")
-    assert np.isfinite(oracle_pkg.bf16_bits_to_f64(yb)).all()
+    for variant in ("auto", "s"):
+        announce(f"fused fp8 {variant} {w.name} a_exp={ea} w_exp={ew}")
+        Y = sw.swiglu_fused_gemm_fp8(A8, W8, ea, ew, variant=variant, workspace=ws)
+        torch.cuda.synchronize()
+        yb = inputs.bits(Y.cpu())
+        assert_parity(yb[rows], ref, f"fp8 {variant} rows {w.name}")
+        assert np.isfinite(oracle_pkg.bf16_bits_to_f64(yb)).all()
 
 
 def _random_shapes(seed, count):
@@ -179,7 +181,7 @@ def test_fp8_random_shapes(dev, orc, M, K, N):
     A8, W8, hA8, hWT8, ea, ew = prepare(orc, dev, A, W1, W2)
     assert np.array_equal(A8.cpu().numpy(), hA8) and np.array_equal(W8.cpu().numpy(), hWT8)
     ref = orc.swiglu_fp8(hA8, hWT8, ea, ew)
-    for ws in (None, sw.make_workspace(M, N, K, "fp8", dev)):
-        Y = sw.swiglu_fused_gemm_fp8(A8, W8, ea, ew, workspace=ws)
+    for variant, ws in (("i", None), ("i", sw.make_workspace(M, N, K, "fp8", dev)), ("s", None)):
+        Y = sw.swiglu_fused_gemm_fp8(A8, W8, ea, ew, variant=variant, workspace=ws)
         torch.cuda.synchronize()
-        assert_parity(inputs.bits(Y.cpu()), ref, f"fp8 {M}x{K}x{N} ws={ws is not None}")
+        assert_parity(inputs.bits(Y.cpu()), ref, f"fp8 {variant} {M}x{K}x{N} ws={ws is not None}")

@@ -568,13 +568,15 @@ def main():
         orc.swiglu_rows(hA, hW1, hW2, np.arange(probe))
         per_row = (time.perf_counter() - t) / probe
         rows = int(min(M, max(probe, args.cpu_seconds / max(per_row, 1e-9))))
-        passes = 1
-        if rows == M:
-            passes = int(max(1, min(20, args.cpu_seconds // max(per_row * M, 1e-9))))
+        # whole passes until two thirds of the target have elapsed (at most 20)
+        passes = 0
         t = time.perf_counter()
-        for _ in range(passes):
+        while True:
             orc.swiglu_rows(hA, hW1, hW2, np.arange(rows))
-        dt = time.perf_counter() - t
+            passes += 1
+            dt = time.perf_counter() - t
+            if rows < M or passes >= 20 or dt >= args.cpu_seconds * 2.0 / 3.0:
+                break
         cpu = {
             "value": round(4 * passes * rows * N * K / dt / 1e12, 6),
             "unit": "TFLOP/s",

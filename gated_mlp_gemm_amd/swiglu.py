@@ -10,6 +10,7 @@ on one ROCm device; outputs are allocated with torch when not given.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -109,11 +110,11 @@ def _dev_tensor(t: torch.Tensor, name: str, shape) -> torch.Tensor:
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t
 
@@ -124,16 +125,33 @@ def _dev_bytes(t: torch.Tensor, name: str, shape) -> torch.Tensor:
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.uint8:
         raise TypeError(f"{name} must hold FP8 codes as uint8, got {t.dtype}")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t
 
 
+# torch's raw-handle accessor skips building a Stream object on every call
+# (about 1.5 us of the host cost of a small call); older builds lack it.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_NO_SWITCH = contextlib.nullcontext()
+
+
+def _on_device(device):
+    """Make `device` current for the call; a no-op when it already is."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _NO_SWITCH
+    return torch.cuda.device(device)
+
+
 def _stream(device) -> int:
+    """The handle of torch's current stream on `device`."""
+    if _raw_stream is not None:
+        idx = torch.cuda.current_device() if device.index is None else device.index
+        return _raw_stream(idx)
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -154,7 +172,7 @@ def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor,
     if W_fused is None:
         W_fused = torch.empty((2 * N, K), dtype=torch.bfloat16, device=W1.device)
     _dev_tensor(W_fused, "W_fused", (2 * N, K))
-    with torch.cuda.device(W1.device):
+    with _on_device(W1.device):
         _check(lib.swiglu_pack_weights(_ptr(W1), _ptr(W2), _ptr(W_fused), K, N,
                                        _stream(W1.device)), "swiglu_pack_weights")
     return W_fused
@@ -171,7 +189,7 @@ def swiglu_pack_weights_nk(W1t: torch.Tensor, W2t: torch.Tensor,
     if W_fused is None:
         W_fused = torch.empty((2 * N, K), dtype=torch.bfloat16, device=W1t.device)
     _dev_tensor(W_fused, "W_fused", (2 * N, K))
-    with torch.cuda.device(W1t.device):
+    with _on_device(W1t.device):
         _check(lib.swiglu_pack_weights_nk(_ptr(W1t), _ptr(W2t), _ptr(W_fused), K, N,
                                           _stream(W1t.device)), "swiglu_pack_weights_nk")
     return W_fused
@@ -241,7 +259,7 @@ def swiglu_fused_gemm(A: torch.Tensor, W_fused: torch.Tensor,
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _dev_tensor(Y, "Y", (M, N))
-    with torch.cuda.device(A.device):
+    with _on_device(A.device):
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W_fused), _ptr(Y), M, N, K, v, ws, wsb,
                                      _stream(A.device)), "swiglu_fused_gemm")
@@ -255,7 +273,7 @@ def _dev_rows(t: torch.Tensor, name: str, shape) -> int:
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
     if t.dim() != 2 or tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
@@ -276,7 +294,7 @@ def swiglu_fused_gemm_strided(A: torch.Tensor, W_fused: torch.Tensor, Y: torch.T
     lda = _dev_rows(A, "A", (M, K))
     ldy = _dev_rows(Y, "Y", (M, N))
     _dev_tensor(W_fused, "W_fused", (2 * N, K))
-    with torch.cuda.device(A.device):
+    with _on_device(A.device):
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_fused_gemm_strided(_ptr(A), lda, _ptr(W_fused), _ptr(Y), ldy, M, N, K,
                                              v, ws, wsb, _stream(A.device)),
@@ -302,7 +320,7 @@ def swiglu_unfused_ablation(A: torch.Tensor, W_fused: torch.Tensor,
             t = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
         outs.append(_dev_tensor(t, name, (M, N)))
     gate_ws, up_ws, Y = outs
-    with torch.cuda.device(A.device):
+    with _on_device(A.device):
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_unfused_ablation(_ptr(A), _ptr(W_fused), _ptr(gate_ws), _ptr(up_ws),
                                            _ptr(Y), M, N, K, ws, wsb, _stream(A.device)),
@@ -321,7 +339,7 @@ def swiglu_down_proj(H: torch.Tensor, W3t: torch.Tensor, Out: Optional[torch.Ten
     if Out is None:
         Out = torch.empty((M, D), dtype=torch.bfloat16, device=H.device)
     _dev_tensor(Out, "Out", (M, D))
-    with torch.cuda.device(H.device):
+    with _on_device(H.device):
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_down_proj(_ptr(H), _ptr(W3t), _ptr(Out), M, N, D, ws, wsb,
                                     _stream(H.device)), "swiglu_down_proj")
@@ -346,7 +364,7 @@ def swiglu_gated_mlp(A: torch.Tensor, W_fused: torch.Tensor, W3t: torch.Tensor,
         Out = torch.empty((M, K), dtype=torch.bfloat16, device=A.device)
     _dev_tensor(H, "H", (M, N))
     _dev_tensor(Out, "Out", (M, K))
-    with torch.cuda.device(A.device):
+    with _on_device(A.device):
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_gated_mlp(_ptr(A), _ptr(W_fused), _ptr(W3t), _ptr(H), _ptr(Out),
                                     M, N, K, v, ws, wsb, _stream(A.device)), "swiglu_gated_mlp")
@@ -361,7 +379,7 @@ def swiglu_silu_mul(gate: torch.Tensor, up: torch.Tensor,
     if Y is None:
         Y = torch.empty_like(gate)
     _dev_tensor(Y, "Y", gate.shape)
-    with torch.cuda.device(gate.device):
+    with _on_device(gate.device):
         _check(lib.swiglu_silu_mul(_ptr(gate), _ptr(up), _ptr(Y), gate.numel(),
                                    _stream(gate.device)), "swiglu_silu_mul")
     return Y
@@ -380,7 +398,7 @@ def swiglu_quantize_fp8(X: torch.Tensor, scale_exp: int,
     if Q is None:
         Q = torch.empty(X.shape, dtype=torch.uint8, device=X.device)
     _dev_bytes(Q, "Q", X.shape)
-    with torch.cuda.device(X.device):
+    with _on_device(X.device):
         _check(lib.swiglu_quantize_fp8(_ptr(X), _ptr(Q), X.numel(), int(scale_exp),
                                        _stream(X.device)), "swiglu_quantize_fp8")
     return Q
@@ -400,7 +418,7 @@ def swiglu_fused_gemm_fp8(A8: torch.Tensor, W_fused8: torch.Tensor, a_exp: int, 
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A8.device)
     _dev_tensor(Y, "Y", (M, N))
-    with torch.cuda.device(A8.device):
+    with _on_device(A8.device):
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_fused_gemm_fp8(_ptr(A8), _ptr(W_fused8), _ptr(Y), M, N, K, int(a_exp),
                                          int(w_exp), v, ws, wsb, _stream(A8.device)),

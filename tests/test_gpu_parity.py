@@ -295,6 +295,21 @@ def _intermediate_within_bound(orc, a_bits, w_bits, got_bits, what):
     assert np.all(err <= bound), f"{what}: max err/bound {float((err / bound).max()):.3f}"
 
 
+def test_ablation_workload_full_size(dev, orc, workload):
+    """The unfused ablation at each workload's full size, with the workspace
+    the benchmark gives it: sampled rows of Gate, Up and Y against the oracle."""
+    d = workload
+    w = d["w"]
+    announce(f"ablation {w.name} full size, workspace")
+    ws = workspace_for(w.M, w.N, w.K, "ablation", dev)
+    Y, g, u = sw.swiglu_unfused_ablation(d["A"], d["Wf"], workspace=ws)
+    torch.cuda.synchronize()
+    rows = d["rows"]
+    _verify_ablation(orc, Y, g, u, d["hA"][rows], d["hW1"], d["hW2"], rows,
+                     f"ablation {w.name}")
+    assert np.isfinite(oracle_pkg.bf16_bits_to_f64(bits_of(Y))).all()
+
+
 def _check_ablation(orc, A, W1, W2, rows, dev, what, use_ws=False):
     Ad = A.to(dev)
     M, K = A.shape
@@ -302,8 +317,14 @@ def _check_ablation(orc, A, W1, W2, rows, dev, what, use_ws=False):
     Y, g, u = sw.swiglu_unfused_ablation(Ad, sw.swiglu_pack_weights(W1.to(dev), W2.to(dev)),
                                          workspace=ws)
     torch.cuda.synchronize()
-    sub = inputs.bits(A)[rows]
-    hW1, hW2 = inputs.bits(W1), inputs.bits(W2)
+    _verify_ablation(orc, Y, g, u, inputs.bits(A)[rows], inputs.bits(W1), inputs.bits(W2),
+                     rows, what)
+    return Y
+
+
+def _verify_ablation(orc, Y, g, u, sub, hW1, hW2, rows, what):
+    """Rows `rows` of the ablation's Gate, Up and Y (device) against the oracle,
+    given those rows of A (`sub`) and the weights as bf16 bits."""
     g_ref, u_ref, y_ref = orc.swiglu_materialised(sub, hW1, hW2)
     gb, ub, yb = bits_of(g)[rows], bits_of(u)[rows], bits_of(Y)[rows]
     # the intermediates: fp32 accumulation + one rounding, against the exact sums
@@ -316,7 +337,6 @@ def _check_ablation(orc, A, W1, W2, rows, dev, what, use_ws=False):
     assert not (bad & same).any(), f"{what}: mismatch not explained by intermediate rounding"
     print(f"  {what}: intermediates differing from the oracle's rounding "
           f"{int((~same).sum())} of {same.size}, y mismatches {int(bad.sum())}", flush=True)
-    return Y
 
 
 @pytest.mark.parametrize("M,K,N", [(5, 16, 24), (130, 200, 72), (257, 136, 264),

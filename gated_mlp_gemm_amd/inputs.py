@@ -84,6 +84,23 @@ def make_mlp_inputs(M: int, K: int, N: int, seed: int):
     return A, W1, W2, W3
 
 
+def device_inputs(M: int, K: int, N: int, seed: int, device):
+    """The recipe of make_inputs drawn by a seeded generator on `device`
+    (A [M,K], W1 [K,N], W2 [K,N], bf16, in that order): for operands of
+    several GiB, which the CPU generator would take minutes to draw.  The
+    numbers differ from make_inputs' for the same seed (another generator);
+    the oracle gets the drawn values copied to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    A = torch.randn(M, K, dtype=torch.float32, device=device, generator=g).to(torch.bfloat16)
+    root_k = math.sqrt(K) if K > 0 else 1.0
+    W1 = (torch.randn(K, N, dtype=torch.float32, device=device, generator=g) / root_k).to(
+        torch.bfloat16)
+    W2 = (torch.randn(K, N, dtype=torch.float32, device=device, generator=g) / root_k).to(
+        torch.bfloat16)
+    return A, W1, W2
+
+
 def workload_inputs(w: Workload):
     return make_inputs(w.M, w.K, w.N, w.seed)
 

@@ -1,0 +1,172 @@
+"""Operands beyond 4 GiB: the 64-bit bases of the weight and activation panels
+and of the output tiles (every in-kernel offset is 32 bits, taken from a
+per-panel or per-tile base), at the largest K the library accepts.
+
+Inputs are drawn on the device (the make_inputs recipe with a device
+generator: several GiB would take the CPU generator minutes); the oracle gets
+the drawn values copied to the host, and the parity predicate is the one of
+the other parity tests:  |y - ref| <= max(1e-3, 1e-2 |ref|).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as oracle_pkg
+from gated_mlp_gemm_amd import inputs
+from gated_mlp_gemm_amd import swiglu as sw
+from test_gpu_parity import (_intermediate_within_bound, announce, assert_parity, ulp_distance,
+                             workspace_for)
+
+pytestmark = pytest.mark.gpu
+
+GIB = 1 << 30
+K_MAX = 1 << 21          # largest K swiglu_fused_gemm accepts
+
+
+@pytest.fixture(autouse=True)
+def _default_dispatch(monkeypatch):
+    monkeypatch.delenv("SWIGLU_M_SWITCH", raising=False)
+    monkeypatch.delenv("SWIGLU_I_TILE", raising=False)
+    monkeypatch.delenv("SWIGLU_TAIL", raising=False)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_pkg.load()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    sw.load_library()
+    return torch.device("cuda:0")
+
+
+def _u16(t: torch.Tensor) -> np.ndarray:
+    return inputs.bits(t.detach().cpu())
+
+
+def _run(A, Wf, variant):
+    ws = None
+    if variant.endswith("+ws"):
+        variant = variant[:-3]
+        ws = workspace_for(A.shape[0], Wf.shape[0] // 2, A.shape[1], variant, A.device)
+    Y = sw.swiglu_fused_gemm(A, Wf, variant=variant, workspace=ws)
+    torch.cuda.synchronize()
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# K at its maximum: W1 and W2 of 4 GiB each, the packed weight 8 GiB, so the
+# weight panels of the later tile columns start beyond 4 GiB
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def max_k(dev):
+    M, K, N = 130, K_MAX, 1024
+    announce(f"inputs M={M} K={K} N={N} (W_fused {2 * N * K * 2 / GIB:.0f} GiB), device draw")
+    A, W1, W2 = inputs.device_inputs(M, K, N, seed=21, device=dev)
+    Wf = sw.swiglu_pack_weights(W1, W2)
+    torch.cuda.synchronize()
+    assert Wf.numel() * 2 > 4 * GIB
+    d = dict(M=M, K=K, N=N, A=A, Wf=Wf, hA=_u16(A), hW1=_u16(W1), hW2=_u16(W2), ref={})
+    del W1, W2
+    yield d
+    d.clear()
+    torch.cuda.empty_cache()
+
+
+def _max_k_reference(orc, d, M):
+    """Whole rows (every tile column, so every weight panel): the first, the
+    middle and the last (ragged tile row at M = 130)."""
+    if M not in d["ref"]:
+        rows = np.unique(np.array([0, M // 2, M - 1]))
+        announce(f"oracle rows {list(rows)}, M={M} K={d['K']}")
+        d["ref"][M] = (rows, orc.swiglu_rows(d["hA"][:M], d["hW1"], d["hW2"], rows))
+    return d["ref"][M]
+
+
+@pytest.mark.parametrize("M", [8, 130])
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
+def test_weights_beyond_4gib_at_max_k(dev, orc, max_k, M, variant):
+    d = max_k
+    rows, ref_rows = _max_k_reference(orc, d, M)
+    announce(f"fused {variant} M={M} K={d['K']} N={d['N']}: "
+             + sw.swiglu_describe_launch(M, d["N"], d["K"], variant.split("+")[0]))
+    Y = _run(d["A"][:M], d["Wf"], variant)
+    assert_parity(_u16(Y)[rows], ref_rows, f"{variant} M={M} rows")
+
+
+# ---------------------------------------------------------------------------
+# M near 2^20: A (4 GiB + a ragged tail of 37 rows) and Y (4.5 GiB) both
+# extend past 4 GiB, so the late tile rows' A panels and output tiles start
+# there
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def big_m(dev, orc):
+    M, K, N = (1 << 20) + 37, 2048, 2304
+    announce(f"inputs M={M} K={K} N={N} (A {M * K * 2 / GIB:.2f} GiB, "
+             f"Y {M * N * 2 / GIB:.2f} GiB), device draw")
+    A, W1, W2 = inputs.device_inputs(M, K, N, seed=22, device=dev)
+    Wf = sw.swiglu_pack_weights(W1, W2)
+    torch.cuda.synchronize()
+    assert A.numel() * 2 > 4 * GIB and M * N * 2 > 4 * GIB
+    rng = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 38, M - 2, M - 1],
+                                     rng.integers(M - (1 << 17), M, 4)]))
+    pr = rng.integers(0, M, 2000)
+    pc = rng.integers(0, N, 2000)
+    # the oracle needs only the sampled rows of A
+    hA_rows = _u16(A[torch.from_numpy(rows).to(dev)])
+    hA_pts = _u16(A[torch.from_numpy(pr).to(dev)])
+    hW1, hW2 = _u16(W1), _u16(W2)
+    announce(f"oracle rows {list(rows)} and {pr.size} points")
+    ref_rows = orc.swiglu_rows(hA_rows, hW1, hW2, np.arange(rows.size))
+    ref_pts = orc.swiglu_points(hA_pts, hW1, hW2, np.arange(pr.size), pc)
+    d = dict(M=M, K=K, N=N, A=A, Wf=Wf, rows=rows, pr=pr, pc=pc, hA_rows=hA_rows, hW1=hW1,
+             hW2=hW2, ref_rows=ref_rows, ref_pts=ref_pts)
+    del W1, W2
+    yield d
+    d.clear()
+    torch.cuda.empty_cache()
+
+
+def _sampled(Y, d):
+    dv = Y.device
+    yr = _u16(Y[torch.from_numpy(d["rows"]).to(dv)])
+    yp = _u16(Y[torch.from_numpy(d["pr"]).to(dv), torch.from_numpy(d["pc"]).to(dv)])
+    return yr, yp
+
+
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
+def test_activations_and_output_beyond_4gib(dev, big_m, variant):
+    d = big_m
+    announce(f"fused {variant} M={d['M']} K={d['K']} N={d['N']}: "
+             + sw.swiglu_describe_launch(d["M"], d["N"], d["K"], variant.split("+")[0]))
+    Y = _run(d["A"], d["Wf"], variant)
+    yr, yp = _sampled(Y, d)
+    del Y
+    assert_parity(yr, d["ref_rows"], f"{variant} rows {list(d['rows'])}")
+    assert_parity(yp, d["ref_pts"], f"{variant} points")
+
+
+def test_ablation_beyond_4gib(dev, orc, big_m):
+    """The unfused ablation (Gate, Up and Y each 4.5 GiB) with the workspace
+    the benchmark gives it: sampled rows of all three against the oracle."""
+    d = big_m
+    announce(f"ablation M={d['M']} K={d['K']} N={d['N']}")
+    ws = workspace_for(d["M"], d["N"], d["K"], "ablation", dev)
+    Y, g, u = sw.swiglu_unfused_ablation(d["A"], d["Wf"], workspace=ws)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(d["rows"]).to(dev)
+    gb, ub, yb = _u16(g[idx]), _u16(u[idx]), _u16(Y[idx])
+    del Y, g, u
+    sub = d["hA_rows"]
+    g_ref, u_ref, y_ref = orc.swiglu_materialised(sub, d["hW1"], d["hW2"])
+    _intermediate_within_bound(orc, sub, d["hW1"], gb, "ablation gate")
+    _intermediate_within_bound(orc, sub, d["hW2"], ub, "ablation up")
+    same = (gb == g_ref) & (ub == u_ref)
+    assert ulp_distance(yb, y_ref)[same].max(initial=0) <= 1
+    assert not (oracle_pkg.mismatches(yb, y_ref) & same).any()
+

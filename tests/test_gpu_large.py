@@ -170,3 +170,86 @@ def test_ablation_beyond_4gib(dev, orc, big_m):
     assert ulp_distance(yb, y_ref)[same].max(initial=0) <= 1
     assert not (oracle_pkg.mismatches(yb, y_ref) & same).any()
 
+
+
+def _amax_exp(t: torch.Tensor) -> int:
+    return sw.swiglu_fp8_scale_exp(float(t.abs().max()))
+
+
+# ---------------------------------------------------------------------------
+# FP8: A8 (4 GiB + 37 rows of codes, quantized from 8 GiB of bf16) and Y
+# (9 GiB) beyond 4 GiB; the oracle quantizes the host values itself
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def big_fp8(dev, orc):
+    M, K, N = (1 << 21) + 37, 2048, 2304
+    announce(f"inputs M={M} K={K} N={N} (A8 {M * K / GIB:.2f} GiB, Y {M * N * 2 / GIB:.2f} GiB)")
+    A, W1, W2 = inputs.device_inputs(M, K, N, seed=23, device=dev)
+    a_exp = _amax_exp(A)
+    w_exp = max(_amax_exp(W1), _amax_exp(W2))
+    Wf = sw.swiglu_pack_weights(W1, W2)
+    A8 = sw.swiglu_quantize_fp8(A, a_exp)
+    W8 = sw.swiglu_quantize_fp8(Wf, w_exp)
+    torch.cuda.synchronize()
+    assert A8.numel() > 4 * GIB
+    rng = np.random.default_rng(23)
+    rows = np.unique(np.concatenate([[0, M // 2, M - 38, M - 1], rng.integers(M - (1 << 18), M, 3)]))
+    idx = torch.from_numpy(rows).to(dev)
+    hA_rows = _u16(A[idx])
+    dA8_rows = A8[idx].cpu().numpy()
+    hW1, hW2 = _u16(W1), _u16(W2)
+    del A, W1, W2, Wf
+    torch.cuda.empty_cache()
+    hA8_rows = orc.quantize_fp8(hA_rows, a_exp)
+    hWT8 = orc.quantize_fp8(np.ascontiguousarray(orc.pack(hW1, hW2).T), w_exp)
+    announce(f"oracle rows {list(rows)}, a_exp={a_exp} w_exp={w_exp}")
+    ref = orc.swiglu_fp8(hA8_rows, hWT8, a_exp, w_exp)
+    d = dict(M=M, K=K, N=N, A8=A8, W8=W8, a_exp=a_exp, w_exp=w_exp, rows=rows, idx=idx,
+             dA8_rows=dA8_rows, hA8_rows=hA8_rows, ref=ref)
+    yield d
+    d.clear()
+    torch.cuda.empty_cache()
+
+
+def test_fp8_quantizer_beyond_4gib(dev, big_fp8):
+    d = big_fp8
+    assert np.array_equal(d["dA8_rows"], d["hA8_rows"]), "quantized rows differ from the oracle's"
+
+
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
+def test_fp8_beyond_4gib(dev, big_fp8, variant):
+    d = big_fp8
+    v = variant.split("+")[0]
+    ws = workspace_for(d["M"], d["N"], d["K"], "fp8", dev) if variant.endswith("+ws") else None
+    announce(f"fp8 {variant} M={d['M']} K={d['K']} N={d['N']}")
+    Y = sw.swiglu_fused_gemm_fp8(d["A8"], d["W8"], d["a_exp"], d["w_exp"], variant=v,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    yb = _u16(Y[d["idx"]])
+    del Y
+    assert_parity(yb, d["ref"], f"fp8 {variant} rows {list(d['rows'])}")
+
+
+# ---------------------------------------------------------------------------
+# The gated MLP block on the large-M operands: H (4.5 GiB) and Out (4 GiB +
+# 37 rows) beyond 4 GiB; the down projection reads H as its activation
+# ---------------------------------------------------------------------------
+def test_mlp_block_beyond_4gib(dev, orc, big_m):
+    d = big_m
+    M, K, N = d["M"], d["K"], d["N"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(24)
+    W3 = (torch.randn(N, K, device=dev, generator=g) / N ** 0.5).to(torch.bfloat16)
+    W3t = W3.t().contiguous()
+    n = sw.swiglu_workspace_size(M, N, K, "down_proj")
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev) if n else None
+    announce(f"gated_mlp auto+ws M={M} K={K} N={N}")
+    Out, H = sw.swiglu_gated_mlp(d["A"], d["Wf"], W3t, variant="auto", workspace=ws)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(d["rows"]).to(dev)
+    hb, ob = _u16(H[idx]), _u16(Out[idx])
+    del Out, H
+    h_ref = orc.swiglu_rows(d["hA_rows"], d["hW1"], d["hW2"], np.arange(d["rows"].size))
+    out_ref = orc.down_proj(h_ref, _u16(W3))
+    assert_parity(hb, h_ref, f"H rows {list(d['rows'])}")
+    assert_parity(ob, out_ref, f"Out rows {list(d['rows'])}")

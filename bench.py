@@ -35,6 +35,11 @@ of M, once with the library's own choice and once forced (SWIGLU_I_TILE,
 SWIGLU_TAIL) through each tile shape and tail schedule, one JSON line per
 (shape, M, schedule): the data the schedule cost model is fitted to
 (``python -m gated_mlp_gemm_amd.schedule_fit FILE``).
+
+--launch-cost times the fused call (bf16 and FP8) on warm inputs through the
+Python binding, straight through the C ABI, and replayed from a HIP graph:
+the host cost per call and where it stops mattering (one JSON line per
+workload; by default the M=128 one).
 """
 from __future__ import annotations
 
@@ -82,6 +87,9 @@ def parse():
     p.add_argument("--fp8", action="store_true",
                    help="time the fused GEMM on FP8 (E4M3) operands against bf16, five workloads")
     p.add_argument("--fp8-workloads", default="0,1,2,3,4")
+    p.add_argument("--launch-cost", action="store_true",
+                   help="host cost per call: binding vs C-ABI vs HIP-graph replay (warm inputs)")
+    p.add_argument("--launch-workloads", default="0")
     p.add_argument("--schedule-calibration", action="store_true",
                    help="time variant I under every forced tile shape / tail schedule")
     p.add_argument("--calibration-m",
@@ -263,6 +271,83 @@ def mlp_blocks(args):
         torch.cuda.empty_cache()
 
 
+def launch_cost(args, calls=3000, per_graph=20, replays=100):
+    """Per-call cost of the fused call, bf16 and FP8, on warm inputs (one copy):
+    through the Python binding and straight through the C ABI (host time of
+    `calls` back-to-back calls, and wall time to their completion), and
+    replayed from a HIP graph of `per_graph` captured calls.  One JSON line
+    per workload."""
+    import torch
+
+    from gated_mlp_gemm_amd import inputs
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    lib = sw.load_library()
+    dev = torch.device("cuda:0")
+
+    def loop(fn):
+        for _ in range(100):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        host = time.perf_counter() - t
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t
+        return round(host / calls * 1e6, 2), round(wall / calls * 1e6, 2)
+
+    def graph(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(replays):
+            g.replay()
+        torch.cuda.synchronize()
+        return round((time.perf_counter() - t) / (replays * per_graph) * 1e6, 2)
+
+    for idx in (int(x) for x in args.launch_workloads.split(",")):
+        w = inputs.WORKLOADS[idx]
+        M, K, N = w.M, w.K, w.N
+        A, W1, W2 = inputs.workload_inputs(w)
+        Ad = A.to(dev)
+        Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+        a_exp = sw.swiglu_fp8_scale_exp(float(Ad.float().abs().max()))
+        w_exp = sw.swiglu_fp8_scale_exp(float(Wf.float().abs().max()))
+        A8, W8 = sw.swiglu_quantize_fp8(Ad, a_exp), sw.swiglu_quantize_fp8(Wf, w_exp)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        s = torch.cuda.current_stream(dev).cuda_stream
+        pa, pw, p8a, p8w, py = Ad.data_ptr(), Wf.data_ptr(), A8.data_ptr(), W8.data_ptr(), Y.data_ptr()
+        paths = {
+            "bf16": (lambda: sw.swiglu_fused_gemm(Ad, Wf, Y=Y),
+                     lambda: lib.swiglu_fused_gemm(pa, pw, py, M, N, K, 0, None, 0, s)),
+            "fp8": (lambda: sw.swiglu_fused_gemm_fp8(A8, W8, a_exp, w_exp, Y=Y),
+                    lambda: lib.swiglu_fused_gemm_fp8(p8a, p8w, py, M, N, K, a_exp, w_exp, 0,
+                                                      None, 0, s)),
+        }
+        rec = {"workload": f"fused SwiGLU GEMM M={M} K={K} N={N} (seed {w.seed}), warm inputs",
+               "M": M, "K": K, "N": N, "calls": calls, "graph_calls": per_graph * replays,
+               "us_per_call": {}}
+        for name, (bound, direct) in paths.items():
+            bh, bw = loop(bound)
+            ch, cw = loop(direct)
+            rec["us_per_call"][name] = {"binding_host": bh, "binding_wall": bw, "c_abi_host": ch,
+                                        "c_abi_wall": cw, "graph_replay": graph(bound)}
+        print(json.dumps(rec), flush=True)
+
+
 def fp8_compare(args):
     """The fused GEMM (AUTO, i.e. variant I) on FP8 E4M3 operands against the
     same call on bf16, and variant S on FP8, per workload (one JSON line each).  The operands are quantized once,
@@ -409,6 +494,9 @@ def main():
         return
     if args.schedule_calibration:
         schedule_calibration(args)
+        return
+    if args.launch_cost:
+        launch_cost(args)
         return
 
     import numpy as np

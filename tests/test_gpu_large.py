@@ -253,3 +253,32 @@ def test_mlp_block_beyond_4gib(dev, orc, big_m):
     out_ref = orc.down_proj(h_ref, _u16(W3))
     assert_parity(hb, h_ref, f"H rows {list(d['rows'])}")
     assert_parity(ob, out_ref, f"Out rows {list(d['rows'])}")
+
+
+# ---------------------------------------------------------------------------
+# The strided entry point at its largest row pitches: A a column slice of a
+# [M, 2^21] matrix (lda = 2^21), Y a column slice of a [M, 2^22] buffer
+# (ldy = 2^22), where a 256-row output tile spans 2^31 bytes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
+def test_strided_at_max_pitches(dev, orc, variant):
+    M, K, N = 300, 200, 136
+    lda, ldy = 1 << 21, 1 << 22
+    announce(f"strided {variant} M={M} K={K} N={N} lda={lda} ldy={ldy}")
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=25)
+    Abig = torch.full((M, lda), 1e4, dtype=torch.bfloat16, device=dev)
+    Abig[:, 8:8 + K] = A.to(dev)
+    sentinel = 0x7F7F
+    Ybig = torch.full((M, ldy), sentinel, dtype=torch.int16, device=dev)
+    Yv = Ybig.view(torch.bfloat16)[:, 16:16 + N]
+    Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    v = variant.split("+")[0]
+    ws = workspace_for(M, N, K, v, dev) if variant.endswith("+ws") else None
+    sw.swiglu_fused_gemm_strided(Abig[:, 8:8 + K], Wf, Yv, variant=v, workspace=ws)
+    torch.cuda.synchronize()
+    stray = int((Ybig[:, :16] != sentinel).sum()) + int((Ybig[:, 16 + N:] != sentinel).sum())
+    assert stray == 0, f"{stray} stores outside the Y view"
+    yb = _u16(Yv)
+    del Abig, Ybig
+    assert_parity(yb, orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2)),
+                  f"strided {variant} at max pitches")

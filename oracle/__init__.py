@@ -77,6 +77,8 @@ class Oracle:
                                             i64, nf64, nu16]
         lib.swo_swiglu_interleaved.argtypes = [_U16P, _U16P, i64, i64, i64,
                                                nf64, nu16]
+        lib.swo_swiglu_block.argtypes = [_U16P, _U16P, _U16P, i64, i64, _I64P, i64,
+                                         i64, i64, nf64, nu16]
         lib.swo_swiglu_points.argtypes = [_U16P, _U16P, _U16P, i64, i64,
                                           _I64P, _I64P, i64, nf64, nu16]
         lib.swo_pack.argtypes = [_U16P, _U16P, _U16P, i64, i64]
@@ -151,6 +153,20 @@ class Oracle:
         y = np.empty((rows.size, N), dtype=np.uint16)
         y64 = np.empty((rows.size, N), dtype=np.float64) if want_f64 else None
         self._lib.swo_swiglu_rows(A, W1, W2, N, K, rows, rows.size, y64, y)
+        return (y, y64) if want_f64 else y
+
+    def swiglu_block(self, A, W1, W2, rows, c0: int, c1: int, want_f64: bool = False):
+        """Outputs Y[rows, c0:c1] (a column window of whole rows)."""
+        A, W1, W2 = self._u16(A), self._u16(W1), self._u16(W2)
+        K = A.shape[1]
+        N = W1.shape[1]
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < A.shape[0])
+        assert 0 <= c0 <= c1 <= N
+        y = np.empty((rows.size, c1 - c0), dtype=np.uint16)
+        y64 = np.empty((rows.size, c1 - c0), dtype=np.float64) if want_f64 else None
+        if rows.size and c1 > c0:
+            self._lib.swo_swiglu_block(A, W1, W2, N, K, rows, rows.size, c0, c1, y64, y)
         return (y, y64) if want_f64 else y
 
     def swiglu_interleaved(self, A, Wf, want_f64: bool = False):

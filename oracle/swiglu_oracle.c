@@ -152,13 +152,14 @@ double swo_silu(double x)
 /* ------------------------------------------------------------------------ */
 
 /*
- * One output row of D = A . B for a row-major bf16 B of shape [K, ncols]:
- * d[c] = sum_{k=0}^{K-1} A[m,k] B[k,c], double, k ascending.  The loop runs
- * c innermost so that B is read along its rows; the order of the terms of
- * each sum is still k = 0, 1, ..., K-1.
+ * One output row of D = A . B over a window of ncols columns of a row-major
+ * bf16 B whose rows are ldb elements apart (B points at the window's first
+ * column): d[c] = sum_{k=0}^{K-1} A[m,k] B[k,c], double, k ascending.  The
+ * loop runs c innermost so that B is read along its rows; the order of the
+ * terms of each sum is still k = 0, 1, ..., K-1.
  */
-static void row_times_matrix(const uint16_t *a_row, const uint16_t *B,
-                             int64_t K, int64_t ncols, double *d)
+static void row_times_window(const uint16_t *a_row, const uint16_t *B,
+                             int64_t K, int64_t ncols, int64_t ldb, double *d)
 {
     for (int64_t c = 0; c < ncols; ++c) d[c] = 0.0;
 #ifdef PLANT_SKIP_LAST_K            /* drops the k = K-1 term              */
@@ -166,11 +167,17 @@ static void row_times_matrix(const uint16_t *a_row, const uint16_t *B,
 #endif
     for (int64_t k = 0; k < K; ++k) {
         const double a = swo_bf16_to_double(a_row[k]);
-        const uint16_t *b = B + k * ncols;
+        const uint16_t *b = B + k * ldb;
         for (int64_t c = 0; c < ncols; ++c) {
             d[c] += a * swo_bf16_to_double(b[c]);
         }
     }
+}
+
+static void row_times_matrix(const uint16_t *a_row, const uint16_t *B,
+                             int64_t K, int64_t ncols, double *d)
+{
+    row_times_window(a_row, B, K, ncols, ncols, d);
 }
 
 /* D[M, ncols] = A[M,K] . B[K,ncols] in double (exposed for the pins). */
@@ -225,6 +232,41 @@ void swo_swiglu_rows(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
             for (int64_t n = 0; n < N; ++n) {
                 gate_up_to_y(g[n], u[n], y64 ? y64 + i * N + n : NULL,
                              ybf ? ybf + i * N + n : NULL);
+            }
+        }
+        free(g);
+        free(u);
+    }
+}
+
+/*
+ * Separate formulation over a column window: for each listed row m, the
+ * outputs n in [c0, c1) (the same sums as swo_swiglu_rows, fewer columns).
+ * Outputs are indexed by position: y64[i*(c1-c0) + j], ybf[...] hold
+ * Y[rows[i], c0 + j] (either may be NULL).
+ */
+void swo_swiglu_block(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
+                      int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                      int64_t c0, int64_t c1, double *y64, uint16_t *ybf)
+{
+    const int64_t w = c1 - c0;
+#ifdef PLANT_BLOCK_OFFSET           /* the window starts one column late   */
+    const int64_t first = c0 + 1 < N ? c0 + 1 : c0;
+#else
+    const int64_t first = c0;
+#endif
+    #pragma omp parallel
+    {
+        double *g = (double *)malloc((size_t)w * sizeof(double));
+        double *u = (double *)malloc((size_t)w * sizeof(double));
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t m = rows[i];
+            row_times_window(A + m * K, W1 + first, K, w, N, g);
+            row_times_window(A + m * K, W2 + first, K, w, N, u);
+            for (int64_t j = 0; j < w; ++j) {
+                gate_up_to_y(g[j], u[j], y64 ? y64 + i * w + j : NULL,
+                             ybf ? ybf + i * w + j : NULL);
             }
         }
         free(g);

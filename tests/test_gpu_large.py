@@ -258,13 +258,33 @@ def test_mlp_block_beyond_4gib(dev, orc, big_m):
 # ---------------------------------------------------------------------------
 # The strided entry point at its largest row pitches: A a column slice of a
 # [M, 2^21] matrix (lda = 2^21), Y a column slice of a [M, 2^22] buffer
-# (ldy = 2^22), where a 256-row output tile spans 2^31 bytes
+# (ldy = 2^22).  A whole 256x256 tile with 256 valid rows then spans 2^31
+# bytes of Y, which is the largest range an epilogue's buffer resource takes
+# (the range limit equals the out-of-range offset): forced through the
+# whole-tile epilogue and through the split tail's reduction kernel.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("variant", ["i", "i+ws", "s"])
-def test_strided_at_max_pitches(dev, orc, variant):
+@pytest.mark.parametrize("variant,tile,tail", [("i", "256", "whole"), ("i+ws", "256", "split"),
+                                               ("i", None, None), ("i+ws", None, None),
+                                               ("s", None, None)])
+def test_strided_at_max_pitches(dev, orc, variant, tile, tail, monkeypatch):
     M, K, N = 300, 200, 136
     lda, ldy = 1 << 21, 1 << 22
-    announce(f"strided {variant} M={M} K={K} N={N} lda={lda} ldy={ldy}")
+    if tile is None:
+        monkeypatch.delenv("SWIGLU_I_TILE", raising=False)
+        monkeypatch.delenv("SWIGLU_TAIL", raising=False)
+    else:
+        monkeypatch.setenv("SWIGLU_I_TILE", tile)
+        monkeypatch.setenv("SWIGLU_TAIL", tail)
+    v = variant.split("+")[0]
+    ws = workspace_for(M, N, K, v, dev) if variant.endswith("+ws") else None
+    desc = sw.swiglu_describe_launch(M, N, K, v, 0 if ws is None else ws.numel())
+    announce(f"strided {variant} M={M} K={K} N={N} lda={lda} ldy={ldy}: {desc}")
+    if tail == "whole":
+        # tile row 0 is a whole 256x256 tile with 256 valid rows
+        assert desc.startswith("gemm_tiles_kernel<256x256x64,") and "(4 tiles;" in desc, desc
+    elif tail == "split":
+        assert desc.startswith("gemm_tiles_kernel<256x256x64,") and "split_reduce_kernel" in desc \
+            and "(0 whole tiles + 4 tiles split" in desc, desc
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=25)
     Abig = torch.full((M, lda), 1e4, dtype=torch.bfloat16, device=dev)
     Abig[:, 8:8 + K] = A.to(dev)
@@ -272,8 +292,6 @@ def test_strided_at_max_pitches(dev, orc, variant):
     Ybig = torch.full((M, ldy), sentinel, dtype=torch.int16, device=dev)
     Yv = Ybig.view(torch.bfloat16)[:, 16:16 + N]
     Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
-    v = variant.split("+")[0]
-    ws = workspace_for(M, N, K, v, dev) if variant.endswith("+ws") else None
     sw.swiglu_fused_gemm_strided(Abig[:, 8:8 + K], Wf, Yv, variant=v, workspace=ws)
     torch.cuda.synchronize()
     stray = int((Ybig[:, :16] != sentinel).sum()) + int((Ybig[:, 16 + N:] != sentinel).sum())
@@ -281,4 +299,4 @@ def test_strided_at_max_pitches(dev, orc, variant):
     yb = _u16(Yv)
     del Abig, Ybig
     assert_parity(yb, orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2)),
-                  f"strided {variant} at max pitches")
+                  f"strided {variant} tile={tile} tail={tail} at max pitches")

@@ -8,9 +8,13 @@ mismatch), with an absolute floor of 1e-3 for outputs near zero:
     |y_gpu - y_ref| <= max(1e-3, 1e-2 |y_ref|)   for every compared element,
 
 where y_ref is the oracle's bf16-rounded output.  The pack is compared bit
-for bit.  Small shapes are checked in full; the five benchmark workloads at
-their full sizes are checked on whole sampled rows plus random single outputs
-(computed one by one by the oracle), and variants I and S are compared with
+for bit.  Small shapes are checked in full.  The five benchmark workloads
+run at their full sizes: the three smaller ones (M=128 K=896 N=4864, M=2048
+K=1536 N=8960, M=512 K=3584 N=18944) are compared with the oracle over the
+whole output; the two large ones (M=8192 K=5120 N=13824, M=4096 K=8192
+N=29568) on one whole row in every 256-row band, every output tile of the
+partly idle last round of tiles (the tiles the schedule splits or quarters)
+in full, and random single outputs; variants I and S are also compared with
 each other over the whole output.
 """
 from __future__ import annotations
@@ -219,7 +223,10 @@ def workload(request, dev):
     Wf = sw.swiglu_pack_weights(W1d, W2d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1000 + w.seed)
-    rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], rng.integers(0, w.M, 4)]))
+    # one row in every 256-row band (the tall tiles' height), and the edges
+    bands = np.arange(0, w.M, 256)
+    band_rows = bands + rng.integers(0, 256, bands.size) % np.minimum(256, w.M - bands)
+    rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], band_rows]))
     pr = rng.integers(0, w.M, 20000)
     pc = rng.integers(0, w.N, 20000)
     # edges of the output: last column, first column of the second tile column
@@ -230,24 +237,102 @@ def workload(request, dev):
                 rows=rows, pr=pr, pc=pc, cache={})
 
 
+# Whole-output comparison up to this many GFLOP of oracle work per workload
+# (the oracle runs ~26 GFLOP/s on 16 host cores; the three smaller workloads
+# cost 2.2, 112.7 and 139.1 GFLOP).
+WHOLE_OUTPUT_GFLOP = 200.0
+
+
+def _whole(d) -> bool:
+    return d["w"].flops / 1e9 <= WHOLE_OUTPUT_GFLOP
+
+
+def tile_order(t, tiles_m, tiles_n, group_m=8):
+    """(tile row, tile column) of tile index t in the GEMM kernels' tile
+    order: groups of group_m tile rows, column by column inside a group."""
+    width = group_m * tiles_n
+    first_m = (t // width) * group_m
+    rows_in_group = min(tiles_m - first_m, group_m)
+    i = t % width
+    return first_m + i % rows_in_group, i // rows_in_group
+
+
+def tail_windows(M, N, K, ws_bytes):
+    """Output windows (row range, Y column range) of the tiles of variant I's
+    partly idle last round (split along K or quartered), read from the launch
+    the library describes: [] when every tile runs whole."""
+    import re
+    desc = sw.swiglu_describe_launch(M, N, K, "i", ws_bytes)
+    shape = re.search(r"<(\d+)x(\d+)x\d+,", desc)
+    tail = re.search(r"\((\d+) (?:whole )?tiles \+ (\d+) tiles", desc)
+    if not (shape and tail):
+        return desc, []
+    bm, bn = int(shape.group(1)), int(shape.group(2))
+    dp, L = int(tail.group(1)), int(tail.group(2))
+    tiles_m, tiles_n = -(-M // bm), -(-2 * N // bn)
+    assert dp + L == tiles_m * tiles_n, desc
+    out = []
+    for t in range(dp, dp + L):
+        tm, tn = tile_order(t, tiles_m, tiles_n)
+        r0, c0 = tm * bm, tn * bn // 2
+        out.append(((r0, min(r0 + bm, M)), (c0, min(c0 + bn // 2, N))))
+    return desc, out
+
+
 def _ref_samples(orc, d):
-    if "ref_rows" not in d["cache"]:
-        announce(f"oracle samples {d['w'].name}")
-        d["cache"]["ref_rows"] = orc.swiglu_rows(d["hA"], d["hW1"], d["hW2"], d["rows"])
-        d["cache"]["ref_pts"] = orc.swiglu_points(d["hA"], d["hW1"], d["hW2"], d["pr"], d["pc"])
-    return d["cache"]["ref_rows"], d["cache"]["ref_pts"]
+    c = d["cache"]
+    if "ref_rows" in c:
+        return
+    w = d["w"]
+    if _whole(d):
+        announce(f"oracle whole output {w.name} ({w.flops / 1e9:.1f} GFLOP)")
+        c["ref_full"] = orc.swiglu(d["hA"], d["hW1"], d["hW2"])
+        c["ref_rows"] = c["ref_full"][d["rows"]]
+        c["ref_pts"] = c["ref_full"][d["pr"], d["pc"]]
+        c["ref_tail"] = []
+        return
+    announce(f"oracle rows {list(d['rows'])}, points and tail tiles {w.name}")
+    c["ref_rows"] = orc.swiglu_rows(d["hA"], d["hW1"], d["hW2"], d["rows"])
+    c["ref_pts"] = orc.swiglu_points(d["hA"], d["hW1"], d["hW2"], d["pr"], d["pc"])
+    ws = sw.swiglu_workspace_size(w.M, w.N, w.K, "i")
+    desc, wins = tail_windows(w.M, w.N, w.K, ws)
+    announce(f"{len(wins)} tail tiles of {desc}")
+    # merge the windows of one tile row that touch into one oracle call
+    by_rows = {}
+    for (r0, r1), (c0, c1) in wins:
+        by_rows.setdefault((r0, r1), []).append((c0, c1))
+    c["ref_tail"] = []
+    for (r0, r1), cols in sorted(by_rows.items()):
+        cols.sort()
+        merged = [list(cols[0])]
+        for c0, c1 in cols[1:]:
+            if c0 == merged[-1][1]:
+                merged[-1][1] = c1
+            else:
+                merged.append([c0, c1])
+        for c0, c1 in merged:
+            ref = orc.swiglu_block(d["hA"], d["hW1"], d["hW2"], np.arange(r0, r1), c0, c1)
+            c["ref_tail"].append(((r0, r1), (c0, c1), ref))
 
 
 @pytest.mark.parametrize("variant", ["i", "i+ws", "s", "auto+ws"])
 def test_workload_full_size(dev, orc, workload, variant):
     d = workload
     w = d["w"]
-    ref_rows, ref_pts = _ref_samples(orc, d)
+    _ref_samples(orc, d)
+    c = d["cache"]
     announce(f"fused {variant} {w.name}")
     Y = run_fused(d["A"], d["Wf"], variant)
     yb = bits_of(Y)
-    assert_parity(yb[d["rows"]], ref_rows, f"{variant} {w.name} rows {list(d['rows'])}")
-    assert_parity(yb[d["pr"], d["pc"]], ref_pts, f"{variant} {w.name} points")
+    if _whole(d):
+        assert_parity(yb, c["ref_full"], f"{variant} {w.name} whole output")
+    else:
+        assert_parity(yb[d["rows"]], c["ref_rows"], f"{variant} {w.name} rows {list(d['rows'])}")
+        assert_parity(yb[d["pr"], d["pc"]], c["ref_pts"], f"{variant} {w.name} points")
+        assert c["ref_tail"], "the large workloads have a partly idle last round"
+        for (r0, r1), (c0, c1), ref in c["ref_tail"]:
+            assert_parity(yb[r0:r1, c0:c1], ref, f"{variant} {w.name} tail tiles rows "
+                                                 f"{r0}..{r1 - 1} cols {c0}..{c1 - 1}")
     assert np.isfinite(oracle_pkg.bf16_bits_to_f64(yb)).all()
     d["cache"][f"Y_{variant}"] = yb
 

@@ -267,6 +267,28 @@ def check_pipeline_vs_numpy(orc):
             assert y[m, n] == b, (seed, m, n)
 
 
+def check_block_window_vs_numpy(orc):
+    """Column windows of listed rows: numpy float64 sums over the window's
+    columns (an independent contraction), and the same elements as the whole
+    rows (first, last, interior and one-column windows)."""
+    for seed, (M, K, N) in enumerate([(6, 40, 24), (13, 96, 72)]):
+        A = inputs.bits(inputs.random_bf16((M, K), 500 + seed))
+        W1 = inputs.bits(inputs.random_bf16((K, N), 600 + seed, 1.0 / math.sqrt(K)))
+        W2 = inputs.bits(inputs.random_bf16((K, N), 700 + seed, 1.0 / math.sqrt(K)))
+        a, w1, w2 = bits_to_f64(A), bits_to_f64(W1), bits_to_f64(W2)
+        rows = np.array([M - 1, 0, M // 2], dtype=np.int64)
+        full = orc.swiglu_rows(A, W1, W2, rows)
+        for c0, c1 in [(0, N), (0, 8), (N - 8, N), (5, 6), (3, N - 2)]:
+            y, y64 = orc.swiglu_block(A, W1, W2, rows, c0, c1, want_f64=True)
+            G, U = a[rows] @ w1[:, c0:c1], a[rows] @ w2[:, c0:c1]
+            with np.errstate(over="ignore"):
+                want = G / (1.0 + np.exp(-G)) * U
+            scale = (np.abs(a[rows]) @ np.abs(w1[:, c0:c1])) * \
+                (np.abs(a[rows]) @ np.abs(w2[:, c0:c1])) + 1e-300
+            assert np.all(np.abs(y64 - want) <= 1e-12 * scale), (seed, c0, c1)
+            assert np.array_equal(y, full[:, c0:c1]), (seed, c0, c1)
+
+
 def check_interleave_invariant(orc):
     for seed, (M, K, N) in enumerate([(5, 24, 8), (37, 120, 72), (9, 896, 40)]):
         A = inputs.bits(inputs.random_bf16((M, K), 100 + seed))
@@ -485,6 +507,7 @@ CHECKS = [
     check_hand_cases,
     check_matmul_vs_numpy,
     check_pipeline_vs_numpy,
+    check_block_window_vs_numpy,
     check_interleave_invariant,
     check_pack,
     check_pack_nk,
@@ -570,6 +593,7 @@ MUTANTS = [
     "PLANT_MLP_UNROUNDED_H",
     "PLANT_FP8_BIAS8",
     "PLANT_FP8_SCALE_ONCE",
+    "PLANT_BLOCK_OFFSET",
 ]
 
 

@@ -1,22 +1,31 @@
 """Benchmark of the fused SwiGLU GEMM on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX]
-                    [--variant auto|i|s] [--no-cpu-baseline]
+                    [--variant auto|i|s] [--no-cpu-baseline] [--no-per-workload]
     python bench.py --sweep [--sweep-m 128,256,...]
 
 A step is one pass of the hot path over one batch of synthetic input: the
 fused call Y = SiLU(A.W1) (.) (A.W2) with the M-based dispatch (the weight
-pack is offline and untimed).  The default workload is M=2048, K=1536,
-N=8960 (seed 1).  Inputs are resident in HBM before timing starts; the timed
-steps rotate over R copies of (A, weights, Y) whose total exceeds 512 MB, so
-the 256 MB Infinity Cache cannot hold the working set across steps.
+pack is offline and untimed).  The headline workload is the largest one,
+M=4096, K=8192, N=29568 (seed 4; a 72B-class gated MLP, 969 MB of packed
+weights).  Inputs are resident in HBM before timing starts; when a step's
+working set is below 512 MB the timed steps rotate over R copies of (A,
+weights, Y), so the 256 MB Infinity Cache cannot hold it across steps.
+
+Protocol: W warm-up steps, continued until at least --warmup-seconds of GPU
+work has run, then exactly K timed steps (HIP events on the launch stream):
+the headline.  Then AUTO again, variant I, variant S and the unfused ablation
+(two GEMMs + SiLU-mul from the same mainloop) run K-step loops in
+alternating repeats, whose medians give the speedup over the ablation.
 
 Prints ONE JSON line: TFLOP/s (4 M N K per step), the fraction of the bf16
-dense MFMA peak, the speedup over the unfused ablation (two GEMMs + SiLU-mul
-from the same mainloop, timed the same way), a roofline record for the fused
-kernel, the CPU oracle's throughput on a bounded sample, and for context the
-same call on FP8 E4M3 operands (`fp8`: operands quantized beforehand, and
-with the activation quantized inside each step).
+dense MFMA peak, the speedup over the unfused ablation, a roofline record for
+the fused call, `per_workload` sub-records for the other four workloads
+(AUTO / I / S / ablation medians and minima per call, TFLOP/s, fraction of
+peak, speedup), the CPU oracle's throughput on a bounded sample of the
+headline workload, and for context the same call on FP8 E4M3 operands
+(`fp8`: operands quantized beforehand, and with the activation quantized
+inside each step).
 
 --sweep instead times variant I, variant S and the ablation over a range of M
 for each of the five K x N shapes of the workloads (inputs drawn on the
@@ -61,20 +70,25 @@ METRIC = "fused SwiGLU-GEMM TFLOP/s + % bf16 MFMA peak; speedup vs unfused ablat
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    # The clock settles under sustained MFMA load within milliseconds (durations
-    # of back-to-back calls rise by ~10 % before levelling off), so the default
-    # warm-up and timed region are long enough to measure the steady state.
-    p.add_argument("--steps", type=int, default=1000)
-    p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", type=int, default=1)
+    # The clock settles under sustained MFMA load (durations of back-to-back
+    # calls rise by ~10 % before levelling off), so every warm-up also runs
+    # for at least --warmup-seconds of GPU work, whatever --warmup says.
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup-seconds", type=float, default=0.3,
+                   help="minimum GPU time of the headline's warm-up (partners: a quarter)")
+    p.add_argument("--repeats", type=int, default=5,
+                   help="alternating repeats of the partner loops (medians and minima)")
+    # the headline workload: M=4096 K=8192 N=29568, the largest configuration
+    p.add_argument("--workload", type=int, default=4)
+    p.add_argument("--no-per-workload", action="store_true",
+                   help="skip the sub-records of the other four workloads")
     p.add_argument("--variant", default="auto", choices=["auto", "i", "s"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the FP8 context timing of the default line")
-    p.add_argument("--no-warm", action="store_true",
-                   help="skip the warm (single cache-resident copy) loop (counter passes)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one device copy of known size (for HBM counter scaling)")
     p.add_argument("--sweep", action="store_true",
@@ -476,6 +490,127 @@ def traffic_record(variant: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _warm_up(step_fn, steps, min_s):
+    """`steps` untimed steps, continued until at least `min_s` seconds of GPU
+    work have run (the clock settles under sustained MFMA load: short runs
+    read fast).  Returns the number of steps run."""
+    import torch
+
+    s = 0
+    t0 = time.perf_counter()
+    while s < steps or time.perf_counter() - t0 < min_s:
+        step_fn(s)
+        s += 1
+        if s % 8 == 0:
+            torch.cuda.synchronize()   # so that wall time follows GPU time
+    torch.cuda.synchronize()
+    return s
+
+
+def _timed(step_fn, steps, stream, start=0):
+    """Milliseconds per step over `steps` back-to-back steps, HIP events on
+    `stream` (the stream the library launches on)."""
+    import torch
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(start, start + steps):
+        step_fn(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _alternating(paths, steps, stream, repeats):
+    """Per-step ms of each path over `repeats` rounds in which every path runs
+    one loop of `steps` steps in turn (so clock drift hits all paths alike):
+    {name: {"median": ms, "min": ms, "all": [ms, ...]}}."""
+    import statistics
+
+    runs = {name: [] for name in paths}
+    for r in range(repeats):
+        for name, fn in paths.items():
+            runs[name].append(_timed(fn, steps, stream, start=r * steps))
+    return {name: {"median": statistics.median(v), "min": min(v), "all": v}
+            for name, v in runs.items()}
+
+
+def _workload_record(args, idx, dev, stream):
+    """One workload (inputs drawn on the device with the workload's recipe and
+    seed): AUTO, variant I, variant S and the unfused ablation in alternating
+    repeats; per-call median and min, TFLOP/s and the fraction of the bf16
+    peak from the median, speedup over the ablation (median over median)."""
+    import torch
+
+    from gated_mlp_gemm_amd import inputs
+    from gated_mlp_gemm_amd import swiglu as sw
+
+    w = inputs.WORKLOADS[idx]
+    M, K, N = w.M, w.K, w.N
+    flops = 4 * M * N * K
+    A, W1, W2 = inputs.device_inputs(M, K, N, w.seed, dev)
+    Wf = sw.swiglu_pack_weights(W1, W2)
+    del W1, W2
+    step_bytes = 2 * (M * K + 2 * K * N + M * N)
+    R = max(1, -(-512 * 2 ** 20 // step_bytes))
+    copies = [(A, Wf)] + [(A.clone(), Wf.clone()) for _ in range(R - 1)]
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    gu = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    scratch = {v: sw.make_workspace(M, N, K, v, dev) for v in ("auto", "i", "ablation")}
+    torch.cuda.synchronize()
+
+    def fused(variant, wsname):
+        def step(s):
+            a, wf = copies[s % R]
+            sw.swiglu_fused_gemm(a, wf, Y=outs[s % R], variant=variant,
+                                 workspace=scratch.get(wsname))
+        return step
+
+    def ablation(s):
+        a, wf = copies[s % R]
+        sw.swiglu_unfused_ablation(a, wf, gate_ws=gu[0], up_ws=gu[1], Y=outs[s % R],
+                                   workspace=scratch["ablation"])
+
+    paths = {"auto": fused("auto", "auto"), "i": fused("i", "i"), "s": fused("s", None),
+             "ablation": ablation}
+    # loops of at least --steps steps and about 5 ms each
+    t0 = time.perf_counter()
+    for s in range(4):
+        paths["auto"](s)
+    torch.cuda.synchronize()
+    est_ms = (time.perf_counter() - t0) * 1e3 / 4
+    steps = max(args.steps, int(5.0 / max(est_ms, 1e-3)))
+    for fn in paths.values():
+        _warm_up(fn, args.warmup, args.warmup_seconds / 4)
+    t = _alternating(paths, steps, stream, args.repeats)
+    med = t["auto"]["median"]
+    tflops = flops / (med * 1e-3) / 1e12
+    ws = scratch["auto"]
+    rec = {
+        "workload": f"fused SwiGLU GEMM M={M} K={K} N={N} (seed {w.seed}, A~N(0,1), "
+                    f"W~N(0,1/K), bf16, drawn on the device)",
+        "M": M, "K": K, "N": N, "rotation_copies": R, "steps_per_loop": steps,
+        "repeats": args.repeats,
+        "us_per_call": {k: {"median": round(v["median"] * 1e3, 2), "min": round(v["min"] * 1e3, 2)}
+                        for k, v in t.items()},
+        "tflops": round(tflops, 2),
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "tflops_per_variant": {k: round(flops / (v["median"] * 1e-3) / 1e12, 2)
+                               for k, v in t.items()},
+        "speedup_vs_ablation": round(t["ablation"]["median"] / med, 4),
+        "speedup_s_vs_ablation": round(t["ablation"]["median"] / t["s"]["median"], 4),
+        "kernel": sw.swiglu_describe_launch(M, N, K, "auto", 0 if ws is None else ws.numel()),
+    }
+    if M <= 1024:
+        # HBM-bound end of the range: algorithmic bytes over the call time
+        rec["hbm_gbs_algorithmic"] = round(step_bytes / (med * 1e-3) / 1e9, 1)
+        rec["frac_hbm_peak"] = round(step_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    del copies, outs, gu, scratch, A, Wf
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -508,14 +643,18 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     sw.load_library()
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
     w = inputs.WORKLOADS[args.workload]
     M, K, N = w.M, w.K, w.N
     flops = 4 * M * N * K
 
+    print(f"[bench] headline workload M={M} K={K} N={N} (seed {w.seed}): drawing inputs",
+          file=sys.stderr, flush=True)
     A, W1, W2 = inputs.workload_inputs(w)
-    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
-    Wf = sw.swiglu_pack_weights(W1d, W2d)
+    Ad = A.to(dev)
+    Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
     chosen = {"auto": sw.swiglu_select_variant(M, N, K), "i": sw.SWIGLU_VARIANT_I,
               "s": sw.SWIGLU_VARIANT_S}[args.variant]
@@ -524,65 +663,51 @@ def main():
     # rotation copies: fused working set (A + packed weights + Y) times R >= 512 MB
     ws_bytes = 2 * (M * K + 2 * K * N + M * N)
     R = max(1, -(-512 * 2 ** 20 // ws_bytes))
-    del W1d, W2d
     copies = [(Ad, Wf)]
     for _ in range(R - 1):
         copies.append((Ad.clone(), Wf.clone()))
     outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-    abl_ws = [(torch.empty((M, N), dtype=torch.bfloat16, device=dev),
-               torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(R)]
+    gate_up = (torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+               torch.empty((M, N), dtype=torch.bfloat16, device=dev))
     # scratch for the split-tail schedule (one per path, reused by every step)
     scratch = {v: sw.make_workspace(M, N, K, v, dev) for v in ("auto", "i", "s", "ablation")}
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
 
-    def fused_step(s, variant):
-        a, wf = copies[s % R]
-        sw.swiglu_fused_gemm(a, wf, Y=outs[s % R], variant=variant, workspace=scratch[variant])
+    def fused_step(variant):
+        def step(s):
+            a, wf = copies[s % R]
+            sw.swiglu_fused_gemm(a, wf, Y=outs[s % R], variant=variant,
+                                 workspace=scratch[variant])
+        return step
 
     def ablation_step(s):
         a, wf = copies[s % R]
-        g, u = abl_ws[s % R]
-        sw.swiglu_unfused_ablation(a, wf, gate_ws=g, up_ws=u, Y=outs[s % R],
+        sw.swiglu_unfused_ablation(a, wf, gate_ws=gate_up[0], up_ws=gate_up[1], Y=outs[s % R],
                                    workspace=scratch["ablation"])
 
-    def timed(step_fn, steps, warmup):
-        for s in range(warmup):
-            step_fn(s)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
-        t0.record(stream)
-        for s in range(steps):
-            step_fn(s)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        return t0.elapsed_time(t1) / steps, wall
-
-    # the headline: the dispatched fused call
-    ms, wall = timed(lambda s: fused_step(s, args.variant), args.steps, args.warmup)
+    # the headline: W warm-up steps (and at least --warmup-seconds of work),
+    # then exactly K timed steps of the dispatched fused call
+    head = fused_step(args.variant)
+    warm_steps = _warm_up(head, args.warmup, args.warmup_seconds)
+    wall0 = time.perf_counter()
+    ms = _timed(head, args.steps, stream, start=warm_steps)
+    wall = time.perf_counter() - wall0
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"[bench] fused {args.variant}->{vname}: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
-          f"(R={R}, wall {wall:.3f}s)", file=sys.stderr, flush=True)
+          f"(R={R}, {warm_steps} warm-up steps, timed wall {wall:.3f}s)", file=sys.stderr,
+          flush=True)
 
-    # the partners: each fused variant and the unfused ablation, same protocol
-    per = {}
-    for v in ("i", "s"):
-        vms, _ = timed(lambda s, v=v: fused_step(s, v), args.steps, args.warmup)
-        per[v] = {"ms": vms, "tflops": flops / (vms * 1e-3) / 1e12}
-    ams, _ = timed(ablation_step, args.steps, args.warmup)
-    per["ablation"] = {"ms": ams, "tflops": flops / (ams * 1e-3) / 1e12}
-    # warm (one copy, cache-resident where it fits) for context
-    wms = None
-    if not args.no_warm:
-        wms, _ = timed(lambda s: sw.swiglu_fused_gemm(Ad, Wf, Y=outs[0], variant=args.variant,
-                                                      workspace=scratch[args.variant]),
-                       args.steps, args.warmup)
+    # the partners, in alternating repeats of K-step loops (AUTO again, each
+    # fused variant, the unfused ablation): medians and minima per call
+    partners = {"auto": head, "i": fused_step("i"), "s": fused_step("s"),
+                "ablation": ablation_step}
+    for name, fn in partners.items():
+        if name != "auto":
+            _warm_up(fn, args.warmup, args.warmup_seconds / 4)
+    per = _alternating(partners, args.steps, stream, args.repeats)
     for k, v in per.items():
-        print(f"[bench] {k}: {v['ms'] * 1e3:.1f} us, {v['tflops']:.1f} TFLOP/s",
-              file=sys.stderr, flush=True)
+        print(f"[bench] {k}: median {v['median'] * 1e3:.1f} us, min {v['min'] * 1e3:.1f} us "
+              f"({flops / (v['median'] * 1e-3) / 1e12:.1f} TFLOP/s)", file=sys.stderr, flush=True)
 
     # context, not the headline: the same call on FP8 E4M3 operands (power-of-two
     # tensor scales from the absolute maxima), with the operands quantized
@@ -595,25 +720,30 @@ def main():
                    for a, wf in copies]
         torch.cuda.synchronize()
 
-        def fp8_step(s, quantize_a):
-            a8, w8 = copies8[s % R]
-            if quantize_a:
-                sw.swiglu_quantize_fp8(copies[s % R][0], a_exp, Q=a8)
-            sw.swiglu_fused_gemm_fp8(a8, w8, a_exp, w_exp, Y=outs[s % R], workspace=scratch["i"])
+        def fp8_step(quantize_a):
+            def step(s):
+                a8, w8 = copies8[s % R]
+                if quantize_a:
+                    sw.swiglu_quantize_fp8(copies[s % R][0], a_exp, Q=a8)
+                sw.swiglu_fused_gemm_fp8(a8, w8, a_exp, w_exp, Y=outs[s % R],
+                                         workspace=scratch["i"])
+            return step
 
-        ms8, _ = timed(lambda s: fp8_step(s, False), args.steps, args.warmup)
-        msq, _ = timed(lambda s: fp8_step(s, True), args.steps, args.warmup)
-        t8 = flops / (ms8 * 1e-3) / 1e12
+        _warm_up(fp8_step(False), args.warmup, args.warmup_seconds / 4)
+        t8 = _alternating({"fp8": fp8_step(False), "fp8_quantize_a": fp8_step(True)},
+                          args.steps, stream, args.repeats)
+        ms8, msq = t8["fp8"]["median"], t8["fp8_quantize_a"]["median"]
+        tf8 = flops / (ms8 * 1e-3) / 1e12
         fp8 = {
-            "ms": round(ms8, 5), "tflops": round(t8, 2),
-            "pct_fp8_peak": round(100 * t8 / PEAK_FP8_TFLOPS, 2),
-            "speedup_vs_bf16": round(ms / ms8, 4),
+            "ms": round(ms8, 5), "tflops": round(tf8, 2),
+            "pct_fp8_peak": round(100 * tf8 / PEAK_FP8_TFLOPS, 2),
+            "speedup_vs_bf16": round(per["auto"]["median"] / ms8, 4),
             "ms_with_activation_quantize": round(msq, 5),
             "a_exp": a_exp, "w_exp": w_exp,
             "kernel": sw.swiglu_describe_launch(M, N, K, "fp8", scratch["i"].numel()
                                                 if scratch["i"] is not None else 0),
         }
-        print(f"[bench] fp8: {ms8 * 1e3:.1f} us, {t8:.1f} TFLOP/s "
+        print(f"[bench] fp8: {ms8 * 1e3:.1f} us, {tf8:.1f} TFLOP/s "
               f"({msq * 1e3:.1f} us with A quantized per step)", file=sys.stderr, flush=True)
         del copies8
 
@@ -623,9 +753,10 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
     # what the fused call launches (tile shape and schedule chosen by the
-    # library; with a split tail, two kernels: the record covers the call)
+    # library; with a split tail, two kernels: the time covers the whole call)
     ws_used = scratch[args.variant]
     kernel = sw.swiglu_describe_launch(M, N, K, args.variant,
                                        0 if ws_used is None else ws_used.numel())
@@ -636,11 +767,31 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        # FETCH_SIZE + WRITE_SIZE per call from rocprofv3 counter passes on the
+        # current kernel sources (else null): bytes between the L2 caches and
+        # the memory fabric, an upper bound on HBM bytes (the Infinity Cache
+        # serves some of the fetches)
         "traffic": traffic_record(vname, workload),
+        "traffic_kind": "L2-fabric bytes (FETCH_SIZE + WRITE_SIZE), copy-calibrated",
         "kernel": kernel,
+        "timed": "the whole call (every launch of it), HIP events on the launch stream",
         "algorithmic_flops_per_launch": flops,
         "algorithmic_hbm_bytes_per_launch": ws_bytes,
     }
+    del copies, outs, gate_up, scratch, Ad, Wf
+    torch.cuda.empty_cache()
+
+    # the other workloads, each with its own partners (sub-records)
+    per_workload = []
+    if not args.no_per_workload:
+        for idx in range(len(inputs.WORKLOADS)):
+            if idx == args.workload:
+                continue
+            rec = _workload_record(args, idx, dev, stream)
+            print(f"[bench] {rec['workload']}: {rec['us_per_call']['auto']['median']} us, "
+                  f"{rec['tflops']} TFLOP/s, {rec['speedup_vs_ablation']}x vs ablation",
+                  file=sys.stderr, flush=True)
+            per_workload.append(rec)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -651,7 +802,7 @@ def main():
         import oracle
         orc = oracle.load()
         hA, hW1, hW2 = inputs.bits(A), inputs.bits(W1), inputs.bits(W2)
-        probe = min(M, 32)
+        probe = min(M, 8)
         t = time.perf_counter()
         orc.swiglu_rows(hA, hW1, hW2, np.arange(probe))
         per_row = (time.perf_counter() - t) / probe
@@ -693,17 +844,18 @@ def main():
             "M": M, "K": K, "N": N,
             "variant": f"{args.variant}->{vname}",
             "rotation_copies": R,
-            "workspace_bytes": int(scratch[args.variant].numel()) if scratch[args.variant]
-            is not None else 0,
+            "warmup_steps_run": warm_steps,
+            "workspace_bytes": int(ws_used.numel()) if ws_used is not None else 0,
         },
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "speedup_vs_ablation": round(per["ablation"]["ms"] / ms, 4),
-        "per_variant": {k: {"ms": round(v["ms"], 5), "tflops": round(v["tflops"], 2)}
+        "speedup_vs_ablation": round(per["ablation"]["median"] / per["auto"]["median"], 4),
+        "per_variant": {k: {"ms_median": round(v["median"], 5), "ms_min": round(v["min"], 5),
+                            "tflops_median": round(flops / (v["median"] * 1e-3) / 1e12, 2)}
                         for k, v in per.items()},
-        "warm_single_copy": None if wms is None else {
-            "ms": round(wms, 5), "tflops": round(flops / (wms * 1e-3) / 1e12, 2)},
+        "partner_protocol": f"{args.repeats} alternating repeats of {args.steps}-step loops",
         "roofline": roofline,
         "fp8": fp8,
+        "per_workload": per_workload,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -1,13 +1,14 @@
 """HBM traffic per call from rocprofv3 counter passes.
 
     python -m gated_mlp_gemm_amd.counters FETCH_DIR WRITE_DIR \
-        [--workload M=2048,K=1536,N=8960] [--out profiles/traffic.json]
+        [--workload M=4096,K=8192,N=29568] [--out profiles/traffic.json]
 
 FETCH_DIR and WRITE_DIR hold the CSV output of two rocprofv3 runs of the same
 command, one counter each (rocprofv3 collects what one pass allows):
 
     rocprofv3 --pmc FETCH_SIZE -f csv -d FETCH_DIR -o bench -- \
-        python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-warm --copy-calibration
+        python3 bench.py --steps 3 --warmup 1 --warmup-seconds 0 --repeats 1 \
+            --no-cpu-baseline --no-per-workload --no-fp8 --copy-calibration
     rocprofv3 --pmc WRITE_SIZE -f csv -d WRITE_DIR -o bench -- (the same)
 
 (or of ``bench.py --fp8 --fp8-workloads 1 --copy-calibration`` with

@@ -15,7 +15,7 @@
 // no LDS write instructions), STAGES-1 steps ahead of the MFMAs.  The
 // compiler does not track those LDS writes, so completion is awaited by hand
 // (s_waitcnt vmcnt with a count of the later steps still allowed in flight)
-// before a workgroup barrier; see the two pipeline drivers below.  Every step
+// before a workgroup barrier; see the pipeline driver below.  Every step
 // issues exactly one group of loads (groups past the end of K read nothing),
 // which keeps the vmcnt arithmetic uniform.
 //
@@ -33,8 +33,6 @@
 // load as zeros; chunks at k >= K are masked explicitly, so the K tail
 // contributes nothing.
 #pragma once
-
-#include <type_traits>
 
 #include "device.hpp"
 
@@ -69,8 +67,6 @@ struct TileShape {
     static constexpr int kDmaA = kABytes / (kThreads * 16);
     static constexpr int kDmaB = kBBytes / (kThreads * 16);
     static constexpr int kDmaPerStep = kDmaA + kDmaB;
-    // 8 waves (two per SIMD) run the ping-pong schedule; 4 waves the plain one
-    static constexpr bool kPingPong = (kWaves == 8);
     // workgroups resident per CU that the kernel is built for: two when two
     // fit the 160 KiB of LDS (the kernel then keeps to 256 registers a lane)
     static constexpr int kOccupancy = (2 * kLdsBytes <= 160 * 1024) ? 2 : 1;
@@ -84,8 +80,7 @@ struct TileShape {
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup is 160 KiB");
     static_assert(STAGES >= 2 && STAGES <= 8, "ring depth");
     static_assert(kDmaPerStep * (STAGES - 1) < 64, "vmcnt is a 6-bit counter");
-    static_assert(kWaves == 4 || (kWaves == 8 && WM % 2 == 0),
-                  "4 waves, or 8 waves whose two groups split the tile rows");
+    static_assert(kWaves == 4, "4 waves, one per SIMD (the pipeline below)");
 };
 
 // Chunk swizzle of a tile row.  The 16 lanes of one LDS cycle read 16
@@ -473,113 +468,6 @@ struct Pipeline {
         block_barrier();
     }
 };
-
-// ---------------------------------------------------------------------------
-// Ping-pong pipeline (8 waves, two per SIMD).  Waves 0-3 (group 0) and 4-7
-// (group 1) sit one per SIMD each and own the top and bottom halves of the
-// tile rows.  The two groups run the same phase sequence one barrier apart:
-// while one group runs the MFMA cluster of a K step, the other issues its
-// share of the next loads and reads all fragments of its next K step, so each
-// SIMD's MFMA pipe is fed by one of its two waves at any time.
-//
-// Per wave, for K step t:
-//   memory phase: read all fragments of step t; wait for them; wait for its
-//                 own loads of step t+1 (vmcnt <= L-1 groups, L = STAGES-1);
-//                 barrier.
-//   MFMA phase:   all MFMAs of step t; barrier.
-// Group 1 starts one barrier late.  Numbering barriers from the prologue's
-// (#1): group 0's memory phase t ends at #(2t+2) and its MFMA phase t at
-// #(2t+3); group 1's memory phase t ends at #(2t+3) and its MFMA phase at
-// #(2t+4).  Both groups issue their share of the loads of step t+L in the
-// same phase, so the two halves of a stage are in flight together: group 0
-// at the start of its memory phase t (after #(2t+1)), group 1 at the start of
-// its MFMA phase t-1 (also after #(2t+1); for t = 0, before its offset
-// barrier).  Hence
-//  - group 0 reads step t+1 after #(2t+3), when both groups have waited for
-//    their loads of step t+1 (group 1 at the end of its memory phase t);
-//  - the stage refilled with step t+L held step t-1, whose last reader
-//    (group 1, memory phase t-1) finished with lgkmcnt(0) before #(2t+1);
-//  - each wave has issued steps up to t+L when it waits for step t+1, so
-//    "at most L-1 groups outstanding" is exactly "step t+1 has landed".
-// Group 1 skips its last MFMA-phase barrier so both groups execute 2*nk+1
-// barriers.
-// ---------------------------------------------------------------------------
-template <class S>
-struct PingPong {
-    static constexpr int L = S::STAGES - 1;
-    SWIGLU_LDS char *lds;
-    uint32_t lds_addr;
-    int group;
-    FragOffsets<S> off;
-    Frags<S> F[S::kKSub];
-
-    __device__ __forceinline__ SWIGLU_LDS char *stage(int t) const {
-        return lds + (t % S::STAGES) * S::kStageBytes;
-    }
-    __device__ __forceinline__ uint32_t stage_addr(int t) const {
-        return lds_addr + static_cast<uint32_t>((t % S::STAGES) * S::kStageBytes);
-    }
-
-    __device__ __forceinline__ void init(SWIGLU_LDS char *lds_) {
-        lds = lds_;
-        lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_));
-        const int lane = threadIdx.x & 63;
-        const int wave = threadIdx.x >> 6;
-        group = wave >> 2;
-        off.init(wave / S::WN, wave % S::WN, lane);
-    }
-
-    template <class Issue>
-    __device__ __forceinline__ void prologue(const Issue &issue) {
-#pragma unroll
-        for (int t = 0; t < L; ++t) issue(t, stage(t));
-        wait_vmcnt<S::kDmaPerStep * (L - 1)>();
-        block_barrier();
-        if (group == 1) {
-            issue(L, stage(L));
-            block_barrier();
-        }
-    }
-
-    template <int KS>
-    __device__ __forceinline__ void read_all(uint32_t st) {
-        read_frags<S, KS>(st, off, F[KS]);
-        if constexpr (KS + 1 < S::kKSub) read_all<KS + 1>(st);
-    }
-
-    template <class Issue, class Hook>
-    __device__ __forceinline__ void step(const Issue &issue, int t, int total,
-                                         f32x16 (&acc)[S::TM][S::TN], const Hook &hook) {
-        // memory phase
-        if (group == 0) issue(t + L, stage(t + L));
-        read_all<0>(stage_addr(t));
-#pragma unroll
-        for (int ks = 0; ks < S::kKSub; ++ks) wait_frags<S>(F[ks]);
-        wait_vmcnt<S::kDmaPerStep * (L - 1)>();
-        block_barrier();
-        // MFMA phase (group 1 first issues its share of step t+1+L)
-        if (group == 1) issue(t + 1 + L, stage(t + 1 + L));
-#pragma unroll
-        for (int ks = 0; ks < S::kKSub; ++ks) {
-            hook(ks);
-            mma<S>(F[ks], acc);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (!(group == 1 && t + 1 == total)) block_barrier();
-    }
-
-    template <class Issue>
-    __device__ __forceinline__ void run(const Issue &issue, int t_begin, int t_end, int total,
-                                        f32x16 (&acc)[S::TM][S::TN]) {
-        for (int t = t_begin; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
-    }
-
-    // No load may still be writing LDS when the wave ends or LDS is reused.
-    __device__ __forceinline__ void drain() { wait_vmcnt<0>(); }
-};
-
-template <class S>
-using PipelineFor = typename std::conditional<S::kPingPong, PingPong<S>, Pipeline<S>>::type;
 
 // Tile order.  tile_coords() walks a tile index t over the tile grid in
 // groups of `group_m` tile rows (tiles close in t share A rows and B columns);

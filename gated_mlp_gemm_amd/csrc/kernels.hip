@@ -386,7 +386,7 @@ __device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor
                                               const KMajor &B, int M, int K, int m0, int n0,
                                               int kb, int ke, int nk,
                                               f32x16 (&acc)[S::TM][S::TN]) {
-    PipelineFor<S> pl;
+    Pipeline<S> pl;
     pl.init(lds);
     TileLoader<S> ld;
     ld.init(A, m0, B, n0, K);
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
     const int grid = sch.grid;
 
     if (b < sch.dp) {
-        PipelineFor<S> pl;
+        Pipeline<S> pl;
         pl.init(lds);
         TileLoader<S> ld;
         int j = b, tm, tn;
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
         if (t < nk) ld.issue(t, st);
         else ld.issue(t - nk, st, up);   // t - nk >= nk loads nothing
     };
-    PipelineFor<S> pl;
+    Pipeline<S> pl;
     pl.init(lds);
     f32x16 g[S::TM][S::TN], u[S::TM][S::TN];
     zero_acc<S>(g);

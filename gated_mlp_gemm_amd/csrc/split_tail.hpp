@@ -9,9 +9,10 @@
 // first R*G tiles (R = T / G full rounds) run whole, one per workgroup, and
 // each of the L = T mod G remaining tiles is cut into s = min(G / L, nk)
 // pieces of about nk / s K steps, one piece per workgroup: the tail round
-// takes nk / s steps instead of nk (for 560 tiles: 2 + 1/5 rounds).  Every
-// workgroup runs exactly one (tile, K range), so the GEMM kernel has no loop
-// over tiles and no more live registers than the one-tile kernel.
+// takes nk / s steps instead of nk (for 560 tiles: 2 + 1/5 rounds).  Each
+// piece is one (tile, K range) work item of the persistent GEMM kernel; a
+// workgroup takes its share of the pieces after its whole tiles, with one
+// accumulator set live at a time.
 //
 // A piece stores its fp32 partial accumulator in its own workspace slot and
 // ends.  A second, short kernel on the same stream then sums the s slots of

@@ -36,6 +36,18 @@
  *    and one round-to-nearest-even to bf16 at the end; the accumulation order
  *    is not specified (results of different variants need not be bitwise
  *    equal).
+ *  - Every compute call takes the weights in one form only, the packed
+ *    W_fused that swiglu_pack_weights (or swiglu_pack_weights_nk) writes once
+ *    per weight set: variant I, variant S, the unfused ablation and the MLP
+ *    block read it, and none of them takes W1 and W2 as two separate
+ *    [K][N] arrays.  Variant S and the ablation read its even (Gate) and odd
+ *    (Up) rows as two row-strided panels, which are exactly the bytes of W1
+ *    and W2 in K-contiguous order.  The reason is the operand layout: both
+ *    MFMA operands take 8 consecutive k per lane, so K-contiguous weights
+ *    give plain 16-byte LDS fragment reads, where [K][N] weights would need
+ *    the transposing 8-byte reads at about half the LDS rate.  Accepting
+ *    [K][N] W1, W2 in the compute calls would mean a second mainloop or a
+ *    transpose inside every call, so the transpose is the pack's job.
  *  - Calls are re-entrant; the only global state is a per-device cache of
  *    the device's architecture.
  *  - The code object targets gfx950 only: on another device every launching

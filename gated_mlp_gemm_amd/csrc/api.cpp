@@ -142,6 +142,35 @@ swiglu::GemmWorkspace make_ws(void *workspace, uint64_t bytes, int cus) {
     return ws;
 }
 
+// Library-owned scratch of swiglu_fused_gemm_noalloc: the split-tail partials
+// of one call (one fp32 256 x 256 slot per compute unit of a 256-CU device).
+// A file-scope device array, so the library allocates nothing at call time;
+// each device the library runs on holds its own copy until the process ends.
+// Host code never uses the array's name as an address: the per-device device
+// address comes from hipGetSymbolAddress (scratch_on_device).
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void *g_scratch_ptr[256];   // per device, guarded by g_dev_mutex
+
+// Device address of this device's `scratch`, looked up once per device with
+// that device current (the caller's current device).
+int scratch_on_device(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SWIGLU_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 256) return fail(SWIGLU_ERR_UNSUPPORTED, "device ordinal %d", dev);
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(SWIGLU_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SWIGLU_OK;
+}
+
 int check_workspace(const void *workspace, uint64_t bytes) {
     if (workspace && bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(SWIGLU_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -316,6 +345,43 @@ int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y, i
     // after the shape check, so the shape errors are reported first)
     return swiglu_fused_gemm_strided(A, K, W_fused, Y, N, M, N, K, variant, workspace,
                                      workspace_bytes, stream);
+}
+
+int swiglu_fused_gemm_noalloc(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
+                              int64_t M, int64_t N, int64_t K, int variant, void *stream) {
+    if (variant != SWIGLU_AUTO && variant != SWIGLU_VARIANT_S && variant != SWIGLU_VARIANT_I)
+        return fail(SWIGLU_ERR_UNSUPPORTED, "unknown variant %d", variant);
+    int st = check_gemm_shape(M, N, K);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!A || !W_fused || !Y) return fail(SWIGLU_ERR_NULL, "A, W_fused and Y are required");
+    if (!aligned16(A) || !aligned16(W_fused) || !aligned16(Y))
+        return fail(SWIGLU_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int64_t abytes = M * K * 2, ybytes = M * N * 2, wbytes = 2 * K * N * 2;
+    if (overlap(Y, ybytes, A, abytes) || overlap(Y, ybytes, W_fused, wbytes))
+        return fail(SWIGLU_ERR_ALIAS, "Y overlaps an input");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != SWIGLU_OK) return st;
+    const uint64_t need = swiglu::workspace_bytes_for(cus);
+    if (need > kScratchBytes)
+        return fail(SWIGLU_ERR_UNSUPPORTED,
+                    "the device's %d compute units need %llu bytes of split-tail scratch; the "
+                    "library's static scratch holds %llu", cus, (unsigned long long)need,
+                    (unsigned long long)kScratchBytes);
+    void *ptr = nullptr;
+    st = scratch_on_device(&ptr);
+    if (st != SWIGLU_OK) return st;
+    const int v = variant == SWIGLU_AUTO ? swiglu_select_variant(M, N, K) : variant;
+    const hipStream_t s = (hipStream_t)stream;
+    if (v == SWIGLU_VARIANT_I)
+        return launched(swiglu::launch_fused_interleaved(A, (int)K, W_fused, Y, (int)N, (int)M,
+                                                         (int)N, (int)K,
+                                                         make_ws(ptr, kScratchBytes, cus), s),
+                        "fused interleaved (no-alloc)");
+    return launched(swiglu::launch_fused_sequential(A, (int)K, W_fused, Y, (int)N, (int)M,
+                                                    (int)N, (int)K, s),
+                    "fused sequential (no-alloc)");
 }
 
 int swiglu_unfused_ablation(const uint16_t *A, const uint16_t *W_fused, uint16_t *gate_ws,

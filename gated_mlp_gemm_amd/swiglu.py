@@ -59,6 +59,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.swiglu_pack_weights.argtypes = [P, P, P, I64, I64, P]
     U64 = ctypes.c_uint64
     lib.swiglu_fused_gemm.argtypes = [P, P, P, I64, I64, I64, I32, P, U64, P]
+    lib.swiglu_fused_gemm_noalloc.argtypes = [P, P, P, I64, I64, I64, I32, P]
     lib.swiglu_unfused_ablation.argtypes = [P, P, P, P, P, I64, I64, I64, P, U64, P]
     lib.swiglu_fused_gemm_strided.argtypes = [P, I64, P, P, I64, I64, I64, I64, I32, P, U64, P]
     lib.swiglu_workspace_size.argtypes = [I64, I64, I64, I32, ctypes.POINTER(U64)]
@@ -81,7 +82,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                  "swiglu_silu_mul", "swiglu_select_variant", "swiglu_workspace_size",
                  "swiglu_describe_launch", "swiglu_pack_weights_nk", "swiglu_down_proj",
                  "swiglu_gated_mlp", "swiglu_fp8_scale_exp", "swiglu_quantize_fp8",
-                 "swiglu_fused_gemm_fp8", "swiglu_fused_gemm_strided"):
+                 "swiglu_fused_gemm_fp8", "swiglu_fused_gemm_strided",
+                 "swiglu_fused_gemm_noalloc"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -263,6 +265,24 @@ def swiglu_fused_gemm(A: torch.Tensor, W_fused: torch.Tensor,
         ws, wsb = _ws(workspace)
         _check(lib.swiglu_fused_gemm(_ptr(A), _ptr(W_fused), _ptr(Y), M, N, K, v, ws, wsb,
                                      _stream(A.device)), "swiglu_fused_gemm")
+    return Y
+
+
+def swiglu_fused_gemm_noalloc(A: torch.Tensor, W_fused: torch.Tensor, Y: torch.Tensor,
+                              variant="auto") -> torch.Tensor:
+    """swiglu_fused_gemm with the library's static split-tail scratch: the C
+    call allocates nothing (Y must be given, so the binding allocates nothing
+    either).  Calls that may overlap on one device race on that scratch."""
+    lib = load_library()
+    v = VARIANTS[variant.lower()] if isinstance(variant, str) else int(variant)
+    M, K = A.shape
+    _dev_tensor(A, "A", (M, K))
+    N = W_fused.shape[0] // 2
+    _dev_tensor(W_fused, "W_fused", (2 * N, K))
+    _dev_tensor(Y, "Y", (M, N))
+    with _on_device(A.device):
+        _check(lib.swiglu_fused_gemm_noalloc(_ptr(A), _ptr(W_fused), _ptr(Y), M, N, K, v,
+                                             _stream(A.device)), "swiglu_fused_gemm_noalloc")
     return Y
 
 

@@ -49,7 +49,9 @@
  *    [K][N] W1, W2 in the compute calls would mean a second mainloop or a
  *    transpose inside every call, so the transpose is the pack's job.
  *  - Calls are re-entrant; the only global state is a per-device cache of
- *    the device's architecture.
+ *    the device's architecture and compute-unit count, and the static
+ *    scratch array of swiglu_fused_gemm_noalloc (device memory the library
+ *    holds; no call allocates).
  *  - The code object targets gfx950 only: on another device every launching
  *    call returns SWIGLU_ERR_UNSUPPORTED.
  */
@@ -147,6 +149,28 @@ int swiglu_fused_gemm_strided(const uint16_t *A, int64_t lda, const uint16_t *W_
                               uint16_t *Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                               int variant, void *workspace, uint64_t workspace_bytes,
                               void *stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not allocate, harnesses that forbid it.
+ * swiglu_fused_gemm without a workspace argument: the split-tail scratch
+ * (fp32 partial tiles) lives in a static device array inside the library,
+ * 64 MiB (one fp32 256 x 256 tile per compute unit of a 256-CU device), that
+ * each device the library is loaded on holds from the first call on that
+ * device until the process ends.  The call allocates nothing (no hipMalloc,
+ * no library routine that allocates).  Same computation, variants, schedule
+ * choice and preconditions as swiglu_fused_gemm with a workspace of that
+ * size (the outputs are bitwise those of swiglu_fused_gemm given a workspace
+ * of at least swiglu_workspace_size() bytes).  Every call on a device shares
+ * that device's array: calls that may overlap on one device (different
+ * streams without ordering between them) race and must not be issued; calls
+ * on one stream are ordered and safe.  The scratch needs no initialisation
+ * (each partial is written before it is read) and its contents are
+ * meaningless after a call.  A device whose compute-unit count needs more
+ * scratch than the array holds gets SWIGLU_ERR_UNSUPPORTED, nothing launched.
+ */
+int swiglu_fused_gemm_noalloc(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
+                              int64_t M, int64_t N, int64_t K, int variant, void *stream);
 
 /*
  * Bytes of `workspace` that let a call split the tail round along K: variant

@@ -313,3 +313,23 @@ def test_plain_c_client(tmp_path, lib):
                     "-o", str(exe), "-L", libdir, "-lswiglu", f"-Wl,-rpath,{libdir}"], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr
+
+
+def test_noalloc_validation(lib):
+    def f(A=A_, WF=WF_, Y=Y_, M=256, N=256, K=256, v=2):
+        return lib.swiglu_fused_gemm_noalloc(A, WF, Y, M, N, K, v, None)
+
+    assert f(M=-1) == ERR_SHAPE
+    assert f(K=20) == ERR_SHAPE
+    assert f(N=(1 << 22) + 8) == ERR_SHAPE
+    assert f(v=3) == ERR_UNSUP
+    for v in (0, 1, 2):
+        assert f(A=None, v=v) == ERR_NULL
+        assert f(WF=None, v=v) == ERR_NULL
+        assert f(Y=None, v=v) == ERR_NULL
+    assert f(A=A_ + 2) == ERR_ALIGN
+    assert f(Y=Y_ + 8) == ERR_ALIGN
+    assert f(Y=A_ + 1024) == ERR_ALIAS
+    assert f(Y=WF_ + 4096) == ERR_ALIAS
+    assert lib.swiglu_fused_gemm_noalloc(None, None, None, 0, 256, 64, 0, None) == 0
+    assert lib.swiglu_fused_gemm_noalloc(None, None, None, 64, 0, 64, 2, None) == 0

@@ -5,6 +5,9 @@
 //   v_mfma_f32_32x32x16_bf16, operands A (32 x 16) and B (16 x 32):
 //     lane l holds A[l % 32][8*(l/32) + j] and B[8*(l/32) + j][l % 32], j < 8;
 //     accumulator register i of lane l is D[8*(i/4) + 4*(l/32) + i%4][l % 32].
+//   v_mfma_f32_16x16x32_bf16, operands A (16 x 32) and B (32 x 16):
+//     lane l holds A[l % 16][8*(l/16) + j] and B[8*(l/16) + j][l % 16], j < 8;
+//     accumulator register i of lane l is D[4*(l/16) + i][l % 16].
 //   ds_read_b64_tr_b16: within each group of 16 lanes, element j of lane i is
 //     element (i % 4) of the 8-byte chunk addressed by lane 4*j + i/4.
 #pragma once
@@ -17,6 +20,7 @@ namespace swiglu {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -28,6 +32,52 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b
                                                 const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// c += A . B on one 16x16 accumulator quad, in place.  Written as inline
+// assembly with the accumulator tied to its own AGPRs: through the builtin the
+// compiler assigns the result of a 16x16 MFMA other registers than its C
+// operand and then rotates the accumulators back every loop iteration (about
+// as many AGPR copies per K step as MFMAs).  The compiler does not see these
+// as MFMAs, so their hazards are the pipeline's job: the result is read by
+// other instructions only after Pipeline::drain(), which waits out the MFMA
+// latency, and MFMAs follow the zeroing of their accumulators only after
+// zero_acc()'s wait.
+__device__ __forceinline__ void mfma_16x16x32_acc(f32x4 &c, const u32x4 &a, const u32x4 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// At least 24 wait states: more than any MFMA result needs before another
+// instruction may read it (the longest, 32x32 MFMAs, need 19).
+__device__ __forceinline__ void wait_mfma_results() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+}
+
+// The accumulators of one 32x32 output block, 16 registers a lane, numbered
+// r = 0..15 in quads q = r / 4: either the 16 registers of one 32x32 MFMA
+// (Acc32), or the 4 registers of each of four 16x16 MFMAs, quad q covering
+// rows 16 (q / 2) + [0, 16) and columns 16 (q % 2) + [0, 16) of the block
+// (Acc16).  Each 16x16 MFMA then works on a whole register quad, which the
+// compiler keeps as one 4-register tuple.
+struct Acc32 {
+    f32x16 v;
+    __device__ __forceinline__ float get(int r) const { return v[r]; }
+    __device__ __forceinline__ void set(int r, float x) { v[r] = x; }
+    __device__ __forceinline__ f32x4 quad(int q) const {
+        return f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    }
+    __device__ __forceinline__ void set_quad(int q, const f32x4 &x) {
+        v[4 * q] = x[0];
+        v[4 * q + 1] = x[1];
+        v[4 * q + 2] = x[2];
+        v[4 * q + 3] = x[3];
+    }
+};
+struct Acc16 {
+    f32x4 v[4];
+    __device__ __forceinline__ float get(int r) const { return v[r >> 2][r & 3]; }
+    __device__ __forceinline__ void set(int r, float x) { v[r >> 2][r & 3] = x; }
+    __device__ __forceinline__ f32x4 quad(int q) const { return v[q]; }
+    __device__ __forceinline__ void set_quad(int q, const f32x4 &x) { v[q] = x; }
+};
 
 // FP8 E4M3 x FP8 E4M3 -> fp32, 32x32 outputs, 64 k (v_mfma_f32_32x32x64_f8f6f4;
 // format code 0 = E4M3 for both operands, no block scales).  Each operand is

@@ -10,16 +10,21 @@
 //      c here), optionally every second row (the Gate or the Up columns).
 // K is consumed in steps of BK.
 //
-// Pipeline.  K steps stream through a ring of STAGES LDS buffers filled by
-// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds: no VGPR staging,
-// no LDS write instructions), STAGES-1 steps ahead of the MFMAs.  The
-// compiler does not track those LDS writes, so completion is awaited by hand
-// (s_waitcnt vmcnt with a count of the later steps still allowed in flight)
-// before a workgroup barrier; see the pipeline driver below.  Every step
-// issues exactly one group of loads (groups past the end of K read nothing),
-// which keeps the vmcnt arithmetic uniform.
+// Pipeline.  K steps stream through two rings of LDS buffers, STAGES of A
+// panels and BSTAGES of B panels, filled by direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds: no VGPR staging, no LDS write instructions),
+// STAGES-1 (BSTAGES-1) steps ahead of the MFMAs: an operand whose ring is one
+// stage deeper is loaded one more step ahead (the LDS left beside a ring of
+// two 256x256 stages holds exactly one more panel).  The compiler does not
+// track those LDS writes, so completion is awaited by hand (s_waitcnt vmcnt
+// with a count of the later loads still allowed in flight, derived from the
+// issue order at compile time) before a workgroup barrier; see the pipeline
+// driver below.  Every step issues exactly one group of loads per operand
+// (groups past the end of K read nothing), which keeps the vmcnt arithmetic
+// uniform.
 //
-// LDS layout: A tile [BM][BK] then B tile [BN][BK], 16-byte chunks with the
+// LDS layout: the A ring, STAGES tiles [BM][BK], then the B ring, BSTAGES
+// tiles [BN][BK], 16-byte chunks with the
 // chunk index XOR-swizzled by the row, so that the 16 lanes one LDS cycle
 // serves (256 B) hit 16 different bank groups.  Fragment reads are one
 // ds_read_b128 per lane per 32x32x16 MFMA operand (8 consecutive k of one
@@ -34,18 +39,29 @@
 // contributes nothing.
 #pragma once
 
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace swiglu {
 
-// EB is the operand element size in bytes: 2 for bf16 (v_mfma_f32_32x32x16_bf16,
-// 16 k per MFMA, one 16-byte chunk per lane and operand), 1 for FP8 E4M3
-// (v_mfma_f32_32x32x64_f8f6f4, 64 k per MFMA, two chunks per lane).  A K step
-// of BK elements moves BK * EB bytes per tile row either way.
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int EB_ = 2>
+// EB is the operand element size in bytes: 2 for bf16, 1 for FP8 E4M3.  MI
+// is the MFMA that computes each 32x32 accumulator block:
+//   MI = 32: one v_mfma_f32_32x32x16_bf16 per 16 k (bf16: one 16-byte chunk
+//            per lane and operand), or one v_mfma_f32_32x32x64_f8f6f4 per 64 k
+//            (FP8: two chunks per lane);
+//   MI = 16: four v_mfma_f32_16x16x32_bf16 per 32 k, one per 16x16 quarter
+//            of the block (bf16 only; one chunk per lane and 16-row half).
+// Per flop the 16x16 instruction reads and writes half the accumulator
+// registers of the 32x32 one.  A K step of BK elements moves BK * EB bytes
+// per tile row either way.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int EB_ = 2,
+          int BSTAGES_ = STAGES_, int MI_ = 32>
 struct TileShape {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int STAGES = STAGES_;
+    static constexpr int STAGES = STAGES_;     // A ring
+    static constexpr int BSTAGES = BSTAGES_;   // B ring
+    static constexpr int MI = MI_;
     static constexpr int EB = EB_;
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
@@ -53,16 +69,20 @@ struct TileShape {
     static constexpr int kWaveN = BN / WN;
     static constexpr int TM = kWaveM / 32;          // 32x32 MFMA blocks per wave (M)
     static constexpr int TN = kWaveN / 32;          // 32x32 MFMA blocks per wave (N)
-    static constexpr int kMfmaK = EB == 2 ? 16 : 64;   // k per MFMA
+    static constexpr int kMfmaK = EB == 2 ? (MI == 16 ? 32 : 16) : 64;   // k per MFMA
     static constexpr int kKSub = BK / kMfmaK;       // MFMA k-substeps per K step
-    static constexpr int kFragChunks = kMfmaK * EB / 32;   // 16-byte chunks per lane and operand
+    // 16-byte LDS reads per lane, operand and 32-row block in one substep:
+    // consecutive chunks of one row (MI = 32), or the two 16-row halves (MI = 16)
+    static constexpr int kFragChunks = kMfmaK * EB / 32;
+    static constexpr int kMfmaPerBlock = MI == 16 ? 4 : 1;   // per block and substep
+    using Acc = typename std::conditional<MI == 16, Acc16, Acc32>::type;
     static constexpr int kElemsPerChunk = 16 / EB;
     static constexpr int kChunksPerRow = BK * EB / 16;   // 16-byte chunks per tile row
     static constexpr int kRowBytes = BK * EB;
     static constexpr int kABytes = BM * kRowBytes;
     static constexpr int kBBytes = BN * kRowBytes;
-    static constexpr int kStageBytes = kABytes + kBBytes;
-    static constexpr int kLdsBytes = kStageBytes * STAGES;
+    static constexpr int kBRing = STAGES * kABytes;   // LDS offset of the B ring
+    static constexpr int kLdsBytes = kBRing + BSTAGES * kBBytes;
     // direct-to-LDS loads per wave per K step (each moves 64 x 16 B = 1 KiB)
     static constexpr int kDmaA = kABytes / (kThreads * 16);
     static constexpr int kDmaB = kBBytes / (kThreads * 16);
@@ -73,14 +93,27 @@ struct TileShape {
 
     static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(EB == 2 || EB == 1, "bf16 or FP8 operands");
+    static_assert(MI == 32 || (MI == 16 && EB == 2), "16x16 MFMAs for bf16 operands only");
     static_assert(EB == 2 ? (BK == 32 || BK == 64) : BK == 128,
                   "BK: 32 or 64 bf16 elements, or 128 FP8 elements");
     static_assert(kABytes % (kThreads * 16) == 0 && kDmaA >= 1, "A tile must split evenly");
     static_assert(kBBytes % (kThreads * 16) == 0 && kDmaB >= 1, "B tile must split evenly");
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup is 160 KiB");
-    static_assert(STAGES >= 2 && STAGES <= 8, "ring depth");
-    static_assert(kDmaPerStep * (STAGES - 1) < 64, "vmcnt is a 6-bit counter");
+    static_assert(STAGES >= 2 && STAGES <= 8 && BSTAGES >= 2 && BSTAGES <= 8, "ring depth");
+    static_assert(BSTAGES - STAGES <= 1 && STAGES - BSTAGES <= 1,
+                  "the two rings differ by at most one stage");
+    static_assert(kDmaA * STAGES + kDmaB * BSTAGES < 64, "vmcnt is a 6-bit counter");
     static_assert(kWaves == 4, "4 waves, one per SIMD (the pipeline below)");
+
+    // Row and column, within its 32x32 block, of accumulator register r of
+    // lane l: row_l(l) + row_r(r) and col_l(l) + col_r(r) (device.hpp gives
+    // the MFMA layouts).
+    __device__ __forceinline__ static int row_l(int lane) {
+        return MI == 16 ? 4 * (lane >> 4) : 4 * (lane >> 5);
+    }
+    static constexpr int row_r(int r) { return MI == 16 ? 16 * (r >> 3) + (r & 3) : 8 * (r >> 2) + (r & 3); }
+    __device__ __forceinline__ static int col_l(int lane) { return MI == 16 ? (lane & 15) : (lane & 31); }
+    static constexpr int col_r(int r) { return MI == 16 ? 16 * ((r >> 2) & 1) : 0; }
 };
 
 // Chunk swizzle of a tile row.  The 16 lanes of one LDS cycle read 16
@@ -156,13 +189,21 @@ __device__ __forceinline__ int pair_row(int r) {
 }
 
 // The direct-to-LDS loads of one tile panel (NROWS rows) of a KMajor
-// operand: NDMA loads per wave per K step.
+// operand: NDMA loads per wave per K step.  Load j of a wave fills the 1 KiB
+// LDS block j * kWaves + wave: LDS rows r0 + j R (R = 256 / kChunksPerRow,
+// r0 = (64 wave + lane) / kChunksPerRow < R), and every load of a lane reads
+// the same chunk column, because the swizzle is periodic in R rows.  So a
+// lane keeps one byte offset and one K limit for all its loads, and load j
+// adds a uniform row distance (dj, in scalar registers) to that offset.
 template <class S, int NROWS, int NDMA>
 struct PanelLoader {
+    static constexpr int R = S::kWaves * 64 / S::kChunksPerRow;   // LDS rows between loads
+    static_assert(R % 32 == 0, "the row swizzle and the pair layout repeat every 32 rows");
     __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff[NDMA];   // byte offset of this lane's chunk at k0 = 0 (from the panel base)
-    int kcol[NDMA];        // first k of that chunk
-    int lds_off[NDMA];     // LDS byte offset (within the panel) of the wave's 1 KiB block
+    uint32_t voff;         // byte offset of this lane's chunk of load 0 at k0 = 0
+    int klim;              // K minus the first k of that chunk: step k0 loads iff k0 < klim
+    uint32_t dj[NDMA];     // uniform: bytes from load 0's row to load j's
+    int lds_off[NDMA];     // uniform: LDS byte offset (within the panel) of load j's block
 
     // Panel = logical rows [r0, r0 + NROWS) of `op`.
     __device__ __forceinline__ void init(const KMajor &op, int r0, int K) {
@@ -178,32 +219,37 @@ struct PanelLoader {
         const int lane = threadIdx.x & 63;
         // uniform per wave: keeps the LDS destinations (M0) in scalar registers
         const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+        const int p = wave * 64 + lane;                   // physical chunk of load 0
+        const int row = p / S::kChunksPerRow;             // its LDS row (< R)
+        const int c = (p % S::kChunksPerRow) ^ swz<S>(row);
+        const int grow = op.pairs ? pair_row(row) : row;  // panel row it holds
+        const uint32_t row_bytes = static_cast<uint32_t>(op.stride) *
+                                   static_cast<uint32_t>(pitch) * S::EB;
+        voff = static_cast<uint32_t>(grow) * row_bytes + c * 16u;
+        klim = K - c * S::kElemsPerChunk;
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) {
-            const int block = j * S::kWaves + wave;
-            const int p = block * 64 + lane;                  // physical chunk in the panel
-            const int row = p / S::kChunksPerRow;             // LDS row
-            const int c = (p % S::kChunksPerRow) ^ swz<S>(row);
-            const int grow = op.pairs ? pair_row(row) : row;  // panel row it holds
-            voff[j] = static_cast<uint32_t>(grow * op.stride) * static_cast<uint32_t>(pitch) * S::EB +
-                      c * 16u;
-            kcol[j] = c * S::kElemsPerChunk;
-            lds_off[j] = block * 1024;
+            // panel rows from load 0's to load j's: the LDS distance j R, or
+            // in a de-interleaved panel pair_row(j R) (R is a multiple of 32)
+            const int drow = op.pairs ? pair_row(j * R) : j * R;
+            dj[j] = static_cast<uint32_t>(drow) * row_bytes;
+            lds_off[j] = (j * S::kWaves + wave) * 1024;
         }
     }
 
     // Branch-free, so that the loads can be scheduled among the MFMAs of the
-    // same K step: chunks at k >= K (the K tail, or a step past the end) get
-    // an out-of-range offset and load nothing.
+    // same K step: at k >= K (the K tail, or a step past the end) a lane's
+    // chunks get an out-of-range offset and load nothing.
     // (No test on the step as a whole: a uniform condition would be turned
-    // back into a branch.  k0 <= K + BK keeps kOutOfRange + 2 k0 below 2^32.)
-    __device__ __forceinline__ void issue(int k0, int K, SWIGLU_LDS char *panel_lds) const {
+    // back into a branch.  k0 <= K + BK keeps kOutOfRange + dj + 2 k0 below
+    // 2^32: dj < 2^31 for at most 256 rows of at most 2^21 elements.)
+    // Load `only` of the panel, or all NDMA loads when only < 0.
+    __device__ __forceinline__ void issue(int k0, SWIGLU_LDS char *panel_lds, int only = -1) const {
         const uint32_t soff = static_cast<uint32_t>(k0) * S::EB;
+        const uint32_t v0 = k0 < klim ? voff : kOutOfRange;
 #pragma unroll
-        for (int j = 0; j < NDMA; ++j) {
-            const uint32_t v = (k0 + kcol[j] < K) ? voff[j] : kOutOfRange;
-            dma16(rsrc, panel_lds + lds_off[j], v, soff);
-        }
+        for (int j = 0; j < NDMA; ++j)
+            if (only < 0 || only == j) dma16(rsrc, panel_lds + lds_off[j], v0 + dj[j], soff);
     }
 };
 
@@ -221,16 +267,18 @@ struct TileLoader {
         b.init(B, n0, K_);
     }
 
-    // Load K step `kstep` into `stage` with B panel `bp`; kstep >= ceil(K/BK)
-    // loads nothing.
-    __device__ __forceinline__ void issue(int kstep, SWIGLU_LDS char *stage,
+    // Load the A (part 0) or B (part 1, from panel `bp`) panel of K step
+    // `kstep` into the ring buffer `dst` (only its load `only`, if >= 0);
+    // kstep >= ceil(K/BK) loads nothing.
+    __device__ __forceinline__ void issue(int kstep, int part, SWIGLU_LDS char *dst, int only,
                                           const PanelLoader<S, S::BN, S::kDmaB> &bp) const {
         const int k0 = kstep * S::BK;
-        a.issue(k0, K, stage);
-        bp.issue(k0, K, stage + S::kABytes);
+        if (part == 0) a.issue(k0, dst, only);
+        else bp.issue(k0, dst, only);
     }
-    __device__ __forceinline__ void issue(int kstep, SWIGLU_LDS char *stage) const {
-        issue(kstep, stage, b);
+    __device__ __forceinline__ void issue(int kstep, int part, SWIGLU_LDS char *dst,
+                                          int only = -1) const {
+        issue(kstep, part, dst, only, b);
     }
 };
 
@@ -254,31 +302,40 @@ __device__ __forceinline__ u32x4 asm_read_b128(uint32_t addr) {
     return r;
 }
 
-// Per-lane LDS byte offsets of the fragment reads, relative to a stage base,
-// one per k-substep and 16-byte chunk for each operand (the swizzle mixes the
-// chunk index into the address); 32-row blocks tm / tn are +32 rows (the
-// swizzle has period 32).  Lane l (half h = l / 32) takes the kFragChunks
-// consecutive chunks starting at chunk kFragChunks * (2 KS + h) of its row:
-// for bf16 the 8 k of its MFMA operand; for FP8 32 consecutive k.  The same
-// lane-to-k assignment serves both operands, so whatever order the FP8 MFMA
-// gives those k within a lane, the products pair A and B at equal k.
+// Per-lane LDS byte offsets of the fragment reads, relative to a ring buffer,
+// one per k-substep and read j for each operand (the swizzle mixes the chunk
+// index into the address); 32-row blocks tm / tn are +32 rows (the swizzle
+// is periodic in 32 rows).
+//  MI = 32: lane l (half h = l / 32) reads the kFragChunks consecutive chunks
+//           starting at chunk kFragChunks * (2 KS + h) of row l % 32: for bf16
+//           the 8 k of its MFMA operand; for FP8 32 consecutive k;
+//  MI = 16: read j is row 16 j + l % 16 (the block's 16-row half j), chunk
+//           4 KS + l / 16: the 8 k of the lane's operand of the 16x16 MFMAs
+//           of that half.
+// The same lane-to-k assignment serves both operands, so whatever order an
+// MFMA gives the k within a lane, the products pair A and B at equal k.
 template <class S>
 struct FragOffsets {
     uint32_t a[S::kKSub][S::kFragChunks];
     uint32_t b[S::kKSub][S::kFragChunks];
 
     __device__ __forceinline__ void init(int wm, int wn, int lane) {
-        const int h = lane >> 5;
-        const int ra = wm * S::kWaveM + (lane & 31);
-        const int rb = wn * S::kWaveN + (lane & 31);
 #pragma unroll
         for (int ks = 0; ks < S::kKSub; ++ks)
 #pragma unroll
             for (int j = 0; j < S::kFragChunks; ++j) {
-                const int c = (ks * 2 + h) * S::kFragChunks + j;
+                int ra, rb, c;
+                if constexpr (S::MI == 16) {
+                    ra = wm * S::kWaveM + 16 * j + (lane & 15);
+                    rb = wn * S::kWaveN + 16 * j + (lane & 15);
+                    c = ks * 4 + (lane >> 4);
+                } else {
+                    ra = wm * S::kWaveM + (lane & 31);
+                    rb = wn * S::kWaveN + (lane & 31);
+                    c = (ks * 2 + (lane >> 5)) * S::kFragChunks + j;
+                }
                 a[ks][j] = static_cast<uint32_t>(ra * S::kRowBytes + ((c ^ swz<S>(ra)) * 16));
-                b[ks][j] = static_cast<uint32_t>(S::kABytes + rb * S::kRowBytes +
-                                                 ((c ^ swz<S>(rb)) * 16));
+                b[ks][j] = static_cast<uint32_t>(rb * S::kRowBytes + ((c ^ swz<S>(rb)) * 16));
             }
     }
 };
@@ -298,16 +355,52 @@ __device__ __forceinline__ void read_b_blocks(uint32_t p, Frags<S> &f, int j) {
     }
 }
 
-// Issue the fragment reads of k-substep KS from the stage at LDS address `stage`.
+// Issue the fragment reads of k-substep KS from the A and B ring buffers at
+// LDS addresses `sa` and `sb`.
 template <class S, int KS>
-__device__ __forceinline__ void read_frags(uint32_t stage, const FragOffsets<S> &o,
+__device__ __forceinline__ void read_frags(uint32_t sa, uint32_t sb, const FragOffsets<S> &o,
                                            Frags<S> &f) {
 #pragma unroll
     for (int j = 0; j < S::kFragChunks; ++j) {
-        read_a_blocks<S, 0>(stage + o.a[KS][j], f, j);
-        read_b_blocks<S, 0>(stage + o.b[KS][j], f, j);
+        read_a_blocks<S, 0>(sa + o.a[KS][j], f, j);
+        read_b_blocks<S, 0>(sb + o.b[KS][j], f, j);
     }
 }
+
+// Load issue order of the pipeline below, and the vmcnt waits it implies.
+// K step t's panels are loaded in group g = t - STAGES (A) and t - BSTAGES
+// (B); the prologue issues the groups -max(STAGES, BSTAGES) .. -1, and the
+// last substep of step t issues group t.  Inside a group the panel of the
+// shallower ring goes first (A when the depths are equal), so that the panel
+// needed soonest is never queued behind the one needed later.
+template <class S>
+struct IssueOrder {
+    static constexpr bool kAFirst = S::STAGES <= S::BSTAGES;
+    static constexpr int kDeep = S::STAGES > S::BSTAGES ? S::STAGES : S::BSTAGES;
+
+    // Loads issued after both panels of K step `s` when the groups up to
+    // `last` have been issued (vmcnt counts completions in issue order, so
+    // waiting for at most this many outstanding loads means step s landed).
+    static constexpr int loads_after(int s, int last) {
+        int total = 0, end_a = 0, end_b = 0;
+        for (int g = -kDeep; g <= last; ++g) {
+            for (int k = 0; k < 2; ++k) {
+                const bool a_part = (k == 0) == kAFirst;
+                const int step = g + (a_part ? S::STAGES : S::BSTAGES);
+                if (step < 0) continue;
+                total += a_part ? S::kDmaA : S::kDmaB;
+                if (step == s) (a_part ? end_a : end_b) = total;
+            }
+        }
+        return total - (end_a > end_b ? end_a : end_b);
+    }
+    // before step 0 (the prologue has issued groups up to -1)
+    static constexpr int kWaitPrologue = loads_after(0, -1);
+    // before step t+1, in step t (groups up to t-1 issued); the same for every t
+    static constexpr int kWaitSteady = loads_after(kDeep + 3, kDeep + 1);
+    static_assert(loads_after(kDeep + 4, kDeep + 2) == kWaitSteady, "steady state");
+    static_assert(kWaitPrologue < 64 && kWaitSteady < 64, "vmcnt is a 6-bit counter");
+};
 
 // Wait until every fragment read issued so far has landed, and make the
 // fragment registers of `f` depend on that wait (volatile asm statements keep
@@ -325,41 +418,70 @@ __device__ __forceinline__ void wait_frags(Frags<S> &f) {
     }
 }
 
-template <class S>
-__device__ __forceinline__ void mma(const Frags<S> &f, f32x16 (&acc)[S::TM][S::TN]) {
+// The MFMAs of one k-substep.  With 16x16 MFMAs (inline assembly, in
+// program order), `load(d)` is called after MFMA floor(d * n / nload) of the
+// n, for d < nload: the substep that refills the ring spreads its loads
+// among its MFMAs this way (the compiler's scheduler cannot see the assembly
+// MFMAs to interleave them); with 32x32 MFMAs the scheduler does it
+// (Pipeline::interleave_mfma_and_loads) and `load` is not called.
+template <class S, int kLoads = 0, class Load = void (*)(int)>
+__device__ __forceinline__ void mma(const Frags<S> &f, typename S::Acc (&acc)[S::TM][S::TN],
+                                    const Load &load = nullptr) {
+    constexpr int kMfma = S::TM * S::TN * S::kMfmaPerBlock;
 #pragma unroll
     for (int tm = 0; tm < S::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < S::TN; ++tn) {
-            if constexpr (S::EB == 2)
-                acc[tm][tn] = mfma_32x32x16(__builtin_bit_cast(bf16x8, f.a[tm][0]),
-                                            __builtin_bit_cast(bf16x8, f.b[tn][0]), acc[tm][tn]);
-            else
-                acc[tm][tn] = mfma_32x32x64_fp8(f.a[tm][0], f.a[tm][1], f.b[tn][0], f.b[tn][1],
-                                                acc[tm][tn]);
+            if constexpr (S::MI == 16) {
+                // quad 2 sm + sn: rows 16 sm, columns 16 sn of the block
+#pragma unroll
+                for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+                    for (int sn = 0; sn < 2; ++sn) {
+                        mfma_16x16x32_acc(acc[tm][tn].v[2 * sm + sn], f.a[tm][sm], f.b[tn][sn]);
+                        if constexpr (kLoads > 0) {
+                            const int i = ((tm * S::TN + tn) * 2 + sm) * 2 + sn;
+#pragma unroll
+                            for (int d = 0; d < kLoads; ++d)
+                                if (d * kMfma / kLoads == i) load(d);
+                        }
+                    }
+            } else if constexpr (S::EB == 2) {
+                acc[tm][tn].v = mfma_32x32x16(__builtin_bit_cast(bf16x8, f.a[tm][0]),
+                                              __builtin_bit_cast(bf16x8, f.b[tn][0]),
+                                              acc[tm][tn].v);
+            } else {
+                acc[tm][tn].v = mfma_32x32x64_fp8(f.a[tm][0], f.a[tm][1], f.b[tn][0], f.b[tn][1],
+                                                  acc[tm][tn].v);
+            }
         }
 }
 
 template <class S>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[S::TM][S::TN]) {
+__device__ __forceinline__ void zero_acc(typename S::Acc (&acc)[S::TM][S::TN]) {
 #pragma unroll
     for (int tm = 0; tm < S::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < S::TN; ++tn)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.0f;
+            for (int q = 0; q < 4; ++q) acc[tm][tn].set_quad(q, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+    // (assembly MFMAs read them: the accumulator writes' two wait states)
+    if constexpr (S::MI == 16) asm volatile("s_nop 1");
 }
 
 // ---------------------------------------------------------------------------
 // Plain pipeline (4 waves, one per SIMD).  A "step sequence" is a run of K
-// steps numbered 0..total-1; `issue(t, stage)` loads sequence step t into an
-// LDS stage.  Before step t+1 is read, each wave waits until at most
-// STAGES-2 later steps' loads are outstanding, then the workgroup meets at
-// one barrier, which also proves that every wave has finished reading step
-// t's buffer; that buffer is refilled with step t+STAGES right after it.  The
-// barrier sits before the MFMAs of step t's last k-substep, so those MFMAs
-// overlap the first fragment reads of step t+1; within a step the reads of
-// substep ks+1 overlap the MFMAs of substep ks.
+// steps numbered 0..total-1; `issue(t, part, dst, j)` loads the A (part 0)
+// or B (part 1) panel of sequence step t into the ring buffer `dst` (only its
+// load j if j >= 0).  Before step
+// t+1 is read, each wave waits until its loads of step t+1 have landed (the
+// later loads IssueOrder counts may stay in flight), then the workgroup meets
+// at one barrier, which also proves that every wave has finished reading
+// step t's buffers; they are refilled with step t+STAGES (A) and
+// t+BSTAGES (B) right after it.  The barrier sits before the MFMAs of step
+// t's last k-substep, so those MFMAs overlap the first fragment reads of step
+// t+1; within a step the reads of substep ks+1 overlap the MFMAs of substep
+// ks.
 // ---------------------------------------------------------------------------
 template <class S>
 struct Pipeline {
@@ -368,11 +490,46 @@ struct Pipeline {
     FragOffsets<S> off;
     Frags<S> f[2];
 
-    __device__ __forceinline__ SWIGLU_LDS char *stage(int t) const {
-        return lds + (t % S::STAGES) * S::kStageBytes;
+    using Order = IssueOrder<S>;
+
+    __device__ __forceinline__ SWIGLU_LDS char *stage_a(int t) const {
+        return lds + (t % S::STAGES) * S::kABytes;
     }
-    __device__ __forceinline__ uint32_t stage_addr(int t) const {
-        return lds_addr + static_cast<uint32_t>((t % S::STAGES) * S::kStageBytes);
+    __device__ __forceinline__ SWIGLU_LDS char *stage_b(int t) const {
+        return lds + S::kBRing + (t % S::BSTAGES) * S::kBBytes;
+    }
+    __device__ __forceinline__ uint32_t addr_a(int t) const {
+        return lds_addr + static_cast<uint32_t>((t % S::STAGES) * S::kABytes);
+    }
+    __device__ __forceinline__ uint32_t addr_b(int t) const {
+        return lds_addr + static_cast<uint32_t>(S::kBRing + (t % S::BSTAGES) * S::kBBytes);
+    }
+
+    // Group g of the issue order: the A panel of step g + STAGES and the B
+    // panel of step g + BSTAGES (each skipped if before step 0), the
+    // shallower ring's first.
+    template <class Issue>
+    __device__ __forceinline__ void issue_group(const Issue &issue, int g) const {
+        const int ta = g + S::STAGES, tb = g + S::BSTAGES;
+        if constexpr (Order::kAFirst) {
+            if (ta >= 0) issue(ta, 0, stage_a(ta), -1);
+            if (tb >= 0) issue(tb, 1, stage_b(tb), -1);
+        } else {
+            if (tb >= 0) issue(tb, 1, stage_b(tb), -1);
+            if (ta >= 0) issue(ta, 0, stage_a(ta), -1);
+        }
+    }
+    // Load d (d < kDmaPerStep) of steady-state group g, in the group's issue
+    // order.
+    template <class Issue>
+    __device__ __forceinline__ void issue_one(const Issue &issue, int g, int d) const {
+        const int ta = g + S::STAGES, tb = g + S::BSTAGES;
+        constexpr int kFirst = Order::kAFirst ? S::kDmaA : S::kDmaB;
+        const bool first = d < kFirst;
+        const bool a_part = first == Order::kAFirst;
+        const int j = first ? d : d - kFirst;
+        if (a_part) issue(ta, 0, stage_a(ta), j);
+        else issue(tb, 1, stage_b(tb), j);
     }
 
     __device__ __forceinline__ void init(SWIGLU_LDS char *lds_) {
@@ -389,12 +546,12 @@ struct Pipeline {
     template <class Issue>
     __device__ __forceinline__ void prologue_issue(const Issue &issue) {
 #pragma unroll
-        for (int t = 0; t < S::STAGES; ++t) issue(t, stage(t));
+        for (int g = -Order::kDeep; g < 0; ++g) issue_group(issue, g);
     }
     __device__ __forceinline__ void prologue_wait() {
-        wait_vmcnt<S::kDmaPerStep * (S::STAGES - 1)>();
+        wait_vmcnt<Order::kWaitPrologue>();
         block_barrier();
-        read_frags<S, 0>(stage_addr(0), off, f[0]);
+        read_frags<S, 0>(addr_a(0), addr_b(0), off, f[0]);
     }
     template <class Issue>
     __device__ __forceinline__ void prologue(const Issue &issue) {
@@ -404,12 +561,12 @@ struct Pipeline {
 
     template <int KS, class Issue, class Hook>
     __device__ __forceinline__ void substeps(const Issue &issue, int t, int total,
-                                             f32x16 (&acc)[S::TM][S::TN], const Hook &hook) {
+                                             typename S::Acc (&acc)[S::TM][S::TN], const Hook &hook) {
         constexpr int last = S::kKSub - 1;
         __builtin_amdgcn_sched_barrier(0);   // keep the previous substep's MFMAs above this wait
         wait_frags<S>(f[KS & 1]);
         if constexpr (KS < last) {
-            read_frags<S, KS + 1>(stage_addr(t), off, f[(KS + 1) & 1]);
+            read_frags<S, KS + 1>(addr_a(t), addr_b(t), off, f[(KS + 1) & 1]);
             hook(KS);
             mma<S>(f[KS & 1], acc);
             substeps<KS + 1>(issue, t, total, acc, hook);
@@ -419,20 +576,26 @@ struct Pipeline {
             // first fragment reads of step t+1 go out before this substep's
             // MFMAs (an LDS read lands asynchronously: its destination must
             // not be registers that MFMAs issued just before it still read),
-            // and the refill of stage t (step t+STAGES) after them, in one
+            // and the refill of step t's buffers (group t: steps t+STAGES and
+            // t+BSTAGES) after them, in one
             // straight-line block, so the scheduler can place those loads --
             // which write LDS, not registers -- among the MFMAs instead of
             // leaving the MFMA pipe idle while they are issued.  After the
             // last step the loads are masked dummies (the issue lambda maps
             // steps past the end to nothing) and the reads are unused; drain()
             // waits for them.
-            wait_vmcnt<S::kDmaPerStep * (S::STAGES - 2)>();
+            wait_vmcnt<Order::kWaitSteady>();
             block_barrier();
-            read_frags<S, 0>(stage_addr(t + 1), off, f[(KS + 1) & 1]);
+            read_frags<S, 0>(addr_a(t + 1), addr_b(t + 1), off, f[(KS + 1) & 1]);
             hook(KS);
-            mma<S>(f[KS & 1], acc);
-            issue(t + S::STAGES, stage(t));
-            interleave_mfma_and_loads();
+            if constexpr (S::MI == 16) {
+                mma<S, S::kDmaPerStep>(f[KS & 1], acc,
+                                       [&](int d) { issue_one(issue, t, d); });
+            } else {
+                mma<S>(f[KS & 1], acc);
+                issue_group(issue, t);
+                interleave_mfma_and_loads();
+            }
         }
     }
 
@@ -440,7 +603,7 @@ struct Pipeline {
     // the step's direct-to-LDS loads, and so on (sched_group_barrier masks:
     // 0x008 MFMA, 0x020 VMEM read).
     __device__ __forceinline__ static void interleave_mfma_and_loads() {
-        constexpr int kMfma = S::TM * S::TN;
+        constexpr int kMfma = S::TM * S::TN * S::kMfmaPerBlock;
         constexpr int kPer = (S::kDmaPerStep + kMfma - 1) / kMfma;
 #pragma unroll
         for (int i = 0; i < kMfma; ++i) {
@@ -451,14 +614,14 @@ struct Pipeline {
 
     template <class Issue, class Hook>
     __device__ __forceinline__ void step(const Issue &issue, int t, int total,
-                                         f32x16 (&acc)[S::TM][S::TN], const Hook &hook) {
+                                         typename S::Acc (&acc)[S::TM][S::TN], const Hook &hook) {
         static_assert(S::kKSub % 2 == 0, "fragment double buffer alternates per substep");
         substeps<0>(issue, t, total, acc, hook);
     }
 
     template <class Issue>
     __device__ __forceinline__ void run(const Issue &issue, int t_begin, int t_end, int total,
-                                        f32x16 (&acc)[S::TM][S::TN]) {
+                                        typename S::Acc (&acc)[S::TM][S::TN]) {
         for (int t = t_begin; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
     }
 
@@ -466,6 +629,8 @@ struct Pipeline {
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         block_barrier();
+        // the last assembly MFMAs' results are read from here on
+        if constexpr (S::MI == 16) wait_mfma_results();
     }
 };
 

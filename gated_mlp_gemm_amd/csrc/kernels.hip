@@ -154,14 +154,6 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t *__res
     }
 }
 
-// ---------------------------------------------------------------------------
-// Accumulator geometry: row of register i of 32x32 block (tm) for this lane.
-// ---------------------------------------------------------------------------
-template <class S>
-__device__ __forceinline__ int acc_row(int wm, int tm, int i, int lane) {
-    return wm * S::kWaveM + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
-
 // Output stores of the epilogues go through a buffer resource that spans the
 // tile's valid rows of a row-major [M][ld] bf16 matrix.  A store whose offset
 // lies past those rows, or that carries kOutOfRange (the column is past the
@@ -195,6 +187,27 @@ __device__ __forceinline__ void store_y_b16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ void store_y_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
     asm volatile("buffer_store_short_d16_hi %0, %1, %2, 0 offen nt" ::"v"(v), "v"(off), "s"(r)
                  : "memory");
+}
+// The same without the hint (variant S).
+__device__ __forceinline__ void store_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+    asm volatile("buffer_store_short_d16_hi %0, %1, %2, 0 offen" ::"v"(v), "v"(off), "s"(r)
+                 : "memory");
+}
+
+// Lane byte offsets of the two 16-column groups of a 32x32 accumulator block
+// in a row-major bf16 matrix with ld elements a row (col_r(r) / 16 selects
+// one): the lane's row `lrow` (relative to the store resource's first row),
+// columns c0 and c0 + 16 (relative to `col_base`); a column at or past
+// `cols_valid` gets kOutOfRange.  MI = 32 blocks use only the first.
+__device__ __forceinline__ void lane_offsets(uint32_t (&voff)[2], uint32_t lrow, int c0,
+                                             int cols_valid, int col_base, int ld) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = c0 + 16 * h;
+        voff[h] = c < cols_valid ? (lrow * static_cast<uint32_t>(ld) +
+                                    static_cast<uint32_t>(col_base + c)) * 2u
+                                 : kOutOfRange;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -240,8 +253,8 @@ struct PairMulEpilogueT {
     // kFromAcc: the blocks are MFMA accumulators (AGPRs), read out in order
     // (read_acc); else ordinary values (the split reduction's sums).
     template <class S, bool kFromAcc = true>
-    __device__ __forceinline__ void unit(const f32x16 &a0, const f32x16 &a1, int u, int m0, int n0,
-                                         int tid) const {
+    __device__ __forceinline__ void unit(const typename S::Acc &a0, const typename S::Acc &a1,
+                                         int u, int m0, int n0, int tid) const {
         const int lane = tid & 63;
         const int wave = tid >> 6;
         const int wm = wave / S::WN, wn = wave % S::WN;
@@ -249,56 +262,58 @@ struct PairMulEpilogueT {
         const int y0 = n0 / 2;                 // first Y column of the tile
         const int ycols_valid = min(S::BN / 2, N - y0);
         const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, ldy);
+        uint32_t voff[2];
         if constexpr (paired<S>()) {
             constexpr int kPairBlocks = S::TN / 2;
             const int tm = u / kPairBlocks, tp = u % kPairBlocks;
-            const f32x16 &g = a0, &up = a1;
-            const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, tm, 0, lane));
-            const int ycol = wn * (S::kWaveN / 2) + tp * 32 + (lane & 31);
-            const uint32_t voff =
-                ycol < ycols_valid
-                    ? (lrow * static_cast<uint32_t>(ldy) + static_cast<uint32_t>(y0 + ycol)) * 2u
-                    : kOutOfRange;
+            const typename S::Acc &g = a0, &up = a1;
+            const uint32_t lrow = static_cast<uint32_t>(wm * S::kWaveM + tm * 32 + S::row_l(lane));
+            lane_offsets(voff, lrow, wn * (S::kWaveN / 2) + tp * 32 + S::col_l(lane), ycols_valid,
+                         y0, ldy);
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
-                // registers i, i+1 are rows 8(i/4) + (i%4) and the next one
-                const float g0 = scaled(acc_value<kFromAcc>(g[i]));
-                const float g1 = scaled(acc_value<kFromAcc>(g[i + 1]));
-                const float u0 = scaled(acc_value<kFromAcc>(up[i]));
-                const float u1 = scaled(acc_value<kFromAcc>(up[i + 1]));
+                // registers i, i+1: rows row_r(i) and row_r(i) + 1, one column
+                const float g0 = scaled(acc_value<kFromAcc>(g.get(i)));
+                const float g1 = scaled(acc_value<kFromAcc>(g.get(i + 1)));
+                const float u0 = scaled(acc_value<kFromAcc>(up.get(i)));
+                const float u1 = scaled(acc_value<kFromAcc>(up.get(i + 1)));
                 const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
-                const uint32_t roff =
-                    static_cast<uint32_t>(acc_row<S>(0, 0, i, 0)) * static_cast<uint32_t>(ldy) * 2u;
-                store_y_b16(r, voff + roff, static_cast<uint16_t>(v));
-                store_y_b16_hi(r, voff + roff + static_cast<uint32_t>(ldy) * 2u, v);
+                const uint32_t off = voff[S::col_r(i) / 16] +
+                                     static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
+                store_y_b16(r, off, static_cast<uint16_t>(v));
+                store_y_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
             }
         } else {
             const int tm = u / S::TN, tn = u % S::TN;
             const bool odd = lane & 1;
             // even lanes finish accumulator registers 0..7, odd lanes 8..15,
-            // which sit 16 rows further down (acc_row with i = 8 + p)
-            const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, 0, odd ? 8 : 0, lane));
-            const int ycol = (wn * S::kWaveN + tn * 32 + (lane & 31)) >> 1;
-            const uint32_t voff =
-                ycol < ycols_valid
-                    ? (lrow * static_cast<uint32_t>(ldy) + static_cast<uint32_t>(y0 + ycol)) * 2u
-                    : kOutOfRange;
+            // which sit 16 rows further down (row_r(8 + p) = 16 + row_r(p))
+            const uint32_t lrow = static_cast<uint32_t>(wm * S::kWaveM + S::row_l(lane) + (odd ? 16 : 0));
+            // the Y column of the pair (Gate column, Up column) the lane is in
+            const int c0 = wn * S::kWaveN + tn * 32 + (S::col_l(lane) & ~1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int ycol = (c0 + 16 * h) >> 1;
+                voff[h] = ycol < ycols_valid
+                              ? (lrow * static_cast<uint32_t>(ldy) + static_cast<uint32_t>(y0 + ycol)) * 2u
+                              : kOutOfRange;
+            }
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
-                const float lo = a0[p], hi = a0[8 + p];
+                const float lo = a0.get(p), hi = a0.get(8 + p);
                 const float recv = swap_adjacent_lanes(by_lane_parity(hi, lo));
                 const float gate = scaled(by_lane_parity(lo, recv));
                 const float upv = scaled(by_lane_parity(recv, hi));
-                const uint32_t roff = static_cast<uint32_t>(acc_row<S>(0, tm, p, 0)) *
+                const uint32_t roff = static_cast<uint32_t>(tm * 32 + S::row_r(p)) *
                                       static_cast<uint32_t>(ldy) * 2u;
-                store_y_b16(r, voff + roff, to_bf16(silu(gate) * upv));
+                store_y_b16(r, voff[S::col_r(p) / 16] + roff, to_bf16(silu(gate) * upv));
             }
         }
     }
 
     template <class S>
-    __device__ __forceinline__ void apply(const f32x16 (&acc)[S::TM][S::TN], int m0, int n0,
-                                          int tid) const {
+    __device__ __forceinline__ void apply(const typename S::Acc (&acc)[S::TM][S::TN], int m0,
+                                          int n0, int tid) const {
         constexpr int kUnits = S::TM * S::TN / unit_blocks<S>();
         __builtin_amdgcn_sched_barrier(0);   // nothing of the epilogue moves into the mainloop
 #pragma unroll
@@ -333,31 +348,28 @@ struct StoreEpilogue {
     int M, N;
 
     template <class S, bool kFromAcc = true>
-    __device__ __forceinline__ void block(const f32x16 &a, int tm, int tn, int m0, int n0,
-                                          int tid) const {
+    __device__ __forceinline__ void block(const typename S::Acc &a, int tm, int tn, int m0,
+                                          int n0, int tid) const {
         const int lane = tid & 63;
         const int wave = tid >> 6;
         const int wm = wave / S::WN, wn = wave % S::WN;
         const int rows_valid = min(S::BM, M - m0);
         const int cols_valid = min(S::BN, N - n0);
         const __amdgpu_buffer_rsrc_t r = out_rsrc(C, m0, rows_valid, N);
-        const uint32_t lrow = static_cast<uint32_t>(acc_row<S>(wm, 0, 0, lane));
-        const int col = wn * S::kWaveN + tn * 32 + (lane & 31);
-        const uint32_t voff =
-            col < cols_valid
-                ? (lrow * static_cast<uint32_t>(N) + static_cast<uint32_t>(n0 + col)) * 2u
-                : kOutOfRange;
+        const uint32_t lrow = static_cast<uint32_t>(wm * S::kWaveM + S::row_l(lane));
+        uint32_t voff[2];
+        lane_offsets(voff, lrow, wn * S::kWaveN + tn * 32 + S::col_l(lane), cols_valid, n0, N);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const uint32_t roff =
-                static_cast<uint32_t>(acc_row<S>(0, tm, i, 0)) * static_cast<uint32_t>(N) * 2u;
-            store_b16(r, voff + roff, to_bf16(acc_value<kFromAcc>(a[i])));
+                static_cast<uint32_t>(tm * 32 + S::row_r(i)) * static_cast<uint32_t>(N) * 2u;
+            store_b16(r, voff[S::col_r(i) / 16] + roff, to_bf16(acc_value<kFromAcc>(a.get(i))));
         }
     }
 
     template <class S>
-    __device__ __forceinline__ void apply(const f32x16 (&acc)[S::TM][S::TN], int m0, int n0,
-                                          int tid) const {
+    __device__ __forceinline__ void apply(const typename S::Acc (&acc)[S::TM][S::TN], int m0,
+                                          int n0, int tid) const {
 #pragma unroll
         for (int tm = 0; tm < S::TM; ++tm)
 #pragma unroll
@@ -372,8 +384,8 @@ struct StoreEpilogue {
     template <class S>
     static constexpr int unit_blocks() { return 1; }
     template <class S, bool kFromAcc = true>
-    __device__ __forceinline__ void unit(const f32x16 &a0, const f32x16 &, int u, int m0, int n0,
-                                         int tid) const {
+    __device__ __forceinline__ void unit(const typename S::Acc &a0, const typename S::Acc &, int u,
+                                         int m0, int n0, int tid) const {
         block<S, kFromAcc>(a0, u / S::TN, u % S::TN, m0, n0, tid);
     }
     template <class S>
@@ -385,14 +397,16 @@ template <class S>
 __device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor &A,
                                               const KMajor &B, int M, int K, int m0, int n0,
                                               int kb, int ke, int nk,
-                                              f32x16 (&acc)[S::TM][S::TN]) {
+                                              typename S::Acc (&acc)[S::TM][S::TN]) {
     Pipeline<S> pl;
     pl.init(lds);
     TileLoader<S> ld;
     ld.init(A, m0, B, n0, K);
     const int len = ke - kb;
     // steps past the range load nothing (K step nk is past the end of K)
-    auto issue = [&](int s, SWIGLU_LDS char *st) { ld.issue(s < len ? kb + s : nk, st); };
+    auto issue = [&](int s, int part, SWIGLU_LDS char *dst, int j) {
+        ld.issue(s < len ? kb + s : nk, part, dst, j);
+    };
     zero_acc<S>(acc);
     pl.prologue(issue);
     pl.run(issue, 0, len, len, acc);
@@ -410,7 +424,7 @@ template <class S>
 struct QuarterOf {
     static constexpr int kStage = (S::BM / 2 + S::BN / 2) * S::kRowBytes;
     static constexpr int kStages = S::kLdsBytes / kStage < 4 ? S::kLdsBytes / kStage : 4;
-    using type = TileShape<S::BM / 2, S::BN / 2, S::BK, 2, 2, kStages, S::EB>;
+    using type = TileShape<S::BM / 2, S::BN / 2, S::BK, 2, 2, kStages, S::EB, kStages, S::MI>;
 };
 
 enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2 };
@@ -443,10 +457,12 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
         ld.init(Ak, tm * S::BM, B, tn * S::BN, K);
         const int nk = sch.nk;
         // steps past the end load nothing (K step nk is past the end of K)
-        auto issue = [&](int s, SWIGLU_LDS char *st) { ld.issue(s < nk ? s : nk, st); };
+        auto issue = [&](int s, int part, SWIGLU_LDS char *dst, int j) {
+            ld.issue(s < nk ? s : nk, part, dst, j);
+        };
         pl.prologue_issue(issue);
         for (; j < sch.dp; j += grid) {
-            f32x16 acc[S::TM][S::TN];
+            typename S::Acc acc[S::TM][S::TN];
             zero_acc<S>(acc);
             pl.prologue_wait();
             pl.run(issue, 0, nk, nk, acc);
@@ -474,7 +490,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
             const int n0 = tn * S::BN + (q & 1) * Q::BN;
             if (m0 >= M || n0 >= B.rows) continue;   // quarter wholly past the output's edge
-            f32x16 acc[Q::TM][Q::TN];
+            typename Q::Acc acc[Q::TM][Q::TN];
             tile_mainloop<Q>(lds, Ak, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
             epi.template apply<Q>(acc, m0, n0, threadIdx.x);
         }
@@ -487,7 +503,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             const int ke = (piece + 1) * sch.nk / sch.pieces;
             int tm, tn;
             tile_coords(t, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
-            f32x16 acc[S::TM][S::TN];
+            typename S::Acc acc[S::TM][S::TN];
             tile_mainloop<S>(lds, Ak, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
             store_partial<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN, acc,
                              threadIdx.x);
@@ -511,7 +527,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch
     const int w = (item % kPerTile) / kUnits;      // GEMM wave
     const int u = item % kUnits;                   // epilogue unit
     const int x = w * 64 + static_cast<int>(threadIdx.x & 63);
-    f32x16 a[kUnitBlocks];
+    typename S::Acc a[kUnitBlocks];
 #pragma unroll
     for (int k = 0; k < kUnitBlocks; ++k)
         a[k] = sum_pieces<S>(sch, i, Epi::template unit_block<S>(u, k), x);
@@ -558,13 +574,13 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
     ld.init(KMajor{A, M, 1, 0, 0, lda}, m0, KMajor{Wf, N, 2, 0}, n0, K);
     PanelLoader<S, S::BN, S::kDmaB> up;
     up.init(KMajor{Wf, N, 2, 1}, n0, K);
-    auto issue = [&](int t, SWIGLU_LDS char *st) {
-        if (t < nk) ld.issue(t, st);
-        else ld.issue(t - nk, st, up);   // t - nk >= nk loads nothing
+    auto issue = [&](int t, int part, SWIGLU_LDS char *dst, int j) {
+        if (t < nk) ld.issue(t, part, dst, j);
+        else ld.issue(t - nk, part, dst, j, up);   // t - nk >= nk loads nothing
     };
     Pipeline<S> pl;
     pl.init(lds);
-    f32x16 g[S::TM][S::TN], u[S::TM][S::TN];
+    typename S::Acc g[S::TM][S::TN], u[S::TM][S::TN];
     zero_acc<S>(g);
     zero_acc<S>(u);
 
@@ -585,9 +601,9 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
                 if (b < kBlocks) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        float x = g[b / S::TN][b % S::TN][i];
+                        float x = g[b / S::TN][b % S::TN].get(i);
                         if constexpr (kScaled) x *= scale;
-                        g[b / S::TN][b % S::TN][i] = silu(x);
+                        g[b / S::TN][b % S::TN].set(i, silu(x));
                     }
                 }
             });
@@ -599,9 +615,9 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
         if (b >= nk * S::kKSub) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float x = g[b / S::TN][b % S::TN][i];
+                float x = g[b / S::TN][b % S::TN].get(i);
                 if constexpr (kScaled) x *= scale;
-                g[b / S::TN][b % S::TN][i] = silu(x);
+                g[b / S::TN][b % S::TN].set(i, silu(x));
             }
         }
     }
@@ -609,21 +625,30 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
     pl.run(issue, nk + kSiluSteps, 2 * nk, 2 * nk, u);
     pl.drain();
 
-    // multiply and store
+    // multiply and store (two rows per conversion, through a buffer resource
+    // over the tile's valid rows, as variant I's epilogue)
     const int cols_valid = min(S::BN, N - n0);
+    const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, ldy);
 #pragma unroll
     for (int tm = 0; tm < S::TM; ++tm) {
 #pragma unroll
         for (int tn = 0; tn < S::TN; ++tn) {
-            const int col = wn * S::kWaveN + tn * 32 + (lane & 31);
+            const uint32_t lrow = static_cast<uint32_t>(wm * S::kWaveM + tm * 32 + S::row_l(lane));
+            uint32_t voff[2];
+            lane_offsets(voff, lrow, wn * S::kWaveN + tn * 32 + S::col_l(lane), cols_valid, n0,
+                         ldy);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = acc_row<S>(wm, tm, i, lane);
-                if (row < rows_valid && col < cols_valid) {
-                    float up = u[tm][tn][i];
-                    if constexpr (kScaled) up *= scale;
-                    Y[(int64_t)(m0 + row) * ldy + n0 + col] = to_bf16(g[tm][tn][i] * up);
+            for (int i = 0; i < 16; i += 2) {
+                float u0 = u[tm][tn].get(i), u1 = u[tm][tn].get(i + 1);
+                if constexpr (kScaled) {
+                    u0 *= scale;
+                    u1 *= scale;
                 }
+                const uint32_t v = pack_bf16x2(g[tm][tn].get(i) * u0, g[tm][tn].get(i + 1) * u1);
+                const uint32_t off = voff[S::col_r(i) / 16] +
+                                     static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
+                store_b16(r, off, static_cast<uint16_t>(v));
+                store_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
             }
         }
     }
@@ -633,25 +658,35 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
 // Tile shapes and launchers
 // ---------------------------------------------------------------------------
 // I and the ablation GEMMs: 4 waves, one per SIMD, each with a 128x128 block
-// (256 accumulator registers, which the compiler keeps in AGPRs), BK = 64 and
-// a two-stage ring (128 KiB of LDS); measured 10-16 % faster than the 8-wave
-// ping-pong 256x256x32 shape on M=2048..8192 outputs.
-using ShapeWide = TileShape<256, 256, 64, 2, 2, 2>;
+// (256 accumulator registers, in AGPRs), BK = 64 and a two-stage ring (128 KiB
+// of LDS); measured 10-16 % faster than an 8-wave ping-pong 256x256x32 shape
+// on M=2048..8192 outputs.  16x16x32 MFMAs: under the power-limited clock of
+// sustained MFMA load they deliver about 12 % more than 32x32x16 ones (an
+// MFMA-only loop on random operands, all CUs: 1978 against 1760 TFLOP/s),
+// and this kernel runs 4-5 % faster with them at M=4096 K=8192 N=29568 and
+// M=8192 K=5120 N=13824 (equal at M <= 2048).  A third stage for one operand
+// (160 KiB) measured -1 % to +1.5 %: the ring keeps two.
+using ShapeWide = TileShape<256, 256, 64, 2, 2, 2, 2, 2, 16>;
 // The alternative for I and the ablation GEMMs: 128x128x64 tiles, 4 waves of
 // 64x64, two stages (64 KiB), so two workgroups share a CU and one's prologue
 // and epilogue overlap the other's mainloop; four times the tiles also fill
-// the last round better.  Chosen per call by quad_tiles_faster().
-using ShapeQuad = TileShape<128, 128, 64, 2, 2, 2>;
+// the last round better.  Chosen per call by quad_tiles_faster().  16x16x32
+// MFMAs, as the 256x256 shape.
+using ShapeQuad = TileShape<128, 128, 64, 2, 2, 2, 2, 2, 16>;
 // S: 128x128 output tiles, 4 waves each holding 64x64 Gate and Up
 // accumulators, two stages (64 KiB), two workgroups per CU; measured against
 // 256x128x64 (one per CU, 3 stages): 34 % faster at M=2048 K=1536 N=8960, 7 %
-// at M=8192 K=5120 N=13824, equal at M=4096 K=8192 N=29568.
+// at M=8192 K=5120 N=13824, equal at M=4096 K=8192 N=29568.  32x32x16
+// MFMAs: with two workgroups per CU each wave has 256 registers, which the
+// 16x16 form's doubled fragment registers next to the Gate and Up
+// accumulators exceed.
 using ShapeSeq = TileShape<128, 128, 64, 2, 2, 2>;
 // M <= 128 (all paths): 128x64 tiles, which put twice the workgroups of a
 // 128x128 tile on the weight stream, with BK = 64 and four stages (96 KiB) to
 // keep HBM loads in flight; measured with weights streamed from HBM against
 // 128x64x32 x 4 stages: 21 % faster at M=128 K=896 N=4864, 24-29 % on K =
-// 5120..8192 (up to 4.2 TB/s of weights).
+// 5120..8192 (up to 4.2 TB/s of weights).  32x32x16 MFMAs: the 16x16x32
+// form measured 2 % slower here (M = 128, bound by the weight stream).
 using ShapeSmall = TileShape<128, 64, 64, 2, 2, 4>;
 // Variant I on FP8 operands: the same three shapes with K steps of 128 FP8
 // values, so every tile row of a stage is 128 bytes and the LDS rings, load

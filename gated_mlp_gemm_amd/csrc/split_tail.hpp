@@ -42,14 +42,13 @@ struct Schedule {
     float *partials;        // one BM*BN slot per piece: slot j = piece j % pieces of split tile j / pieces
 };
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 // A partial tile is stored thread-major: float4 number i of GEMM thread x at
 // float4 index i * threads + x, so every access is a coalesced 16-byte one.
-// Float4 number i of a thread holds registers 4(i%4)..4(i%4)+3 of its
-// accumulator block i/4 (block = tm * TN + tn).
+// Float4 number i of a thread holds register quad i%4 of its accumulator
+// block i/4 (block = tm * TN + tn).
 template <class S>
-__device__ __forceinline__ void store_partial(float *slot, const f32x16 (&acc)[S::TM][S::TN],
+__device__ __forceinline__ void store_partial(float *slot,
+                                              const typename S::Acc (&acc)[S::TM][S::TN],
                                               int tid) {
     f32x4 *dst = reinterpret_cast<f32x4 *>(slot);
 #pragma unroll
@@ -59,9 +58,7 @@ __device__ __forceinline__ void store_partial(float *slot, const f32x16 (&acc)[S
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = (tm * S::TN + tn) * 4 + j;
-                dst[i * S::kThreads + tid] =
-                    f32x4{acc[tm][tn][4 * j], acc[tm][tn][4 * j + 1], acc[tm][tn][4 * j + 2],
-                          acc[tm][tn][4 * j + 3]};
+                dst[i * S::kThreads + tid] = acc[tm][tn].quad(j);
             }
 }
 
@@ -71,7 +68,8 @@ __device__ __forceinline__ void store_partial(float *slot, const f32x16 (&acc)[S
 // round trip per piece); the additions still run strictly in piece order, so
 // the result does not depend on the grouping.
 template <class S>
-__device__ __forceinline__ f32x16 sum_pieces(const Schedule &sch, int i, int blk, int x) {
+__device__ __forceinline__ typename S::Acc sum_pieces(const Schedule &sch, int i, int blk,
+                                                     int x) {
     constexpr int64_t kSlot4 = static_cast<int64_t>(S::BM) * S::BN / 4;   // float4 per slot
     constexpr int kGroup = 4;
     const f32x4 *first = reinterpret_cast<const f32x4 *>(sch.partials) +
@@ -96,14 +94,9 @@ __device__ __forceinline__ f32x16 sum_pieces(const Schedule &sch, int i, int blk
             for (int j = 0; j < 4; ++j)
                 if (p + g < sch.pieces) sum[j] += v[g][j];
     }
-    f32x16 a;
+    typename S::Acc a;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        a[4 * j] = sum[j].x;
-        a[4 * j + 1] = sum[j].y;
-        a[4 * j + 2] = sum[j].z;
-        a[4 * j + 3] = sum[j].w;
-    }
+    for (int j = 0; j < 4; ++j) a.set_quad(j, sum[j]);
     return a;
 }
 

@@ -196,7 +196,7 @@ def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("fetch_dir")
     p.add_argument("write_dir")
-    p.add_argument("--workload", default="M=2048,K=1536,N=8960")
+    p.add_argument("--workload", default="M=4096,K=8192,N=29568")
     p.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     p.add_argument("--paths", default=",".join(PATHS),
                    help="which paths of the run to record (default: all found)")

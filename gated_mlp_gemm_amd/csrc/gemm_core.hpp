@@ -99,9 +99,7 @@ struct TileShape {
     static_assert(kABytes % (kThreads * 16) == 0 && kDmaA >= 1, "A tile must split evenly");
     static_assert(kBBytes % (kThreads * 16) == 0 && kDmaB >= 1, "B tile must split evenly");
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup is 160 KiB");
-    static_assert(STAGES >= 2 && STAGES <= 8 && BSTAGES >= 2 && BSTAGES <= 8, "ring depth");
-    static_assert(BSTAGES - STAGES <= 1 && STAGES - BSTAGES <= 1,
-                  "the two rings differ by at most one stage");
+    static_assert(STAGES >= 2 && STAGES <= 16 && BSTAGES >= 2 && BSTAGES <= 16, "ring depth");
     static_assert(kDmaA * STAGES + kDmaB * BSTAGES < 64, "vmcnt is a 6-bit counter");
     static_assert(kWaves == 4, "4 waves, one per SIMD (the pipeline below)");
 
@@ -397,8 +395,15 @@ struct IssueOrder {
     // before step 0 (the prologue has issued groups up to -1)
     static constexpr int kWaitPrologue = loads_after(0, -1);
     // before step t+1, in step t (groups up to t-1 issued); the same for every t
-    static constexpr int kWaitSteady = loads_after(kDeep + 3, kDeep + 1);
-    static_assert(loads_after(kDeep + 4, kDeep + 2) == kWaitSteady, "steady state");
+    static constexpr int kWaitSteady = loads_after(2 * kDeep + 3, 2 * kDeep + 1);
+    static_assert(loads_after(2 * kDeep + 4, 2 * kDeep + 2) == kWaitSteady, "steady state");
+    // every wait from the first step on is the steady one
+    static constexpr bool steady_from_start() {
+        for (int t = 0; t <= 2 * kDeep; ++t)
+            if (loads_after(t + 1, t - 1) != kWaitSteady) return false;
+        return true;
+    }
+    static_assert(steady_from_start(), "the first steps wait as the steady state does");
     static_assert(kWaitPrologue < 64 && kWaitSteady < 64, "vmcnt is a 6-bit counter");
 };
 
@@ -418,35 +423,15 @@ __device__ __forceinline__ void wait_frags(Frags<S> &f) {
     }
 }
 
-// The MFMAs of one k-substep.  With 16x16 MFMAs (inline assembly, in
-// program order), `load(d)` is called after MFMA floor(d * n / nload) of the
-// n, for d < nload: the substep that refills the ring spreads its loads
-// among its MFMAs this way (the compiler's scheduler cannot see the assembly
-// MFMAs to interleave them); with 32x32 MFMAs the scheduler does it
-// (Pipeline::interleave_mfma_and_loads) and `load` is not called.
-template <class S, int kLoads = 0, class Load = void (*)(int)>
-__device__ __forceinline__ void mma(const Frags<S> &f, typename S::Acc (&acc)[S::TM][S::TN],
-                                    const Load &load = nullptr) {
-    constexpr int kMfma = S::TM * S::TN * S::kMfmaPerBlock;
+// The MFMAs of one k-substep (32x32 MFMAs; the 16x16 ones go through mma16).
+template <class S>
+__device__ __forceinline__ void mma(const Frags<S> &f, typename S::Acc (&acc)[S::TM][S::TN]) {
+    static_assert(S::MI == 32, "16x16 MFMAs: mma16");
 #pragma unroll
     for (int tm = 0; tm < S::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < S::TN; ++tn) {
-            if constexpr (S::MI == 16) {
-                // quad 2 sm + sn: rows 16 sm, columns 16 sn of the block
-#pragma unroll
-                for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-                    for (int sn = 0; sn < 2; ++sn) {
-                        mfma_16x16x32_acc(acc[tm][tn].v[2 * sm + sn], f.a[tm][sm], f.b[tn][sn]);
-                        if constexpr (kLoads > 0) {
-                            const int i = ((tm * S::TN + tn) * 2 + sm) * 2 + sn;
-#pragma unroll
-                            for (int d = 0; d < kLoads; ++d)
-                                if (d * kMfma / kLoads == i) load(d);
-                        }
-                    }
-            } else if constexpr (S::EB == 2) {
+            if constexpr (S::EB == 2) {
                 acc[tm][tn].v = mfma_32x32x16(__builtin_bit_cast(bf16x8, f.a[tm][0]),
                                               __builtin_bit_cast(bf16x8, f.b[tn][0]),
                                               acc[tm][tn].v);
@@ -455,6 +440,69 @@ __device__ __forceinline__ void mma(const Frags<S> &f, typename S::Acc (&acc)[S:
                                                   acc[tm][tn].v);
             }
         }
+}
+
+// Fragment read R of k-substep KS (R < kFragChunks (TM + TN), in the order of
+// read_frags: for each read j, the TM A blocks, then the TN B blocks).
+template <class S, int KS, int R>
+__device__ __forceinline__ void read_frag_one(uint32_t sa, uint32_t sb, const FragOffsets<S> &o,
+                                              Frags<S> &f) {
+    constexpr int kPer = S::TM + S::TN;
+    constexpr int j = R / kPer, b = R % kPer;
+    if constexpr (b < S::TM)
+        f.a[b][j] = asm_read_b128<b * 32 * S::kRowBytes>(sa + o.a[KS][j]);
+    else
+        f.b[b - S::TM][j] = asm_read_b128<(b - S::TM) * 32 * S::kRowBytes>(sb + o.b[KS][j]);
+}
+
+// The 16x16 MFMAs of one k-substep, issued one by one (inline assembly, in
+// program order) on the fragments `cur`, and between them:
+//  - the fragment reads of the next k-substep KSN (from the ring buffers at
+//    LDS addresses sa / sb, into `nxt`): read R after MFMA R n / (2 r) of the
+//    n, so that all r of them go out in the first half of the substep and
+//    have landed when the next substep starts;
+//  - if kLoads > 0, `load(d)` after MFMA d n / kLoads (the direct-to-LDS
+//    loads of the substep that refills the ring).
+// A 16x16x32 MFMA keeps the MFMA pipe busy for only 16 cycles, so a run of
+// reads or loads issued back to back would leave it idle; spread out, each
+// issues in the shadow of the MFMA before it.  (The compiler's scheduler
+// cannot interleave them: it does not see the assembly MFMAs.)  The reads
+// write the other fragment buffer, which the previous substep's MFMAs read:
+// those were issued before these reads, and a read's data lands long after
+// an MFMA has taken its operands.
+template <class S, int KSN, int kLoads, int I, class Load, int... R, int... D>
+__device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa,
+                                         uint32_t sb, const FragOffsets<S> &o,
+                                         typename S::Acc (&acc)[S::TM][S::TN], const Load &load,
+                                         std::integer_sequence<int, R...>,
+                                         std::integer_sequence<int, D...>) {
+    constexpr int kMfma = S::TM * S::TN * 4;
+    constexpr int kReads = sizeof...(R);
+    constexpr int tm = I / (4 * S::TN), tn = (I / 4) % S::TN, sm = (I / 2) % 2, sn = I % 2;
+    // quad 2 sm + sn of block (tm, tn): rows 16 sm, columns 16 sn
+    mfma_16x16x32_acc(acc[tm][tn].v[2 * sm + sn], cur.a[tm][sm], cur.b[tn][sn]);
+    (
+        [&] {
+            if constexpr (R * (kMfma / 2) / kReads == I) read_frag_one<S, KSN, R>(sa, sb, o, nxt);
+        }(),
+        ...);
+    (
+        [&] {
+            if constexpr (kLoads > 0 && D * kMfma / (kLoads > 0 ? kLoads : 1) == I) load(D);
+        }(),
+        ...);
+}
+template <class S, int KSN, int kLoads, int I = 0, class Load>
+__device__ __forceinline__ void mma16(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa, uint32_t sb,
+                                      const FragOffsets<S> &o,
+                                      typename S::Acc (&acc)[S::TM][S::TN], const Load &load) {
+    static_assert(S::MI == 16, "16x16 MFMAs");
+    if constexpr (I < S::TM * S::TN * 4) {
+        mma16_at<S, KSN, kLoads, I>(cur, nxt, sa, sb, o, acc, load,
+                                    std::make_integer_sequence<int, S::kFragChunks * (S::TM + S::TN)>{},
+                                    std::make_integer_sequence<int, (kLoads > 0 ? kLoads : 1)>{});
+        mma16<S, KSN, kLoads, I + 1>(cur, nxt, sa, sb, o, acc, load);
+    }
 }
 
 template <class S>
@@ -566,9 +614,15 @@ struct Pipeline {
         __builtin_amdgcn_sched_barrier(0);   // keep the previous substep's MFMAs above this wait
         wait_frags<S>(f[KS & 1]);
         if constexpr (KS < last) {
-            read_frags<S, KS + 1>(addr_a(t), addr_b(t), off, f[(KS + 1) & 1]);
-            hook(KS);
-            mma<S>(f[KS & 1], acc);
+            if constexpr (S::MI == 16) {
+                hook(KS);
+                mma16<S, KS + 1, 0>(f[KS & 1], f[(KS + 1) & 1], addr_a(t), addr_b(t), off, acc,
+                                    [](int) {});
+            } else {
+                read_frags<S, KS + 1>(addr_a(t), addr_b(t), off, f[(KS + 1) & 1]);
+                hook(KS);
+                mma<S>(f[KS & 1], acc);
+            }
             substeps<KS + 1>(issue, t, total, acc, hook);
         } else {
             // Step t+1's loads have landed (own wait, then everyone's via the
@@ -586,12 +640,14 @@ struct Pipeline {
             // waits for them.
             wait_vmcnt<Order::kWaitSteady>();
             block_barrier();
-            read_frags<S, 0>(addr_a(t + 1), addr_b(t + 1), off, f[(KS + 1) & 1]);
-            hook(KS);
             if constexpr (S::MI == 16) {
-                mma<S, S::kDmaPerStep>(f[KS & 1], acc,
-                                       [&](int d) { issue_one(issue, t, d); });
+                hook(KS);
+                mma16<S, 0, S::kDmaPerStep>(f[KS & 1], f[(KS + 1) & 1], addr_a(t + 1),
+                                            addr_b(t + 1), off, acc,
+                                            [&](int d) { issue_one(issue, t, d); });
             } else {
+                read_frags<S, 0>(addr_a(t + 1), addr_b(t + 1), off, f[(KS + 1) & 1]);
+                hook(KS);
                 mma<S>(f[KS & 1], acc);
                 issue_group(issue, t);
                 interleave_mfma_and_loads();

@@ -470,38 +470,45 @@ __device__ __forceinline__ void read_frag_one(uint32_t sa, uint32_t sb, const Fr
 // write the other fragment buffer, which the previous substep's MFMAs read:
 // those were issued before these reads, and a read's data lands long after
 // an MFMA has taken its operands.
-template <class S, int KSN, int kLoads, int I, class Load, int... R, int... D>
+template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, int I, class Load,
+          int... R, int... D>
 __device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa,
                                          uint32_t sb, const FragOffsets<S> &o,
                                          typename S::Acc (&acc)[S::TM][S::TN], const Load &load,
                                          std::integer_sequence<int, R...>,
                                          std::integer_sequence<int, D...>) {
-    constexpr int kMfma = S::TM * S::TN * 4;
-    constexpr int kReads = sizeof...(R);
+    constexpr int kSpan = kEnd - kBegin;
+    constexpr int kNReads = sizeof...(R);
     constexpr int tm = I / (4 * S::TN), tn = (I / 4) % S::TN, sm = (I / 2) % 2, sn = I % 2;
     // quad 2 sm + sn of block (tm, tn): rows 16 sm, columns 16 sn
     mfma_16x16x32_acc(acc[tm][tn].v[2 * sm + sn], cur.a[tm][sm], cur.b[tn][sn]);
     (
         [&] {
-            if constexpr (R * (kMfma / 2) / kReads == I) read_frag_one<S, KSN, R>(sa, sb, o, nxt);
+            if constexpr (kReads && kBegin + R * (kSpan / 2) / kNReads == I)
+                read_frag_one<S, KSN, R>(sa, sb, o, nxt);
         }(),
         ...);
     (
         [&] {
-            if constexpr (kLoads > 0 && D * kMfma / (kLoads > 0 ? kLoads : 1) == I) load(D);
+            if constexpr (kLoads > 0 && kBegin + D * kSpan / (kLoads > 0 ? kLoads : 1) == I)
+                load(D);
         }(),
         ...);
 }
-template <class S, int KSN, int kLoads, int I = 0, class Load>
+// MFMAs [kBegin, kEnd) of the substep, with the reads (if kReads) and loads
+// spread over that range.
+template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, int I = kBegin,
+          class Load>
 __device__ __forceinline__ void mma16(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa, uint32_t sb,
                                       const FragOffsets<S> &o,
                                       typename S::Acc (&acc)[S::TM][S::TN], const Load &load) {
     static_assert(S::MI == 16, "16x16 MFMAs");
-    if constexpr (I < S::TM * S::TN * 4) {
-        mma16_at<S, KSN, kLoads, I>(cur, nxt, sa, sb, o, acc, load,
-                                    std::make_integer_sequence<int, S::kFragChunks * (S::TM + S::TN)>{},
-                                    std::make_integer_sequence<int, (kLoads > 0 ? kLoads : 1)>{});
-        mma16<S, KSN, kLoads, I + 1>(cur, nxt, sa, sb, o, acc, load);
+    if constexpr (I < kEnd) {
+        mma16_at<S, KSN, kReads, kLoads, kBegin, kEnd, I>(
+            cur, nxt, sa, sb, o, acc, load,
+            std::make_integer_sequence<int, S::kFragChunks * (S::TM + S::TN)>{},
+            std::make_integer_sequence<int, (kLoads > 0 ? kLoads : 1)>{});
+        mma16<S, KSN, kReads, kLoads, kBegin, kEnd, I + 1>(cur, nxt, sa, sb, o, acc, load);
     }
 }
 
@@ -539,6 +546,15 @@ struct Pipeline {
     Frags<S> f[2];
 
     using Order = IssueOrder<S>;
+    static constexpr int kMfma16 = S::TM * S::TN * 4;   // 16x16 MFMAs per substep
+    // 16x16 MFMAs of the last substep issued before its wait and barrier, so
+    // the MFMA pipe works while the workgroup meets: a quarter of the
+    // substep's (measured at M=4096 K=8192 N=29568 and M=2048 K=1536 N=8960
+    // with 0, 4, 8, 16, 24, 32, 40 of the 256x256 tile's 64: 16 fastest, +1 %
+    // and +5 % over none; more delays the refill loads)
+    static constexpr int kEarlyMfma = kMfma16 / 4;
+    static_assert(S::MI != 16 || (kEarlyMfma > 0 && kEarlyMfma < kMfma16),
+                  "MFMAs on both sides of the barrier");
 
     __device__ __forceinline__ SWIGLU_LDS char *stage_a(int t) const {
         return lds + (t % S::STAGES) * S::kABytes;
@@ -616,8 +632,8 @@ struct Pipeline {
         if constexpr (KS < last) {
             if constexpr (S::MI == 16) {
                 hook(KS);
-                mma16<S, KS + 1, 0>(f[KS & 1], f[(KS + 1) & 1], addr_a(t), addr_b(t), off, acc,
-                                    [](int) {});
+                mma16<S, KS + 1, true, 0, 0, kMfma16>(f[KS & 1], f[(KS + 1) & 1], addr_a(t),
+                                                      addr_b(t), off, acc, [](int) {});
             } else {
                 read_frags<S, KS + 1>(addr_a(t), addr_b(t), off, f[(KS + 1) & 1]);
                 hook(KS);
@@ -638,14 +654,20 @@ struct Pipeline {
             // last step the loads are masked dummies (the issue lambda maps
             // steps past the end to nothing) and the reads are unused; drain()
             // waits for them.
-            wait_vmcnt<Order::kWaitSteady>();
-            block_barrier();
             if constexpr (S::MI == 16) {
+                // the first kEarlyMfma MFMAs of this substep (operands already
+                // in registers) go out before the wait and the barrier
                 hook(KS);
-                mma16<S, 0, S::kDmaPerStep>(f[KS & 1], f[(KS + 1) & 1], addr_a(t + 1),
-                                            addr_b(t + 1), off, acc,
-                                            [&](int d) { issue_one(issue, t, d); });
+                mma16<S, 0, false, 0, 0, kEarlyMfma>(f[KS & 1], f[(KS + 1) & 1], 0, 0, off, acc,
+                                                     [](int) {});
+                wait_vmcnt<Order::kWaitSteady>();
+                block_barrier();
+                mma16<S, 0, true, S::kDmaPerStep, kEarlyMfma, kMfma16>(
+                    f[KS & 1], f[(KS + 1) & 1], addr_a(t + 1), addr_b(t + 1), off, acc,
+                    [&](int d) { issue_one(issue, t, d); });
             } else {
+                wait_vmcnt<Order::kWaitSteady>();
+                block_barrier();
                 read_frags<S, 0>(addr_a(t + 1), addr_b(t + 1), off, f[(KS + 1) & 1]);
                 hook(KS);
                 mma<S>(f[KS & 1], acc);

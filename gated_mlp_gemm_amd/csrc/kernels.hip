@@ -664,9 +664,11 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
 // sustained MFMA load they deliver about 12 % more than 32x32x16 ones (an
 // MFMA-only loop on random operands, all CUs: 1978 against 1760 TFLOP/s),
 // and this kernel runs 4-5 % faster with them at M=4096 K=8192 N=29568 and
-// M=8192 K=5120 N=13824 (equal at M <= 2048).  A third stage for one operand
-// (160 KiB) measured -1 % to +1.5 %: the ring keeps two.
-using ShapeWide = TileShape<256, 256, 64, 2, 2, 2, 2, 2, 16>;
+// M=8192 K=5120 N=13824 (equal at M <= 2048).  A third stage for the weight
+// panel (B ring 3 deep, all 160 KiB of LDS): +0.8 % at M=4096 K=8192
+// N=29568, +1.1 % at M=8192 K=5120 N=13824, +2.6 % at M=2048 K=1536 N=8960
+// with the interleaved 16x16 schedule (a third A stage instead: 9 % slower).
+using ShapeWide = TileShape<256, 256, 64, 2, 2, 2, 2, 3, 16>;
 // The alternative for I and the ablation GEMMs: 128x128x64 tiles, 4 waves of
 // 64x64, two stages (64 KiB), so two workgroups share a CU and one's prologue
 // and epilogue overlap the other's mainloop; four times the tiles also fill

@@ -45,7 +45,7 @@ PATHS = {
           (("split_reduce_kernel", "PairMulEpilogueT<false>"), 1)],
     "fp8": [(("gemm_tiles_kernel", "PairMulEpilogueT<true>"), 1),
             (("split_reduce_kernel", "PairMulEpilogueT<true>"), 1)],
-    "s": [(("fused_sequential_kernel",), 1)],
+    "s": [(("fused_sequential",), 1)],
     "ablation": [(("gemm_tiles_kernel", "StoreEpilogue"), 2),
                  (("split_reduce_kernel", "StoreEpilogue"), 2),
                  (("silu_mul_kernel",), 1)],

@@ -45,6 +45,11 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b
 __device__ __forceinline__ void mfma_16x16x32_acc(f32x4 &c, const u32x4 &a, const u32x4 &b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
+// The same with a zero accumulator input: c = a b, the first MFMA of a
+// contraction (no zeroing of c before it, which the compiler could move).
+__device__ __forceinline__ void mfma_16x16x32_init(f32x4 &c, const u32x4 &a, const u32x4 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+}
 // At least 24 wait states: more than any MFMA result needs before another
 // instruction may read it (the longest, 32x32 MFMAs, need 19).
 __device__ __forceinline__ void wait_mfma_results() {

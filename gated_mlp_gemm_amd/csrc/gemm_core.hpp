@@ -200,8 +200,9 @@ struct PanelLoader {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t voff;         // byte offset of this lane's chunk of load 0 at k0 = 0
     int klim;              // K minus the first k of that chunk: step k0 loads iff k0 < klim
-    uint32_t dj[NDMA];     // uniform: bytes from load 0's row to load j's
-    int lds_off[NDMA];     // uniform: LDS byte offset (within the panel) of load j's block
+    uint32_t row_bytes;    // uniform: bytes from one panel row to the next
+    int pairs;             // uniform: a de-interleaved panel (KMajor::pairs)
+    int lds_base;          // uniform: LDS byte offset of the wave's block of load 0
 
     // Panel = logical rows [r0, r0 + NROWS) of `op`.
     __device__ __forceinline__ void init(const KMajor &op, int r0, int K) {
@@ -220,19 +221,19 @@ struct PanelLoader {
         const int p = wave * 64 + lane;                   // physical chunk of load 0
         const int row = p / S::kChunksPerRow;             // its LDS row (< R)
         const int c = (p % S::kChunksPerRow) ^ swz<S>(row);
-        const int grow = op.pairs ? pair_row(row) : row;  // panel row it holds
-        const uint32_t row_bytes = static_cast<uint32_t>(op.stride) *
-                                   static_cast<uint32_t>(pitch) * S::EB;
+        pairs = op.pairs;
+        const int grow = pairs ? pair_row(row) : row;     // panel row it holds
+        row_bytes = static_cast<uint32_t>(op.stride) * static_cast<uint32_t>(pitch) * S::EB;
         voff = static_cast<uint32_t>(grow) * row_bytes + c * 16u;
         klim = K - c * S::kElemsPerChunk;
-#pragma unroll
-        for (int j = 0; j < NDMA; ++j) {
-            // panel rows from load 0's to load j's: the LDS distance j R, or
-            // in a de-interleaved panel pair_row(j R) (R is a multiple of 32)
-            const int drow = op.pairs ? pair_row(j * R) : j * R;
-            dj[j] = static_cast<uint32_t>(drow) * row_bytes;
-            lds_off[j] = (j * S::kWaves + wave) * 1024;
-        }
+        lds_base = wave * 1024;
+    }
+
+    // Uniform bytes from load 0's panel row to load j's: the LDS distance
+    // j R rows, or in a de-interleaved panel pair_row(j R) (R is a multiple
+    // of 32).
+    __device__ __forceinline__ uint32_t dj(int j) const {
+        return static_cast<uint32_t>(pairs ? pair_row(j * R) : j * R) * row_bytes;
     }
 
     // Branch-free, so that the loads can be scheduled among the MFMAs of the
@@ -247,7 +248,8 @@ struct PanelLoader {
         const uint32_t v0 = k0 < klim ? voff : kOutOfRange;
 #pragma unroll
         for (int j = 0; j < NDMA; ++j)
-            if (only < 0 || only == j) dma16(rsrc, panel_lds + lds_off[j], v0 + dj[j], soff);
+            if (only < 0 || only == j)
+                dma16(rsrc, panel_lds + lds_base + j * S::kWaves * 1024, v0 + dj(j), soff);
     }
 };
 
@@ -470,8 +472,8 @@ __device__ __forceinline__ void read_frag_one(uint32_t sa, uint32_t sb, const Fr
 // write the other fragment buffer, which the previous substep's MFMAs read:
 // those were issued before these reads, and a read's data lands long after
 // an MFMA has taken its operands.
-template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, int I, class Load,
-          int... R, int... D>
+template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, bool kInit, int I,
+          class Load, int... R, int... D>
 __device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa,
                                          uint32_t sb, const FragOffsets<S> &o,
                                          typename S::Acc (&acc)[S::TM][S::TN], const Load &load,
@@ -481,7 +483,8 @@ __device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uin
     constexpr int kNReads = sizeof...(R);
     constexpr int tm = I / (4 * S::TN), tn = (I / 4) % S::TN, sm = (I / 2) % 2, sn = I % 2;
     // quad 2 sm + sn of block (tm, tn): rows 16 sm, columns 16 sn
-    mfma_16x16x32_acc(acc[tm][tn].v[2 * sm + sn], cur.a[tm][sm], cur.b[tn][sn]);
+    if constexpr (kInit) mfma_16x16x32_init(acc[tm][tn].v[2 * sm + sn], cur.a[tm][sm], cur.b[tn][sn]);
+    else mfma_16x16x32_acc(acc[tm][tn].v[2 * sm + sn], cur.a[tm][sm], cur.b[tn][sn]);
     (
         [&] {
             if constexpr (kReads && kBegin + R * (kSpan / 2) / kNReads == I)
@@ -496,19 +499,19 @@ __device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uin
         ...);
 }
 // MFMAs [kBegin, kEnd) of the substep, with the reads (if kReads) and loads
-// spread over that range.
-template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, int I = kBegin,
-          class Load>
+// spread over that range; kInit: they start the accumulators (C = 0).
+template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, bool kInit = false,
+          int I = kBegin, class Load>
 __device__ __forceinline__ void mma16(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa, uint32_t sb,
                                       const FragOffsets<S> &o,
                                       typename S::Acc (&acc)[S::TM][S::TN], const Load &load) {
     static_assert(S::MI == 16, "16x16 MFMAs");
     if constexpr (I < kEnd) {
-        mma16_at<S, KSN, kReads, kLoads, kBegin, kEnd, I>(
+        mma16_at<S, KSN, kReads, kLoads, kBegin, kEnd, kInit, I>(
             cur, nxt, sa, sb, o, acc, load,
             std::make_integer_sequence<int, S::kFragChunks * (S::TM + S::TN)>{},
             std::make_integer_sequence<int, (kLoads > 0 ? kLoads : 1)>{});
-        mma16<S, KSN, kReads, kLoads, kBegin, kEnd, I + 1>(cur, nxt, sa, sb, o, acc, load);
+        mma16<S, KSN, kReads, kLoads, kBegin, kEnd, kInit, I + 1>(cur, nxt, sa, sb, o, acc, load);
     }
 }
 
@@ -623,7 +626,9 @@ struct Pipeline {
         prologue_wait();
     }
 
-    template <int KS, class Issue, class Hook>
+    // kInit: the step starts the accumulators (16x16 MFMAs only: its first
+    // substep's MFMAs take C = 0, no zero_acc() before it).
+    template <int KS, bool kInit, class Issue, class Hook>
     __device__ __forceinline__ void substeps(const Issue &issue, int t, int total,
                                              typename S::Acc (&acc)[S::TM][S::TN], const Hook &hook) {
         constexpr int last = S::kKSub - 1;
@@ -632,14 +637,14 @@ struct Pipeline {
         if constexpr (KS < last) {
             if constexpr (S::MI == 16) {
                 hook(KS);
-                mma16<S, KS + 1, true, 0, 0, kMfma16>(f[KS & 1], f[(KS + 1) & 1], addr_a(t),
-                                                      addr_b(t), off, acc, [](int) {});
+                mma16<S, KS + 1, true, 0, 0, kMfma16, kInit && KS == 0>(
+                    f[KS & 1], f[(KS + 1) & 1], addr_a(t), addr_b(t), off, acc, [](int) {});
             } else {
                 read_frags<S, KS + 1>(addr_a(t), addr_b(t), off, f[(KS + 1) & 1]);
                 hook(KS);
                 mma<S>(f[KS & 1], acc);
             }
-            substeps<KS + 1>(issue, t, total, acc, hook);
+            substeps<KS + 1, kInit>(issue, t, total, acc, hook);
         } else {
             // Step t+1's loads have landed (own wait, then everyone's via the
             // barrier), and every wave has finished reading stage t.  The
@@ -690,17 +695,25 @@ struct Pipeline {
         }
     }
 
-    template <class Issue, class Hook>
+    template <bool kInit = false, class Issue, class Hook>
     __device__ __forceinline__ void step(const Issue &issue, int t, int total,
                                          typename S::Acc (&acc)[S::TM][S::TN], const Hook &hook) {
         static_assert(S::kKSub % 2 == 0, "fragment double buffer alternates per substep");
-        substeps<0>(issue, t, total, acc, hook);
+        static_assert(!kInit || S::MI == 16, "accumulator start by MFMA: 16x16 path");
+        substeps<0, kInit>(issue, t, total, acc, hook);
     }
 
     template <class Issue>
     __device__ __forceinline__ void run(const Issue &issue, int t_begin, int t_end, int total,
                                         typename S::Acc (&acc)[S::TM][S::TN]) {
         for (int t = t_begin; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
+    }
+    // The same, with step t_begin (< t_end) starting the accumulators.
+    template <class Issue>
+    __device__ __forceinline__ void run_init(const Issue &issue, int t_begin, int t_end, int total,
+                                             typename S::Acc (&acc)[S::TM][S::TN]) {
+        step<true>(issue, t_begin, total, acc, [](int) {});
+        run(issue, t_begin + 1, t_end, total, acc);
     }
 
     __device__ __forceinline__ void drain() {

@@ -584,6 +584,8 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
     zero_acc<S>(g);
     zero_acc<S>(u);
 
+    constexpr int kBlocks = S::TM * S::TN;
+    constexpr int kSiluSteps = (kBlocks + S::kKSub - 1) / S::kKSub;
     // Gate loop
     pl.prologue(issue);
     pl.run(issue, 0, nk, 2 * nk, g);
@@ -591,8 +593,6 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
     // SiLU window: the first Up K steps run with one 32x32 Gate block activated
     // per k-substep, so the VALU/transcendental work interleaves with the Up
     // MFMAs (independent registers) while the Up tiles stream into LDS.
-    constexpr int kBlocks = S::TM * S::TN;
-    constexpr int kSiluSteps = (kBlocks + S::kKSub - 1) / S::kKSub;
 #pragma unroll
     for (int j = 0; j < kSiluSteps; ++j) {
         if (j < nk) {
@@ -655,6 +655,120 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
 }
 
 // ---------------------------------------------------------------------------
+// Variant S, persistent [abstract; gist: Method, Kernel-1]: the same
+// sequence per output tile (Gate contraction, SiLU on the register-resident
+// Gate accumulator while the first Up steps run, Up contraction, multiply and
+// store), on tiles as large as variant I's in registers -- BM x BN outputs
+// with BM x BN Gate and BM x BN Up accumulators -- and with variant I's
+// persistent loop: workgroup b runs tiles b, b + grid, ... (XCD-ordered), and
+// puts the first K steps of its next tile in flight before the epilogue of
+// the current one.  bf16 operands; 16x16 MFMAs.
+// ---------------------------------------------------------------------------
+// SiLU on a Gate accumulator block of 16x16 quads, each quad written back to
+// its AGPRs (the empty tie keeps the compiler from moving the activated block
+// into VGPRs, which the Up loop's fragments need).
+// After the last assembly MFMA into `acc`: wait until its results are
+// written, and redefine the accumulators after that wait, so that no copy
+// the compiler makes of them (it does not know the MFMAs' latency) can read
+// them earlier.
+template <class S>
+__device__ __forceinline__ void settle_acc(typename S::Acc (&acc)[S::TM][S::TN]) {
+    wait_mfma_results();
+#pragma unroll
+    for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+        for (int c = 0; c < S::TN; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) asm volatile("" : "+a"(acc[a][c].v[q]));
+}
+
+template <class S>
+__global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_persistent_kernel(
+    const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y, int M,
+    int N, int K, int lda, int ldy, int tiles_m, int tiles_n) {
+    static_assert(S::MI == 16 && S::EB == 2, "16x16 MFMAs on bf16 operands");
+    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+    SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
+    const int ntiles = tiles_m * tiles_n;
+    const int grid = gridDim.x;
+    int j = blockIdx.x;
+    if (j >= ntiles) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    const int nk = (K + S::BK - 1) / S::BK;
+
+    // One step sequence of 2*nk K steps per tile: steps [0, nk) contract
+    // against the Gate columns of W_fused (even packed rows), steps [nk, 2nk)
+    // against the Up columns (odd packed rows); the loads run ahead across
+    // the boundary, and into the next tile.
+    TileLoader<S> ld;
+    PanelLoader<S, S::BN, S::kDmaB> up;
+    int tm, tn;
+    auto start = [&](int jj) {
+        tile_coords(xcd_order(jj, ntiles), tiles_m, tiles_n, 8, tm, tn);
+        ld.init(KMajor{A, M, 1, 0, 0, lda}, tm * S::BM, KMajor{Wf, N, 2, 0, 0, 0}, tn * S::BN, K);
+        up.init(KMajor{Wf, N, 2, 1, 0, 0}, tn * S::BN, K);
+    };
+    // (a uniform select of the Gate or Up panel, not a branch: these loads
+    // are issued one by one among the MFMAs)
+    auto issue = [&](int t, int part, SWIGLU_LDS char *dst, int jj) {
+        const bool gate = t < nk;
+        ld.issue(gate ? t : t - nk, part, dst, jj, gate ? ld.b : up);   // t - nk >= nk: nothing
+    };
+    Pipeline<S> pl;
+    pl.init(lds);
+    start(j);
+    pl.prologue_issue(issue);
+    for (; j < ntiles; j += grid) {
+        typename S::Acc g[S::TM][S::TN], u[S::TM][S::TN];
+        pl.prologue_wait();
+        // Gate loop, then the Up loop, each started by its first K step's
+        // MFMAs (C = 0).  The Gate accumulators are held untouched until
+        // the epilogue applies SiLU: the compiler, which does not know the
+        // assembly MFMAs' latency, must have no reason to copy accumulators
+        // next to MFMAs still writing them.
+        pl.run_init(issue, 0, nk, 2 * nk, g);
+        settle_acc<S>(g);
+        pl.run_init(issue, nk, 2 * nk, 2 * nk, u);
+        pl.drain();
+        const int m0 = tm * S::BM, n0 = tn * S::BN;   // this tile's first row and Y column
+        if (j + grid < ntiles) {
+            start(j + grid);
+            pl.prologue_issue(issue);
+        }
+        // multiply and store: two rows per conversion, through a buffer
+        // resource over the tile's valid rows
+        const int rows_valid = min(S::BM, M - m0);
+        const int cols_valid = min(S::BN, N - n0);
+        const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, ldy);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < S::TM; ++a) {
+#pragma unroll
+            for (int c = 0; c < S::TN; ++c) {
+                const uint32_t lrow = static_cast<uint32_t>(wm * S::kWaveM + a * 32 + S::row_l(lane));
+                uint32_t voff[2];
+                lane_offsets(voff, lrow, wn * S::kWaveN + c * 32 + S::col_l(lane), cols_valid, n0,
+                             ldy);
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float u0 = read_acc(u[a][c].get(i)), u1 = read_acc(u[a][c].get(i + 1));
+                    const float g0 = read_acc(g[a][c].get(i)), g1 = read_acc(g[a][c].get(i + 1));
+                    const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+                    const uint32_t off = voff[S::col_r(i) / 16] +
+                                         static_cast<uint32_t>(S::row_r(i)) *
+                                             static_cast<uint32_t>(ldy) * 2u;
+                    store_y_b16(r, off, static_cast<uint16_t>(v));
+                    store_y_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tile shapes and launchers
 // ---------------------------------------------------------------------------
 // I and the ablation GEMMs: 4 waves, one per SIMD, each with a 128x128 block
@@ -683,6 +797,10 @@ using ShapeQuad = TileShape<128, 128, 64, 2, 2, 2, 2, 2, 16>;
 // 16x16 form's doubled fragment registers next to the Gate and Up
 // accumulators exceed.
 using ShapeSeq = TileShape<128, 128, 64, 2, 2, 2>;
+// S above M = 128, persistent: 256 x 128 output tiles (Gate and Up each 128 x
+// 64 per wave: 256 accumulator registers, as variant I's 256x256 tile),
+// 16x16 MFMAs, rings of 3 A and 3 B stages (144 KiB).
+using ShapeSeqP = TileShape<256, 128, 64, 2, 2, 3, 2, 3, 16>;
 // M <= 128 (all paths): 128x64 tiles, which put twice the workgroups of a
 // 128x128 tile on the weight stream, with BK = 64 and four stages (96 KiB) to
 // keep HBM loads in flight; measured with weights streamed from HBM against
@@ -969,12 +1087,17 @@ int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *e
                                ws.cus, buf, n);
 }
 
-int describe_fused_sequential(int M, int N, char *buf, size_t n) {
-    const bool small = M <= 128;
-    const int bm = small ? ShapeSmall::BM : ShapeSeq::BM, bn = small ? ShapeSmall::BN : ShapeSeq::BN;
-    const int bk = small ? ShapeSmall::BK : ShapeSeq::BK;
-    return std::snprintf(buf, n, "fused_sequential_kernel<%dx%dx%d> (%lld tiles)", bm, bn, bk,
-                         static_cast<long long>(cdiv(M, bm)) * cdiv(N, bn));
+int describe_fused_sequential(int M, int N, int cus, char *buf, size_t n) {
+    if (M <= 128)
+        return std::snprintf(buf, n, "fused_sequential_kernel<%dx%dx%d> (%lld tiles)",
+                             ShapeSmall::BM, ShapeSmall::BN, ShapeSmall::BK,
+                             static_cast<long long>(cdiv(M, ShapeSmall::BM)) * cdiv(N, ShapeSmall::BN));
+    using P = ShapeSeqP;
+    const long long tiles = static_cast<long long>(cdiv(M, P::BM)) * cdiv(N, P::BN);
+    const long long wgs = cus > 0 && cus < tiles ? cus : tiles;
+    return std::snprintf(buf, n,
+                         "fused_sequential_persistent_kernel<%dx%dx%d> (%lld tiles; %lld workgroups)",
+                         P::BM, P::BN, P::BK, tiles, wgs);
 }
 
 // Variant I on FP8 operands: the same GEMM over W_fused with K steps of 128
@@ -1012,13 +1135,18 @@ int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf
 }
 
 hipError_t launch_fused_sequential(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
-                                   int ldy, int M, int N, int K, hipStream_t stream) {
+                                   int ldy, int M, int N, int K, int cus, hipStream_t stream) {
     const void *a = A, *w = Wf;
     if (M <= 128)
         return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, a, w,
                                         Y, M, N, K, lda, ldy, 1.0f);
-    return launch_tiles<ShapeSeq>(fused_sequential_kernel<ShapeSeq>, M, N, stream, a, w, Y, M,
-                                  N, K, lda, ldy, 1.0f);
+    using P = ShapeSeqP;
+    const int tiles_m = cdiv(M, P::BM), tiles_n = cdiv(N, P::BN);
+    const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
+    const int grid = static_cast<int>(cus > 0 && cus < tiles ? cus : tiles);
+    hipLaunchKernelGGL(fused_sequential_persistent_kernel<P>, dim3(grid), dim3(P::kThreads), 0,
+                       stream, a, w, Y, M, N, K, lda, ldy, tiles_m, tiles_n);
+    return hipGetLastError();
 }
 
 // Variant S on FP8 operands: the same kernel with K steps of 128 FP8 values.

@@ -659,7 +659,9 @@ def test_describe_launch(dev, monkeypatch):
     monkeypatch.delenv("SWIGLU_TAIL")
     monkeypatch.setenv("SWIGLU_I_TILE", "128")
     assert "128x128x64" in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
-    assert sw.swiglu_describe_launch(2048, 8960, 1536, "s").startswith("fused_sequential_kernel<")
+    d = sw.swiglu_describe_launch(2048, 8960, 1536, "s")
+    assert d.startswith("fused_sequential_persistent_kernel<256x128x64> (560 tiles; 256 workgroups)"), d
+    assert sw.swiglu_describe_launch(128, 8960, 1536, "s").startswith("fused_sequential_kernel<")
     assert sw.swiglu_describe_launch(2048, 8960, 1536, "ablation").startswith("2 x gemm_tiles")
     assert "128x128x64" in sw.swiglu_describe_launch(128, 4864, 896, "i")    # forced at M <= 128
     monkeypatch.setenv("SWIGLU_I_TILE", "256")

@@ -55,6 +55,15 @@ def build(isa: bool = False, verbose: bool = False) -> str:
     return LIBRARY
 
 
+def device_assembly(path: str) -> str:
+    """Compile csrc/kernels.hip's device code alone, with the library's flags,
+    to gfx950 assembly at `path`; returns `path`."""
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    _run([HIPCC, *COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, "kernels.hip"),
+          "-o", path])
+    return path
+
+
 if __name__ == "__main__":
     path = build(isa="--isa" in sys.argv, verbose=True)
     print(path)

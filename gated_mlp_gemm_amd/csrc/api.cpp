@@ -280,7 +280,7 @@ int swiglu_describe_launch(int64_t M, int64_t N, int64_t K, int variant,
     } else if (v == kDescribeDownProj) {
         swiglu::describe_gemm((int)M, (int)K, (int)N, ws, "StoreEpilogue", buf, buf_bytes);
     } else if (v == SWIGLU_VARIANT_S) {
-        swiglu::describe_fused_sequential((int)M, (int)N, cus, buf, buf_bytes);
+        swiglu::describe_fused_sequential((int)M, (int)N, (int)K, ws, buf, buf_bytes);
     } else if (v == SWIGLU_VARIANT_I) {
         swiglu::describe_gemm((int)M, (int)(2 * N), (int)K, ws, "PairMulEpilogue", buf, buf_bytes,
                               true);
@@ -334,7 +334,8 @@ int swiglu_fused_gemm_strided(const uint16_t *A, int64_t lda, const uint16_t *W_
                                                          s),
                         "fused interleaved");
     return launched(swiglu::launch_fused_sequential(A, (int)lda, W_fused, Y, (int)ldy, (int)M,
-                                                    (int)N, (int)K, cus, s),
+                                                    (int)N, (int)K,
+                                                    make_ws(workspace, workspace_bytes, cus), s),
                     "fused sequential");
 }
 
@@ -380,7 +381,8 @@ int swiglu_fused_gemm_noalloc(const uint16_t *A, const uint16_t *W_fused, uint16
                                                          make_ws(ptr, kScratchBytes, cus), s),
                         "fused interleaved (no-alloc)");
     return launched(swiglu::launch_fused_sequential(A, (int)K, W_fused, Y, (int)N, (int)M,
-                                                    (int)N, (int)K, cus, s),
+                                                    (int)N, (int)K,
+                                                    make_ws(ptr, kScratchBytes, cus), s),
                     "fused sequential (no-alloc)");
 }
 
@@ -532,7 +534,7 @@ int swiglu_gated_mlp(const uint16_t *A, const uint16_t *W_fused, const uint16_t 
                        ? swiglu::launch_fused_interleaved(A, (int)K, W_fused, H, (int)N, (int)M,
                                                           (int)N, (int)K, ws, s)
                        : swiglu::launch_fused_sequential(A, (int)K, W_fused, H, (int)N, (int)M,
-                                                         (int)N, (int)K, cus, s);
+                                                         (int)N, (int)K, ws, s);
     if (e != hipSuccess) return launched(e, "gated MLP: fused SwiGLU");
     return launched(swiglu::launch_down_proj(H, W3t, Out, (int)M, (int)N, (int)K, ws, s),
                     "gated MLP: down projection");

@@ -682,89 +682,140 @@ __device__ __forceinline__ void settle_acc(typename S::Acc (&acc)[S::TM][S::TN])
             for (int q = 0; q < 4; ++q) asm volatile("" : "+a"(acc[a][c].v[q]));
 }
 
+// The S epilogue of one tile: Y = SiLU(Gate) * Up, two rows per conversion,
+// through a buffer resource over the tile's valid rows.
 template <class S>
-__global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_persistent_kernel(
-    const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y, int M,
-    int N, int K, int lda, int ldy, int tiles_m, int tiles_n) {
-    static_assert(S::MI == 16 && S::EB == 2, "16x16 MFMAs on bf16 operands");
-    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
-    SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
-    const int ntiles = tiles_m * tiles_n;
-    const int grid = gridDim.x;
-    int j = blockIdx.x;
-    if (j >= ntiles) return;
+__device__ __forceinline__ void seq_epilogue(const typename S::Acc (&g)[S::TM][S::TN],
+                                             const typename S::Acc (&u)[S::TM][S::TN],
+                                             uint16_t *Y, int M, int N, int ldy, int m0, int n0) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / S::WN, wn = wave % S::WN;
-    const int nk = (K + S::BK - 1) / S::BK;
+    const int rows_valid = min(S::BM, M - m0);
+    const int cols_valid = min(S::BN, N - n0);
+    const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, ldy);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int a = 0; a < S::TM; ++a) {
+#pragma unroll
+        for (int c = 0; c < S::TN; ++c) {
+            const uint32_t lrow = static_cast<uint32_t>(wm * S::kWaveM + a * 32 + S::row_l(lane));
+            uint32_t voff[2];
+            lane_offsets(voff, lrow, wn * S::kWaveN + c * 32 + S::col_l(lane), cols_valid, n0,
+                         ldy);
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const float u0 = read_acc(u[a][c].get(i)), u1 = read_acc(u[a][c].get(i + 1));
+                const float g0 = read_acc(g[a][c].get(i)), g1 = read_acc(g[a][c].get(i + 1));
+                const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+                const uint32_t off = voff[S::col_r(i) / 16] +
+                                     static_cast<uint32_t>(S::row_r(i)) *
+                                         static_cast<uint32_t>(ldy) * 2u;
+                store_y_b16(r, off, static_cast<uint16_t>(v));
+                store_y_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
+        }
+    }
+}
 
-    // One step sequence of 2*nk K steps per tile: steps [0, nk) contract
-    // against the Gate columns of W_fused (even packed rows), steps [nk, 2nk)
-    // against the Up columns (odd packed rows); the loads run ahead across
-    // the boundary, and into the next tile.
+// The loaders of an S tile: the A rows and the Gate panel (even packed rows),
+// and the Up panel (odd packed rows), of the tile at (m0, n0).
+template <class S>
+struct SeqLoaders {
     TileLoader<S> ld;
     PanelLoader<S, S::BN, S::kDmaB> up;
-    int tm, tn;
-    auto start = [&](int jj) {
-        tile_coords(xcd_order(jj, ntiles), tiles_m, tiles_n, 8, tm, tn);
-        ld.init(KMajor{A, M, 1, 0, 0, lda}, tm * S::BM, KMajor{Wf, N, 2, 0, 0, 0}, tn * S::BN, K);
-        up.init(KMajor{Wf, N, 2, 1, 0, 0}, tn * S::BN, K);
-    };
-    // (a uniform select of the Gate or Up panel, not a branch: these loads
-    // are issued one by one among the MFMAs)
-    auto issue = [&](int t, int part, SWIGLU_LDS char *dst, int jj) {
+    int nk;
+
+    __device__ __forceinline__ void init(const void *A, const void *Wf, int M, int N, int K,
+                                         int lda, int m0, int n0) {
+        nk = (K + S::BK - 1) / S::BK;
+        ld.init(KMajor{A, M, 1, 0, 0, lda}, m0, KMajor{Wf, N, 2, 0, 0, 0}, n0, K);
+        up.init(KMajor{Wf, N, 2, 1, 0, 0}, n0, K);
+    }
+    // Step t of the tile's sequence of 2 nk K steps: Gate steps [0, nk), Up
+    // steps [nk, 2 nk); steps past the end load nothing.  (A uniform select of
+    // the panel, not a branch: these loads are issued one by one among the
+    // MFMAs.)
+    __device__ __forceinline__ void operator()(int t, int part, SWIGLU_LDS char *dst,
+                                               int j) const {
         const bool gate = t < nk;
-        ld.issue(gate ? t : t - nk, part, dst, jj, gate ? ld.b : up);   // t - nk >= nk: nothing
-    };
-    Pipeline<S> pl;
-    pl.init(lds);
-    start(j);
-    pl.prologue_issue(issue);
-    for (; j < ntiles; j += grid) {
-        typename S::Acc g[S::TM][S::TN], u[S::TM][S::TN];
-        pl.prologue_wait();
-        // Gate loop, then the Up loop, each started by its first K step's
-        // MFMAs (C = 0).  The Gate accumulators are held untouched until
-        // the epilogue applies SiLU: the compiler, which does not know the
-        // assembly MFMAs' latency, must have no reason to copy accumulators
-        // next to MFMAs still writing them.
-        pl.run_init(issue, 0, nk, 2 * nk, g);
-        settle_acc<S>(g);
-        pl.run_init(issue, nk, 2 * nk, 2 * nk, u);
-        pl.drain();
-        const int m0 = tm * S::BM, n0 = tn * S::BN;   // this tile's first row and Y column
-        if (j + grid < ntiles) {
-            start(j + grid);
-            pl.prologue_issue(issue);
-        }
-        // multiply and store: two rows per conversion, through a buffer
-        // resource over the tile's valid rows
-        const int rows_valid = min(S::BM, M - m0);
-        const int cols_valid = min(S::BN, N - n0);
-        const __amdgpu_buffer_rsrc_t r = out_rsrc(Y, m0, rows_valid, ldy);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int a = 0; a < S::TM; ++a) {
-#pragma unroll
-            for (int c = 0; c < S::TN; ++c) {
-                const uint32_t lrow = static_cast<uint32_t>(wm * S::kWaveM + a * 32 + S::row_l(lane));
-                uint32_t voff[2];
-                lane_offsets(voff, lrow, wn * S::kWaveN + c * 32 + S::col_l(lane), cols_valid, n0,
-                             ldy);
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float u0 = read_acc(u[a][c].get(i)), u1 = read_acc(u[a][c].get(i + 1));
-                    const float g0 = read_acc(g[a][c].get(i)), g1 = read_acc(g[a][c].get(i + 1));
-                    const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
-                    const uint32_t off = voff[S::col_r(i) / 16] +
-                                         static_cast<uint32_t>(S::row_r(i)) *
-                                             static_cast<uint32_t>(ldy) * 2u;
-                    store_y_b16(r, off, static_cast<uint16_t>(v));
-                    store_y_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
-                }
-                __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
+        ld.issue(gate ? t : t - nk, part, dst, j, gate ? ld.b : up);
+    }
+};
+
+// The two contractions of an S tile, each started by its first K step's
+// MFMAs (C = 0).  The Gate accumulators are held untouched until the
+// epilogue applies SiLU: the compiler, which does not know the assembly
+// MFMAs' latency, must have no reason to copy accumulators next to MFMAs
+// still writing them.
+template <class S>
+__device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoaders<S> &issue,
+                                                 typename S::Acc (&g)[S::TM][S::TN],
+                                                 typename S::Acc (&u)[S::TM][S::TN]) {
+    const int nk = issue.nk;
+    pl.run_init(issue, 0, nk, 2 * nk, g);
+    settle_acc<S>(g);
+    pl.run_init(issue, nk, 2 * nk, 2 * nk, u);
+    pl.drain();
+}
+
+// Variant S, persistent, on 16x16 MFMAs: workgroup b runs whole tiles b,
+// b + grid, ... below dp (XCD-ordered) and puts the first K steps of its next
+// tile in flight before each epilogue; then its share of the 4 * quarter_tiles
+// quarter-size tiles of the last round's tiles [dp, dp + quarter_tiles)
+// (quarter q: row half q/2 % 2, column half q % 2 of tile dp + q / 4), each run
+// on its own with a deeper ring.
+template <class S>
+__global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_persistent_kernel(
+    const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y, int M,
+    int N, int K, int lda, int ldy, int tiles_m, int tiles_n, int dp, int quarter_tiles) {
+    static_assert(S::MI == 16 && S::EB == 2, "16x16 MFMAs on bf16 operands");
+    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+    SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
+    const int grid = gridDim.x;
+    const int b = blockIdx.x;
+
+    if (b < dp) {
+        SeqLoaders<S> issue;
+        int j = b, tm, tn;
+        tile_coords(xcd_order(j, dp), tiles_m, tiles_n, 8, tm, tn);
+        issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
+        Pipeline<S> pl;
+        pl.init(lds);
+        pl.prologue_issue(issue);
+        for (; j < dp; j += grid) {
+            typename S::Acc g[S::TM][S::TN], u[S::TM][S::TN];
+            pl.prologue_wait();
+            seq_contractions<S>(pl, issue, g, u);
+            const int m0 = tm * S::BM, n0 = tn * S::BN;
+            if (j + grid < dp) {
+                tile_coords(xcd_order(j + grid, dp), tiles_m, tiles_n, 8, tm, tn);
+                issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
+                pl.prologue_issue(issue);
             }
+            seq_epilogue<S>(g, u, Y, M, N, ldy, m0, n0);
         }
+    }
+
+    using Q = typename QuarterOf<S>::type;
+    static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
+    const int nq = 4 * quarter_tiles;
+    for (int i = b; i < nq; i += grid) {
+        const int q = xcd_order(i, nq);
+        int tm, tn;
+        tile_coords(dp + q / 4, tiles_m, tiles_n, 8, tm, tn);
+        const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
+        const int n0 = tn * S::BN + (q & 1) * Q::BN;
+        if (m0 >= M || n0 >= N) continue;   // quarter wholly past the output's edge
+        SeqLoaders<Q> issue;
+        issue.init(A, Wf, M, N, K, lda, m0, n0);
+        Pipeline<Q> pl;
+        pl.init(lds);
+        typename Q::Acc g[Q::TM][Q::TN], u[Q::TM][Q::TN];
+        pl.prologue(issue);
+        seq_contractions<Q>(pl, issue, g, u);
+        seq_epilogue<Q>(g, u, Y, M, N, ldy, m0, n0);
     }
 }
 
@@ -1087,17 +1138,63 @@ int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *e
                                ws.cus, buf, n);
 }
 
-int describe_fused_sequential(int M, int N, int cus, char *buf, size_t n) {
+// Work schedule of the persistent S kernel: whole 256x128 tiles, unless the
+// last round is partly idle; then its L tiles run whichever way is predicted
+// faster (ws.tail forces one): whole (one more round), or as 4L quarter-size
+// tiles (ceil(4L / G) rounds of quarter steps).
+struct SeqSchedule {
+    int tiles_m, tiles_n;
+    int dp;              // tiles [0, dp) run whole
+    int quarter_tiles;   // tiles [dp, dp + quarter_tiles) run as four quarters each
+    int grid;
+};
+// One K step of a round of whole tiles, and of a round of quarter tiles
+// (measured: rounds of 256x128 and 128x64 tiles at M=4096 K=8192 N=29568 and
+// M=2048 K=1536 N=8960; a quarter step takes 0.65 of a whole one for a
+// quarter of its work).  Over 13 shapes from M=256 to 8192 the choice is
+// the faster one, or within 2 % of it.
+constexpr double kSeqStepUs = 0.9;
+constexpr double kSeqQuarterStepUs = 0.6;
+
+static SeqSchedule make_seq_schedule(int M, int N, int K, const GemmWorkspace &ws) {
+    using P = ShapeSeqP;
+    SeqSchedule s{};
+    s.tiles_m = cdiv(M, P::BM);
+    s.tiles_n = cdiv(N, P::BN);
+    const int64_t T = static_cast<int64_t>(s.tiles_m) * s.tiles_n;
+    s.dp = static_cast<int>(T);
+    const int G = ws.cus;
+    const int64_t L = G > 0 ? T % G : 0;
+    if (L > 0 && ws.tail != kTailWhole) {
+        const int nk = cdiv(K, P::BK);
+        const double whole = kRoundUs + 2 * nk * kSeqStepUs;
+        const double quarters = cdiv(4 * L, G) * (kRoundUs + 2 * nk * kSeqQuarterStepUs);
+        if (ws.tail == kTailQuarters || quarters < whole) {
+            s.dp = static_cast<int>(T - L);
+            s.quarter_tiles = static_cast<int>(L);
+        }
+    }
+    const int64_t work = s.dp > 4LL * s.quarter_tiles ? s.dp : 4LL * s.quarter_tiles;
+    s.grid = static_cast<int>(G > 0 && G < work ? G : work);
+    return s;
+}
+
+int describe_fused_sequential(int M, int N, int K, const GemmWorkspace &ws, char *buf, size_t n) {
     if (M <= 128)
         return std::snprintf(buf, n, "fused_sequential_kernel<%dx%dx%d> (%lld tiles)",
                              ShapeSmall::BM, ShapeSmall::BN, ShapeSmall::BK,
                              static_cast<long long>(cdiv(M, ShapeSmall::BM)) * cdiv(N, ShapeSmall::BN));
     using P = ShapeSeqP;
-    const long long tiles = static_cast<long long>(cdiv(M, P::BM)) * cdiv(N, P::BN);
-    const long long wgs = cus > 0 && cus < tiles ? cus : tiles;
+    const SeqSchedule s = make_seq_schedule(M, N, K, ws);
+    if (s.quarter_tiles)
+        return std::snprintf(buf, n,
+                             "fused_sequential_persistent_kernel<%dx%dx%d> (%d tiles + %d tiles "
+                             "run as %d %dx%d tiles; %d workgroups)",
+                             P::BM, P::BN, P::BK, s.dp, s.quarter_tiles, 4 * s.quarter_tiles,
+                             P::BM / 2, P::BN / 2, s.grid);
     return std::snprintf(buf, n,
-                         "fused_sequential_persistent_kernel<%dx%dx%d> (%lld tiles; %lld workgroups)",
-                         P::BM, P::BN, P::BK, tiles, wgs);
+                         "fused_sequential_persistent_kernel<%dx%dx%d> (%d tiles; %d workgroups)",
+                         P::BM, P::BN, P::BK, s.dp, s.grid);
 }
 
 // Variant I on FP8 operands: the same GEMM over W_fused with K steps of 128
@@ -1135,17 +1232,18 @@ int describe_gemm_fp8(int M, int cols, int K, const GemmWorkspace &ws, char *buf
 }
 
 hipError_t launch_fused_sequential(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
-                                   int ldy, int M, int N, int K, int cus, hipStream_t stream) {
+                                   int ldy, int M, int N, int K, const GemmWorkspace &ws,
+                                   hipStream_t stream) {
     const void *a = A, *w = Wf;
     if (M <= 128)
         return launch_tiles<ShapeSmall>(fused_sequential_kernel<ShapeSmall>, M, N, stream, a, w,
                                         Y, M, N, K, lda, ldy, 1.0f);
     using P = ShapeSeqP;
-    const int tiles_m = cdiv(M, P::BM), tiles_n = cdiv(N, P::BN);
-    const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
-    const int grid = static_cast<int>(cus > 0 && cus < tiles ? cus : tiles);
-    hipLaunchKernelGGL(fused_sequential_persistent_kernel<P>, dim3(grid), dim3(P::kThreads), 0,
-                       stream, a, w, Y, M, N, K, lda, ldy, tiles_m, tiles_n);
+    const SeqSchedule s = make_seq_schedule(M, N, K, ws);
+    if (s.grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fused_sequential_persistent_kernel<P>, dim3(s.grid), dim3(P::kThreads), 0,
+                       stream, a, w, Y, M, N, K, lda, ldy, s.tiles_m, s.tiles_n, s.dp,
+                       s.quarter_tiles);
     return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ uint64_t workspace_bytes_for(int cus);
 // ablation's and the down projection's).
 int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *epi, char *buf,
                   size_t n, bool fused_i = false);
-int describe_fused_sequential(int M, int N, int cus, char *buf, size_t n);
+int describe_fused_sequential(int M, int N, int K, const GemmWorkspace &ws, char *buf, size_t n);
 
 hipError_t launch_pack(const uint16_t *W1, const uint16_t *W2, uint16_t *Wf, int64_t K,
                        int64_t N, hipStream_t stream);
@@ -43,9 +43,11 @@ hipError_t launch_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *y, in
 hipError_t launch_fused_interleaved(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
                                     int ldy, int M, int N, int K, const GemmWorkspace &ws,
                                     hipStream_t stream);
-// cus: compute units of the device (the persistent kernel's grid)
+// ws: only its compute-unit count (the persistent kernel's grid) and tail
+// choice are used
 hipError_t launch_fused_sequential(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
-                                   int ldy, int M, int N, int K, int cus, hipStream_t stream);
+                                   int ldy, int M, int N, int K, const GemmWorkspace &ws,
+                                   hipStream_t stream);
 // phase 0: C = A . W1 (Gate columns of W_fused), phase 1: C = A . W2 (Up columns)
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Wf, int phase, uint16_t *C,
                              int M, int N, int K, const GemmWorkspace &ws, hipStream_t stream);

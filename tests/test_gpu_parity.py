@@ -660,7 +660,12 @@ def test_describe_launch(dev, monkeypatch):
     monkeypatch.setenv("SWIGLU_I_TILE", "128")
     assert "128x128x64" in sw.swiglu_describe_launch(2048, 8960, 1536, "i", 0)
     d = sw.swiglu_describe_launch(2048, 8960, 1536, "s")
-    assert d.startswith("fused_sequential_persistent_kernel<256x128x64> (560 tiles; 256 workgroups)"), d
+    assert d == ("fused_sequential_persistent_kernel<256x128x64> (512 tiles + 48 tiles run as "
+                 "192 128x64 tiles; 256 workgroups)"), d
+    monkeypatch.setenv("SWIGLU_TAIL", "whole")
+    d = sw.swiglu_describe_launch(2048, 8960, 1536, "s")
+    assert d == "fused_sequential_persistent_kernel<256x128x64> (560 tiles; 256 workgroups)", d
+    monkeypatch.delenv("SWIGLU_TAIL")
     assert sw.swiglu_describe_launch(128, 8960, 1536, "s").startswith("fused_sequential_kernel<")
     assert sw.swiglu_describe_launch(2048, 8960, 1536, "ablation").startswith("2 x gemm_tiles")
     assert "128x128x64" in sw.swiglu_describe_launch(128, 4864, 896, "i")    # forced at M <= 128
@@ -757,3 +762,33 @@ def test_random_shapes(dev, orc, M, K, N):
     Wf = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
     for variant in ("i", "i+ws", "s"):
         assert_parity(bits_of(run_fused(Ad, Wf, variant)), ref, f"{variant} {M}x{K}x{N}")
+
+
+# Variant S above 128 rows: whole 256x128 tiles, and the last round's tiles as
+# 128x64 quarters.  Forced each way on ragged shapes: a partial last tile row
+# and column, a quarter wholly past the M edge (M=300: rows 384..511) and one
+# past the N edge (N=904: columns 960..1023), a K tail (K=200), and more tiles
+# than compute units so the persistent loop takes several tiles (M=4100).
+@pytest.mark.parametrize("tail", ["whole", "quarter"])
+@pytest.mark.parametrize("M,K,N", [(300, 200, 1000), (300, 520, 904), (4100, 136, 2056)])
+def test_sequential_tail_modes(dev, orc, monkeypatch, tail, M, K, N):
+    announce(f"S tail={tail} M={M} K={K} N={N}")
+    monkeypatch.setenv("SWIGLU_TAIL", tail)
+    d = sw.swiglu_describe_launch(M, N, K, "s")
+    tiles = math.ceil(M / 256) * math.ceil(N / 128)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rem = tiles % cus
+    if tail == "quarter" and rem:
+        assert f"{tiles - rem} tiles + {rem} tiles run as {4 * rem} 128x64 tiles" in d, d
+    else:
+        assert f"({tiles} tiles;" in d, d
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M + N + K)
+    ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
+    Ad, Wf = A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    Y = sw.swiglu_fused_gemm(Ad, Wf, variant="s")
+    torch.cuda.synchronize()
+    assert_parity(bits_of(Y), ref, f"S tail={tail}")
+    # the same arithmetic per element whichever way the tile runs
+    Yi = sw.swiglu_fused_gemm(Ad, Wf, variant="i")
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yi.view(torch.int16))

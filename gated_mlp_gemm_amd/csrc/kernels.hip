@@ -511,18 +511,20 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
     }
 }
 
-// The split tiles' epilogue: one wave per (split tile, GEMM wave, epilogue
-// unit), four per workgroup.  The wave takes the registers of the GEMM wave it
-// stands for -- its lane l holds what GEMM thread 64 w + l held, summed over
-// the pieces -- so the epilogue's lane layout is the GEMM's.
+// The split tiles' epilogue: one single-wave workgroup per (split tile, GEMM
+// wave, epilogue unit), so the partials' reads spread over as many CUs as
+// possible (against four waves per workgroup: the M=128 down projection,
+// 18 pieces, 15.6 -> 14.3 us a call; M=2048 K=1536 N=8960 with a 5-way split
+// tail 121.1 -> 119.4 us; same results).  The wave takes the
+// registers of the GEMM wave it stands for -- its lane l holds what GEMM
+// thread 64 w + l held, summed over the pieces -- so the epilogue's lane
+// layout is the GEMM's.
 template <class S, class Epi>
-__global__ __launch_bounds__(256) void split_reduce_kernel(Epi epi, Schedule sch) {
+__global__ __launch_bounds__(64) void split_reduce_kernel(Epi epi, Schedule sch) {
     constexpr int kUnitBlocks = Epi::template unit_blocks<S>();
     constexpr int kUnits = S::TM * S::TN / kUnitBlocks;
     constexpr int kPerTile = S::kWaves * kUnits;
-    // uniform per wave (scalar registers: the output resource derived from it
-    // must be scalar)
-    const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int item = blockIdx.x;
     const int i = item / kPerTile;                 // split tile
     const int w = (item % kPerTile) / kUnits;      // GEMM wave
     const int u = item % kUnits;                   // epilogue unit
@@ -711,8 +713,8 @@ __device__ __forceinline__ void seq_epilogue(const typename S::Acc (&g)[S::TM][S
                 const uint32_t off = voff[S::col_r(i) / 16] +
                                      static_cast<uint32_t>(S::row_r(i)) *
                                          static_cast<uint32_t>(ldy) * 2u;
-                store_y_b16(r, off, static_cast<uint16_t>(v));
-                store_y_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
+                store_b16(r, off, static_cast<uint16_t>(v));
+                store_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
             }
             __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
         }
@@ -1041,11 +1043,10 @@ static hipError_t launch_gemm(KMajor A, KMajor B, int M, int cols, int K, Epi ep
                        0, stream, A, B, M, K, epi, sch);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // S::kWaves * (epilogue units per wave) waves per split tile, four per workgroup
+    // S::kWaves * (epilogue units per wave) single-wave workgroups per split tile
     constexpr int kWavesPerTile = S::kWaves * S::TM * S::TN / Epi::template unit_blocks<S>();
-    static_assert(kWavesPerTile % 4 == 0, "whole workgroups per split tile");
-    const int rgrid = sch.split_tiles * (kWavesPerTile / 4);
-    hipLaunchKernelGGL((split_reduce_kernel<S, Epi>), dim3(rgrid), dim3(256), 0, stream, epi, sch);
+    const int rgrid = sch.split_tiles * kWavesPerTile;
+    hipLaunchKernelGGL((split_reduce_kernel<S, Epi>), dim3(rgrid), dim3(64), 0, stream, epi, sch);
     return hipGetLastError();
 }
 

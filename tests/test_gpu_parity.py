@@ -337,6 +337,42 @@ def test_workload_full_size(dev, orc, workload, variant):
     d["cache"][f"Y_{variant}"] = yb
 
 
+@pytest.mark.parametrize("variant", ["i+ws", "s"])
+def test_workload_whole_output_vs_fp32_gemm(dev, workload, variant):
+    """The whole output at full size on the workloads too large for the
+    oracle's whole-output run, against an independent reference on the GPU:
+    torch's fp32 GEMM (a library kernel sharing no code with this one) for
+    Gate and Up, SiLU and the product in fp64, rounded once to bf16, under
+    the oracle comparison's rule (max(1e-3, 1 % of |ref|)).  fp32 sums of
+    K <= 8192 products of bf16 values are within ~1e-5 (relative to the sum
+    of magnitudes) of the exact ones, far inside that rule."""
+    d = workload
+    w = d["w"]
+    if _whole(d):
+        pytest.skip("the whole output is compared with the oracle")
+    announce(f"fused {variant} {w.name} whole output vs fp32 GEMM")
+    Y = run_fused(d["A"], d["Wf"], variant)
+    torch.backends.cuda.matmul.allow_tf32 = False
+    W1f, W2f = d["W1"].float(), d["W2"].float()
+    bad, worst = 0, 0.0
+    for r0 in range(0, w.M, 1024):
+        a = d["A"][r0:r0 + 1024].float()
+        g = (a @ W1f).double()
+        u = (a @ W2f).double()
+        ref = (g * torch.sigmoid(g) * u).to(torch.bfloat16).float()
+        y = Y[r0:r0 + 1024].float()
+        err = (y - ref).abs()
+        bound = torch.clamp(1e-2 * ref.abs(), min=1e-3)
+        bad += int((~(err <= bound)).sum().item())
+        big = ref.abs() > 0.1
+        if big.any():
+            worst = max(worst, float((err[big] / ref[big].abs()).max().item()))
+    del W1f, W2f
+    print(f"  {variant} {w.name} whole output vs fp32 GEMM: {w.M * w.N} outputs, "
+          f"{bad} outside the rule, max rel err {worst:.2e} (|ref| > 0.1)", flush=True)
+    assert bad == 0
+
+
 @pytest.mark.parametrize("pair", [("i", "s"), ("i+ws", "s"), ("i", "i+ws")])
 def test_workload_variants_agree(dev, workload, pair):
     """Over the whole output, each path is within 1 % of the truth, hence the

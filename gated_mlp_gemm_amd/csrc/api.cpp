@@ -122,14 +122,44 @@ int tile_override() {
 
 // SWIGLU_TAIL=whole, split or quarter forces how the tiles of a partly idle
 // last round run (split only takes effect with a workspace; quarter only for
-// the 256x256 tile); unset or anything else: the cost model decides.
+// the 256x256 tile); fixup forces variant I at M <= 128 to split all its
+// tiles along K and reduce them in the kernel (with a workspace; whole keeps
+// it from doing so); unset or anything else: the cost model decides.
 int tail_override() {
     const char *s = std::getenv("SWIGLU_TAIL");
     if (s == nullptr) return swiglu::kTailAuto;
     if (std::strcmp(s, "whole") == 0) return swiglu::kTailWhole;
     if (std::strcmp(s, "split") == 0) return swiglu::kTailPieces;
     if (std::strcmp(s, "quarter") == 0) return swiglu::kTailQuarters;
+    if (std::strcmp(s, "fixup") == 0) return swiglu::kTailFixup;
     return swiglu::kTailAuto;
+}
+
+// Arrival counters of the split GEMM tiles that are reduced in the kernel
+// (split_tail.hpp): library-owned device memory, zero when the library is
+// loaded and left zero by every call that completes.  Each call takes the
+// next of kCounterBlocks blocks of its device's array in turn, so up to
+// kCounterBlocks such calls may run at once on one device (on different
+// streams).  Host code uses the per-device address from hipGetSymbolAddress.
+constexpr int kCounterBlocks = 64;
+constexpr int kCountersPerBlock = 1024;
+static __device__ __align__(256) unsigned split_counters[kCounterBlocks * kCountersPerBlock] = {};
+unsigned *g_counters_ptr[256];   // per device, guarded by g_dev_mutex
+unsigned g_counter_next[256];    // next block per device, guarded by g_dev_mutex
+
+// The current device's next counter block, or nullptr (then no call reduces
+// in the kernel).
+unsigned *next_counter_block() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return nullptr;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_counters_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(split_counters)) != hipSuccess) return nullptr;
+        g_counters_ptr[dev] = static_cast<unsigned *>(p);
+    }
+    const unsigned block = g_counter_next[dev]++ % kCounterBlocks;
+    return g_counters_ptr[dev] + static_cast<size_t>(block) * kCountersPerBlock;
 }
 
 swiglu::GemmWorkspace make_ws(void *workspace, uint64_t bytes, int cus) {
@@ -139,6 +169,8 @@ swiglu::GemmWorkspace make_ws(void *workspace, uint64_t bytes, int cus) {
     ws.cus = cus;
     ws.tile = tile_override();
     ws.tail = tail_override();
+    ws.counters = ws.base ? next_counter_block() : nullptr;
+    ws.max_counters = ws.counters ? kCountersPerBlock : 0;
     return ws;
 }
 

@@ -427,7 +427,7 @@ struct QuarterOf {
     using type = TileShape<S::BM / 2, S::BN / 2, S::BK, 2, 2, kStages, S::EB, kStages, S::MI>;
 };
 
-enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2 };
+enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2, kTailReduceInKernel = 3 };
 
 // One accumulator per tile: D = A . B^T over the tiles of `sch`, then `epi`.
 // Persistent: workgroup b runs whole tiles b, b + grid, ... below sch.dp
@@ -493,6 +493,52 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             typename Q::Acc acc[Q::TM][Q::TN];
             tile_mainloop<Q>(lds, Ak, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
             epi.template apply<Q>(acc, m0, n0, threadIdx.x);
+        }
+    } else if constexpr (TAIL == kTailReduceInKernel) {
+        // every tile split, reduced by its last piece (split_tail.hpp); the
+        // arrival count is broadcast through LDS word 0 (the ring is idle
+        // between work items)
+        unsigned *arrival = reinterpret_cast<unsigned *>(smem);
+        const int np = sch.split_tiles * sch.pieces;
+        for (int j = b; j < np; j += grid) {
+            const int i = j / sch.pieces;
+            const int piece = j % sch.pieces;
+            const int kb = piece * sch.nk / sch.pieces;
+            const int ke = (piece + 1) * sch.nk / sch.pieces;
+            int tm, tn;
+            tile_coords(sch.dp + i, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
+            typename S::Acc acc[S::TM][S::TN];
+            tile_mainloop<S>(lds, Ak, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
+            const float *slots = sch.partials + static_cast<int64_t>(i) * sch.pieces * S::BM * S::BN;
+            store_partial_coherent<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN,
+                                      acc, threadIdx.x);
+            wait_vmcnt<0>();   // this wave's partial is visible device-wide
+            __syncthreads();   // ... and every wave's
+            if (threadIdx.x == 0)
+                *arrival = __hip_atomic_fetch_add(sch.counters + i, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const unsigned seen = *arrival;
+            __syncthreads();   // read by all before the next item's loads reuse LDS
+            if (seen + 1 != static_cast<unsigned>(sch.pieces)) continue;
+            // the last piece: the counter is free for the next call
+            if (threadIdx.x == 0)
+                __hip_atomic_store(sch.counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            constexpr int kUnitBlocks = Epi::template unit_blocks<S>();
+            constexpr int kUnits = S::TM * S::TN / kUnitBlocks;
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) {
+                typename S::Acc a[kUnitBlocks];
+#pragma unroll
+                for (int k = 0; k < kUnitBlocks; ++k) {
+                    const int blk = Epi::template unit_block<S>(u, k);
+                    a[k] = sum_pieces_fixup<S>(slots, sch.pieces, piece, acc, blk / S::TN,
+                                               blk % S::TN, threadIdx.x);
+                }
+                epi.template unit<S, false>(a[0], a[kUnitBlocks - 1], u, tm * S::BM, tn * S::BN,
+                                            threadIdx.x);
+                __builtin_amdgcn_sched_barrier(0);   // one unit's temporaries live at a time
+            }
         }
     } else if constexpr (TAIL == kTailSplit) {
         const int np = sch.split_tiles * sch.pieces;
@@ -842,6 +888,9 @@ using ShapeWide = TileShape<256, 256, 64, 2, 2, 2, 2, 3, 16>;
 // the last round better.  Chosen per call by quad_tiles_faster().  16x16x32
 // MFMAs, as the 256x256 shape.
 using ShapeQuad = TileShape<128, 128, 64, 2, 2, 2, 2, 2, 16>;
+// M <= 128 split along K and reduced in the kernel: five-stage rings (160 KiB),
+// so a piece of up to five K steps has all its loads in flight at once
+using ShapeSplitK = TileShape<128, 128, 64, 2, 2, 5, 2, 5, 16>;
 // S: 128x128 output tiles, 4 waves each holding 64x64 Gate and Up
 // accumulators, two stages (64 KiB), two workgroups per CU; measured against
 // 256x128x64 (one per CU, 3 stages): 34 % faster at M=2048 K=1536 N=8960, 7 %
@@ -1086,6 +1135,51 @@ static bool small_m_quad_tiles(int M, int cols, const GemmWorkspace &ws) {
     return rows_quad <= rows_small;
 }
 
+// M <= 128 (one tile row): every tile split into s = min(G / T, nk) pieces
+// along K and reduced in the kernel, when 3 <= s <= kMaxFixupPieces and each
+// piece has at least 16 K steps, or when SWIGLU_TAIL=fixup forces it (s
+// capped); needs the workspace for the partials and a counter block.
+// Otherwise a schedule with pieces == 0.  Each piece writes a 64 KiB fp32
+// partial and the last reads s - 1 of them, so short pieces lose: against the
+// 128x64 tiles run whole (same box, M=128): K=8192 N=4864 44.2 against
+// 56.3 us, K=3584 N=4864 24.7 against 29.1, but K=896 N=4864 (3 pieces of 4-5
+// steps) 16.0 against 10.4, and M=64 K=8192 N=6144 (2 pieces, no more
+// workgroups than 128x64 tiles) 51.7 against 49.1.  More pieces are left to
+// the split tail's reduction kernel, which spreads the sums over the chip.
+template <class S>
+static Schedule make_fixup_schedule(int M, int cols, int K, const GemmWorkspace &ws) {
+    Schedule none{};
+    if (M > S::BM || ws.cus <= 0 || ws.base == nullptr || ws.counters == nullptr) return none;
+    if (ws.tail != kTailAuto && ws.tail != kTailFixup) return none;
+    Schedule sch{};
+    sch.tiles_m = 1;
+    sch.tiles_n = cdiv(cols, S::BN);
+    sch.nk = cdiv(K, S::BK);
+    sch.group_m = 8;
+    const int T = sch.tiles_n;
+    int s = ws.cus / T < sch.nk ? ws.cus / T : sch.nk;
+    if (ws.tail == kTailAuto && (s < 3 || s > kMaxFixupPieces || sch.nk < 16 * s)) return none;
+    if (s > kMaxFixupPieces) s = kMaxFixupPieces;
+    if (s < 2 || T > ws.max_counters) return none;
+    if (static_cast<uint64_t>(T) * s * S::BM * S::BN * sizeof(float) > ws.bytes) return none;
+    sch.dp = 0;
+    sch.split_tiles = T;
+    sch.pieces = s;
+    sch.partials = reinterpret_cast<float *>(ws.base);
+    sch.counters = ws.counters;
+    sch.grid = T * s;
+    return sch;
+}
+
+template <class S, class Epi>
+static hipError_t launch_reduce_in_kernel(KMajor A, KMajor B, int M, int K, Epi epi,
+                                          const Schedule &sch, hipStream_t stream) {
+    B.pairs = Epi::template paired<S>() ? 1 : 0;   // de-interleaved weight panels
+    hipLaunchKernelGGL((gemm_tiles_kernel<S, Epi, kTailReduceInKernel>), dim3(sch.grid),
+                       dim3(S::kThreads), 0, stream, A, B, M, K, epi, sch);
+    return hipGetLastError();
+}
+
 hipError_t launch_fused_interleaved(const uint16_t *A, int lda, const uint16_t *Wf, uint16_t *Y,
                                     int ldy, int M, int N, int K, const GemmWorkspace &ws,
                                     hipStream_t stream) {
@@ -1093,6 +1187,8 @@ hipError_t launch_fused_interleaved(const uint16_t *A, int lda, const uint16_t *
     const KMajor B{Wf, 2 * N, 1, 0};
     const PairMulEpilogue epi{Y, M, N, ldy, 1.0f};
     if (M <= 128) {
+        const Schedule fx = make_fixup_schedule<ShapeSplitK>(M, 2 * N, K, ws);
+        if (fx.pieces) return launch_reduce_in_kernel<ShapeSplitK>(Ak, B, M, K, epi, fx, stream);
         if (small_m_quad_tiles(M, 2 * N, ws))
             return launch_gemm<ShapeQuad>(Ak, B, M, 2 * N, K, epi, ws, stream);
         return launch_gemm<ShapeSmall>(Ak, B, M, 2 * N, K, epi, ws, stream);
@@ -1126,6 +1222,15 @@ static int describe(const char *kernel, const char *epi, const Schedule &sch, in
 
 int describe_gemm(int M, int cols, int K, const GemmWorkspace &ws, const char *epi, char *buf,
                   size_t n, bool fused_i) {
+    if (M <= 128 && fused_i) {
+        using P = ShapeSplitK;
+        const Schedule fx = make_fixup_schedule<P>(M, cols, K, ws);
+        if (fx.pieces)
+            return std::snprintf(buf, n,
+                                 "gemm_tiles_kernel<%dx%dx%d,%s> (%d tiles split %d ways along K,"
+                                 " reduced in the kernel; %d workgroups)",
+                                 P::BM, P::BN, P::BK, epi, fx.split_tiles, fx.pieces, fx.grid);
+    }
     if (M <= 128 && fused_i && small_m_quad_tiles(M, cols, ws))
         return describe<ShapeQuad>("gemm_tiles_kernel", epi,
                                    make_schedule<ShapeQuad>(M, cols, K, ws), ws.cus, buf, n);

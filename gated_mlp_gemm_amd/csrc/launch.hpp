@@ -15,9 +15,11 @@ struct GemmWorkspace {
     int cus;          // compute units of the device
     int tile;         // variant I / ablation GEMM tile: 0 = by the cost model, 256 or 128 = forced
     int tail;         // partly idle last round: 0 = by the cost model, else a TailChoice
+    unsigned *counters;   // arrival counters for a split reduced in the kernel (zero between calls)
+    int max_counters;     // counters available at `counters`
 };
 // How the tiles of a partly idle last round run (GemmWorkspace::tail).
-enum TailChoice { kTailAuto = 0, kTailWhole = 1, kTailPieces = 2, kTailQuarters = 3 };
+enum TailChoice { kTailAuto = 0, kTailWhole = 1, kTailPieces = 2, kTailQuarters = 3, kTailFixup = 4 };
 // Scratch that lets the single-accumulator GEMMs split the tiles of a partial
 // last round along K (the same for every shape: one fp32 256 x 256 tile slot
 // per compute unit).

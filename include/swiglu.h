@@ -49,9 +49,13 @@
  *    [K][N] W1, W2 in the compute calls would mean a second mainloop or a
  *    transpose inside every call, so the transpose is the pack's job.
  *  - Calls are re-entrant; the only global state is a per-device cache of
- *    the device's architecture and compute-unit count, and the static
- *    scratch array of swiglu_fused_gemm_noalloc (device memory the library
- *    holds; no call allocates).
+ *    the device's architecture and compute-unit count, the static scratch
+ *    array of swiglu_fused_gemm_noalloc, and a static array of arrival
+ *    counters for the split reduced in the kernel (device memory the library
+ *    holds; no call allocates).  The counters start at zero and every call
+ *    that completes leaves them at zero; each such call takes the next of 64
+ *    counter blocks of its device in turn, so at most 64 of them may run at
+ *    once on one device (different streams).
  *  - The code object targets gfx950 only: on another device every launching
  *    call returns SWIGLU_ERR_UNSUPPORTED.
  */
@@ -109,9 +113,10 @@ int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2,
  *   SiLU(D[m][2n]) * D[m][2n+1].
  * variant SWIGLU_VARIANT_S (the pages' Kernel-1; paper abstract and
  *   gist.science technical summary, Method, Kernel-1): per output tile, the
- *   Gate contraction (even columns), then SiLU on the register-resident Gate
- *   accumulator interleaved with the first Up steps while the Up tiles load,
- *   then the Up contraction (odd columns) and a multiply-and-store epilogue.
+ *   Gate contraction (even columns), then the Up contraction (odd columns)
+ *   with the Gate accumulator held in registers, then SiLU on it and the
+ *   multiply-and-store epilogue (the Up tiles' loads run ahead across the
+ *   Gate->Up boundary).
  * variant SWIGLU_AUTO: whichever swiglu_select_variant(M, N, K) names.
  *
  * A: [M][K], W_fused: packed [2N][K], Y: [M][N]; device pointers.
@@ -125,9 +130,13 @@ int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2,
  * needed); or, given at least swiglu_workspace_size() bytes of workspace,
  * split along K, the pieces leaving fp32 partial tiles in the workspace that
  * a second kernel on the same stream sums, in a fixed order, before the
- * epilogue.  Every schedule gives bitwise reproducible results for a given
- * (M, N, K, workspace size, device).  NULL or too small: no split.  Variant S
- * does not use it.
+ * epilogue.  At M <= 128 with long K (at least 3 pieces of at least 16 K
+ * steps of 64, at most 4 pieces) variant I instead splits every tile along K
+ * and sums the partials in the same kernel: the last piece of each tile to
+ * finish (counted with a library-owned arrival counter, see the global state
+ * below) reads the others' partials from the workspace.  Every schedule gives
+ * bitwise reproducible results for a given (M, N, K, workspace size, device).
+ * NULL or too small: no split.  Variant S does not use it.
  */
 int swiglu_fused_gemm(const uint16_t *A, const uint16_t *W_fused, uint16_t *Y,
                       int64_t M, int64_t N, int64_t K, int variant,

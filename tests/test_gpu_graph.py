@@ -70,7 +70,7 @@ def _setup(case, dev):
     return call, outs, Ad
 
 
-CASES = [("i", 128, 896, 4864, False), ("i", 2048, 1536, 8960, True),
+CASES = [("i", 128, 896, 4864, False), ("i", 128, 3584, 4864, True), ("i", 2048, 1536, 8960, True),
          ("i", 600, 4096, 392, True), ("s", 300, 512, 1000, False),
          ("fp8", 128, 896, 4864, False), ("fp8", 2048, 1536, 8960, True),
          ("mlp", 256, 512, 768, True)]

@@ -828,3 +828,43 @@ def test_sequential_tail_modes(dev, orc, monkeypatch, tail, M, K, N):
     Yi = sw.swiglu_fused_gemm(Ad, Wf, variant="i")
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), Yi.view(torch.int16))
+
+
+# Variant I at M <= 128 with a workspace: every 128x128 tile split into
+# s = min(CUs / tiles, K steps) pieces along K and reduced in the kernel by its
+# last piece (device-scope partials in the workspace, library-owned arrival
+# counters), by default when 3 <= s <= 4 with at least 16 K steps a piece,
+# forced by SWIGLU_TAIL=fixup (s capped at 4).  Ragged M, a K tail, a single
+# row, uneven pieces (14 steps in 3), a shape the default takes (3584 = 56
+# steps in 3 pieces), and a long K with more tiles' pieces than the cap.  Each
+# case runs twice on the same workspace (filled with NaN patterns): both calls
+# equal bit for bit, which also shows the counters were left at zero.
+@pytest.mark.parametrize("M,K,N", [(128, 896, 4864), (100, 520, 4600), (1, 896, 4864),
+                                   (64, 200, 8192), (128, 3584, 4864), (128, 4864, 896)])
+def test_reduce_in_kernel(dev, orc, monkeypatch, M, K, N):
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=M + 3 * K + 7 * N)
+    ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
+    Ad, Wf = A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    tiles = math.ceil(2 * N / 128)
+    s = min(cus // tiles, math.ceil(K / 64))
+    ws = workspace_for(M, N, K, "i", dev)
+    for tail in ("auto", "fixup"):
+        if tail == "auto":
+            monkeypatch.delenv("SWIGLU_TAIL", raising=False)
+        else:
+            monkeypatch.setenv("SWIGLU_TAIL", tail)
+        announce(f"I tail={tail} M={M} K={K} N={N}")
+        d = sw.swiglu_describe_launch(M, N, K, "i", ws.numel())
+        nk = math.ceil(K / 64)
+        in_kernel = s >= 2 if tail == "fixup" else (3 <= s <= 4 and nk >= 16 * s)
+        assert ("reduced in the kernel" in d) == in_kernel, d
+        if in_kernel:
+            assert f"({tiles} tiles split {min(s, 4)} ways along K" in d, d
+        y1 = sw.swiglu_fused_gemm(Ad, Wf, variant="i", workspace=ws)
+        y2 = sw.swiglu_fused_gemm(Ad, Wf, variant="i", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+        assert_parity(bits_of(y1), ref, f"I tail={tail} {M}x{K}x{N}")
+    monkeypatch.delenv("SWIGLU_TAIL", raising=False)
+    assert "reduced in the kernel" not in sw.swiglu_describe_launch(M, N, K, "i", 0)

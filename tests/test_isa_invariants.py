@@ -19,10 +19,10 @@ that has these MFMAs:
   * no MFMA reads an operand a VALU instruction wrote fewer than 2 wait
     states before;
 
-and in every kernel: no VGPR spills.  Wait states are counted in program
-(text) order, backwards across block labels: one per instruction, N+1 for
-s_nop N.  That is conservative where a textually preceding block is not a
-predecessor.
+and in every kernel: no VGPR spills.  Wait states are counted backwards
+along every control-flow path into the instruction (the previous
+instruction unless it is an unconditional branch or the end, and every
+branch to a label in front of it): one per instruction, N+1 for s_nop N.
 """
 from __future__ import annotations
 
@@ -75,7 +75,7 @@ def assembly():
         lines = []
         for raw in body.split("\n"):
             line = raw.split(";")[0].strip()
-            if not line or line.startswith(".") or line.endswith(":"):
+            if not line or (line.startswith(".") and not line.endswith(":")):
                 continue
             lines.append(line)
         kernels[m.group(1)] = lines
@@ -88,6 +88,50 @@ def assembly():
         elif line.startswith(".vgpr_spill_count:") and name:
             spills[name] = int(line.split(":", 1)[1])
     return kernels, spills
+
+
+_NO_FALLTHROUGH = ("s_branch", "s_endpgm", "s_setpc_b64")
+
+
+def _flow(lines):
+    """Instructions (labels dropped) and, for each, the instructions that can
+    run right before it."""
+    ins, label_at, pending = [], {}, []
+    for line in lines:
+        if line.endswith(":"):
+            pending.append(line[:-1])
+            continue
+        for name in pending:
+            label_at[name] = len(ins)
+        pending = []
+        ins.append(line)
+    preds = [[] for _ in ins]
+    for i, line in enumerate(ins):
+        op = line.split()[0]
+        if i + 1 < len(ins) and op not in _NO_FALLTHROUGH:
+            preds[i + 1].append(i)
+        if op == "s_branch" or op.startswith("s_cbranch"):
+            target = line.split()[-1]
+            if target in label_at:
+                preds[label_at[target]].append(i)
+    return ins, preds
+
+
+def _hit_before(ins, preds, i, hit, limit):
+    """(instruction, wait states between) for an instruction satisfying `hit`
+    that can run fewer than `limit` wait states before instruction i, or None."""
+    stack, seen = [(p, 0) for p in preds[i]], set()
+    while stack:
+        j, waited = stack.pop()
+        if (j, waited) in seen:
+            continue
+        seen.add((j, waited))
+        if hit(ins[j]):
+            return ins[j], waited
+        waited += _wait_states(ins[j])
+        if waited < limit:
+            stack.extend((p, waited) for p in preds[j])
+    return None
 
 
 def _asm_mfma_kernels(kernels):
@@ -117,9 +161,11 @@ def test_no_accumulator_moves(assembly):
     assert not bad, bad
 
 
-def _late_accumulator_accesses(ins):
+def _late_accumulator_accesses(lines):
     """(access, MFMA, wait states between) for each VALU access of an
-    accumulator fewer than XDL_TO_VALU wait states after an MFMA writing it."""
+    accumulator that can come fewer than XDL_TO_VALU wait states after an
+    MFMA writing it."""
+    ins, preds = _flow(lines)
     problems = []
     for i, line in enumerate(ins):
         if line.startswith("v_accvgpr_read"):
@@ -128,21 +174,17 @@ def _late_accumulator_accesses(ins):
             regs = _regs(_operands(line)[0])
         else:
             continue
-        waited = 0
-        for j in range(i - 1, -1, -1):
-            prev = ins[j]
-            if prev.startswith("v_mfma") and _regs(_operands(prev)[0]) & regs:
-                problems.append((line, prev, waited))
-                break
-            waited += _wait_states(prev)
-            if waited >= XDL_TO_VALU:
-                break
+        found = _hit_before(ins, preds, i, lambda x: x.startswith("v_mfma") and
+                            bool(_regs(_operands(x)[0]) & regs), XDL_TO_VALU)
+        if found:
+            problems.append((line, *found))
     return problems
 
 
-def _early_mfma_operands(ins):
-    """(MFMA, VALU write, wait states between) for each MFMA operand written by
-    a VALU instruction fewer than VALU_TO_XDL wait states before."""
+def _early_mfma_operands(lines):
+    """(MFMA, VALU write, wait states between) for each MFMA operand that a
+    VALU instruction can write fewer than VALU_TO_XDL wait states before."""
+    ins, preds = _flow(lines)
     problems = []
     for i, line in enumerate(ins):
         if not line.startswith("v_mfma"):
@@ -150,17 +192,16 @@ def _early_mfma_operands(ins):
         srcs = set()
         for op in _operands(line)[1:]:
             srcs |= _regs(op)
-        waited = 0
-        for j in range(i - 1, -1, -1):
-            prev = ins[j]
-            if prev.startswith("v_") and not prev.startswith("v_mfma"):
-                ops = _operands(prev)
-                if ops and _regs(ops[0]) & srcs:
-                    problems.append((line, prev, waited))
-                    break
-            waited += _wait_states(prev)
-            if waited >= VALU_TO_XDL:
-                break
+
+        def writes_src(x):
+            if not x.startswith("v_") or x.startswith("v_mfma"):
+                return False
+            ops = _operands(x)
+            return bool(ops) and bool(_regs(ops[0]) & srcs)
+
+        found = _hit_before(ins, preds, i, writes_src, VALU_TO_XDL)
+        if found:
+            problems.append((line, *found))
     return problems
 
 
@@ -179,6 +220,14 @@ def test_checkers_on_known_sequences():
     assert _early_mfma_operands(["v_mov_b32 v9, 0", mfma])
     assert not _early_mfma_operands(["v_accvgpr_write_b32 a5, 0", "s_nop 1", mfma])
     assert not _early_mfma_operands(["v_mov_b32 v12, 0", mfma])
+    # control flow: no path from the MFMA past an unconditional branch ...
+    assert not _late_accumulator_accesses([mfma, "s_branch .LBB0_2", ".LBB0_1:",
+                                           "v_accvgpr_read_b32 v20, a6", ".LBB0_2:", "s_endpgm"])
+    # ... but a branch to the label is one, and so is a loop's back edge
+    assert _late_accumulator_accesses([mfma, "s_cbranch_scc1 .LBB0_1", "s_nop 7", "s_nop 7",
+                                       "s_nop 7", ".LBB0_1:", "v_accvgpr_read_b32 v20, a6"])
+    assert _late_accumulator_accesses([".LBB0_1:", "v_accvgpr_read_b32 v20, a6", "s_nop 7",
+                                       "s_nop 7", "s_nop 7", mfma, "s_cbranch_scc1 .LBB0_1"])
 
 
 def test_accumulator_access_waits_for_mfma(assembly):

@@ -36,7 +36,7 @@ def orc():
     return oracle_pkg.load()
 
 
-def _check(dev, orc, M, K, N, seed, variant, forced):
+def _check(dev, orc, M, K, N, seed, variant, forced, expect=None):
     A, W1, W2 = inputs.make_inputs(M, K, N, seed=seed)
     ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
     Ad = A.to(dev)
@@ -47,6 +47,8 @@ def _check(dev, orc, M, K, N, seed, variant, forced):
     print(f"\n[case] no-alloc {variant} M={M} K={K} N={N}: {desc}", flush=True)
     if forced:
         assert "split_reduce_kernel" in desc, desc
+    if expect:
+        assert expect in desc, desc
     Y_ws = sw.swiglu_fused_gemm(Ad, Wf, variant=variant, workspace=ws if n else None)
     Y_na = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
     sw.swiglu_fused_gemm_noalloc(Ad, Wf, Y_na, variant=variant)
@@ -68,3 +70,9 @@ def test_noalloc_matches_workspace_call(dev, orc, monkeypatch):
     monkeypatch.delenv("SWIGLU_TAIL")
     _check(dev, orc, 777, 520, 2056, 73, "auto", forced=False)
     _check(dev, orc, 257, 136, 264, 74, "s", forced=False)
+    # M <= 128: split along K and reduced in the kernel (library-owned
+    # counters beside the static partials), twice in a row, then smaller
+    _check(dev, orc, 128, 3584, 4864, 75, "i", forced=False, expect="reduced in the kernel")
+    _check(dev, orc, 128, 3584, 4864, 76, "i", forced=False, expect="reduced in the kernel")
+    monkeypatch.setenv("SWIGLU_TAIL", "fixup")
+    _check(dev, orc, 100, 520, 4600, 77, "auto", forced=False, expect="reduced in the kernel")

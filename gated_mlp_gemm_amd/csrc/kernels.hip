@@ -730,7 +730,7 @@ __device__ __forceinline__ void settle_acc(typename S::Acc (&acc)[S::TM][S::TN])
             for (int q = 0; q < 4; ++q) asm volatile("" : "+a"(acc[a][c].v[q]));
 }
 
-// The S epilogue of one tile: Y = SiLU(Gate) * Up, two rows per conversion,
+// The S epilogue of one tile: Y = g * Up with g = SiLU(Gate), two rows per conversion,
 // through a buffer resource over the tile's valid rows.
 template <class S>
 __device__ __forceinline__ void seq_epilogue(const typename S::Acc (&g)[S::TM][S::TN],
@@ -755,7 +755,7 @@ __device__ __forceinline__ void seq_epilogue(const typename S::Acc (&g)[S::TM][S
             for (int i = 0; i < 16; i += 2) {
                 const float u0 = read_acc(u[a][c].get(i)), u1 = read_acc(u[a][c].get(i + 1));
                 const float g0 = read_acc(g[a][c].get(i)), g1 = read_acc(g[a][c].get(i + 1));
-                const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+                const uint32_t v = pack_bf16x2(g0 * u0, g1 * u1);   // g: SiLU(Gate) already
                 const uint32_t off = voff[S::col_r(i) / 16] +
                                      static_cast<uint32_t>(S::row_r(i)) *
                                          static_cast<uint32_t>(ldy) * 2u;
@@ -792,11 +792,32 @@ struct SeqLoaders {
     }
 };
 
+// SiLU on every Gate accumulator, in place: read out through volatile
+// assembly (so after the wait for the Gate MFMAs), written back and pinned to
+// the accumulator registers.
+template <class S>
+__device__ __forceinline__ void silu_acc(typename S::Acc (&g)[S::TM][S::TN]) {
+#pragma unroll
+    for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+        for (int c = 0; c < S::TN; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 x = g[a][c].v[q];
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = silu(read_acc(x[e]));
+                g[a][c].v[q] = y;
+                asm volatile("" : "+a"(g[a][c].v[q]));
+            }
+}
+
 // The two contractions of an S tile, each started by its first K step's
-// MFMAs (C = 0).  The Gate accumulators are held untouched until the
-// epilogue applies SiLU: the compiler, which does not know the assembly
-// MFMAs' latency, must have no reason to copy accumulators next to MFMAs
-// still writing them.
+// MFMAs (C = 0), with SiLU applied to the Gate accumulators in between --
+// while the first Up K steps' loads, issued during the last Gate steps, are
+// in flight, and before any Up MFMA runs: the compiler, which does not know
+// the assembly MFMAs' latency, must have no reason to copy accumulators next
+// to MFMAs still writing them.
 template <class S>
 __device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoaders<S> &issue,
                                                  typename S::Acc (&g)[S::TM][S::TN],
@@ -804,6 +825,7 @@ __device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoade
     const int nk = issue.nk;
     pl.run_init(issue, 0, nk, 2 * nk, g);
     settle_acc<S>(g);
+    silu_acc<S>(g);
     pl.run_init(issue, nk, 2 * nk, 2 * nk, u);
     pl.drain();
 }

@@ -113,10 +113,10 @@ int swiglu_pack_weights(const uint16_t *W1, const uint16_t *W2,
  *   SiLU(D[m][2n]) * D[m][2n+1].
  * variant SWIGLU_VARIANT_S (the pages' Kernel-1; paper abstract and
  *   gist.science technical summary, Method, Kernel-1): per output tile, the
- *   Gate contraction (even columns), then the Up contraction (odd columns)
- *   with the Gate accumulator held in registers, then SiLU on it and the
- *   multiply-and-store epilogue (the Up tiles' loads run ahead across the
- *   Gate->Up boundary).
+ *   Gate contraction (even columns), then SiLU on the register-resident Gate
+ *   accumulator while the first Up tiles' loads (issued across the Gate->Up
+ *   boundary) are in flight, then the Up contraction (odd columns) and a
+ *   multiply-and-store epilogue.
  * variant SWIGLU_AUTO: whichever swiglu_select_variant(M, N, K) names.
  *
  * A: [M][K], W_fused: packed [2N][K], Y: [M][N]; device pointers.

@@ -203,6 +203,10 @@ struct PanelLoader {
     uint32_t row_bytes;    // uniform: bytes from one panel row to the next
     int pairs;             // uniform: a de-interleaved panel (KMajor::pairs)
     int lds_base;          // uniform: LDS byte offset of the wave's block of load 0
+    // When K is a multiple of BK (issue<true>): each load's offset, computed
+    // once per panel.
+    uint32_t vo[NDMA];
+    int klen;
 
     // Panel = logical rows [r0, r0 + NROWS) of `op`.
     __device__ __forceinline__ void init(const KMajor &op, int r0, int K) {
@@ -215,6 +219,7 @@ struct PanelLoader {
         if (bytes < 0) bytes = 0;
         if (bytes > 0x7FFFFFF0LL) bytes = 0x7FFFFFF0LL;
         rsrc = make_rsrc(panel, static_cast<uint32_t>(bytes));
+        klen = K;
         const int lane = threadIdx.x & 63;
         // uniform per wave: keeps the LDS destinations (M0) in scalar registers
         const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -227,6 +232,8 @@ struct PanelLoader {
         voff = static_cast<uint32_t>(grow) * row_bytes + c * 16u;
         klim = K - c * S::kElemsPerChunk;
         lds_base = wave * 1024;
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) vo[j] = voff + dj(j);
     }
 
     // Uniform bytes from load 0's panel row to load j's: the LDS distance
@@ -243,13 +250,28 @@ struct PanelLoader {
     // back into a branch.  k0 <= K + BK keeps kOutOfRange + dj + 2 k0 below
     // 2^32: dj < 2^31 for at most 256 rows of at most 2^21 elements.)
     // Load `only` of the panel, or all NDMA loads when only < 0.
+    //  kEven (K a multiple of BK): every chunk of a step below K is inside K,
+    //  so the loads take the offsets computed at init with no per-lane
+    //  arithmetic (each vector instruction among the MFMAs delays them by
+    //  about as much as it takes to issue).  A step at or past K (the ring
+    //  running ahead of a tile's last step) loads the last step again, into a
+    //  stage no step reads (a uniform clamp: no per-lane masking).
+    template <bool kEven = false>
     __device__ __forceinline__ void issue(int k0, SWIGLU_LDS char *panel_lds, int only = -1) const {
-        const uint32_t soff = static_cast<uint32_t>(k0) * S::EB;
-        const uint32_t v0 = k0 < klim ? voff : kOutOfRange;
+        if constexpr (kEven) {
+            const uint32_t soff = static_cast<uint32_t>(k0 < klen ? k0 : klen - S::BK) * S::EB;
 #pragma unroll
-        for (int j = 0; j < NDMA; ++j)
-            if (only < 0 || only == j)
-                dma16(rsrc, panel_lds + lds_base + j * S::kWaves * 1024, v0 + dj(j), soff);
+            for (int j = 0; j < NDMA; ++j)
+                if (only < 0 || only == j)
+                    dma16(rsrc, panel_lds + lds_base + j * S::kWaves * 1024, vo[j], soff);
+        } else {
+            const uint32_t soff = static_cast<uint32_t>(k0) * S::EB;
+            const uint32_t v0 = k0 < klim ? voff : kOutOfRange;
+#pragma unroll
+            for (int j = 0; j < NDMA; ++j)
+                if (only < 0 || only == j)
+                    dma16(rsrc, panel_lds + lds_base + j * S::kWaves * 1024, v0 + dj(j), soff);
+        }
     }
 };
 
@@ -270,15 +292,17 @@ struct TileLoader {
     // Load the A (part 0) or B (part 1, from panel `bp`) panel of K step
     // `kstep` into the ring buffer `dst` (only its load `only`, if >= 0);
     // kstep >= ceil(K/BK) loads nothing.
+    template <bool kEven = false>
     __device__ __forceinline__ void issue(int kstep, int part, SWIGLU_LDS char *dst, int only,
                                           const PanelLoader<S, S::BN, S::kDmaB> &bp) const {
         const int k0 = kstep * S::BK;
-        if (part == 0) a.issue(k0, dst, only);
-        else bp.issue(k0, dst, only);
+        if (part == 0) a.template issue<kEven>(k0, dst, only);
+        else bp.template issue<kEven>(k0, dst, only);
     }
+    template <bool kEven = false>
     __device__ __forceinline__ void issue(int kstep, int part, SWIGLU_LDS char *dst,
                                           int only = -1) const {
-        issue(kstep, part, dst, only, b);
+        issue<kEven>(kstep, part, dst, only, b);
     }
 };
 

@@ -393,7 +393,7 @@ struct StoreEpilogue {
 };
 
 // K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
-template <class S>
+template <class S, bool kEven = false>
 __device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor &A,
                                               const KMajor &B, int M, int K, int m0, int n0,
                                               int kb, int ke, int nk,
@@ -405,7 +405,7 @@ __device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor
     const int len = ke - kb;
     // steps past the range load nothing (K step nk is past the end of K)
     auto issue = [&](int s, int part, SWIGLU_LDS char *dst, int j) {
-        ld.issue(s < len ? kb + s : nk, part, dst, j);
+        ld.template issue<kEven>(s < len ? kb + s : nk, part, dst, j);
     };
     zero_acc<S>(acc);
     pl.prologue(issue);
@@ -440,10 +440,13 @@ enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2, kTailReduceInKe
 //    for split_reduce_kernel to finish;
 //  - with kTailQuarter: work item q is quarter q % 4 (row half q/2 % 2, column
 //    half q % 2) of tile dp + q / 4, run whole as a quarter-size tile.
-template <class S, class Epi, int TAIL>
-__global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
-    KMajor Ak, KMajor B, int M, int K, Epi epi, Schedule sch) {
-    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+//
+// kEven: K is a multiple of BK (the loads' offsets are fixed per tile, see
+// PanelLoader::issue); the kernel runs the body compiled for its K.
+template <class S, class Epi, int TAIL, bool kEven>
+__device__ __forceinline__ void gemm_tiles_body(char *smem, const KMajor &Ak, const KMajor &B,
+                                                int M, int K, const Epi &epi,
+                                                const Schedule &sch) {
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
     const int b = blockIdx.x;
     const int grid = sch.grid;
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
         const int nk = sch.nk;
         // steps past the end load nothing (K step nk is past the end of K)
         auto issue = [&](int s, int part, SWIGLU_LDS char *dst, int j) {
-            ld.issue(s < nk ? s : nk, part, dst, j);
+            ld.template issue<kEven>(s < nk ? s : nk, part, dst, j);
         };
         pl.prologue_issue(issue);
         for (; j < sch.dp; j += grid) {
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             const int n0 = tn * S::BN + (q & 1) * Q::BN;
             if (m0 >= M || n0 >= B.rows) continue;   // quarter wholly past the output's edge
             typename Q::Acc acc[Q::TM][Q::TN];
-            tile_mainloop<Q>(lds, Ak, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
+            tile_mainloop<Q, kEven>(lds, Ak, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
             epi.template apply<Q>(acc, m0, n0, threadIdx.x);
         }
     } else if constexpr (TAIL == kTailReduceInKernel) {
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             int tm, tn;
             tile_coords(sch.dp + i, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
             typename S::Acc acc[S::TM][S::TN];
-            tile_mainloop<S>(lds, Ak, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
+            tile_mainloop<S, kEven>(lds, Ak, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
             const float *slots = sch.partials + static_cast<int64_t>(i) * sch.pieces * S::BM * S::BN;
             store_partial_coherent<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN,
                                       acc, threadIdx.x);
@@ -550,11 +553,18 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
             int tm, tn;
             tile_coords(t, sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
             typename S::Acc acc[S::TM][S::TN];
-            tile_mainloop<S>(lds, Ak, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
+            tile_mainloop<S, kEven>(lds, Ak, B, M, K, tm * S::BM, tn * S::BN, kb, ke, sch.nk, acc);
             store_partial<S>(sch.partials + static_cast<int64_t>(j) * S::BM * S::BN, acc,
                              threadIdx.x);
         }
     }
+}
+template <class S, class Epi, int TAIL>
+__global__ __launch_bounds__(S::kThreads, S::kOccupancy) void gemm_tiles_kernel(
+    KMajor Ak, KMajor B, int M, int K, Epi epi, Schedule sch) {
+    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+    if (K % S::BK == 0) gemm_tiles_body<S, Epi, TAIL, true>(smem, Ak, B, M, K, epi, sch);
+    else gemm_tiles_body<S, Epi, TAIL, false>(smem, Ak, B, M, K, epi, sch);
 }
 
 // The split tiles' epilogue: one single-wave workgroup per (split tile, GEMM
@@ -769,7 +779,7 @@ __device__ __forceinline__ void seq_epilogue(const typename S::Acc (&g)[S::TM][S
 
 // The loaders of an S tile: the A rows and the Gate panel (even packed rows),
 // and the Up panel (odd packed rows), of the tile at (m0, n0).
-template <class S>
+template <class S, bool kEven = false>
 struct SeqLoaders {
     TileLoader<S> ld;
     PanelLoader<S, S::BN, S::kDmaB> up;
@@ -788,7 +798,7 @@ struct SeqLoaders {
     __device__ __forceinline__ void operator()(int t, int part, SWIGLU_LDS char *dst,
                                                int j) const {
         const bool gate = t < nk;
-        ld.issue(gate ? t : t - nk, part, dst, j, gate ? ld.b : up);
+        ld.template issue<kEven>(gate ? t : t - nk, part, dst, j, gate ? ld.b : up);
     }
 };
 
@@ -818,8 +828,8 @@ __device__ __forceinline__ void silu_acc(typename S::Acc (&g)[S::TM][S::TN]) {
 // in flight, and before any Up MFMA runs: the compiler, which does not know
 // the assembly MFMAs' latency, must have no reason to copy accumulators next
 // to MFMAs still writing them.
-template <class S>
-__device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoaders<S> &issue,
+template <class S, bool kEven>
+__device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoaders<S, kEven> &issue,
                                                  typename S::Acc (&g)[S::TM][S::TN],
                                                  typename S::Acc (&u)[S::TM][S::TN]) {
     const int nk = issue.nk;
@@ -836,18 +846,16 @@ __device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoade
 // quarter-size tiles of the last round's tiles [dp, dp + quarter_tiles)
 // (quarter q: row half q/2 % 2, column half q % 2 of tile dp + q / 4), each run
 // on its own with a deeper ring.
-template <class S>
-__global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_persistent_kernel(
-    const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y, int M,
-    int N, int K, int lda, int ldy, int tiles_m, int tiles_n, int dp, int quarter_tiles) {
-    static_assert(S::MI == 16 && S::EB == 2, "16x16 MFMAs on bf16 operands");
-    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+template <class S, bool kEven>
+__device__ __forceinline__ void fused_sequential_persistent_body(
+    char *smem, const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y,
+    int M, int N, int K, int lda, int ldy, int tiles_m, int tiles_n, int dp, int quarter_tiles) {
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
     const int grid = gridDim.x;
     const int b = blockIdx.x;
 
     if (b < dp) {
-        SeqLoaders<S> issue;
+        SeqLoaders<S, kEven> issue;
         int j = b, tm, tn;
         tile_coords(xcd_order(j, dp), tiles_m, tiles_n, 8, tm, tn);
         issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
@@ -878,7 +886,7 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_persistent_ke
         const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
         const int n0 = tn * S::BN + (q & 1) * Q::BN;
         if (m0 >= M || n0 >= N) continue;   // quarter wholly past the output's edge
-        SeqLoaders<Q> issue;
+        SeqLoaders<Q, kEven> issue;
         issue.init(A, Wf, M, N, K, lda, m0, n0);
         Pipeline<Q> pl;
         pl.init(lds);
@@ -887,6 +895,19 @@ __global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_persistent_ke
         seq_contractions<Q>(pl, issue, g, u);
         seq_epilogue<Q>(g, u, Y, M, N, ldy, m0, n0);
     }
+}
+template <class S>
+__global__ __launch_bounds__(S::kThreads, 1) void fused_sequential_persistent_kernel(
+    const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y, int M,
+    int N, int K, int lda, int ldy, int tiles_m, int tiles_n, int dp, int quarter_tiles) {
+    static_assert(S::MI == 16 && S::EB == 2, "16x16 MFMAs on bf16 operands");
+    __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+    if (K % S::BK == 0)
+        fused_sequential_persistent_body<S, true>(smem, A, Wf, Y, M, N, K, lda, ldy, tiles_m,
+                                                  tiles_n, dp, quarter_tiles);
+    else
+        fused_sequential_persistent_body<S, false>(smem, A, Wf, Y, M, N, K, lda, ldy, tiles_m,
+                                                   tiles_n, dp, quarter_tiles);
 }
 
 // ---------------------------------------------------------------------------

@@ -747,6 +747,20 @@ struct Pipeline {
         // the last assembly MFMAs' results are read from here on
         if constexpr (S::MI == 16) wait_mfma_results();
     }
+    // drain(), then redefine the accumulators after its wait, so that every
+    // later read of them depends on the wait (the compiler does not know the
+    // assembly MFMAs' latency and could otherwise move a read above it).
+    __device__ __forceinline__ void drain(typename S::Acc (&acc)[S::TM][S::TN]) {
+        drain();
+        if constexpr (S::MI == 16) {
+#pragma unroll
+            for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+                for (int c = 0; c < S::TN; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) asm volatile("" : "+a"(acc[a][c].v[q]));
+        }
+    }
 };
 
 // Tile order.  tile_coords() walks a tile index t over the tile grid in

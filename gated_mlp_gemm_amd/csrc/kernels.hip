@@ -166,8 +166,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(uint16_t *base, int m
     return make_rsrc(base + static_cast<int64_t>(m0) * ld,
                      static_cast<uint32_t>(rows) * static_cast<uint32_t>(ld) * 2u);
 }
-__device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), 0, 0);
+// `off` is the lane's byte offset and `soff` a uniform one (a row term):
+// both count in the range check, so a row past the resource is dropped too,
+// and the uniform part costs no vector instruction.
+__device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
+                                          uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), static_cast<int>(soff), 0);
 }
 // Variant I's output Y is written once and never read back by the kernel: its
 // stores carry the non-temporal hint (nt), so they do not displace the A and
@@ -178,19 +182,25 @@ __device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t r, uint32_t off
 // much per flop, 7.6-10.7 % faster on the first two, +1.9 / -1.2 % on the
 // others.  Variant S keeps plain stores (1-1.8 % slower with the hint), and so
 // do the ablation's Gate and Up, which the next kernel reads back.
-__device__ __forceinline__ void store_y_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), 0, 2 /* nt */);
+__device__ __forceinline__ void store_y_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
+                                            uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), static_cast<int>(soff),
+                                          2 /* nt */);
 }
 // The high 16 bits of v, with the same range check and hint
 // (buffer_store_short_d16_hi, which the store builtin does not produce: it
 // would shift first).
-__device__ __forceinline__ void store_y_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
-    asm volatile("buffer_store_short_d16_hi %0, %1, %2, 0 offen nt" ::"v"(v), "v"(off), "s"(r)
+__device__ __forceinline__ void store_y_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               uint32_t soff, uint32_t v) {
+    asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen nt" ::"v"(v), "v"(off), "s"(r),
+                 "s"(soff)
                  : "memory");
 }
 // The same without the hint (variant S).
-__device__ __forceinline__ void store_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
-    asm volatile("buffer_store_short_d16_hi %0, %1, %2, 0 offen" ::"v"(v), "v"(off), "s"(r)
+__device__ __forceinline__ void store_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
+                                             uint32_t v) {
+    asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen" ::"v"(v), "v"(off), "s"(r),
+                 "s"(soff)
                  : "memory");
 }
 
@@ -278,10 +288,10 @@ struct PairMulEpilogueT {
                 const float u0 = scaled(acc_value<kFromAcc>(up.get(i)));
                 const float u1 = scaled(acc_value<kFromAcc>(up.get(i + 1)));
                 const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
-                const uint32_t off = voff[S::col_r(i) / 16] +
-                                     static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
-                store_y_b16(r, off, static_cast<uint16_t>(v));
-                store_y_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
+                const uint32_t roff =
+                    static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
+                store_y_b16(r, voff[S::col_r(i) / 16], roff, static_cast<uint16_t>(v));
+                store_y_b16_hi(r, voff[S::col_r(i) / 16], roff + static_cast<uint32_t>(ldy) * 2u, v);
             }
         } else {
             const int tm = u / S::TN, tn = u % S::TN;
@@ -306,7 +316,7 @@ struct PairMulEpilogueT {
                 const float upv = scaled(by_lane_parity(recv, hi));
                 const uint32_t roff = static_cast<uint32_t>(tm * 32 + S::row_r(p)) *
                                       static_cast<uint32_t>(ldy) * 2u;
-                store_y_b16(r, voff[S::col_r(p) / 16] + roff, to_bf16(silu(gate) * upv));
+                store_y_b16(r, voff[S::col_r(p) / 16], roff, to_bf16(silu(gate) * upv));
             }
         }
     }
@@ -363,7 +373,7 @@ struct StoreEpilogue {
         for (int i = 0; i < 16; ++i) {
             const uint32_t roff =
                 static_cast<uint32_t>(tm * 32 + S::row_r(i)) * static_cast<uint32_t>(N) * 2u;
-            store_b16(r, voff[S::col_r(i) / 16] + roff, to_bf16(acc_value<kFromAcc>(a.get(i))));
+            store_b16(r, voff[S::col_r(i) / 16], roff, to_bf16(acc_value<kFromAcc>(a.get(i))));
         }
     }
 
@@ -393,6 +403,21 @@ struct StoreEpilogue {
 };
 
 // K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
+// The K steps [0, len) of one tile into `acc`.  With 16x16 MFMAs the first
+// step's MFMAs start the accumulators (C = 0): no vector instructions zero its
+// 256 registers first.  32x32 MFMAs accumulate onto zeros (zero_acc_mi32
+// before the prologue's wait, while the loads are in flight).
+template <class S>
+__device__ __forceinline__ void zero_acc_mi32(typename S::Acc (&acc)[S::TM][S::TN]) {
+    if constexpr (S::MI != 16) zero_acc<S>(acc);
+}
+template <class S, class Issue>
+__device__ __forceinline__ void run_tile(Pipeline<S> &pl, const Issue &issue, int len,
+                                         typename S::Acc (&acc)[S::TM][S::TN]) {
+    if constexpr (S::MI == 16) pl.run_init(issue, 0, len, len, acc);
+    else pl.run(issue, 0, len, len, acc);
+}
+
 template <class S, bool kEven = false>
 __device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor &A,
                                               const KMajor &B, int M, int K, int m0, int n0,
@@ -407,10 +432,10 @@ __device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor
     auto issue = [&](int s, int part, SWIGLU_LDS char *dst, int j) {
         ld.template issue<kEven>(s < len ? kb + s : nk, part, dst, j);
     };
-    zero_acc<S>(acc);
+    zero_acc_mi32<S>(acc);
     pl.prologue(issue);
-    pl.run(issue, 0, len, len, acc);
-    pl.drain();
+    run_tile<S>(pl, issue, len, acc);
+    pl.drain(acc);
 }
 
 // The quarter-size tile of a 4-wave shape S, used for a tail round: half the
@@ -466,10 +491,10 @@ __device__ __forceinline__ void gemm_tiles_body(char *smem, const KMajor &Ak, co
         pl.prologue_issue(issue);
         for (; j < sch.dp; j += grid) {
             typename S::Acc acc[S::TM][S::TN];
-            zero_acc<S>(acc);
+            zero_acc_mi32<S>(acc);
             pl.prologue_wait();
-            pl.run(issue, 0, nk, nk, acc);
-            pl.drain();
+            run_tile<S>(pl, issue, nk, acc);
+            pl.drain(acc);
             const int m0 = tm * S::BM, n0 = tn * S::BN;
             if (j + grid < sch.dp) {
                 tile_coords(xcd_order(j + grid, sch.dp), sch.tiles_m, sch.tiles_n, sch.group_m, tm,
@@ -703,10 +728,10 @@ __global__ __launch_bounds__(S::kThreads, S::kOccupancy) void fused_sequential_k
                     u1 *= scale;
                 }
                 const uint32_t v = pack_bf16x2(g[tm][tn].get(i) * u0, g[tm][tn].get(i + 1) * u1);
-                const uint32_t off = voff[S::col_r(i) / 16] +
-                                     static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
-                store_b16(r, off, static_cast<uint16_t>(v));
-                store_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
+                const uint32_t roff =
+                    static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
+                store_b16(r, voff[S::col_r(i) / 16], roff, static_cast<uint16_t>(v));
+                store_b16_hi(r, voff[S::col_r(i) / 16], roff + static_cast<uint32_t>(ldy) * 2u, v);
             }
         }
     }
@@ -766,11 +791,10 @@ __device__ __forceinline__ void seq_epilogue(const typename S::Acc (&g)[S::TM][S
                 const float u0 = read_acc(u[a][c].get(i)), u1 = read_acc(u[a][c].get(i + 1));
                 const float g0 = read_acc(g[a][c].get(i)), g1 = read_acc(g[a][c].get(i + 1));
                 const uint32_t v = pack_bf16x2(g0 * u0, g1 * u1);   // g: SiLU(Gate) already
-                const uint32_t off = voff[S::col_r(i) / 16] +
-                                     static_cast<uint32_t>(S::row_r(i)) *
-                                         static_cast<uint32_t>(ldy) * 2u;
-                store_b16(r, off, static_cast<uint16_t>(v));
-                store_b16_hi(r, off + static_cast<uint32_t>(ldy) * 2u, v);
+                const uint32_t roff =
+                    static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
+                store_b16(r, voff[S::col_r(i) / 16], roff, static_cast<uint16_t>(v));
+                store_b16_hi(r, voff[S::col_r(i) / 16], roff + static_cast<uint32_t>(ldy) * 2u, v);
             }
             __builtin_amdgcn_sched_barrier(0);   // one block's temporaries live at a time
         }
@@ -837,7 +861,7 @@ __device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoade
     settle_acc<S>(g);
     silu_acc<S>(g);
     pl.run_init(issue, nk, 2 * nk, 2 * nk, u);
-    pl.drain();
+    pl.drain(u);
 }
 
 // Variant S, persistent, on 16x16 MFMAs: workgroup b runs whole tiles b,

@@ -173,35 +173,42 @@ __device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t r, uint32_t off
                                           uint16_t v) {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), static_cast<int>(soff), 0);
 }
-// Variant I's output Y is written once and never read back by the kernel: its
-// stores carry the non-temporal hint (nt), so they do not displace the A and
-// weight panels that tiles still running read from L2 and the Infinity Cache.
-// Measured against plain stores (same box, inputs and outputs rotated): bf16
-// 1.8 % faster at M=2048 K=1536 N=8960 and 2.3 % at M=512 K=3584 N=18944,
-// 0.4-0.5 % slower at K = 5120 and 8192; FP8, whose Y write weighs twice as
-// much per flop, 7.6-10.7 % faster on the first two, +1.9 / -1.2 % on the
-// others.  Variant S keeps plain stores (1-1.8 % slower with the hint), and so
-// do the ablation's Gate and Up, which the next kernel reads back.
+// Variant I's output Y is written once and never read back by the kernel.
+// With the 32x32 MFMA layout (FP8 operands; bf16 at M <= 128) its stores
+// carry the non-temporal hint (nt), so they do not displace the A and weight
+// panels that tiles still running read from L2 and the Infinity Cache:
+// measured against plain stores, FP8 7.6-10.7 % faster at M=2048 K=1536
+// N=8960 and M=512 K=3584 N=18944.  With the 16x16 layout a store covers
+// 32-byte pieces of four rows, and under the hint partly written lines left
+// L2 early: 2.1-2.4x Y's bytes written (plain stores: 1.0x), and plain stores
+// are faster on all four bf16 workloads above M = 128 (1.2-4.2 %, same box).
+// Variant S keeps plain stores, and so do the ablation's Gate and Up, which
+// the next kernel reads back.
+template <bool kNt>
 __device__ __forceinline__ void store_y_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
                                             uint16_t v) {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(off), static_cast<int>(soff),
-                                          2 /* nt */);
+                                          kNt ? 2 /* nt */ : 0);
 }
 // The high 16 bits of v, with the same range check and hint
 // (buffer_store_short_d16_hi, which the store builtin does not produce: it
 // would shift first).
+template <bool kNt>
 __device__ __forceinline__ void store_y_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                                uint32_t soff, uint32_t v) {
-    asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen nt" ::"v"(v), "v"(off), "s"(r),
-                 "s"(soff)
-                 : "memory");
+    if constexpr (kNt)
+        asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen nt" ::"v"(v), "v"(off),
+                     "s"(r), "s"(soff)
+                     : "memory");
+    else
+        asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen" ::"v"(v), "v"(off), "s"(r),
+                     "s"(soff)
+                     : "memory");
 }
 // The same without the hint (variant S).
 __device__ __forceinline__ void store_b16_hi(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
                                              uint32_t v) {
-    asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen" ::"v"(v), "v"(off), "s"(r),
-                 "s"(soff)
-                 : "memory");
+    store_y_b16_hi<false>(r, off, soff, v);
 }
 
 // Lane byte offsets of the two 16-column groups of a 32x32 accumulator block
@@ -290,8 +297,9 @@ struct PairMulEpilogueT {
                 const uint32_t v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
                 const uint32_t roff =
                     static_cast<uint32_t>(S::row_r(i)) * static_cast<uint32_t>(ldy) * 2u;
-                store_y_b16(r, voff[S::col_r(i) / 16], roff, static_cast<uint16_t>(v));
-                store_y_b16_hi(r, voff[S::col_r(i) / 16], roff + static_cast<uint32_t>(ldy) * 2u, v);
+                store_y_b16<S::MI == 32>(r, voff[S::col_r(i) / 16], roff, static_cast<uint16_t>(v));
+                store_y_b16_hi<S::MI == 32>(r, voff[S::col_r(i) / 16],
+                                            roff + static_cast<uint32_t>(ldy) * 2u, v);
             }
         } else {
             const int tm = u / S::TN, tn = u % S::TN;
@@ -316,7 +324,7 @@ struct PairMulEpilogueT {
                 const float upv = scaled(by_lane_parity(recv, hi));
                 const uint32_t roff = static_cast<uint32_t>(tm * 32 + S::row_r(p)) *
                                       static_cast<uint32_t>(ldy) * 2u;
-                store_y_b16(r, voff[S::col_r(p) / 16], roff, to_bf16(silu(gate) * upv));
+                store_y_b16<S::MI == 32>(r, voff[S::col_r(p) / 16], roff, to_bf16(silu(gate) * upv));
             }
         }
     }

@@ -158,6 +158,31 @@ def test_small_shapes_forced_tile(dev, orc, M, K, N, tile, monkeypatch):
         assert_parity(bits_of(run_fused(Ad, Wf, variant)), ref, f"{variant}@{tile} {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("K", [128, 192, 320, 136, 264, 1032, 2056])
+@pytest.mark.parametrize("tail", ["auto", "whole", "quarter", "split"])
+def test_k_step_bodies(dev, orc, K, tail, monkeypatch):
+    """Every GEMM and S kernel runs one of two bodies, chosen by K at entry: K a
+    multiple of 64 (fixed per-tile load offsets; the steps the ring loads
+    ahead past a tile's last step reload that step into unread stages) or
+    ragged K (per-lane masking of the chunks past K).  Short K puts most
+    steps next to the end (2, 3 and 5 K steps; 17 and 33 ragged ones), on
+    ragged M and 2N edges, with every tail schedule and both tile shapes."""
+    M, N = 520, 392
+    monkeypatch.setenv("SWIGLU_TAIL", tail)
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=K * 13 + 5)
+    ref = orc.swiglu(inputs.bits(A), inputs.bits(W1), inputs.bits(W2))
+    Ad, Wf = A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    for tile in ("256", "128"):
+        monkeypatch.setenv("SWIGLU_I_TILE", tile)
+        for variant in ("i", "i+ws"):
+            announce(f"fused {variant} tile={tile} tail={tail} M={M} K={K} N={N}")
+            assert_parity(bits_of(run_fused(Ad, Wf, variant)), ref,
+                          f"{variant}@{tile}/{tail} {M}x{K}x{N}")
+    monkeypatch.delenv("SWIGLU_I_TILE")
+    announce(f"fused s tail={tail} M={M} K={K} N={N}")
+    assert_parity(bits_of(run_fused(Ad, Wf, "s")), ref, f"s/{tail} {M}x{K}x{N}")
+
+
 def _pad(a, rows, cols):
     out = np.zeros((rows, cols), dtype=np.float32)
     a = np.asarray(a, dtype=np.float32)

@@ -481,6 +481,41 @@ __device__ __forceinline__ void read_frag_one(uint32_t sa, uint32_t sb, const Fr
         f.b[b - S::TM][j] = asm_read_b128<(b - S::TM) * 32 * S::kRowBytes>(sb + o.b[KS][j]);
 }
 
+// Where a substep's fragment reads find their ring stage.  RuntimeReads: the
+// stages' LDS addresses sa / sb, known at run time (a per-lane add per read
+// address).  FixedReads: stage offsets OFFA / OFFB from the LDS base known at
+// compile time (a ring walked in unrolled groups of its period): each read
+// address is a loop-invariant per-lane base plus the 64 KiB-aligned part of
+// the offset, and the rest rides in the instruction's immediate offset.
+template <class S>
+struct RuntimeReads {
+    uint32_t sa, sb;
+    const FragOffsets<S> *o;
+    template <int KS, int R>
+    __device__ __forceinline__ void read(Frags<S> &f) const {
+        read_frag_one<S, KS, R>(sa, sb, *o, f);
+    }
+};
+template <class S, int OFFA, int OFFB>
+struct FixedReads {
+    uint32_t lds_addr;
+    const FragOffsets<S> *o;
+    template <int OFF>
+    __device__ __forceinline__ static u32x4 at(uint32_t lane_base) {
+        static_assert((OFF & 0xFFFF) + 16 <= 0x10000, "16-bit immediate offset");
+        return asm_read_b128<(OFF & 0xFFFF)>(lane_base + static_cast<uint32_t>(OFF & ~0xFFFF));
+    }
+    template <int KS, int R>
+    __device__ __forceinline__ void read(Frags<S> &f) const {
+        constexpr int kPer = S::TM + S::TN;
+        constexpr int j = R / kPer, b = R % kPer;
+        if constexpr (b < S::TM)
+            f.a[b][j] = at<OFFA + b * 32 * S::kRowBytes>(lds_addr + o->a[KS][j]);
+        else
+            f.b[b - S::TM][j] = at<OFFB + (b - S::TM) * 32 * S::kRowBytes>(lds_addr + o->b[KS][j]);
+    }
+};
+
 // The 16x16 MFMAs of one k-substep, issued one by one (inline assembly, in
 // program order) on the fragments `cur`, and between them:
 //  - the fragment reads of the next k-substep KSN (from the ring buffers at
@@ -497,9 +532,8 @@ __device__ __forceinline__ void read_frag_one(uint32_t sa, uint32_t sb, const Fr
 // those were issued before these reads, and a read's data lands long after
 // an MFMA has taken its operands.
 template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, bool kInit, int I,
-          class Load, int... R, int... D>
-__device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa,
-                                         uint32_t sb, const FragOffsets<S> &o,
+          class Reads, class Load, int... R, int... D>
+__device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, const Reads &rd,
                                          typename S::Acc (&acc)[S::TM][S::TN], const Load &load,
                                          std::integer_sequence<int, R...>,
                                          std::integer_sequence<int, D...>) {
@@ -512,7 +546,7 @@ __device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uin
     (
         [&] {
             if constexpr (kReads && kBegin + R * (kSpan / 2) / kNReads == I)
-                read_frag_one<S, KSN, R>(sa, sb, o, nxt);
+                rd.template read<KSN, R>(nxt);
         }(),
         ...);
     (
@@ -525,17 +559,16 @@ __device__ __forceinline__ void mma16_at(const Frags<S> &cur, Frags<S> &nxt, uin
 // MFMAs [kBegin, kEnd) of the substep, with the reads (if kReads) and loads
 // spread over that range; kInit: they start the accumulators (C = 0).
 template <class S, int KSN, bool kReads, int kLoads, int kBegin, int kEnd, bool kInit = false,
-          int I = kBegin, class Load>
-__device__ __forceinline__ void mma16(const Frags<S> &cur, Frags<S> &nxt, uint32_t sa, uint32_t sb,
-                                      const FragOffsets<S> &o,
+          int I = kBegin, class Reads, class Load>
+__device__ __forceinline__ void mma16(const Frags<S> &cur, Frags<S> &nxt, const Reads &rd,
                                       typename S::Acc (&acc)[S::TM][S::TN], const Load &load) {
     static_assert(S::MI == 16, "16x16 MFMAs");
     if constexpr (I < kEnd) {
         mma16_at<S, KSN, kReads, kLoads, kBegin, kEnd, kInit, I>(
-            cur, nxt, sa, sb, o, acc, load,
+            cur, nxt, rd, acc, load,
             std::make_integer_sequence<int, S::kFragChunks * (S::TM + S::TN)>{},
             std::make_integer_sequence<int, (kLoads > 0 ? kLoads : 1)>{});
-        mma16<S, KSN, kReads, kLoads, kBegin, kEnd, kInit, I + 1>(cur, nxt, sa, sb, o, acc, load);
+        mma16<S, KSN, kReads, kLoads, kBegin, kEnd, kInit, I + 1>(cur, nxt, rd, acc, load);
     }
 }
 
@@ -612,15 +645,33 @@ struct Pipeline {
     }
     // Load d (d < kDmaPerStep) of steady-state group g, in the group's issue
     // order.
-    template <class Issue>
+    // (SA, SB >= 0: group g's stages, known at compile time in an unrolled ring)
+    template <int SA = -1, int SB = -1, class Issue>
     __device__ __forceinline__ void issue_one(const Issue &issue, int g, int d) const {
         const int ta = g + S::STAGES, tb = g + S::BSTAGES;
         constexpr int kFirst = Order::kAFirst ? S::kDmaA : S::kDmaB;
         const bool first = d < kFirst;
         const bool a_part = first == Order::kAFirst;
         const int j = first ? d : d - kFirst;
-        if (a_part) issue(ta, 0, stage_a(ta), j);
-        else issue(tb, 1, stage_b(tb), j);
+        if constexpr (SA >= 0) {
+            if (a_part) issue(ta, 0, lds + SA * S::kABytes, j);
+            else issue(tb, 1, lds + S::kBRing + SB * S::kBBytes, j);
+        } else {
+            if (a_part) issue(ta, 0, stage_a(ta), j);
+            else issue(tb, 1, stage_b(tb), j);
+        }
+    }
+    // Ring period: the steps after which both rings are back at stage 0.
+    static constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+    static constexpr int kPeriod = S::STAGES / gcd(S::STAGES, S::BSTAGES) * S::BSTAGES;
+    // Fragment reads of step t (stage offsets known when PH >= 0: t % kPeriod == PH).
+    template <int PH>
+    __device__ __forceinline__ auto reads_of(int t) const {
+        if constexpr (PH >= 0)
+            return FixedReads<S, (PH % S::STAGES) * S::kABytes,
+                              S::kBRing + (PH % S::BSTAGES) * S::kBBytes>{lds_addr, &off};
+        else
+            return RuntimeReads<S>{addr_a(t), addr_b(t), &off};
     }
 
     __device__ __forceinline__ void init(SWIGLU_LDS char *lds_) {
@@ -652,7 +703,7 @@ struct Pipeline {
 
     // kInit: the step starts the accumulators (16x16 MFMAs only: its first
     // substep's MFMAs take C = 0, no zero_acc() before it).
-    template <int KS, bool kInit, class Issue, class Hook>
+    template <int KS, bool kInit, int PH, class Issue, class Hook>
     __device__ __forceinline__ void substeps(const Issue &issue, int t, int total,
                                              typename S::Acc (&acc)[S::TM][S::TN], const Hook &hook) {
         constexpr int last = S::kKSub - 1;
@@ -662,13 +713,13 @@ struct Pipeline {
             if constexpr (S::MI == 16) {
                 hook(KS);
                 mma16<S, KS + 1, true, 0, 0, kMfma16, kInit && KS == 0>(
-                    f[KS & 1], f[(KS + 1) & 1], addr_a(t), addr_b(t), off, acc, [](int) {});
+                    f[KS & 1], f[(KS + 1) & 1], reads_of<PH>(t), acc, [](int) {});
             } else {
                 read_frags<S, KS + 1>(addr_a(t), addr_b(t), off, f[(KS + 1) & 1]);
                 hook(KS);
                 mma<S>(f[KS & 1], acc);
             }
-            substeps<KS + 1, kInit>(issue, t, total, acc, hook);
+            substeps<KS + 1, kInit, PH>(issue, t, total, acc, hook);
         } else {
             // Step t+1's loads have landed (own wait, then everyone's via the
             // barrier), and every wave has finished reading stage t.  The
@@ -687,13 +738,18 @@ struct Pipeline {
                 // the first kEarlyMfma MFMAs of this substep (operands already
                 // in registers) go out before the wait and the barrier
                 hook(KS);
-                mma16<S, 0, false, 0, 0, kEarlyMfma>(f[KS & 1], f[(KS + 1) & 1], 0, 0, off, acc,
-                                                     [](int) {});
+                mma16<S, 0, false, 0, 0, kEarlyMfma>(f[KS & 1], f[(KS + 1) & 1],
+                                                     RuntimeReads<S>{0, 0, &off}, acc, [](int) {});
                 wait_vmcnt<Order::kWaitSteady>();
                 block_barrier();
+                constexpr int kNext = PH >= 0 ? (PH + 1) % kPeriod : -1;
                 mma16<S, 0, true, S::kDmaPerStep, kEarlyMfma, kMfma16>(
-                    f[KS & 1], f[(KS + 1) & 1], addr_a(t + 1), addr_b(t + 1), off, acc,
-                    [&](int d) { issue_one(issue, t, d); });
+                    f[KS & 1], f[(KS + 1) & 1], reads_of<kNext>(t + 1), acc, [&](int d) {
+                        if constexpr (PH >= 0)
+                            issue_one<PH % S::STAGES, PH % S::BSTAGES>(issue, t, d);
+                        else
+                            issue_one(issue, t, d);
+                    });
             } else {
                 wait_vmcnt<Order::kWaitSteady>();
                 block_barrier();
@@ -719,25 +775,47 @@ struct Pipeline {
         }
     }
 
-    template <bool kInit = false, class Issue, class Hook>
+    // PH >= 0: t % kPeriod == PH, so every ring stage the step touches is a
+    // compile-time offset (no stage arithmetic in the step).
+    template <bool kInit = false, int PH = -1, class Issue, class Hook>
     __device__ __forceinline__ void step(const Issue &issue, int t, int total,
                                          typename S::Acc (&acc)[S::TM][S::TN], const Hook &hook) {
         static_assert(S::kKSub % 2 == 0, "fragment double buffer alternates per substep");
         static_assert(!kInit || S::MI == 16, "accumulator start by MFMA: 16x16 path");
-        substeps<0, kInit>(issue, t, total, acc, hook);
+        static_assert(PH < 0 || S::MI == 16, "fixed stages: 16x16 path");
+        substeps<0, kInit, PH>(issue, t, total, acc, hook);
+    }
+    template <int PH, class Issue>
+    __device__ __forceinline__ void steps_of_period(const Issue &issue, int t0, int total,
+                                                    typename S::Acc (&acc)[S::TM][S::TN]) {
+        if constexpr (PH < kPeriod) {
+            step<false, PH>(issue, t0 + PH, total, acc, [](int) {});
+            steps_of_period<PH + 1>(issue, t0, total, acc);
+        }
     }
 
-    template <class Issue>
+    // Steps [t_begin, t_end).  kUnroll (16x16 MFMAs): whole periods of the
+    // ring starting at a multiple of kPeriod run as one unrolled group of
+    // steps with compile-time stages; the steps before the first and after
+    // the last such group run with the stages computed at run time.  (Those
+    // per-step stage computations -- the remainder by 3 of a three-stage ring,
+    // the per-stage read addresses -- sat between the MFMAs of the steps.)
+    template <bool kUnroll = false, class Issue>
     __device__ __forceinline__ void run(const Issue &issue, int t_begin, int t_end, int total,
                                         typename S::Acc (&acc)[S::TM][S::TN]) {
-        for (int t = t_begin; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
+        int t = t_begin;
+        if constexpr (kUnroll && S::MI == 16) {
+            for (; t < t_end && t % kPeriod != 0; ++t) step(issue, t, total, acc, [](int) {});
+            for (; t + kPeriod <= t_end; t += kPeriod) steps_of_period<0>(issue, t, total, acc);
+        }
+        for (; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
     }
     // The same, with step t_begin (< t_end) starting the accumulators.
-    template <class Issue>
+    template <bool kUnroll = false, class Issue>
     __device__ __forceinline__ void run_init(const Issue &issue, int t_begin, int t_end, int total,
                                              typename S::Acc (&acc)[S::TM][S::TN]) {
         step<true>(issue, t_begin, total, acc, [](int) {});
-        run(issue, t_begin + 1, t_end, total, acc);
+        run<kUnroll>(issue, t_begin + 1, t_end, total, acc);
     }
 
     __device__ __forceinline__ void drain() {

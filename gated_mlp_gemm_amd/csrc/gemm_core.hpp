@@ -608,11 +608,15 @@ struct Pipeline {
     using Order = IssueOrder<S>;
     static constexpr int kMfma16 = S::TM * S::TN * 4;   // 16x16 MFMAs per substep
     // 16x16 MFMAs of the last substep issued before its wait and barrier, so
-    // the MFMA pipe works while the workgroup meets: a quarter of the
-    // substep's (measured at M=4096 K=8192 N=29568 and M=2048 K=1536 N=8960
-    // with 0, 4, 8, 16, 24, 32, 40 of the 256x256 tile's 64: 16 fastest, +1 %
-    // and +5 % over none; more delays the refill loads)
-    static constexpr int kEarlyMfma = kMfma16 / 4;
+    // the MFMA pipe works while the workgroup meets: an eighth of the
+    // substep's.  Measured with the 256x256 tile's 64: with the ring stages
+    // computed at run time, 16 was fastest of 0, 4, 8, 16, 24, 32, 40 (+1 %
+    // and +5 % over none at M=4096 K=8192 N=29568 and M=2048 K=1536 N=8960);
+    // with the unrolled ring walk (fewer instructions to issue around the
+    // barrier) 2, 4 and 8 are within 0.3 % of each other and 0.2-1.5 %
+    // faster than 16 on those two workloads, M=8192 K=5120 N=13824 and
+    // variant S, 24 and 32 are 0.8-4.6 % slower (more delays the refill loads).
+    static constexpr int kEarlyMfma = kMfma16 / 8;
     static_assert(S::MI != 16 || (kEarlyMfma > 0 && kEarlyMfma < kMfma16),
                   "MFMAs on both sides of the barrier");
 
@@ -785,12 +789,13 @@ struct Pipeline {
         static_assert(PH < 0 || S::MI == 16, "fixed stages: 16x16 path");
         substeps<0, kInit, PH>(issue, t, total, acc, hook);
     }
-    template <int PH, class Issue>
+    // Steps t0 .. t0 + kPeriod - 1 with t0 % kPeriod == P0 (I counts them).
+    template <int P0, int I, class Issue>
     __device__ __forceinline__ void steps_of_period(const Issue &issue, int t0, int total,
                                                     typename S::Acc (&acc)[S::TM][S::TN]) {
-        if constexpr (PH < kPeriod) {
-            step<false, PH>(issue, t0 + PH, total, acc, [](int) {});
-            steps_of_period<PH + 1>(issue, t0, total, acc);
+        if constexpr (I < kPeriod) {
+            step<false, (P0 + I) % kPeriod>(issue, t0 + I, total, acc, [](int) {});
+            steps_of_period<P0, I + 1>(issue, t0, total, acc);
         }
     }
 
@@ -806,7 +811,7 @@ struct Pipeline {
         int t = t_begin;
         if constexpr (kUnroll && S::MI == 16) {
             for (; t < t_end && t % kPeriod != 0; ++t) step(issue, t, total, acc, [](int) {});
-            for (; t + kPeriod <= t_end; t += kPeriod) steps_of_period<0>(issue, t, total, acc);
+            for (; t + kPeriod <= t_end; t += kPeriod) steps_of_period<0, 0>(issue, t, total, acc);
         }
         for (; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
     }
@@ -816,6 +821,18 @@ struct Pipeline {
                                              typename S::Acc (&acc)[S::TM][S::TN]) {
         step<true>(issue, t_begin, total, acc, [](int) {});
         run<kUnroll>(issue, t_begin + 1, t_end, total, acc);
+    }
+    // Steps [0, t_end), step 0 starting the accumulators.  kUnroll: the
+    // unrolled groups start right after it, at step 1 (phase 1 of the ring
+    // period), so that only (t_end - 1) % kPeriod steps run the generic step.
+    template <bool kUnroll = false, class Issue>
+    __device__ __forceinline__ void run_init0(const Issue &issue, int t_end, int total,
+                                              typename S::Acc (&acc)[S::TM][S::TN]) {
+        step<true>(issue, 0, total, acc, [](int) {});
+        int t = 1;
+        if constexpr (kUnroll && S::MI == 16)
+            for (; t + kPeriod <= t_end; t += kPeriod) steps_of_period<1, 0>(issue, t, total, acc);
+        for (; t < t_end; ++t) step(issue, t, total, acc, [](int) {});
     }
 
     __device__ __forceinline__ void drain() {

@@ -289,7 +289,7 @@ __device__ __forceinline__ void zero_acc_mi32(typename S::Acc (&acc)[S::TM][S::T
 template <class S, bool kUnroll = false, class Issue>
 __device__ __forceinline__ void run_tile(Pipeline<S> &pl, const Issue &issue, int len,
                                          typename S::Acc (&acc)[S::TM][S::TN]) {
-    if constexpr (S::MI == 16) pl.template run_init<kUnroll>(issue, 0, len, len, acc);
+    if constexpr (S::MI == 16) pl.template run_init0<kUnroll>(issue, len, len, acc);
     else pl.run(issue, 0, len, len, acc);
 }
 
@@ -732,7 +732,7 @@ __device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoade
                                                  typename S::Acc (&g)[S::TM][S::TN],
                                                  typename S::Acc (&u)[S::TM][S::TN]) {
     const int nk = issue.nk;
-    pl.template run_init<kEven>(issue, 0, nk, 2 * nk, g);
+    pl.template run_init0<kEven>(issue, nk, 2 * nk, g);
     settle_acc<S>(g);
     silu_acc<S>(g);
     pl.template run_init<kEven>(issue, nk, 2 * nk, 2 * nk, u);
@@ -849,8 +849,11 @@ using ShapeSeqP = TileShape<256, 128, 64, 2, 2, 3, 2, 3, 16>;
 // 128x128 tile on the weight stream, with BK = 64 and four stages (96 KiB) to
 // keep HBM loads in flight; measured with weights streamed from HBM against
 // 128x64x32 x 4 stages: 21 % faster at M=128 K=896 N=4864, 24-29 % on K =
-// 5120..8192 (up to 4.2 TB/s of weights).  32x32x16 MFMAs: the 16x16x32
-// form measured 2 % slower here (M = 128, bound by the weight stream).
+// 5120..8192 (up to 4.2 TB/s of weights); five or six stages (120 / 144 KiB,
+// still one workgroup per CU) ran 0-14 % slower for variants I and S and the
+// ablation at M = 32 and 128 on all five K x N workload shapes.  32x32x16
+// MFMAs: the 16x16x32 form measured 2 % slower here (M = 128, bound by the
+// weight stream).
 using ShapeSmall = TileShape<128, 64, 64, 2, 2, 4>;
 // Variant I on FP8 operands: the same three shapes with K steps of 128 FP8
 // values, so every tile row of a stage is 128 bytes and the LDS rings, load

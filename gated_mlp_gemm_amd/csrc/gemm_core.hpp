@@ -131,10 +131,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 // One 16-byte-per-lane direct-to-LDS load; `lds` is the wave's 1 KiB block.
+// IMM, the instruction's immediate offset, is added to the global address
+// and to the LDS destination alike: loads into consecutive KiB of LDS can
+// share one LDS base (M0) when their global offsets are reduced by IMM.
+template <int IMM = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, SWIGLU_LDS char *lds,
                                       uint32_t voff, uint32_t soff) {
+    static_assert(IMM >= 0 && IMM < 4096, "12-bit immediate offset");
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, reinterpret_cast<SWIGLU_LDS void *>(lds), 16,
-                                             static_cast<int>(voff), static_cast<int>(soff), 0,
+                                             static_cast<int>(voff), static_cast<int>(soff), IMM,
                                              0);
 }
 
@@ -204,8 +209,16 @@ struct PanelLoader {
     int pairs;             // uniform: a de-interleaved panel (KMajor::pairs)
     int lds_base;          // uniform: LDS byte offset of the wave's block of load 0
     // When K is a multiple of BK (issue<true>): each load's offset, computed
-    // once per panel.
+    // once per panel, for a wave-major assignment of the LDS blocks: the
+    // loads go in groups of kGroup, and group g of a wave fills kGroup
+    // consecutive KiB, blocks (g kWaves + wave) kGroup + i, so that the
+    // group's loads share one M0 and differ in the immediate offset i KiB
+    // (vo holds the offset less that immediate).  The LDS contents are those
+    // of the other assignment: block b holds LDS rows b * 1024 / kRowBytes on.
+    static constexpr int kGroup = NDMA < 4 ? NDMA : 4;
+    static_assert(NDMA % kGroup == 0, "whole groups of loads");
     uint32_t vo[NDMA];
+    int lds_even;          // uniform: LDS byte offset of the wave's group 0
     int klen;
 
     // Panel = logical rows [r0, r0 + NROWS) of `op`.
@@ -232,8 +245,18 @@ struct PanelLoader {
         voff = static_cast<uint32_t>(grow) * row_bytes + c * 16u;
         klim = K - c * S::kElemsPerChunk;
         lds_base = wave * 1024;
+        lds_even = wave * kGroup * 1024;
+        // (the rows of a block i of a group are at least 8 i: offsets >= i KiB
+        // whenever a row has at least 128 bytes, as when K is a multiple of BK)
 #pragma unroll
-        for (int j = 0; j < NDMA; ++j) vo[j] = voff + dj(j);
+        for (int j = 0; j < NDMA; ++j) {
+            const int g = j / kGroup, i = j % kGroup;
+            const int blk = (g * S::kWaves + wave) * kGroup + i;
+            const int r = blk * (1024 / S::kRowBytes) + lane / S::kChunksPerRow;
+            const int cj = (lane % S::kChunksPerRow) ^ swz<S>(r);
+            const int gr = pairs ? pair_row(r) : r;
+            vo[j] = static_cast<uint32_t>(gr) * row_bytes + cj * 16u - static_cast<uint32_t>(i) * 1024u;
+        }
     }
 
     // Uniform bytes from load 0's panel row to load j's: the LDS distance
@@ -256,14 +279,23 @@ struct PanelLoader {
     //  about as much as it takes to issue).  A step at or past K (the ring
     //  running ahead of a tile's last step) loads the last step again, into a
     //  stage no step reads (a uniform clamp: no per-lane masking).
+    template <int... J>
+    __device__ __forceinline__ void issue_even(uint32_t soff, SWIGLU_LDS char *panel_lds, int only,
+                                               std::integer_sequence<int, J...>) const {
+        (
+            [&] {
+                if (only < 0 || only == J)
+                    dma16<(J % kGroup) * 1024>(
+                        rsrc, panel_lds + lds_even + (J / kGroup) * S::kWaves * kGroup * 1024,
+                        vo[J], soff);
+            }(),
+            ...);
+    }
     template <bool kEven = false>
     __device__ __forceinline__ void issue(int k0, SWIGLU_LDS char *panel_lds, int only = -1) const {
         if constexpr (kEven) {
             const uint32_t soff = static_cast<uint32_t>(k0 < klen ? k0 : klen - S::BK) * S::EB;
-#pragma unroll
-            for (int j = 0; j < NDMA; ++j)
-                if (only < 0 || only == j)
-                    dma16(rsrc, panel_lds + lds_base + j * S::kWaves * 1024, vo[j], soff);
+            issue_even(soff, panel_lds, only, std::make_integer_sequence<int, NDMA>{});
         } else {
             const uint32_t soff = static_cast<uint32_t>(k0) * S::EB;
             const uint32_t v0 = k0 < klim ? voff : kOutOfRange;

@@ -275,7 +275,6 @@ struct StoreEpilogue {
     __device__ __forceinline__ static int unit_block(int u, int) { return u; }
 };
 
-// K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
 // The K steps [0, len) of one tile into `acc`.  With 16x16 MFMAs the first
 // step's MFMAs start the accumulators (C = 0): no vector instructions zero its
 // 256 registers first.  32x32 MFMAs accumulate onto zeros (zero_acc_mi32
@@ -293,6 +292,7 @@ __device__ __forceinline__ void run_tile(Pipeline<S> &pl, const Issue &issue, in
     else pl.run(issue, 0, len, len, acc);
 }
 
+// K steps [kb, ke) of the S tile at (m0, n0) of D = A . B^T, into acc.
 template <class S, bool kEven = false>
 __device__ __forceinline__ void tile_mainloop(SWIGLU_LDS char *lds, const KMajor &A,
                                               const KMajor &B, int M, int K, int m0, int n0,

@@ -333,8 +333,15 @@ enum TailMode { kTailNone = 0, kTailSplit = 1, kTailQuarter = 2, kTailReduceInKe
 // Persistent: workgroup b runs whole tiles b, b + grid, ... below sch.dp
 // (XCD-ordered), one after the other; before the epilogue of each it puts the
 // first K steps of its next tile in flight, so their load latency hides behind
-// the epilogue and no workgroup launch sits between tiles.  Then it takes its
-// share of the tiles [dp, dp + split_tiles) of a partly idle last round:
+// the epilogue and no workgroup launch sits between tiles.  It also takes its
+// share of the tiles [dp, dp + split_tiles) of the partly idle last round:
+// quartered tiles before its whole tiles, so that the workgroups with such a
+// share run their whole tiles out of step with the others and the epilogues
+// of a round, which all store their tile at once when every workgroup starts
+// together, are spread out (M=2048 K=1536 N=8960: 101.9 -> 96.2 us a call,
+// M=512 K=3584 N=18944: 125.6 -> 119-123); split pieces after them (before
+// them measured 2.5 % slower on M=4096 K=8192 N=29568, 0.6 % on M=8192
+// K=5120 N=13824):
 //  - with kTailSplit: work item j (j = b, b + grid, ...) is piece j % pieces
 //    of split tile dp + j / pieces, which stores its partial (split_tail.hpp)
 //    for split_reduce_kernel to finish;
@@ -351,38 +358,43 @@ __device__ __forceinline__ void gemm_tiles_body(char *smem, const KMajor &Ak, co
     const int b = blockIdx.x;
     const int grid = sch.grid;
 
-    if (b < sch.dp) {
-        Pipeline<S> pl;
-        pl.init(lds);
-        TileLoader<S> ld;
-        int j = b, tm, tn;
-        tile_coords(xcd_order(j, sch.dp), sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
-        ld.init(Ak, tm * S::BM, B, tn * S::BN, K);
-        const int nk = sch.nk;
-        // steps past the end load nothing (K step nk is past the end of K)
-        auto issue = [&](int s, int part, SWIGLU_LDS char *dst, int j) {
-            ld.template issue<kEven>(s < nk ? s : nk, part, dst, j);
-        };
-        pl.prologue_issue(issue);
-        for (; j < sch.dp; j += grid) {
-            typename S::Acc acc[S::TM][S::TN];
-            zero_acc_mi32<S>(acc);
-            pl.prologue_wait();
-            run_tile<S, kEven>(pl, issue, nk, acc);
-            pl.drain(acc);
-            const int m0 = tm * S::BM, n0 = tn * S::BN;
-            if (j + grid < sch.dp) {
-                tile_coords(xcd_order(j + grid, sch.dp), sch.tiles_m, sch.tiles_n, sch.group_m, tm,
-                            tn);
-                ld.init(Ak, tm * S::BM, B, tn * S::BN, K);
-                pl.prologue_issue(issue);
+    auto whole_tiles = [&] {
+        if (b < sch.dp) {
+            Pipeline<S> pl;
+            pl.init(lds);
+            TileLoader<S> ld;
+            int j = b, tm, tn;
+            tile_coords(xcd_order(j, sch.dp), sch.tiles_m, sch.tiles_n, sch.group_m, tm, tn);
+            ld.init(Ak, tm * S::BM, B, tn * S::BN, K);
+            const int nk = sch.nk;
+            // steps past the end load nothing (K step nk is past the end of K)
+            auto issue = [&](int s, int part, SWIGLU_LDS char *dst, int j) {
+                ld.template issue<kEven>(s < nk ? s : nk, part, dst, j);
+            };
+            pl.prologue_issue(issue);
+            for (; j < sch.dp; j += grid) {
+                typename S::Acc acc[S::TM][S::TN];
+                zero_acc_mi32<S>(acc);
+                pl.prologue_wait();
+                run_tile<S, kEven>(pl, issue, nk, acc);
+                pl.drain(acc);
+                const int m0 = tm * S::BM, n0 = tn * S::BN;
+                if (j + grid < sch.dp) {
+                    tile_coords(xcd_order(j + grid, sch.dp), sch.tiles_m, sch.tiles_n, sch.group_m, tm,
+                                tn);
+                    ld.init(Ak, tm * S::BM, B, tn * S::BN, K);
+                    pl.prologue_issue(issue);
+                }
+                epi.template apply<S>(acc, m0, n0, threadIdx.x);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            epi.template apply<S>(acc, m0, n0, threadIdx.x);
-            __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
 
     if constexpr (TAIL == kTailQuarter) {
+        // the quarter-size tiles first: the workgroups that have one then
+        // finish their whole tiles a quarter tile later than the others, so
+        // the epilogues of a round do not all store at the same moment
         using Q = typename QuarterOf<S>::type;
         static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
         const int nq = 4 * sch.split_tiles;
@@ -397,7 +409,11 @@ __device__ __forceinline__ void gemm_tiles_body(char *smem, const KMajor &Ak, co
             tile_mainloop<Q, kEven>(lds, Ak, B, M, K, m0, n0, 0, sch.nk, sch.nk, acc);
             epi.template apply<Q>(acc, m0, n0, threadIdx.x);
         }
-    } else if constexpr (TAIL == kTailReduceInKernel) {
+        whole_tiles();
+    } else {
+        whole_tiles();
+    }
+    if constexpr (TAIL == kTailReduceInKernel) {
         // every tile split, reduced by its last piece (split_tail.hpp); the
         // arrival count is broadcast through LDS word 0 (the ring is idle
         // between work items)

@@ -755,12 +755,12 @@ __device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoade
     pl.drain(u);
 }
 
-// Variant S, persistent, on 16x16 MFMAs: workgroup b runs whole tiles b,
-// b + grid, ... below dp (XCD-ordered) and puts the first K steps of its next
-// tile in flight before each epilogue; then its share of the 4 * quarter_tiles
-// quarter-size tiles of the last round's tiles [dp, dp + quarter_tiles)
-// (quarter q: row half q/2 % 2, column half q % 2 of tile dp + q / 4), each run
-// on its own with a deeper ring.
+// Variant S, persistent, on 16x16 MFMAs: workgroup b first runs its share of
+// the 4 * quarter_tiles quarter-size tiles of the last round's tiles
+// [dp, dp + quarter_tiles) (quarter q: row half q/2 % 2, column half q % 2 of
+// tile dp + q / 4), each on its own with a deeper ring; then whole tiles b,
+// b + grid, ... below dp (XCD-ordered), putting the first K steps of its next
+// tile in flight before each epilogue.
 template <class S, bool kEven>
 __device__ __forceinline__ void fused_sequential_persistent_body(
     char *smem, const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y,
@@ -768,6 +768,28 @@ __device__ __forceinline__ void fused_sequential_persistent_body(
     SWIGLU_LDS char *lds = (SWIGLU_LDS char *)smem;
     const int grid = gridDim.x;
     const int b = blockIdx.x;
+
+    // the quarter-size tiles of the last round first (as in gemm_tiles_body:
+    // their workgroups then run their whole tiles out of step with the rest)
+    using Q = typename QuarterOf<S>::type;
+    static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
+    const int nq = 4 * quarter_tiles;
+    for (int i = b; i < nq; i += grid) {
+        const int q = xcd_order(i, nq);
+        int tm, tn;
+        tile_coords(dp + q / 4, tiles_m, tiles_n, 8, tm, tn);
+        const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
+        const int n0 = tn * S::BN + (q & 1) * Q::BN;
+        if (m0 >= M || n0 >= N) continue;   // quarter wholly past the output's edge
+        SeqLoaders<Q, kEven> issue;
+        issue.init(A, Wf, M, N, K, lda, m0, n0);
+        Pipeline<Q> pl;
+        pl.init(lds);
+        typename Q::Acc g[Q::TM][Q::TN], u[Q::TM][Q::TN];
+        pl.prologue(issue);
+        seq_contractions<Q>(pl, issue, g, u);
+        seq_epilogue<Q>(g, u, Y, M, N, ldy, m0, n0);
+    }
 
     if (b < dp) {
         SeqLoaders<S, kEven> issue;
@@ -789,26 +811,6 @@ __device__ __forceinline__ void fused_sequential_persistent_body(
             }
             seq_epilogue<S>(g, u, Y, M, N, ldy, m0, n0);
         }
-    }
-
-    using Q = typename QuarterOf<S>::type;
-    static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
-    const int nq = 4 * quarter_tiles;
-    for (int i = b; i < nq; i += grid) {
-        const int q = xcd_order(i, nq);
-        int tm, tn;
-        tile_coords(dp + q / 4, tiles_m, tiles_n, 8, tm, tn);
-        const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
-        const int n0 = tn * S::BN + (q & 1) * Q::BN;
-        if (m0 >= M || n0 >= N) continue;   // quarter wholly past the output's edge
-        SeqLoaders<Q, kEven> issue;
-        issue.init(A, Wf, M, N, K, lda, m0, n0);
-        Pipeline<Q> pl;
-        pl.init(lds);
-        typename Q::Acc g[Q::TM][Q::TN], u[Q::TM][Q::TN];
-        pl.prologue(issue);
-        seq_contractions<Q>(pl, issue, g, u);
-        seq_epilogue<Q>(g, u, Y, M, N, ldy, m0, n0);
     }
 }
 template <class S>

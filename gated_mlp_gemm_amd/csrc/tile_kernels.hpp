@@ -755,12 +755,12 @@ __device__ __forceinline__ void seq_contractions(Pipeline<S> &pl, const SeqLoade
     pl.drain(u);
 }
 
-// Variant S, persistent, on 16x16 MFMAs: workgroup b first runs its share of
-// the 4 * quarter_tiles quarter-size tiles of the last round's tiles
-// [dp, dp + quarter_tiles) (quarter q: row half q/2 % 2, column half q % 2 of
-// tile dp + q / 4), each on its own with a deeper ring; then whole tiles b,
+// Variant S, persistent, on 16x16 MFMAs: workgroup b runs whole tiles b,
 // b + grid, ... below dp (XCD-ordered), putting the first K steps of its next
-// tile in flight before each epilogue.
+// tile in flight before each epilogue, and its share of the 4 * quarter_tiles
+// quarter-size tiles of the last round's tiles [dp, dp + quarter_tiles)
+// (quarter q: row half q/2 % 2, column half q % 2 of tile dp + q / 4), each on
+// its own with a deeper ring, before or after them (below).
 template <class S, bool kEven>
 __device__ __forceinline__ void fused_sequential_persistent_body(
     char *smem, const void *__restrict__ A, const void *__restrict__ Wf, uint16_t *__restrict__ Y,
@@ -769,47 +769,55 @@ __device__ __forceinline__ void fused_sequential_persistent_body(
     const int grid = gridDim.x;
     const int b = blockIdx.x;
 
-    // the quarter-size tiles of the last round first (as in gemm_tiles_body:
-    // their workgroups then run their whole tiles out of step with the rest)
+    // The quarter-size tiles of the last round before the whole tiles when a
+    // tile is at most 64 K steps long (as in gemm_tiles_body: those
+    // workgroups then run their whole tiles out of step with the rest and the
+    // epilogues of a round spread out; M=2048 K=1536 N=8960 119.1 -> 115.9
+    // us), after them on longer tiles (at K=8192 N=29568 quarters first
+    // measured 8.5 % slower at M=256 and 11 % at M=2048).
     using Q = typename QuarterOf<S>::type;
     static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
     const int nq = 4 * quarter_tiles;
-    for (int i = b; i < nq; i += grid) {
-        const int q = xcd_order(i, nq);
-        int tm, tn;
-        tile_coords(dp + q / 4, tiles_m, tiles_n, 8, tm, tn);
-        const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
-        const int n0 = tn * S::BN + (q & 1) * Q::BN;
-        if (m0 >= M || n0 >= N) continue;   // quarter wholly past the output's edge
-        SeqLoaders<Q, kEven> issue;
-        issue.init(A, Wf, M, N, K, lda, m0, n0);
-        Pipeline<Q> pl;
-        pl.init(lds);
-        typename Q::Acc g[Q::TM][Q::TN], u[Q::TM][Q::TN];
-        pl.prologue(issue);
-        seq_contractions<Q>(pl, issue, g, u);
-        seq_epilogue<Q>(g, u, Y, M, N, ldy, m0, n0);
-    }
-
-    if (b < dp) {
-        SeqLoaders<S, kEven> issue;
-        int j = b, tm, tn;
-        tile_coords(xcd_order(j, dp), tiles_m, tiles_n, 8, tm, tn);
-        issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
-        Pipeline<S> pl;
-        pl.init(lds);
-        pl.prologue_issue(issue);
-        for (; j < dp; j += grid) {
-            typename S::Acc g[S::TM][S::TN], u[S::TM][S::TN];
-            pl.prologue_wait();
-            seq_contractions<S>(pl, issue, g, u);
-            const int m0 = tm * S::BM, n0 = tn * S::BN;
-            if (j + grid < dp) {
-                tile_coords(xcd_order(j + grid, dp), tiles_m, tiles_n, 8, tm, tn);
-                issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
-                pl.prologue_issue(issue);
+    const bool quarters_first = (K + S::BK - 1) / S::BK <= 64;
+#pragma nounroll
+    for (int pass = 0; pass < 2; ++pass) {
+        if ((pass == 0) == quarters_first) {
+            for (int i = b; i < nq; i += grid) {
+                const int q = xcd_order(i, nq);
+                int tm, tn;
+                tile_coords(dp + q / 4, tiles_m, tiles_n, 8, tm, tn);
+                const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
+                const int n0 = tn * S::BN + (q & 1) * Q::BN;
+                if (m0 >= M || n0 >= N) continue;   // quarter wholly past the output's edge
+                SeqLoaders<Q, kEven> issue;
+                issue.init(A, Wf, M, N, K, lda, m0, n0);
+                Pipeline<Q> pl;
+                pl.init(lds);
+                typename Q::Acc g[Q::TM][Q::TN], u[Q::TM][Q::TN];
+                pl.prologue(issue);
+                seq_contractions<Q>(pl, issue, g, u);
+                seq_epilogue<Q>(g, u, Y, M, N, ldy, m0, n0);
             }
-            seq_epilogue<S>(g, u, Y, M, N, ldy, m0, n0);
+        } else if (b < dp) {
+            SeqLoaders<S, kEven> issue;
+            int j = b, tm, tn;
+            tile_coords(xcd_order(j, dp), tiles_m, tiles_n, 8, tm, tn);
+            issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
+            Pipeline<S> pl;
+            pl.init(lds);
+            pl.prologue_issue(issue);
+            for (; j < dp; j += grid) {
+                typename S::Acc g[S::TM][S::TN], u[S::TM][S::TN];
+                pl.prologue_wait();
+                seq_contractions<S>(pl, issue, g, u);
+                const int m0 = tm * S::BM, n0 = tn * S::BN;
+                if (j + grid < dp) {
+                    tile_coords(xcd_order(j + grid, dp), tiles_m, tiles_n, 8, tm, tn);
+                    issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
+                    pl.prologue_issue(issue);
+                }
+                seq_epilogue<S>(g, u, Y, M, N, ldy, m0, n0);
+            }
         }
     }
 }

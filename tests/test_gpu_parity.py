@@ -855,6 +855,35 @@ def test_sequential_tail_modes(dev, orc, monkeypatch, tail, M, K, N):
     assert torch.equal(Y.view(torch.int16), Yi.view(torch.int16))
 
 
+# Variant S runs its quarter tail before its whole tiles when a tile is at
+# most 64 K steps long, after them on longer tiles.  The cases above take the
+# first order; these the second: M=2048, N=4224 is 264 tiles of 256x128, so
+# 256 run whole and 8 as 32 quarters (the last tile column, every tile row),
+# with 66 K steps (K a multiple of 64, and ragged).  Rows sampled against the
+# oracle cross whole and quarter tiles; the whole output against variant I.
+@pytest.mark.parametrize("K", [4224, 4168])
+def test_sequential_quarters_after_long_tiles(dev, orc, monkeypatch, K):
+    M, N = 2048, 4224
+    monkeypatch.setenv("SWIGLU_TAIL", "quarter")
+    announce(f"S long tiles, quarter tail last M={M} K={K} N={N}")
+    d = sw.swiglu_describe_launch(M, N, K, "s")
+    tiles = math.ceil(M / 256) * math.ceil(N / 128)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rem = tiles % cus
+    if rem and tiles > cus:
+        assert f"{tiles - rem} tiles + {rem} tiles run as {4 * rem} 128x64 tiles" in d, d
+    A, W1, W2 = inputs.make_inputs(M, K, N, seed=K + 17)
+    rows = np.array([0, 1, 127, 128, 255, 256, 700, 1023, 1024, 1535, 1792, 2047])
+    ref = orc.swiglu_rows(inputs.bits(A), inputs.bits(W1), inputs.bits(W2), rows)
+    Ad, Wf = A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+    Y = sw.swiglu_fused_gemm(Ad, Wf, variant="s")
+    torch.cuda.synchronize()
+    assert_parity(bits_of(Y)[rows], ref, f"S long tiles K={K} rows")
+    Yi = sw.swiglu_fused_gemm(Ad, Wf, variant="i")
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yi.view(torch.int16))
+
+
 # Variant I at M <= 128 with a workspace: every 128x128 tile split into
 # s = min(CUs / tiles, K steps) pieces along K and reduced in the kernel by its
 # last piece (device-scope partials in the workspace, library-owned arrival

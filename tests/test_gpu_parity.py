@@ -297,8 +297,11 @@ def tail_windows(M, N, K, ws_bytes):
     tiles_m, tiles_n = -(-M // bm), -(-2 * N // bn)
     assert dp + L == tiles_m * tiles_n, desc
     out = []
+    # the library's group size: 4 tile rows for at most 8 tile rows and at
+    # most 32 K steps of 64, else 8
+    group_m = 4 if tiles_m <= 8 and -(-K // 64) <= 32 else 8
     for t in range(dp, dp + L):
-        tm, tn = tile_order(t, tiles_m, tiles_n)
+        tm, tn = tile_order(t, tiles_m, tiles_n, group_m)
         r0, c0 = tm * bm, tn * bn // 2
         out.append(((r0, min(r0 + bm, M)), (c0, min(c0 + bn // 2, N))))
     return desc, out

@@ -779,13 +779,15 @@ __device__ __forceinline__ void fused_sequential_persistent_body(
     static_assert(Q::kLdsBytes <= S::kLdsBytes, "quarter ring fits the tile's LDS");
     const int nq = 4 * quarter_tiles;
     const bool quarters_first = (K + S::BK - 1) / S::BK <= 64;
+    // tile rows walked together, as the GEMM kernels' schedule chooses them
+    const int group_m = tiles_m <= 8 && (K + S::BK - 1) / S::BK <= 32 ? 4 : 8;
 #pragma nounroll
     for (int pass = 0; pass < 2; ++pass) {
         if ((pass == 0) == quarters_first) {
             for (int i = b; i < nq; i += grid) {
                 const int q = xcd_order(i, nq);
                 int tm, tn;
-                tile_coords(dp + q / 4, tiles_m, tiles_n, 8, tm, tn);
+                tile_coords(dp + q / 4, tiles_m, tiles_n, group_m, tm, tn);
                 const int m0 = tm * S::BM + ((q >> 1) & 1) * Q::BM;
                 const int n0 = tn * S::BN + (q & 1) * Q::BN;
                 if (m0 >= M || n0 >= N) continue;   // quarter wholly past the output's edge
@@ -801,7 +803,7 @@ __device__ __forceinline__ void fused_sequential_persistent_body(
         } else if (b < dp) {
             SeqLoaders<S, kEven> issue;
             int j = b, tm, tn;
-            tile_coords(xcd_order(j, dp), tiles_m, tiles_n, 8, tm, tn);
+            tile_coords(xcd_order(j, dp), tiles_m, tiles_n, group_m, tm, tn);
             issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
             Pipeline<S> pl;
             pl.init(lds);
@@ -812,7 +814,7 @@ __device__ __forceinline__ void fused_sequential_persistent_body(
                 seq_contractions<S>(pl, issue, g, u);
                 const int m0 = tm * S::BM, n0 = tn * S::BN;
                 if (j + grid < dp) {
-                    tile_coords(xcd_order(j + grid, dp), tiles_m, tiles_n, 8, tm, tn);
+                    tile_coords(xcd_order(j + grid, dp), tiles_m, tiles_n, group_m, tm, tn);
                     issue.init(A, Wf, M, N, K, lda, tm * S::BM, tn * S::BN);
                     pl.prologue_issue(issue);
                 }
@@ -883,8 +885,9 @@ using ShapeSeqP = TileShape<256, 128, 64, 2, 2, 3, 2, 3, 16>;
 using ShapeSmall = TileShape<128, 64, 64, 2, 2, 4>;
 // Variant I on FP8 operands: the same three shapes with K steps of 128 FP8
 // values, so every tile row of a stage is 128 bytes and the LDS rings, load
-// counts and swizzles are those of the bf16 shapes.
-using ShapeWide8 = TileShape<256, 256, 128, 2, 2, 2, 1>;
+// counts and swizzles are those of the bf16 shapes (the 256x256 one with a
+// three-stage weight ring, as bf16's: 0-1.3 % faster than two stages).
+using ShapeWide8 = TileShape<256, 256, 128, 2, 2, 2, 1, 3>;
 using ShapeQuad8 = TileShape<128, 128, 128, 2, 2, 2, 1>;
 using ShapeSmall8 = TileShape<128, 64, 128, 2, 2, 4, 1>;
 using ShapeSeq8 = TileShape<128, 128, 128, 2, 2, 2, 1>;
